@@ -1,0 +1,212 @@
+"""Float64 CPU oracle for one training step of the ReLU MLP.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, calls or
+links this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may use it.  It shares no code with the
+HIP implementation (no kernels, headers, helpers or constants).
+
+What it computes is the plain definition of the step in the Meganeura README
+("Example" section): ``h = relu(matmul(x, w1))``, ``logits = matmul(h, w2)``,
+``loss = cross_entropy_loss(logits, labels)``, with the gradient the
+framework's autodiff derives ("Example": autodiff happens inside
+``build_session``) and a plain SGD update (README "Contents": SGD is one of
+the optimizers a session can carry).  The arXiv abstract of "Meganeura:
+Portable GPU Training and Inference through Vulkan and Metal" fixes the
+evaluation protocol this oracle serves: a strict-f32 contract and a validated
+fast-path contract, with forward and backward gated separately.
+
+Notation (weights are [in, out], ``out = in @ W``, as in the README example):
+
+    a_0 = x                                  [B, d_0]
+    z_l = a_{l-1} W_l,  l = 1..L             [B, d_l]
+    m_l = [z_l > 0],    a_l = z_l * m_l      l = 1..L-1 (ReLU, ReLU'(0) = 0)
+    mu_b  = max_c z_L[b,c]
+    lse_b = mu_b + log sum_c exp(z_L[b,c] - mu_b)
+    s_b   = sum_c t[b,c]
+    l_b   = s_b * lse_b - sum_c t[b,c] z_L[b,c]
+    loss  = (1/B) sum_b l_b
+    G_L   = (exp(z_L - lse) * s - t) / B     (dloss/dlogits)
+    dW_l  = a_{l-1}^T G_l
+    G_{l-1} = (G_l W_l^T) * m_{l-1}          (old W_l)
+    W_l  <- W_l - lr * dW_l                  (after every dW_l is formed)
+
+Readings where the pages are silent (each is also listed in the design
+notes): no bias; dense labels with any non-negative rows (s_b = 1 for the
+one-hot rows the workloads use, which gives (softmax - onehot)/B); mean over
+the batch; the row max is subtracted before exponentiating; ReLU'(0) = 0;
+SGD without momentum or decay; the loss returned is the one at the
+pre-update weights.
+
+Every input is upcast to float64 first; nothing here rounds to float32 or
+bfloat16, so the same oracle serves both contracts.
+
+ReLU kinks.  Where |z| is within the rounding-error bound of a float32 (or
+bfloat16-operand) evaluation, the sign of z -- and so the mask bit -- is not
+determined by the inputs at working precision, and both mask values give a
+correct derivative.  ``forward`` accepts an optional ``kink_choice`` per
+hidden layer; the choice is honoured only inside that band (|z| <= band,
+band = beta * (|a_{l-1}| @ |W_l|)) and the function reports how many bits it
+took from the choice and how many bits outside the band disagree with it.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# Rounding-error bands for the mask tie-break.
+# --------------------------------------------------------------------------
+
+def gamma(k: int, u: float) -> float:
+    """Higham's gamma_k = k u / (1 - k u): relative bound on a k-term
+    floating-point dot product's error, in units of sum |a_i b_i|."""
+    ku = k * u
+    if ku >= 1.0:
+        return math.inf
+    return ku / (1.0 - ku)
+
+
+def kink_betas(dims: Sequence[int], precision: str, safety: float = 2.0) -> List[float]:
+    """Per-hidden-layer band factor beta_l (l = 1..L-1).
+
+    f32: the product chain up to layer l accumulates at most
+    sum_{j<=l} gamma_{d_{j-1}}(2^-24) relative error in |a||w| units.
+    bf16 operands add two roundings to 8 significant bits per product
+    (2 * 2^-8) on top of the f32 accumulation.  A safety factor of 2 covers
+    the error already present in a_{l-1}."""
+    u32 = 2.0 ** -24
+    ub = 2.0 ** -8
+    out = []
+    acc = 0.0
+    for l in range(1, len(dims) - 1):
+        k = dims[l - 1]
+        step = gamma(k, u32)
+        if precision == "bf16":
+            step += 2.0 * ub + ub * ub
+        acc += step
+        out.append(safety * acc)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Forward: matmul -> ReLU -> ... -> matmul  (README "Example").
+# --------------------------------------------------------------------------
+
+def forward(x, weights: Sequence, kink_choice: Optional[Sequence] = None,
+            kink_beta: Optional[Sequence[float]] = None) -> Dict:
+    """Forward pass in float64.
+
+    Returns a dict with ``a`` (a_0..a_{L-1}), ``z`` (z_1..z_L), ``m``
+    (m_1..m_{L-1}, bool), ``logits`` (= z_L), and, when ``kink_choice`` is
+    given, ``adopted`` (bits taken from the choice inside the band) and
+    ``outside`` (bits of the choice that disagree with sign(z) outside the
+    band) per hidden layer."""
+    W = [_f64(w) for w in weights]
+    L = len(W)
+    a = [_f64(x)]
+    zs, ms, adopted, outside = [], [], [], []
+    for l in range(1, L + 1):
+        z = a[-1] @ W[l - 1]
+        zs.append(z)
+        if l == L:
+            break
+        m = z > 0.0
+        if kink_choice is not None:
+            band = kink_beta[l - 1] * (np.abs(a[-1]) @ np.abs(W[l - 1]))
+            choice = np.asarray(kink_choice[l - 1]).astype(bool)
+            in_band = np.abs(z) <= band
+            differ = choice != m
+            adopted.append(int(np.count_nonzero(differ & in_band)))
+            outside.append(int(np.count_nonzero(differ & ~in_band)))
+            m = np.where(in_band, choice, m)
+        ms.append(m)
+        a.append(z * m)
+    out = {"a": a, "z": zs, "m": ms, "logits": zs[-1]}
+    if kink_choice is not None:
+        out["adopted"] = adopted
+        out["outside"] = outside
+    return out
+
+
+# --------------------------------------------------------------------------
+# Softmax cross-entropy against dense labels (README "Example":
+# cross_entropy_loss(logits, labels) with labels of the logits' shape).
+# --------------------------------------------------------------------------
+
+def softmax_xent(logits, labels) -> Dict:
+    """Mean softmax cross-entropy and its gradient w.r.t. the logits.
+
+    Per row: mu = max z, lse = mu + log sum exp(z - mu), s = sum t,
+    loss_b = s*lse - sum t*z; loss = mean_b loss_b; dlogits = (p*s - t)/B
+    with p = exp(z - lse)."""
+    z = _f64(logits)
+    t = _f64(labels)
+    B = z.shape[0]
+    mu = z.max(axis=1, keepdims=True)
+    ssum = np.exp(z - mu).sum(axis=1, keepdims=True)
+    lse = mu + np.log(ssum)
+    s = t.sum(axis=1, keepdims=True)
+    rowloss = (s * lse)[:, 0] - (t * z).sum(axis=1)
+    p = np.exp(z - lse)
+    dlogits = (p * s - t) / B
+    return {"loss": float(rowloss.mean()), "rowloss": rowloss,
+            "dlogits": dlogits, "lse": lse[:, 0], "p": p}
+
+
+# --------------------------------------------------------------------------
+# Backward (the derivative the README's autodiff produces for this graph).
+# --------------------------------------------------------------------------
+
+def backward(fwd: Dict, dlogits, weights: Sequence) -> Dict:
+    """Gradients of the mean loss w.r.t. every W_l, at the given weights.
+
+    dW_l = a_{l-1}^T G_l; G_{l-1} = (G_l W_l^T) * m_{l-1}."""
+    W = [_f64(w) for w in weights]
+    L = len(W)
+    G = _f64(dlogits)
+    dW = [None] * L
+    Gs = [None] * (L + 1)
+    Gs[L] = G
+    for l in range(L, 0, -1):
+        dW[l - 1] = fwd["a"][l - 1].T @ G
+        if l > 1:
+            G = (G @ W[l - 1].T) * fwd["m"][l - 2]
+            Gs[l - 1] = G
+    return {"dW": dW, "G": Gs}
+
+
+def sgd(weights: Sequence, grads: Sequence, lr: float) -> List[np.ndarray]:
+    """Plain SGD: W_l - lr * dW_l for every layer."""
+    return [_f64(w) - float(lr) * _f64(g) for w, g in zip(weights, grads)]
+
+
+# --------------------------------------------------------------------------
+# One whole training step.
+# --------------------------------------------------------------------------
+
+def train_step(x, labels, weights: Sequence, lr: float,
+               kink_choice: Optional[Sequence] = None,
+               kink_beta: Optional[Sequence[float]] = None) -> Dict:
+    """Forward, mean softmax-CE, backward and SGD for one batch.
+
+    Returns loss (at the pre-update weights), dlogits, dW (per layer),
+    W_new (per layer), and the forward dict under "fwd"."""
+    fwd = forward(x, weights, kink_choice, kink_beta)
+    ce = softmax_xent(fwd["logits"], labels)
+    bwd = backward(fwd, ce["dlogits"], weights)
+    W_new = sgd(weights, bwd["dW"], lr)
+    return {"loss": ce["loss"], "rowloss": ce["rowloss"],
+            "dlogits": ce["dlogits"], "dW": bwd["dW"], "G": bwd["G"],
+            "W_new": W_new, "fwd": fwd}
+
+
+def loss_only(x, labels, weights: Sequence) -> float:
+    """Mean loss at the given weights (forward + CE only)."""
+    return softmax_xent(forward(x, weights)["logits"], labels)["loss"]
