@@ -1,0 +1,176 @@
+#!/usr/bin/env python3
+"""Throughput of the MLP training step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path (forward GEMMs with fused ReLU/mask,
+softmax cross-entropy, dX and dW+SGD GEMMs) over one batch of synthetic
+input, through the C ABI.  Inputs are generated from fixed seeds, copied to
+HBM before the timed region, and reused cyclically (the batch-1024 workload
+draws a fresh batch for each of its 100 steps).  W untimed warm-up steps,
+then K steps bracketed by device synchronisations.  After the timed region
+the same K steps run again with per-launch HIP events on the library's
+stream, to price the dominant kernel against its roofline; then the float64
+oracle is timed on the host cores over a bounded sample.  Prints ONE JSON
+line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks (dense).
+PEAK = {"f32_mfma_tflops": 157.3, "bf16_mfma_tflops": 2516.6, "hbm_gbps": 8000.0}
+DEFAULT_WORKLOAD = "mnist_b1024"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--profile-steps", type=int, default=None,
+                    help="steps of the per-launch event pass (default: --steps)")
+    return ap.parse_args()
+
+
+def roofline(rows, precision, steps):
+    """Dominant kernel (largest total time) priced against its roofline."""
+    rows = [r for r in rows if r["launches"] > 0]
+    dom = max(rows, key=lambda r: r["total_ms"])
+    avg_s = dom["total_ms"] / dom["launches"] / 1e3
+    ridge = (PEAK["bf16_mfma_tflops"] if precision == "bf16" else PEAK["f32_mfma_tflops"]) * 1e12 \
+        / (PEAK["hbm_gbps"] * 1e9)
+    intensity = dom["flops"] / dom["bytes"] if dom["bytes"] else float("inf")
+    if dom["flops"] > 0 and intensity >= ridge:
+        peak = PEAK["bf16_mfma_tflops"] if precision == "bf16" else PEAK["f32_mfma_tflops"]
+        achieved = dom["flops"] / avg_s / 1e12
+        bound, unit = "mfma", "TFLOP/s"
+    else:
+        peak = PEAK["hbm_gbps"]
+        achieved = dom["bytes"] / avg_s / 1e9
+        bound, unit = "hbm", "GB/s"
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom["name"],
+            "avg_us": round(avg_s * 1e6, 3), "algorithmic_flops": dom["flops"],
+            "algorithmic_bytes": dom["bytes"]}
+
+
+def cpu_baseline(w, budget_s):
+    """The float64 oracle as it stands, on this host's cores, over a bounded
+    sample of the workload's steps."""
+    import numpy as np
+    from mlp_gemm_softmax_amd import synth
+    from oracle import mlp_oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    Ws = synth.workload_weights(w)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        x, t, _ = synth.workload_batch(w, n)
+        r = mlp_oracle.train_step(x, t, Ws, w.lr)
+        Ws = [a.astype(np.float32) for a in r["W_new"]]
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 20000:
+            break
+    # batch generation is inside the loop; it is small next to the f64 step
+    return {"value": round(n / el, 4), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} consecutive training steps of {w.name} (float64 numpy, BLAS threads "
+                      f"{cores}), {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from mlp_gemm_softmax_amd import binding, synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    print(f"[bench] workload {w.name} dims={w.dims} B={w.batch} {w.precision} "
+          f"steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+
+    net = binding.Mlp(w.dims, w.batch, w.precision, device="cuda:0")
+    net.set_params([torch.from_numpy(a).to(dev) for a in synth.workload_weights(w)])
+    n_batches = w.steps if w.fresh_batch else 1
+    batches = []
+    for s in range(n_batches):
+        x, t, _ = synth.workload_batch(w, s)
+        batches.append((torch.from_numpy(x).to(dev), torch.from_numpy(t).to(dev)))
+    loss_dev = torch.zeros(1, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def run(k, offset=0):
+        for i in range(k):
+            xb, tb = batches[(offset + i) % n_batches]
+            net.train_step_async(xb, tb, w.lr, loss_dev)
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(args.steps, args.warmup)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    final_loss = float(loss_dev.item())
+
+    # Per-launch HIP events on the library's stream, same step sequence.
+    pk = args.profile_steps or args.steps
+    net.profile(True)
+    net.profile_reset()
+    run(pk)
+    torch.cuda.synchronize()
+    rows = net.profile_read()
+    net.profile(False)
+    roof = roofline(rows, w.precision, pk)
+    print("[bench] per-launch (ms avg): " + ", ".join(
+        f"{r['name']}={r['total_ms'] / max(r['launches'], 1):.4f}" for r in rows),
+        file=sys.stderr, flush=True)
+
+    steps_per_s = args.steps / el
+    flops = w.gemm_flops()
+    out = {
+        "metric": "MLP train steps/sec + achieved TFLOP/s (fraction of MFMA/HBM roofline), 1 GPU",
+        "value": round(steps_per_s, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(el / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.precision == "bf16" else "f32",
+        "data": "synthetic (seeded; MNIST-shaped uniform [0,1) pixels or N(0,1) features, uniform class ids)",
+        "config": {"workload": w.name, "dims": list(w.dims), "batch": w.batch, "lr": w.lr,
+                   "precision": w.precision, "fresh_batch_per_step": w.fresh_batch},
+        "achieved_tflops": round(flops * steps_per_s / 1e12, 4),
+        "step_flops": flops,
+        "final_loss": final_loss,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
+    net.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

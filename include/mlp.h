@@ -1,0 +1,173 @@
+/*
+ * mlp.h -- C ABI of libmlp.so: the compiled training step of a bias-free ReLU
+ * MLP on one AMD Instinct MI355X (gfx950).
+ *
+ * The graph is the one in the Meganeura README ("Example" section):
+ *     h      = relu(matmul(x, w1))          ... repeated for every hidden layer
+ *     logits = matmul(h, wL)
+ *     loss   = cross_entropy_loss(logits, labels)
+ * with the backward pass the framework's autodiff derives for it and a plain
+ * SGD update (README "Contents": SGD sessions).  A step is a fixed sequence
+ * of hand-written HIP kernels: MFMA GEMMs with fused ReLU/mask, mask-multiply
+ * and SGD epilogues, and one row-wise softmax cross-entropy kernel.
+ *
+ * Two arithmetic contracts, following the split between a strict-f32 mode
+ * and validated fast paths in the abstract of "Meganeura: Portable GPU
+ * Training and Inference through Vulkan and Metal":
+ *   MLP_F32  -- every product and sum in IEEE float32 (f32 MFMA);
+ *   MLP_BF16 -- GEMM operands rounded to bfloat16 (round-to-nearest-even),
+ *               float32 accumulation, float32 softmax-CE, float32 master
+ *               weights and update.
+ *
+ * Conventions for every entry point
+ *   - Layers are numbered 0 .. n_layers-1; weight l has shape
+ *     [dims[l], dims[l+1]] ([in, out], out = in @ W, as in the README).
+ *   - Every tensor is row-major and contiguous with its logical shape; no
+ *     padding is visible (README "Contents": checkpoints hold logical tensors
+ *     without device padding).
+ *   - Pointers named *dev* or documented as device pointers are HIP device
+ *     memory, 16-byte aligned; they are owned by the caller.  Host pointers
+ *     are documented as such.
+ *   - The library never allocates device memory: all of its state lives in
+ *     the caller-provided workspace, which must stay alive until
+ *     mlp_destroy.  All device work is enqueued on the config's stream, and
+ *     inputs must be ready in that stream's order.  One context may be used
+ *     by one host thread at a time; calls on one context are not
+ *     re-entrant.
+ *   - Every argument is checked before anything is enqueued (the README's
+ *     "preflight the restore before mutation"): on an error return the
+ *     context and device state are unchanged, and mlp_last_error() describes
+ *     the problem.  A HIP failure after work was enqueued returns
+ *     MLP_ERR_HIP and poisons the context: later calls return MLP_ERR_STATE
+ *     until mlp_set_params has been called for every layer.
+ */
+#ifndef MLP_H_
+#define MLP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLP_ABI_VERSION 1
+
+typedef struct mlp_ctx mlp_ctx;
+
+typedef enum mlp_status {
+    MLP_OK = 0,
+    MLP_ERR_ARG = 1,        /* null/misaligned pointer, bad index, non-finite lr */
+    MLP_ERR_SHAPE = 2,      /* dims or batch outside the supported range */
+    MLP_ERR_WORKSPACE = 3,  /* workspace null, too small or misaligned */
+    MLP_ERR_HIP = 4,        /* a HIP runtime call failed */
+    MLP_ERR_STATE = 5       /* context poisoned by an earlier HIP failure */
+} mlp_status;
+
+typedef enum mlp_precision {
+    MLP_F32 = 0,
+    MLP_BF16 = 1
+} mlp_precision;
+
+/* What mlp_read_state copies out (debug-session reads, README "Debugging"). */
+typedef enum mlp_state_kind {
+    MLP_STATE_ACT = 0,      /* a_l = relu(z_l), l = 1..n_layers-1: float32 [B, dims[l]]
+                               (bf16 activations are widened to float32) */
+    MLP_STATE_MASK = 1,     /* m_l = [z_l > 0], l = 1..n_layers-1: uint8 [B, dims[l]] */
+    MLP_STATE_DLOGITS = 2,  /* dloss/dlogits of the last step: float32 [B, C] (layer ignored) */
+    MLP_STATE_LOGITS = 3    /* logits of the last forward: float32 [B, C] (layer ignored) */
+} mlp_state_kind;
+
+/* Static shape of the graph: fixed at creation, as the README's typed
+ * static graph fixes input shapes (g.input("x", &[32, 784])). */
+typedef struct mlp_config {
+    int32_t n_layers;        /* number of weight matrices L, 1 <= L <= 16 */
+    const int32_t* dims;     /* host array of L+1 widths d0..dL, each 1 .. 1<<20 */
+    int32_t batch;           /* B, 1 .. 1<<20 */
+    int32_t precision;       /* mlp_precision */
+    void* stream;            /* hipStream_t for all work; NULL = the null stream */
+} mlp_config;
+
+/* Library ABI version (MLP_ABI_VERSION). */
+int32_t mlp_abi_version(void);
+
+/* Device workspace the configuration needs, in bytes (a multiple of 256);
+ * 0 if the configuration is invalid.  Host only. */
+size_t mlp_workspace_bytes(const mlp_config* cfg);
+
+/* Create a context that lives in `workspace` (device memory of at least
+ * mlp_workspace_bytes(cfg) bytes, 256-byte aligned, owned by the caller).
+ * Enqueues the zeroing of the library's counters on cfg->stream.  The
+ * weights are undefined until mlp_set_params has been called for every
+ * layer.  The analogue of the README's build_session: kernels are compiled
+ * ahead of time, so this only plans buffers and launch shapes. */
+mlp_status mlp_create(const mlp_config* cfg, void* workspace, size_t bytes, mlp_ctx** out);
+
+/* Free the host-side context.  Device memory is the caller's. */
+void mlp_destroy(mlp_ctx* ctx);
+
+/* Copy weight `layer` in: w is a device float32 [dims[layer], dims[layer+1]]
+ * array.  In MLP_BF16 mode the bfloat16 operand copy is refreshed too. */
+mlp_status mlp_set_params(mlp_ctx* ctx, int32_t layer, const float* w);
+
+/* Copy the float32 master of weight `layer` out to device memory `dst`
+ * ([dims[layer], dims[layer+1]]). */
+mlp_status mlp_read_params(mlp_ctx* ctx, int32_t layer, float* dst);
+
+/* Forward pass only.  x: device float32 [B, d0].  logits: device float32
+ * [B, C] or NULL.  labels: device float32 [B, C] (dense, non-negative rows)
+ * or NULL.  loss: host float, written (after a stream synchronisation) with
+ * the mean softmax cross-entropy when labels and loss are both non-NULL.
+ * Without a loss request the call returns once the work is enqueued. */
+mlp_status mlp_forward(mlp_ctx* ctx, const float* x, float* logits,
+                       const float* labels, float* loss);
+
+/* One training step: forward, mean softmax-CE, backward and
+ * W_l <- W_l - lr * dW_l for every layer, all gradients taken at the
+ * pre-update weights.  x: device float32 [B, d0]; labels: device float32
+ * [B, C]; lr: finite.  loss: host float or NULL; the call synchronises the
+ * stream and writes the mean loss at the pre-update weights. */
+mlp_status mlp_train_step(mlp_ctx* ctx, const float* x, const float* labels,
+                          float lr, float* loss);
+
+/* As mlp_train_step, but nothing waits: the mean loss is written to
+ * `loss_dev` (device float32, or NULL to drop it) in stream order. */
+mlp_status mlp_train_step_async(mlp_ctx* ctx, const float* x, const float* labels,
+                                float lr, float* loss_dev);
+
+/* Gradients without an update, from the same kernels and accumulation order
+ * as a training step.  dw: host array of n_layers device pointers, each a
+ * float32 [dims[l], dims[l+1]] output.  dlogits: device float32 [B, C] or
+ * NULL.  loss: host float or NULL (the call synchronises when non-NULL). */
+mlp_status mlp_grads(mlp_ctx* ctx, const float* x, const float* labels,
+                     float* const* dw, float* dlogits, float* loss);
+
+/* Copy an intermediate of the last step or forward to device memory `dst`
+ * (see mlp_state_kind for shapes; `layer` is 1..n_layers-1 for ACT/MASK). */
+mlp_status mlp_read_state(mlp_ctx* ctx, int32_t which, int32_t layer, void* dst);
+
+/* Per-launch timing.  When enabled, every kernel launch of a step is
+ * bracketed by a pair of HIP events on the context's stream (the README's
+ * per-dispatch GPU timing).  mlp_profile_read sums the recorded durations
+ * per launch slot after the caller has synchronised the stream. */
+mlp_status mlp_profile_enable(mlp_ctx* ctx, int32_t enable);
+mlp_status mlp_profile_reset(mlp_ctx* ctx);
+/* Number of launch slots in one training step. */
+int32_t mlp_profile_slots(const mlp_ctx* ctx);
+/* Slot `idx`: kernel name (copied into `name`, NUL-terminated), total
+ * milliseconds and launch count since the last reset, and the slot's
+ * algorithmic flops and HBM bytes per launch. */
+mlp_status mlp_profile_read(mlp_ctx* ctx, int32_t idx, char* name, size_t name_len,
+                            double* total_ms, int64_t* launches,
+                            double* flops, double* bytes);
+
+const char* mlp_status_string(mlp_status s);
+/* Message of the last error on this context ("" if none); valid until the
+ * next call on the context.  With ctx == NULL: the last creation error. */
+const char* mlp_last_error(const mlp_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLP_H_ */

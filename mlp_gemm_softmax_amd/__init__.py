@@ -6,12 +6,12 @@ The step runs in hand-written HIP kernels for gfx950 behind the C ABI in
 torch tensors into that ABI.  The binding is imported lazily so that the
 seeded input generator (``synth``) works without the shared library.
 """
+import importlib
 
 __all__ = ["synth", "binding"]
 
 
 def __getattr__(name):
-    if name == "binding":
-        from . import binding
-        return binding
+    if name in ("binding", "synth", "build"):
+        return importlib.import_module(f"{__name__}.{name}")
     raise AttributeError(name)

@@ -1,0 +1,99 @@
+// Host-visible launch interface of the step's kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace mlp {
+
+// Operand layouts of C[M,N] = A[M,K] . B[K,N] (row-major storage):
+//   NN: A stored [M][K], B stored [K][N]   forward  a_{l-1} . W_l
+//   NT: A stored [M][K], B stored [N][K]   dX       G_l . W_l^T
+//   TN: A stored [K][M], B stored [K][N]   dW       a_{l-1}^T . G_l
+enum class Layout : int { NN = 0, NT = 1, TN = 2 };
+
+// Fused epilogues applied to the float32 accumulator v at (row, col):
+//   Store    C = v                                  (logits)
+//   ReluMask C = max(v, 0) (f32 or bf16), mask = v > 0
+//   MaskMul  C = mask ? v : 0 (f32 or bf16)        (dX through the ReLU)
+//   Sgd      W = W - lr * v, optional bf16 copy    (dW + in-place update)
+//   Grad     C = v                                  (dW, no update)
+enum class Epi : int { Store = 0, ReluMask = 1, MaskMul = 2, Sgd = 3, Grad = 4 };
+
+struct GemmParams {
+    const void* A;       // float or bf16, per the kernel's precision
+    const void* B;
+    int64_t lda, ldb;
+    int M, N, K;
+    float* C;            // f32 output, or the f32 master W for Sgd
+    bf16_t* Cb;          // bf16 output (ReluMask/MaskMul in bf16 mode, Sgd shadow)
+    uint8_t* mask;       // ReluMask writes, MaskMul reads; [M][N], leading dim ldc
+    int64_t ldc;
+    float lr;
+    int splits;          // K split into `splits` chunks of `kchunk`
+    int kchunk;
+    float* partials;     // [splits][M][N] float32 when splits > 1
+    unsigned* tickets;   // one zeroed counter per output tile when splits > 1
+    int tiles_m, tiles_n;
+};
+
+// Tile configurations of the MFMA GEMM (workgroup tile BM x BN, 4 waves).
+enum class TileCfg : int { T128x128 = 0, T64x64 = 1, T32x128 = 2, T128x32 = 3, T128x64 = 4 };
+void tile_shape(TileCfg cfg, int* bm, int* bn);
+
+struct GemmLaunch {
+    Layout layout;
+    Epi epi;
+    bool bf16;       // bf16 operands (MLP_BF16) or f32 operands
+    TileCfg cfg;
+    int vec;         // 4 (or 8 for bf16) if k-contiguous operands allow wide loads, else 1
+    int grid;        // workgroups
+};
+
+hipError_t launch_gemm(const GemmLaunch& L, const GemmParams& p, hipStream_t s);
+
+// ---- skinny batch (B <= 16) float32 kernels ------------------------------
+struct SkinnyParams {
+    const float* A;   // NN: x [MB][K] ; NT: W [Kout][N] ; TN: a [MB][K]
+    const float* B;   // NN: W [K][N]  ; NT: G [MB][N]   ; TN: G [MB][N]
+    int MB;           // batch rows
+    int K, N;         // NN: out [MB][N] = x.W ; NT: out [MB][Kout=K] ; TN: W [K][N]
+    float* C;         // output / W master
+    bf16_t* Cb;
+    uint8_t* mask;
+    float lr;
+    int splits, kchunk;
+    float* partials;
+    unsigned* tickets;
+};
+struct SkinnyLaunch {
+    Layout layout;
+    Epi epi;
+    int grid;
+    int waves;       // waves per workgroup
+};
+hipError_t launch_skinny(const SkinnyLaunch& L, const SkinnyParams& p, hipStream_t s);
+
+// ---- softmax cross-entropy -------------------------------------------------
+struct XentParams {
+    const float* logits;   // [B][C]
+    const float* labels;   // [B][C]
+    float* dlogits;        // [B][C] f32
+    bf16_t* dlogits_b;     // [B][C] bf16 copy or null
+    float* rowloss;        // [B]
+    float* loss;           // scalar mean loss
+    unsigned* ticket;      // zeroed counter
+    int B, C;
+    float inv_b;
+};
+hipError_t launch_xent(const XentParams& p, int* grid_out, hipStream_t s);
+
+// ---- f32 -> bf16 cast -----------------------------------------------------
+hipError_t launch_cast_bf16(const float* src, bf16_t* dst, size_t n, hipStream_t s);
+// ---- bf16 -> f32 widen (state read-back) -----------------------------------
+hipError_t launch_widen_bf16(const bf16_t* src, float* dst, size_t n, hipStream_t s);
+
+}  // namespace mlp

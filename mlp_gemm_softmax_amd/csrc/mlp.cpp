@@ -1,0 +1,808 @@
+// Step engine and C ABI of libmlp.so (declared in include/mlp.h).
+//
+// mlp_create plans one static graph: it carves the caller's workspace into
+// fixed buffers (weights, bf16 operand copies, activations, masks, logits,
+// dlogits, a ping-pong pair of dZ buffers, split-K partials and integer
+// tickets) and picks a tile shape and K split for every product.  A training
+// step is then a fixed launch sequence on one stream:
+//
+//   [bf16: cast x]
+//   for l = 0..L-2:  NN  a_{l+1}, m_{l+1} = relu(a_l W_l)        (ReluMask)
+//                    NN  logits = a_{L-1} W_{L-1}                (Store)
+//                    softmax-CE -> dlogits, row losses, mean loss
+//   for l = L-1..0:  NT  G_l = (G_{l+1} W_l^T) * m_l  if l > 0   (MaskMul)
+//                    TN  W_l -= lr * a_l^T G_{l+1}               (Sgd)
+//
+// The dX product of a layer is enqueued before its dW+SGD product, which
+// overwrites the weights it reads (the step's gradients are all taken at the
+// pre-update weights).  With B <= 16 in float32 the three products use the
+// skinny-batch streaming kernels instead of the tiled MFMA GEMM.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/mlp.h"
+#include "kernels.hpp"
+
+namespace mlp {
+hipError_t launch_gemm_f32(const GemmLaunch& L, const GemmParams& p, hipStream_t st);
+hipError_t launch_gemm_bf16(const GemmLaunch& L, const GemmParams& p, hipStream_t st);
+
+hipError_t launch_gemm(const GemmLaunch& L, const GemmParams& p, hipStream_t st) {
+    return L.bf16 ? launch_gemm_bf16(L, p, st) : launch_gemm_f32(L, p, st);
+}
+
+void tile_shape(TileCfg cfg, int* bm, int* bn) {
+    switch (cfg) {
+    case TileCfg::T128x128: *bm = 128; *bn = 128; return;
+    case TileCfg::T64x64: *bm = 64; *bn = 64; return;
+    case TileCfg::T32x128: *bm = 32; *bn = 128; return;
+    case TileCfg::T128x32: *bm = 128; *bn = 32; return;
+    case TileCfg::T128x64: *bm = 128; *bn = 64; return;
+    }
+    *bm = *bn = 0;
+}
+}  // namespace mlp
+
+using namespace mlp;
+
+namespace {
+
+constexpr int kMaxLayers = 16;
+constexpr int kMaxDim = 1 << 20;
+constexpr int kSkinnyMaxBatch = 16;
+constexpr size_t kAlign = 256;
+
+thread_local std::string g_create_error;
+
+struct GemmPlan {
+    TileCfg cfg;
+    int splits = 1, kchunk = 0, tiles_m = 1, tiles_n = 1, grid = 1;
+    int vec = 1;
+};
+
+struct SkinnyPlan {
+    int grid = 1, waves = 4, splits = 1, kchunk = 0, tickets = 0;
+};
+
+struct Slot {
+    std::string name;
+    double flops = 0, bytes = 0;
+    double total_ms = 0;
+    int64_t launches = 0;
+};
+
+struct Pending {
+    int slot;
+    hipEvent_t beg, end;
+};
+
+}  // namespace
+
+struct mlp_ctx {
+    int L = 0;
+    int dims[kMaxLayers + 1] = {};
+    int B = 0;
+    bool bf16 = false;
+    bool skinny = false;
+    hipStream_t stream = nullptr;
+
+    // workspace buffers
+    float* W[kMaxLayers] = {};
+    bf16_t* Wb[kMaxLayers] = {};
+    void* act[kMaxLayers] = {};        // a_l, l = 1..L-1 (f32 or bf16)
+    uint8_t* mask[kMaxLayers] = {};    // m_l, l = 1..L-1
+    bf16_t* xb = nullptr;
+    float* logits = nullptr;
+    float* dlogits = nullptr;
+    bf16_t* dlogits_b = nullptr;
+    void* dz[2] = {};
+    float* partials = nullptr;
+    unsigned* tickets = nullptr;
+    unsigned* xent_ticket = nullptr;
+    float* rowloss = nullptr;
+    float* loss_slot = nullptr;
+
+    GemmPlan fwd[kMaxLayers], dx[kMaxLayers], dw[kMaxLayers];
+    SkinnyPlan sfwd[kMaxLayers], sdx[kMaxLayers], sdw[kMaxLayers];
+
+    unsigned params_set = 0;   // bit l: W_l written since creation / poisoning
+    bool poisoned = false;
+    std::string err;
+
+    bool profiling = false;
+    std::vector<Slot> slots;
+    std::vector<Pending> pending;
+    std::vector<hipEvent_t> event_pool;
+};
+
+namespace {
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+mlp_status set_err(mlp_ctx* c, mlp_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (c) c->err = buf; else g_create_error = buf;
+    return s;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ------------------------------------------------------------------ plans --
+
+GemmPlan plan_gemm(int M, int N, int K, bool bf16, bool kvec_ok) {
+    GemmPlan g;
+    auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    if (M <= 32) g.cfg = TileCfg::T32x128;
+    else if (N <= 32) g.cfg = TileCfg::T128x32;
+    else if (tiles(128, 128) >= 240) g.cfg = TileCfg::T128x128;
+    else if (tiles(128, 64) >= 240) g.cfg = TileCfg::T128x64;
+    else g.cfg = TileCfg::T64x64;
+    int bm, bn;
+    tile_shape(g.cfg, &bm, &bn);
+    g.tiles_m = (M + bm - 1) / bm;
+    g.tiles_n = (N + bn - 1) / bn;
+    const int nt = g.tiles_m * g.tiles_n;
+    const int bk = bf16 ? 64 : 32;
+    const int target = 512;
+    const int kmin = bf16 ? 256 : 128;
+    int s = std::max(1, std::min((target + nt - 1) / nt, K / kmin));
+    int kchunk = (K + s - 1) / s;
+    kchunk = (kchunk + bk - 1) / bk * bk;
+    s = (K + kchunk - 1) / kchunk;
+    g.splits = std::max(1, s);
+    g.kchunk = g.splits > 1 ? kchunk : std::max(K, 1);
+    g.grid = nt * g.splits;
+    g.vec = kvec_ok ? (bf16 ? 8 : 4) : 1;
+    return g;
+}
+
+SkinnyPlan plan_skinny_nn(int N, int K, int B) {
+    SkinnyPlan s;
+    const int ncb = (N + 255) / 256;
+    // waves of a workgroup split its K chunk; their partial columns meet in
+    // LDS ((waves-1) * B * 1 KiB), kept under 64 KiB
+    s.waves = B <= 8 ? 8 : 4;
+    const int target = 512;
+    int sp = std::max(1, std::min((target + ncb - 1) / ncb, K / 64));
+    int kchunk = (K + sp - 1) / sp;
+    kchunk = (kchunk + 3) / 4 * 4;
+    sp = (K + kchunk - 1) / kchunk;
+    s.splits = sp;
+    s.kchunk = kchunk;
+    s.grid = ncb * sp;
+    s.tickets = ncb;
+    return s;
+}
+
+double es(bool bf16) { return bf16 ? 2.0 : 4.0; }
+
+// Slot names and algorithmic work, in launch order.
+void build_slots(mlp_ctx* c) {
+    c->slots.clear();
+    const int L = c->L, B = c->B;
+    const double e = es(c->bf16);
+    auto add = [&](const std::string& n, double f, double b) {
+        Slot s;
+        s.name = n;
+        s.flops = f;
+        s.bytes = b;
+        c->slots.push_back(s);
+    };
+    const char* kind = c->skinny ? "skinny" : (c->bf16 ? "mfma_bf16" : "mfma_f32");
+    if (c->bf16) add("cast_x_bf16", 0, (double)B * c->dims[0] * 6);
+    for (int l = 0; l < L; ++l) {
+        const double M = B, N = c->dims[l + 1], K = c->dims[l];
+        const bool last = l == L - 1;
+        const double out = last ? M * N * 4 : M * N * (e + 1);
+        add(std::string(kind) + "_nn_" + (last ? "store" : "relu_mask") + "_l" + std::to_string(l),
+            2 * M * N * K, M * K * e + K * N * e + out);
+    }
+    const int C = c->dims[L];
+    add("softmax_xent", 0, (double)B * C * (12 + (c->bf16 ? 2 : 0)) + B * 4.0);
+    for (int l = L - 1; l >= 0; --l) {
+        const double din = c->dims[l], dout = c->dims[l + 1];
+        if (l > 0)
+            add(std::string(kind) + "_nt_mask_l" + std::to_string(l), 2.0 * B * din * dout,
+                B * dout * e + din * dout * e + B * din * (1 + e));
+        add(std::string(kind) + "_tn_sgd_l" + std::to_string(l), 2.0 * B * din * dout,
+            B * din * e + B * dout * e + din * dout * (8 + (c->bf16 ? 2 : 0)));
+    }
+}
+
+// ---------------------------------------------------------------- launches --
+
+struct Runner {
+    mlp_ctx* c;
+    int slot = 0;
+    hipError_t err = hipSuccess;
+
+    hipEvent_t ev() {
+        if (!c->event_pool.empty()) {
+            hipEvent_t e = c->event_pool.back();
+            c->event_pool.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+
+    template <class F>
+    void run(int slot_id, F&& f) {
+        if (err != hipSuccess) return;
+        hipEvent_t b = nullptr, e = nullptr;
+        if (c->profiling && slot_id >= 0) {
+            b = ev();
+            e = ev();
+            if (b && e) hipEventRecord(b, c->stream);
+        }
+        err = f();
+        if (b && e) {
+            hipEventRecord(e, c->stream);
+            c->pending.push_back({slot_id, b, e});
+        }
+    }
+};
+
+hipError_t run_gemm(mlp_ctx* c, const GemmPlan& g, Layout lay, Epi epi, const void* A, int64_t lda,
+                    const void* Bm, int64_t ldb, int M, int N, int K, float* C, bf16_t* Cb,
+                    uint8_t* mask, float lr) {
+    GemmLaunch L;
+    L.layout = lay;
+    L.epi = epi;
+    L.bf16 = c->bf16;
+    L.cfg = g.cfg;
+    L.vec = g.vec;
+    L.grid = g.grid;
+    GemmParams p;
+    p.A = A;
+    p.B = Bm;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.C = C;
+    p.Cb = Cb;
+    p.mask = mask;
+    p.ldc = N;
+    p.lr = lr;
+    p.splits = g.splits;
+    p.kchunk = g.kchunk;
+    p.partials = c->partials;
+    p.tickets = c->tickets;
+    p.tiles_m = g.tiles_m;
+    p.tiles_n = g.tiles_n;
+    return launch_gemm(L, p, c->stream);
+}
+
+hipError_t run_skinny(mlp_ctx* c, const SkinnyPlan& s, Layout lay, Epi epi, const float* A,
+                      const float* Bm, int K, int N, float* C, uint8_t* mask, float lr) {
+    SkinnyLaunch L;
+    L.layout = lay;
+    L.epi = epi;
+    L.grid = s.grid;
+    L.waves = s.waves;
+    SkinnyParams p;
+    p.A = A;
+    p.B = Bm;
+    p.MB = c->B;
+    p.K = K;
+    p.N = N;
+    p.C = C;
+    p.Cb = nullptr;
+    p.mask = mask;
+    p.lr = lr;
+    p.splits = s.splits;
+    p.kchunk = s.kchunk;
+    p.partials = c->partials;
+    p.tickets = c->tickets;
+    return launch_skinny(L, p, c->stream);
+}
+
+enum class Mode { Forward, Train, Grads };
+
+// Enqueue the step.  Returns the first HIP error (launches stop there).
+hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, float lr,
+                   float* const* dw_out, float* loss_dev) {
+    Runner r{c};
+    const int L = c->L, B = c->B;
+    int slot = 0;
+    const void* a_prev;
+    if (c->bf16) {
+        r.run(slot++, [&] { return launch_cast_bf16(x, c->xb, (size_t)B * c->dims[0], c->stream); });
+        a_prev = c->xb;
+    } else {
+        a_prev = x;
+    }
+    // ---- forward
+    for (int l = 0; l < L; ++l) {
+        const int K = c->dims[l], N = c->dims[l + 1];
+        const bool last = l == L - 1;
+        const void* Wop = c->bf16 ? (const void*)c->Wb[l] : (const void*)c->W[l];
+        if (c->skinny) {
+            r.run(slot++, [&] {
+                return run_skinny(c, c->sfwd[l], Layout::NN, last ? Epi::Store : Epi::ReluMask,
+                                  (const float*)a_prev, (const float*)Wop, K, N,
+                                  last ? c->logits : (float*)c->act[l + 1],
+                                  last ? nullptr : c->mask[l + 1], 0.f);
+            });
+        } else {
+            r.run(slot++, [&] {
+                float* Cf = last ? c->logits : (c->bf16 ? nullptr : (float*)c->act[l + 1]);
+                bf16_t* Cb = (!last && c->bf16) ? (bf16_t*)c->act[l + 1] : nullptr;
+                return run_gemm(c, c->fwd[l], Layout::NN, last ? Epi::Store : Epi::ReluMask, a_prev, K,
+                                Wop, N, B, N, K, Cf, Cb, last ? nullptr : c->mask[l + 1], 0.f);
+            });
+        }
+        if (!last) a_prev = c->act[l + 1];
+    }
+    if (mode == Mode::Forward && !labels) return r.err;
+
+    // ---- loss
+    const int C = c->dims[L];
+    r.run(slot++, [&] {
+        XentParams xp;
+        xp.logits = c->logits;
+        xp.labels = labels;
+        xp.dlogits = c->dlogits;
+        xp.dlogits_b = c->bf16 ? c->dlogits_b : nullptr;
+        xp.rowloss = c->rowloss;
+        xp.loss = loss_dev ? loss_dev : c->loss_slot;
+        xp.ticket = c->xent_ticket;
+        xp.B = B;
+        xp.C = C;
+        xp.inv_b = 1.0f / (float)B;
+        return launch_xent(xp, nullptr, c->stream);
+    });
+    if (mode == Mode::Forward) return r.err;
+
+    // ---- backward
+    const void* G = c->bf16 ? (const void*)c->dlogits_b : (const void*)c->dlogits;
+    int pp = 0;
+    for (int l = L - 1; l >= 0; --l) {
+        const int din = c->dims[l], dout = c->dims[l + 1];
+        const void* Wop = c->bf16 ? (const void*)c->Wb[l] : (const void*)c->W[l];
+        const void* Gnext = nullptr;
+        if (l > 0) {
+            void* out = c->dz[pp];
+            pp ^= 1;
+            if (c->skinny) {
+                r.run(slot++, [&] {
+                    return run_skinny(c, c->sdx[l], Layout::NT, Epi::MaskMul, (const float*)Wop,
+                                      (const float*)G, din, dout, (float*)out, c->mask[l], 0.f);
+                });
+            } else {
+                r.run(slot++, [&] {
+                    return run_gemm(c, c->dx[l], Layout::NT, Epi::MaskMul, G, dout, Wop, dout, B, din,
+                                    dout, c->bf16 ? nullptr : (float*)out,
+                                    c->bf16 ? (bf16_t*)out : nullptr, c->mask[l], 0.f);
+                });
+            }
+            Gnext = out;
+        }
+        const void* a_in = l == 0 ? (c->bf16 ? (const void*)c->xb : (const void*)x) : c->act[l];
+        const bool grads = mode == Mode::Grads;
+        float* Wdst = grads ? dw_out[l] : c->W[l];
+        bf16_t* Wbdst = (!grads && c->bf16) ? c->Wb[l] : nullptr;
+        if (c->skinny) {
+            r.run(slot++, [&] {
+                return run_skinny(c, c->sdw[l], Layout::TN, grads ? Epi::Grad : Epi::Sgd,
+                                  (const float*)a_in, (const float*)G, din, dout, Wdst, nullptr, lr);
+            });
+        } else {
+            r.run(slot++, [&] {
+                return run_gemm(c, c->dw[l], Layout::TN, grads ? Epi::Grad : Epi::Sgd, a_in, din, G, dout,
+                                din, dout, B, Wdst, Wbdst, nullptr, lr);
+            });
+        }
+        G = Gnext;
+    }
+    return r.err;
+}
+
+mlp_status hip_fail(mlp_ctx* c, hipError_t e, const char* what) {
+    c->poisoned = true;
+    c->params_set = 0;
+    return set_err(c, MLP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+mlp_status check_ready(mlp_ctx* c) {
+    if (!c) return MLP_ERR_ARG;
+    c->err.clear();
+    const unsigned all = c->L >= 32 ? ~0u : ((1u << c->L) - 1u);
+    if (c->poisoned && c->params_set != all)
+        return set_err(c, MLP_ERR_STATE, "context poisoned by an earlier HIP failure; set every layer");
+    if (c->params_set != all)
+        return set_err(c, MLP_ERR_STATE, "weights not initialised: call mlp_set_params for every layer");
+    return MLP_OK;
+}
+
+mlp_status collect_profile(mlp_ctx* c) {
+    // Fold completed event pairs into their slots (caller has synchronised).
+    std::vector<Pending> keep;
+    for (const Pending& p : c->pending) {
+        float ms = 0.f;
+        const hipError_t e = hipEventElapsedTime(&ms, p.beg, p.end);
+        if (e == hipErrorNotReady) {
+            keep.push_back(p);
+            continue;
+        }
+        if (e == hipSuccess && p.slot < (int)c->slots.size()) {
+            c->slots[p.slot].total_ms += ms;
+            c->slots[p.slot].launches += 1;
+        }
+        c->event_pool.push_back(p.beg);
+        c->event_pool.push_back(p.end);
+    }
+    c->pending.swap(keep);
+    return MLP_OK;
+}
+
+// ---------------------------------------------------------------- layout --
+
+struct Layout_ {
+    size_t off = 0;
+    size_t take(size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + std::max<size_t>(bytes, 1), kAlign);
+        return o;
+    }
+};
+
+mlp_status validate(const mlp_config* cfg, mlp_ctx* tmp) {
+    if (!cfg) return set_err(nullptr, MLP_ERR_ARG, "config is NULL");
+    if (cfg->n_layers < 1 || cfg->n_layers > kMaxLayers)
+        return set_err(nullptr, MLP_ERR_SHAPE, "n_layers %d outside 1..%d", cfg->n_layers, kMaxLayers);
+    if (!cfg->dims) return set_err(nullptr, MLP_ERR_ARG, "dims is NULL");
+    if (cfg->batch < 1 || cfg->batch > kMaxDim)
+        return set_err(nullptr, MLP_ERR_SHAPE, "batch %d outside 1..%d", cfg->batch, kMaxDim);
+    if (cfg->precision != MLP_F32 && cfg->precision != MLP_BF16)
+        return set_err(nullptr, MLP_ERR_ARG, "unknown precision %d", cfg->precision);
+    for (int i = 0; i <= cfg->n_layers; ++i)
+        if (cfg->dims[i] < 1 || cfg->dims[i] > kMaxDim)
+            return set_err(nullptr, MLP_ERR_SHAPE, "dims[%d] = %d outside 1..%d", i, cfg->dims[i], kMaxDim);
+    for (int i = 0; i < cfg->n_layers; ++i)
+        if ((int64_t)cfg->dims[i] * cfg->dims[i + 1] > ((int64_t)1 << 31) ||
+            (int64_t)cfg->batch * cfg->dims[i] > ((int64_t)1 << 31))
+            return set_err(nullptr, MLP_ERR_SHAPE, "layer %d has more than 2^31 elements", i);
+    if ((int64_t)cfg->batch * cfg->dims[cfg->n_layers] > ((int64_t)1 << 31))
+        return set_err(nullptr, MLP_ERR_SHAPE, "logits have more than 2^31 elements");
+    tmp->L = cfg->n_layers;
+    for (int i = 0; i <= tmp->L; ++i) tmp->dims[i] = cfg->dims[i];
+    tmp->B = cfg->batch;
+    tmp->bf16 = cfg->precision == MLP_BF16;
+    tmp->stream = (hipStream_t)cfg->stream;
+    bool all4 = true;
+    for (int i = 0; i <= tmp->L; ++i) all4 = all4 && (tmp->dims[i] % 4 == 0);
+    tmp->skinny = !tmp->bf16 && tmp->B <= kSkinnyMaxBatch && all4;
+    return MLP_OK;
+}
+
+// Plans every product and returns the workspace layout size; with base !=
+// nullptr also assigns the buffer pointers.
+size_t plan_and_carve(mlp_ctx* c, char* base) {
+    const int L = c->L, B = c->B;
+    const size_t e = c->bf16 ? 2 : 4;
+    size_t max_partial = 0, max_tickets = 1;
+    for (int l = 0; l < L; ++l) {
+        const int din = c->dims[l], dout = c->dims[l + 1];
+        if (c->skinny) {
+            c->sfwd[l] = plan_skinny_nn(dout, din, B);
+            if (c->sfwd[l].splits > 1) {
+                max_partial = std::max(max_partial, (size_t)c->sfwd[l].splits * B * dout);
+                max_tickets = std::max(max_tickets, (size_t)c->sfwd[l].tickets);
+            }
+            c->sdx[l].grid = (din + 15) / 16;
+            c->sdw[l].grid = ((dout + 1023) / 1024) * ((din + 15) / 16);
+            continue;
+        }
+        const int vq = c->bf16 ? 8 : 4;
+        // forward NN: A = a_l [B][din] (k-contiguous, K = din)
+        c->fwd[l] = plan_gemm(B, dout, din, c->bf16, din % vq == 0);
+        // dX NT: A = G [B][dout], B = W [din][dout] (both k-contiguous, K = dout)
+        c->dx[l] = plan_gemm(B, din, dout, c->bf16, dout % vq == 0);
+        // dW TN: M = din, N = dout, K = B
+        c->dw[l] = plan_gemm(din, dout, B, c->bf16, true);
+        for (const GemmPlan* g : {&c->fwd[l], &c->dx[l], &c->dw[l]}) {
+            if (g->splits > 1) {
+                int bm, bn;
+                tile_shape(g->cfg, &bm, &bn);
+                const size_t M = (size_t)g->tiles_m * bm, N = (size_t)g->tiles_n * bn;
+                (void)M;
+                (void)N;
+                max_tickets = std::max(max_tickets, (size_t)g->tiles_m * g->tiles_n);
+            }
+        }
+        if (c->fwd[l].splits > 1) max_partial = std::max(max_partial, (size_t)c->fwd[l].splits * B * dout);
+        if (c->dx[l].splits > 1) max_partial = std::max(max_partial, (size_t)c->dx[l].splits * B * din);
+        if (c->dw[l].splits > 1) max_partial = std::max(max_partial, (size_t)c->dw[l].splits * din * dout);
+    }
+    int max_hidden = 1;
+    for (int l = 1; l < L; ++l) max_hidden = std::max(max_hidden, c->dims[l]);
+    const int C = c->dims[L];
+
+    Layout_ lay;
+    size_t oW[kMaxLayers], oWb[kMaxLayers], oA[kMaxLayers], oM[kMaxLayers];
+    for (int l = 0; l < L; ++l) oW[l] = lay.take((size_t)c->dims[l] * c->dims[l + 1] * 4);
+    for (int l = 0; l < L; ++l) oWb[l] = c->bf16 ? lay.take((size_t)c->dims[l] * c->dims[l + 1] * 2) : 0;
+    for (int l = 1; l < L; ++l) oA[l] = lay.take((size_t)B * c->dims[l] * e);
+    for (int l = 1; l < L; ++l) oM[l] = lay.take((size_t)B * c->dims[l]);
+    const size_t oXb = c->bf16 ? lay.take((size_t)B * c->dims[0] * 2) : 0;
+    const size_t oLog = lay.take((size_t)B * C * 4);
+    const size_t oDl = lay.take((size_t)B * C * 4);
+    const size_t oDlb = c->bf16 ? lay.take((size_t)B * C * 2) : 0;
+    const size_t oDz0 = lay.take((size_t)B * max_hidden * e);
+    const size_t oDz1 = lay.take((size_t)B * max_hidden * e);
+    const size_t oPart = lay.take(max_partial * 4);
+    const size_t oTick = lay.take((max_tickets + 1) * sizeof(unsigned));
+    const size_t oRow = lay.take((size_t)B * 4);
+    const size_t oLoss = lay.take(16);
+    c->slots.clear();
+    if (base) {
+        for (int l = 0; l < L; ++l) {
+            c->W[l] = (float*)(base + oW[l]);
+            c->Wb[l] = c->bf16 ? (bf16_t*)(base + oWb[l]) : nullptr;
+        }
+        for (int l = 1; l < L; ++l) {
+            c->act[l] = base + oA[l];
+            c->mask[l] = (uint8_t*)(base + oM[l]);
+        }
+        c->xb = c->bf16 ? (bf16_t*)(base + oXb) : nullptr;
+        c->logits = (float*)(base + oLog);
+        c->dlogits = (float*)(base + oDl);
+        c->dlogits_b = c->bf16 ? (bf16_t*)(base + oDlb) : nullptr;
+        c->dz[0] = base + oDz0;
+        c->dz[1] = base + oDz1;
+        c->partials = (float*)(base + oPart);
+        c->tickets = (unsigned*)(base + oTick);
+        c->xent_ticket = c->tickets + max_tickets;
+        c->rowloss = (float*)(base + oRow);
+        c->loss_slot = (float*)(base + oLoss);
+    }
+    return lay.off;
+}
+
+size_t tickets_bytes(mlp_ctx* c) {
+    return (size_t)((char*)c->rowloss - (char*)c->tickets);
+}
+
+}  // namespace
+
+// =================================================================== ABI ===
+
+extern "C" {
+
+int32_t mlp_abi_version(void) { return MLP_ABI_VERSION; }
+
+const char* mlp_status_string(mlp_status s) {
+    switch (s) {
+    case MLP_OK: return "MLP_OK";
+    case MLP_ERR_ARG: return "MLP_ERR_ARG";
+    case MLP_ERR_SHAPE: return "MLP_ERR_SHAPE";
+    case MLP_ERR_WORKSPACE: return "MLP_ERR_WORKSPACE";
+    case MLP_ERR_HIP: return "MLP_ERR_HIP";
+    case MLP_ERR_STATE: return "MLP_ERR_STATE";
+    }
+    return "MLP_ERR_UNKNOWN";
+}
+
+const char* mlp_last_error(const mlp_ctx* c) { return c ? c->err.c_str() : g_create_error.c_str(); }
+
+size_t mlp_workspace_bytes(const mlp_config* cfg) {
+    mlp_ctx tmp;
+    if (validate(cfg, &tmp) != MLP_OK) return 0;
+    return plan_and_carve(&tmp, nullptr);
+}
+
+mlp_status mlp_create(const mlp_config* cfg, void* workspace, size_t bytes, mlp_ctx** out) {
+    g_create_error.clear();
+    if (!out) return set_err(nullptr, MLP_ERR_ARG, "out is NULL");
+    *out = nullptr;
+    mlp_ctx* c = new mlp_ctx();
+    mlp_status st = validate(cfg, c);
+    if (st != MLP_OK) {
+        delete c;
+        return st;
+    }
+    const size_t need = plan_and_carve(c, nullptr);
+    if (!workspace || ((uintptr_t)workspace % kAlign) != 0 || bytes < need) {
+        delete c;
+        return set_err(nullptr, MLP_ERR_WORKSPACE,
+                       "workspace %p of %zu bytes: need %zu bytes, %zu-byte aligned", workspace, bytes,
+                       need, kAlign);
+    }
+    plan_and_carve(c, (char*)workspace);
+    build_slots(c);
+    const hipError_t e = hipMemsetAsync(c->tickets, 0, tickets_bytes(c), c->stream);
+    if (e != hipSuccess) {
+        set_err(nullptr, MLP_ERR_HIP, "zeroing counters: %s", hipGetErrorString(e));
+        delete c;
+        return MLP_ERR_HIP;
+    }
+    *out = c;
+    return MLP_OK;
+}
+
+void mlp_destroy(mlp_ctx* c) {
+    if (!c) return;
+    for (const Pending& p : c->pending) {
+        hipEventDestroy(p.beg);
+        hipEventDestroy(p.end);
+    }
+    for (hipEvent_t e : c->event_pool) hipEventDestroy(e);
+    delete c;
+}
+
+mlp_status mlp_set_params(mlp_ctx* c, int32_t layer, const float* w) {
+    if (!c) return MLP_ERR_ARG;
+    c->err.clear();
+    if (layer < 0 || layer >= c->L) return set_err(c, MLP_ERR_ARG, "layer %d outside 0..%d", layer, c->L - 1);
+    if (!w || !aligned16(w)) return set_err(c, MLP_ERR_ARG, "w must be a 16-byte aligned device pointer");
+    const size_t n = (size_t)c->dims[layer] * c->dims[layer + 1];
+    hipError_t e = hipMemcpyAsync(c->W[layer], w, n * 4, hipMemcpyDeviceToDevice, c->stream);
+    if (e == hipSuccess && c->bf16) e = launch_cast_bf16(c->W[layer], c->Wb[layer], n, c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "mlp_set_params");
+    c->params_set |= 1u << layer;
+    const unsigned all = (1u << c->L) - 1u;
+    if (c->params_set == all) c->poisoned = false;
+    return MLP_OK;
+}
+
+mlp_status mlp_read_params(mlp_ctx* c, int32_t layer, float* dst) {
+    if (!c) return MLP_ERR_ARG;
+    c->err.clear();
+    if (layer < 0 || layer >= c->L) return set_err(c, MLP_ERR_ARG, "layer %d outside 0..%d", layer, c->L - 1);
+    if (!dst || !aligned16(dst)) return set_err(c, MLP_ERR_ARG, "dst must be a 16-byte aligned device pointer");
+    if (c->poisoned) return set_err(c, MLP_ERR_STATE, "context poisoned by an earlier HIP failure");
+    const size_t n = (size_t)c->dims[layer] * c->dims[layer + 1];
+    const hipError_t e = hipMemcpyAsync(dst, c->W[layer], n * 4, hipMemcpyDeviceToDevice, c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "mlp_read_params");
+    return MLP_OK;
+}
+
+static mlp_status read_loss(mlp_ctx* c, float* loss) {
+    hipError_t e = hipMemcpyAsync(loss, c->loss_slot, 4, hipMemcpyDeviceToHost, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "loss read-back");
+    if (c->profiling) collect_profile(c);
+    return MLP_OK;
+}
+
+mlp_status mlp_forward(mlp_ctx* c, const float* x, float* logits, const float* labels, float* loss) {
+    mlp_status st = check_ready(c);
+    if (st != MLP_OK) return st;
+    if (!x || !aligned16(x)) return set_err(c, MLP_ERR_ARG, "x must be a 16-byte aligned device pointer");
+    if (logits && !aligned16(logits)) return set_err(c, MLP_ERR_ARG, "logits must be 16-byte aligned");
+    if (labels && !aligned16(labels)) return set_err(c, MLP_ERR_ARG, "labels must be 16-byte aligned");
+    hipError_t e = enqueue(c, Mode::Forward, x, labels, 0.f, nullptr, nullptr);
+    if (e == hipSuccess && logits)
+        e = hipMemcpyAsync(logits, c->logits, (size_t)c->B * c->dims[c->L] * 4, hipMemcpyDeviceToDevice,
+                           c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "mlp_forward");
+    if (labels && loss) return read_loss(c, loss);
+    return MLP_OK;
+}
+
+mlp_status mlp_train_step_async(mlp_ctx* c, const float* x, const float* labels, float lr, float* loss_dev) {
+    mlp_status st = check_ready(c);
+    if (st != MLP_OK) return st;
+    if (!x || !aligned16(x)) return set_err(c, MLP_ERR_ARG, "x must be a 16-byte aligned device pointer");
+    if (!labels || !aligned16(labels))
+        return set_err(c, MLP_ERR_ARG, "labels must be a 16-byte aligned device pointer");
+    if (!std::isfinite(lr)) return set_err(c, MLP_ERR_ARG, "lr must be finite");
+    if (loss_dev && ((uintptr_t)loss_dev & 3u)) return set_err(c, MLP_ERR_ARG, "loss_dev must be 4-byte aligned");
+    const hipError_t e = enqueue(c, Mode::Train, x, labels, lr, nullptr, loss_dev);
+    if (e != hipSuccess) return hip_fail(c, e, "mlp_train_step");
+    return MLP_OK;
+}
+
+mlp_status mlp_train_step(mlp_ctx* c, const float* x, const float* labels, float lr, float* loss) {
+    mlp_status st = mlp_train_step_async(c, x, labels, lr, nullptr);
+    if (st != MLP_OK) return st;
+    if (loss) return read_loss(c, loss);
+    return MLP_OK;
+}
+
+mlp_status mlp_grads(mlp_ctx* c, const float* x, const float* labels, float* const* dw, float* dlogits,
+                     float* loss) {
+    mlp_status st = check_ready(c);
+    if (st != MLP_OK) return st;
+    if (!x || !aligned16(x)) return set_err(c, MLP_ERR_ARG, "x must be a 16-byte aligned device pointer");
+    if (!labels || !aligned16(labels))
+        return set_err(c, MLP_ERR_ARG, "labels must be a 16-byte aligned device pointer");
+    if (!dw) return set_err(c, MLP_ERR_ARG, "dw is NULL");
+    for (int l = 0; l < c->L; ++l)
+        if (!dw[l] || !aligned16(dw[l])) return set_err(c, MLP_ERR_ARG, "dw[%d] must be a 16-byte aligned device pointer", l);
+    if (dlogits && !aligned16(dlogits)) return set_err(c, MLP_ERR_ARG, "dlogits must be 16-byte aligned");
+    hipError_t e = enqueue(c, Mode::Grads, x, labels, 0.f, dw, nullptr);
+    if (e == hipSuccess && dlogits)
+        e = hipMemcpyAsync(dlogits, c->dlogits, (size_t)c->B * c->dims[c->L] * 4, hipMemcpyDeviceToDevice,
+                           c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "mlp_grads");
+    if (loss) return read_loss(c, loss);
+    return MLP_OK;
+}
+
+mlp_status mlp_read_state(mlp_ctx* c, int32_t which, int32_t layer, void* dst) {
+    if (!c) return MLP_ERR_ARG;
+    c->err.clear();
+    if (!dst || !aligned16(dst)) return set_err(c, MLP_ERR_ARG, "dst must be a 16-byte aligned device pointer");
+    if (c->poisoned) return set_err(c, MLP_ERR_STATE, "context poisoned by an earlier HIP failure");
+    const size_t BC = (size_t)c->B * c->dims[c->L];
+    hipError_t e = hipSuccess;
+    switch (which) {
+    case MLP_STATE_ACT:
+    case MLP_STATE_MASK: {
+        if (layer < 1 || layer >= c->L)
+            return set_err(c, MLP_ERR_ARG, "layer %d outside 1..%d", layer, c->L - 1);
+        const size_t n = (size_t)c->B * c->dims[layer];
+        if (which == MLP_STATE_MASK)
+            e = hipMemcpyAsync(dst, c->mask[layer], n, hipMemcpyDeviceToDevice, c->stream);
+        else if (c->bf16)
+            e = launch_widen_bf16((const bf16_t*)c->act[layer], (float*)dst, n, c->stream);
+        else
+            e = hipMemcpyAsync(dst, c->act[layer], n * 4, hipMemcpyDeviceToDevice, c->stream);
+        break;
+    }
+    case MLP_STATE_DLOGITS:
+        e = hipMemcpyAsync(dst, c->dlogits, BC * 4, hipMemcpyDeviceToDevice, c->stream);
+        break;
+    case MLP_STATE_LOGITS:
+        e = hipMemcpyAsync(dst, c->logits, BC * 4, hipMemcpyDeviceToDevice, c->stream);
+        break;
+    default:
+        return set_err(c, MLP_ERR_ARG, "unknown state kind %d", which);
+    }
+    if (e != hipSuccess) return hip_fail(c, e, "mlp_read_state");
+    return MLP_OK;
+}
+
+mlp_status mlp_profile_enable(mlp_ctx* c, int32_t enable) {
+    if (!c) return MLP_ERR_ARG;
+    c->profiling = enable != 0;
+    return MLP_OK;
+}
+
+mlp_status mlp_profile_reset(mlp_ctx* c) {
+    if (!c) return MLP_ERR_ARG;
+    collect_profile(c);
+    for (Slot& s : c->slots) {
+        s.total_ms = 0;
+        s.launches = 0;
+    }
+    return MLP_OK;
+}
+
+int32_t mlp_profile_slots(const mlp_ctx* c) { return c ? (int32_t)c->slots.size() : 0; }
+
+mlp_status mlp_profile_read(mlp_ctx* c, int32_t idx, char* name, size_t name_len, double* total_ms,
+                            int64_t* launches, double* flops, double* bytes) {
+    if (!c) return MLP_ERR_ARG;
+    c->err.clear();
+    if (idx < 0 || idx >= (int32_t)c->slots.size()) return set_err(c, MLP_ERR_ARG, "slot %d out of range", idx);
+    collect_profile(c);
+    const Slot& s = c->slots[idx];
+    if (name && name_len) {
+        std::strncpy(name, s.name.c_str(), name_len - 1);
+        name[name_len - 1] = 0;
+    }
+    if (total_ms) *total_ms = s.total_ms;
+    if (launches) *launches = s.launches;
+    if (flops) *flops = s.flops;
+    if (bytes) *bytes = s.bytes;
+    return MLP_OK;
+}
+
+}  // extern "C"

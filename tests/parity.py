@@ -1,0 +1,159 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+compare it with the float64 oracle on the same seeded inputs.
+
+Gates (strict f32 / bf16 fast path):
+  loss       |L_gpu - L_ref| / |L_ref|              <= 1e-5 / 2e-2
+  gradients  max|dW_gpu - dW_ref| <= tol * max|dW_ref|, per tensor (also dlogits)
+  update     max|dW'_gpu - dW'_ref| <= tol * max|dW'_ref| + ulp(max|W|),  dW' = W' - W_old
+  weights    max|W'_gpu - W'_ref| <= tol * max|W'_ref|
+  masks      identical outside the rounding band of the oracle (inside it either
+             value is a correct ReLU derivative and the oracle follows the GPU's)
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import mlp_oracle
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+GRAD_TOL = {"f32": 1e-4, "bf16": 2e-2}
+# fraction of hidden units allowed to sit in the rounding band and differ
+MAX_ADOPTED = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def to_dev(arrs, dev):
+    import torch
+    return [torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in arrs]
+
+
+def gpu_grads(net, x, t):
+    """(loss, dW list, dlogits, masks) from mlp_grads + mlp_read_state."""
+    from mlp_gemm_softmax_amd import binding
+    loss, dws, dl = net.grads(x, t)
+    masks = [net.read_state(binding.STATE_MASK, l).cpu().numpy() for l in range(1, net.n_layers)]
+    return loss, [d.cpu().numpy() for d in dws], dl.cpu().numpy(), masks
+
+
+def gpu_train(net, x, t, lr):
+    from mlp_gemm_softmax_amd import binding
+    loss = net.train_step(x, t, lr)
+    masks = [net.read_state(binding.STATE_MASK, l).cpu().numpy() for l in range(1, net.n_layers)]
+    return loss, [w.cpu().numpy() for w in net.read_params()], masks
+
+
+def oracle_step(x, t, Ws, lr, dims, precision, masks):
+    betas = mlp_oracle.kink_betas(dims, precision)
+    return mlp_oracle.train_step(x, t, Ws, lr, kink_choice=masks, kink_beta=betas)
+
+
+def check_masks(ref, B, dims, precision, label=""):
+    fwd = ref["fwd"]
+    if len(dims) <= 2:
+        return
+    for l, (ad, out) in enumerate(zip(fwd["adopted"], fwd["outside"]), start=1):
+        assert out == 0, f"{label} layer {l}: {out} mask bits differ outside the rounding band"
+        frac = ad / float(B * dims[l])
+        assert frac <= MAX_ADOPTED[precision], f"{label} layer {l}: {ad} band bits differ ({frac:.2e})"
+
+
+def rel_max(a, ref):
+    a = np.asarray(a, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = np.max(np.abs(ref))
+    err = np.max(np.abs(a - ref)) if a.size else 0.0
+    return err, scale
+
+
+def check_grads(loss, dws, dlogits, ref, precision, label=""):
+    tol = TOL[precision]
+    gtol = GRAD_TOL[precision]
+    rel = abs(loss - ref["loss"]) / max(abs(ref["loss"]), 1e-30)
+    assert rel <= tol, f"{label} loss {loss!r} vs {ref['loss']!r}: rel {rel:.3e} > {tol}"
+    err, scale = rel_max(dlogits, ref["dlogits"])
+    assert err <= gtol * scale, f"{label} dlogits: {err:.3e} > {gtol} * {scale:.3e}"
+    for l, (g, r) in enumerate(zip(dws, ref["dW"])):
+        err, scale = rel_max(g, r)
+        assert err <= gtol * scale + 1e-30, f"{label} dW{l}: {err:.3e} > {gtol} * {scale:.3e}"
+
+
+def check_update(loss, W_new, W_old, ref, precision, label=""):
+    tol = TOL[precision]
+    gtol = GRAD_TOL[precision]
+    rel = abs(loss - ref["loss"]) / max(abs(ref["loss"]), 1e-30)
+    assert rel <= tol, f"{label} loss {loss!r} vs {ref['loss']!r}: rel {rel:.3e} > {tol}"
+    for l, (g, r, w0) in enumerate(zip(W_new, ref["W_new"], W_old)):
+        w0 = np.asarray(w0, np.float64)
+        err, scale = rel_max(g, r)
+        assert err <= gtol * scale + 1e-30, f"{label} W'{l}: {err:.3e} > {gtol} * {scale:.3e}"
+        d_gpu = np.asarray(g, np.float64) - w0
+        d_ref = r - w0
+        ulp = float(np.spacing(np.float32(max(np.max(np.abs(r)), np.max(np.abs(w0))))))
+        err, scale = rel_max(d_gpu, d_ref)
+        assert err <= gtol * scale + ulp, f"{label} dW'{l}: {err:.3e} > {gtol} * {scale:.3e} + {ulp:.1e}"
+
+
+def check_fused_update_matches_grads(W_new, W_old, dws, lr):
+    """The fused SGD epilogue equals fl32(W - fl32(lr*dW)) of the stored
+    gradient (same kernel, same accumulation order) up to the rounding that
+    separates a fused multiply-add from two rounded operations:
+    |W'_gpu - fl32(W - fl32(lr*dW))| <= ulp(lr*dW)/2 + ulp(max(|W'_gpu|, |expect|))."""
+    for l, (g, w0, dw) in enumerate(zip(W_new, W_old, dws)):
+        step = (np.float32(lr) * np.float32(dw)).astype(np.float32)
+        expect = (np.float32(w0) - step).astype(np.float32)
+        bound = 0.5 * np.spacing(np.abs(step)).astype(np.float64) + \
+            np.spacing(np.maximum(np.abs(expect), np.abs(g)).astype(np.float32)).astype(np.float64)
+        bad = np.abs(g.astype(np.float64) - expect) > bound
+        assert not np.any(bad), f"W'{l}: {int(bad.sum())} elements beyond the fma/two-rounding bound"
+
+
+def _exact_everywhere(x, t, Ws, bf16):
+    """True if every partial sum of the step is an integer (times 1/B for the
+    backward) below 2^23, so that float32 arithmetic in any order is exact;
+    with bf16 operands also every GEMM operand must fit 8 significant bits."""
+    B = x.shape[0]
+    r = mlp_oracle.train_step(x, t, Ws, 0.0)
+    a = r["fwd"]["a"]
+    G = r["G"]
+    lim = 2.0 ** 23
+    for l, W in enumerate(Ws):
+        Wa = np.abs(np.asarray(W, np.float64))
+        if np.max(np.abs(a[l]) @ Wa) >= lim:
+            return False
+        Gl = np.abs(G[l + 1]) * B
+        if np.max(np.abs(a[l]).T @ Gl) >= lim:
+            return False
+        if l > 0 and np.max(Gl @ Wa.T) >= lim:
+            return False
+        if bf16:
+            if np.max(np.abs(a[l])) > 256 or np.max(Wa) > 256 or np.max(Gl) > 256:
+                return False
+            if not np.all(Gl == np.round(Gl)):
+                return False
+    return True
+
+
+def integer_problem(dims, B, seed, xmax=2, wmax=2, gap=50, bf16=False):
+    """Integer-valued x and weights for which every product, partial sum,
+    softmax and loss of the step is exact in float32 (and in bf16 operands):
+    the last layer's column 0 beats every other column by gap * sum(a) >= 110
+    per row, so softmax is exactly one-hot in float32 and dlogits =
+    (e_0 - t)/B.  B must be a power of two."""
+    assert B & (B - 1) == 0
+    rng = np.random.default_rng([seed, 99])
+    for _ in range(200):
+        x = rng.integers(0, xmax + 1, (B, dims[0])).astype(np.float32)
+        Ws = [rng.integers(-wmax, wmax + 1, (dims[l], dims[l + 1])).astype(np.float32)
+              for l in range(len(dims) - 1)]
+        WL = Ws[-1]
+        WL[:, 0] = WL[:, 1:].max(axis=1) + gap if WL.shape[1] > 1 else gap
+        a = x.astype(np.float64)
+        for W in Ws[:-1]:
+            a = np.maximum(a @ W, 0)
+        if not np.all(a.sum(axis=1) * gap >= 110):
+            continue
+        ids = rng.integers(0, dims[-1], B)
+        t = np.zeros((B, dims[-1]), np.float32)
+        t[np.arange(B), ids] = 1.0
+        if _exact_everywhere(x, t, Ws, bf16):
+            return x, t, Ws
+    raise RuntimeError("no exactly representable integer problem found")

@@ -1,0 +1,119 @@
+"""Host-only checks of the C ABI: libmlp.so loads, exports every entry point
+include/mlp.h declares, and rejects bad arguments in preflight (before any
+HIP call, so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mlp_gemm_softmax_amd import binding
+from mlp_gemm_softmax_amd.synth import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mlp.h")
+
+
+def _lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libmlp.so not built (run __graft_entry__.build())")
+    return binding.lib()
+
+
+def declared_entry_points():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mlp_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_entry_points() == sorted(binding.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in declared_entry_points():
+        assert hasattr(lib, name), name
+    assert lib.mlp_abi_version() == 1
+
+
+def test_status_strings():
+    lib = _lib()
+    names = [lib.mlp_status_string(i).decode() for i in range(6)]
+    assert names == ["MLP_OK", "MLP_ERR_ARG", "MLP_ERR_SHAPE", "MLP_ERR_WORKSPACE",
+                     "MLP_ERR_HIP", "MLP_ERR_STATE"]
+
+
+def _cfg(dims, batch, precision=binding.MLP_F32):
+    return binding.make_config(dims, batch, precision)
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_workspace_bytes_for_workloads(name):
+    lib = _lib()
+    w = WORKLOADS[name]
+    prec = binding.MLP_BF16 if w.precision == "bf16" else binding.MLP_F32
+    n = lib.mlp_workspace_bytes(ctypes.byref(_cfg(w.dims, w.batch, prec)))
+    assert n > 0 and n % 256 == 0
+    # at least the float32 weights, activations and logits
+    weights = sum(4 * w.dims[i] * w.dims[i + 1] for i in range(len(w.dims) - 1))
+    assert n >= weights + 4 * w.batch * w.dims[-1]
+
+
+@pytest.mark.parametrize("dims,batch,prec", [
+    ((), 4, 0),                       # no layers
+    ((10,), 4, 0),
+    ((10, 0, 3), 4, 0),               # zero width
+    ((10, 5, 3), 0, 0),               # zero batch
+    ((10, 5, 3), 4, 7),               # bad precision
+    ((10, 1 << 21, 3), 4, 0),         # width beyond the limit
+    (tuple([4] * 18), 4, 0),          # 17 layers > 16
+    ((1 << 20, 1 << 20), 1, 0),       # 2^40-element weight
+])
+def test_invalid_configs_need_no_workspace(dims, batch, prec):
+    lib = _lib()
+    if len(dims) == 0:
+        cfg = binding.MlpConfig(0, None, batch, prec, None)
+    else:
+        cfg = _cfg(dims, batch, prec)
+    assert lib.mlp_workspace_bytes(ctypes.byref(cfg)) == 0
+    h = ctypes.c_void_p()
+    st = lib.mlp_create(ctypes.byref(cfg), ctypes.c_void_p(4096), 1 << 30, ctypes.byref(h))
+    assert st in (binding.MLP_ERR_ARG, binding.MLP_ERR_SHAPE)
+    assert not h.value
+    assert lib.mlp_last_error(None).decode() != ""
+
+
+def test_null_config_and_out():
+    lib = _lib()
+    h = ctypes.c_void_p()
+    assert lib.mlp_workspace_bytes(None) == 0
+    assert lib.mlp_create(None, ctypes.c_void_p(256), 1 << 20, ctypes.byref(h)) == binding.MLP_ERR_ARG
+    cfg = _cfg((8, 4, 2), 2)
+    assert lib.mlp_create(ctypes.byref(cfg), ctypes.c_void_p(256), 1 << 20, None) == binding.MLP_ERR_ARG
+
+
+@pytest.mark.parametrize("ptr,delta", [(0, 0), (256 + 16, 0), (256, -256)])
+def test_workspace_preflight(ptr, delta):
+    """Null, misaligned or short workspaces fail before any device work."""
+    lib = _lib()
+    cfg = _cfg((784, 128, 10), 32)
+    need = lib.mlp_workspace_bytes(ctypes.byref(cfg))
+    h = ctypes.c_void_p()
+    st = lib.mlp_create(ctypes.byref(cfg), ctypes.c_void_p(ptr), need + delta, ctypes.byref(h))
+    assert st == binding.MLP_ERR_WORKSPACE
+    assert "workspace" in lib.mlp_last_error(None).decode()
+
+
+def test_null_context_calls():
+    lib = _lib()
+    assert lib.mlp_set_params(None, 0, None) == binding.MLP_ERR_ARG
+    assert lib.mlp_read_params(None, 0, None) == binding.MLP_ERR_ARG
+    assert lib.mlp_forward(None, None, None, None, None) == binding.MLP_ERR_ARG
+    assert lib.mlp_train_step(None, None, None, 0.1, None) == binding.MLP_ERR_ARG
+    assert lib.mlp_train_step_async(None, None, None, 0.1, None) == binding.MLP_ERR_ARG
+    assert lib.mlp_grads(None, None, None, None, None, None) == binding.MLP_ERR_ARG
+    assert lib.mlp_read_state(None, 0, 1, None) == binding.MLP_ERR_ARG
+    assert lib.mlp_profile_enable(None, 1) == binding.MLP_ERR_ARG
+    assert lib.mlp_profile_slots(None) == 0
+    lib.mlp_destroy(None)

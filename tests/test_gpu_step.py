@@ -1,0 +1,356 @@
+"""GPU parity of the HIP training step against the float64 oracle, through
+the C ABI (libmlp.so via the ctypes binding)."""
+import ctypes
+import math
+
+import numpy as np
+import pytest
+
+from mlp_gemm_softmax_amd import synth
+from oracle import mlp_oracle
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch, torch.device("cuda:0")
+
+
+def make_net(dims, B, precision, Ws, dev):
+    from mlp_gemm_softmax_amd import binding
+    net = binding.Mlp(dims, B, precision, device=str(dev))
+    net.set_params(P.to_dev(Ws, dev))
+    return net
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+# --------------------------------------------------------------- exactness --
+
+EXACT_CASES = [
+    # dims, B, precision
+    # dims, B, precision, operand range
+    ((200, 300, 36), 64, "f32", 2),          # ragged tiles, split-K in dW
+    ((96, 160, 130, 40), 128, "f32", 1),     # three layers, two masks
+    ((784, 128, 16), 32, "f32", 2),          # the README MLP's widths, 32x128 tiles
+    ((256, 520, 64), 8, "f32", 2),           # skinny-batch kernels, ragged columns
+    ((1024, 1100, 260), 16, "f32", 1),       # skinny-batch with K splits
+    ((200, 300, 36), 64, "bf16", 1),
+    ((120, 136, 24), 256, "bf16", 1),
+]
+
+
+@pytest.mark.parametrize("dims,B,precision,vmax", EXACT_CASES)
+def test_exact_integer_step_is_bitwise(torch_dev, dims, B, precision, vmax):
+    """P7: integer operands make every product, sum, softmax and update exact,
+    so the GPU must equal the float32-rounded oracle bit for bit, whatever
+    its tiling, split-K or summation order."""
+    torch, dev = torch_dev
+    _announce(f"exact dims={dims} B={B} {precision}")
+    x, t, Ws = P.integer_problem(dims, B, seed=len(dims) * 1000 + B, xmax=vmax, wmax=vmax,
+                                 bf16=precision == "bf16")
+    lr = 0.0625
+    ref = mlp_oracle.train_step(x, t, Ws, lr)
+    net = make_net(dims, B, precision, Ws, dev)
+    xd, td = P.to_dev([x, t], dev)
+    loss, dws, dl, masks = P.gpu_grads(net, xd, td)
+    logits, _ = net.forward(xd)
+    assert np.float32(loss) == np.float32(ref["loss"])
+    np.testing.assert_array_equal(logits.cpu().numpy(), ref["fwd"]["logits"].astype(np.float32))
+    np.testing.assert_array_equal(dl, ref["dlogits"].astype(np.float32))
+    for m_gpu, m_ref in zip(masks, ref["fwd"]["m"]):
+        np.testing.assert_array_equal(m_gpu.astype(bool), m_ref)
+    for g, r in zip(dws, ref["dW"]):
+        np.testing.assert_array_equal(g, r.astype(np.float32))
+    loss2, W_new, _ = P.gpu_train(net, xd, td, lr)
+    assert np.float32(loss2) == np.float32(ref["loss"])
+    for g, r in zip(W_new, ref["W_new"]):
+        np.testing.assert_array_equal(g, r.astype(np.float32))
+    net.close()
+
+
+# ------------------------------------------------------ workload parity ----
+
+def _workload_parity(torch_dev, name, steps_to_check=(0,)):
+    torch, dev = torch_dev
+    w = synth.WORKLOADS[name]
+    prec = w.precision
+    Ws = synth.workload_weights(w)
+    _announce(f"workload {name} dims={w.dims} B={w.batch} {prec}")
+    net = make_net(w.dims, w.batch, prec, Ws, dev)
+    x, t, _ = synth.workload_batch(w, 0)
+    xd, td = P.to_dev([x, t], dev)
+    # gradients, no update
+    loss, dws, dl, masks = P.gpu_grads(net, xd, td)
+    ref = P.oracle_step(x, t, Ws, w.lr, w.dims, prec, masks)
+    P.check_masks(ref, w.batch, w.dims, prec, name)
+    P.check_grads(loss, dws, dl, ref, prec, name)
+    # fused update from the same weights
+    loss2, W_new, masks2 = P.gpu_train(net, xd, td, w.lr)
+    ref2 = P.oracle_step(x, t, Ws, w.lr, w.dims, prec, masks2)
+    P.check_update(loss2, W_new, Ws, ref2, prec, name)
+    P.check_fused_update_matches_grads(W_new, Ws, dws, w.lr)
+    net.close()
+
+
+def test_parity_mnist_b32(torch_dev):
+    _workload_parity(torch_dev, "mnist_b32")
+
+
+def test_parity_mnist_b1024(torch_dev):
+    _workload_parity(torch_dev, "mnist_b1024")
+
+
+def test_parity_wide_f32(torch_dev):
+    _workload_parity(torch_dev, "wide_f32")
+
+
+def test_parity_wide_bf16(torch_dev):
+    _workload_parity(torch_dev, "wide_bf16")
+
+
+def test_parity_skinny_b8(torch_dev):
+    _workload_parity(torch_dev, "skinny_b8")
+
+
+# ------------------------------------------------- multi-step trajectories --
+
+def _oracle_trajectory(w, Ws, steps):
+    """Oracle states W_s (rounded to float32 after every step, so that each
+    one is a valid GPU input) and the oracle's loss at each step."""
+    states, losses = [], []
+    cur = [np.asarray(a, np.float32) for a in Ws]
+    for s in range(steps):
+        states.append(cur)
+        x, t, _ = synth.workload_batch(w, s)
+        r = mlp_oracle.train_step(x, t, cur, w.lr)
+        losses.append(r["loss"])
+        cur = [a.astype(np.float32) for a in r["W_new"]]
+    return states, losses
+
+
+@pytest.mark.parametrize("name,checked", [("mnist_b32", range(10)),
+                                          ("mnist_b1024", (0, 1, 49, 99))])
+def test_oracle_forced_steps(torch_dev, name, checked):
+    """Multi-step parity: at each checked step s the GPU starts from the
+    oracle's own (float32-rounded) state W_s and must reproduce the oracle's
+    step s at the strict gates."""
+    torch, dev = torch_dev
+    w = synth.WORKLOADS[name]
+    states, _ = _oracle_trajectory(w, synth.workload_weights(w), max(checked) + 1)
+    net = make_net(w.dims, w.batch, "f32", states[0], dev)
+    for s in checked:
+        _announce(f"{name} forced step {s}")
+        net.set_params(P.to_dev(states[s], dev))
+        x, t, _ = synth.workload_batch(w, s)
+        xd, td = P.to_dev([x, t], dev)
+        loss, W_new, masks = P.gpu_train(net, xd, td, w.lr)
+        ref = P.oracle_step(x, t, states[s], w.lr, w.dims, "f32", masks)
+        P.check_masks(ref, w.batch, w.dims, "f32", f"{name}@{s}")
+        P.check_update(loss, W_new, states[s], ref, "f32", f"{name}@{s}")
+    net.close()
+
+
+@pytest.mark.parametrize("name,steps,tol", [("mnist_b32", 10, 1e-3), ("mnist_b1024", 100, 1e-2)])
+def test_free_running_loss_curve(torch_dev, name, steps, tol):
+    """The GPU's own trajectory (its updated weights feed the next step)
+    tracks the oracle's loss curve.  Not bit-reproducible across
+    implementations, so the gate is a loose relative bound per step."""
+    torch, dev = torch_dev
+    w = synth.WORKLOADS[name]
+    Ws = synth.workload_weights(w)
+    _, ref_losses = _oracle_trajectory(w, Ws, steps)
+    net = make_net(w.dims, w.batch, "f32", Ws, dev)
+    batches = [P.to_dev(synth.workload_batch(w, s)[:2], dev) for s in range(steps)]
+    losses = [net.train_step(b[0], b[1], w.lr) for b in batches]
+    for s, (g, r) in enumerate(zip(losses, ref_losses)):
+        assert abs(g - r) <= tol * abs(r), f"step {s}: {g} vs {r}"
+    net.close()
+
+
+# --------------------------------------------------------- ragged / edges --
+
+EDGE_CASES = [
+    ((33, 70, 17, 10), 37, "f32"),
+    ((100, 31, 7), 5, "f32"),        # small batch, widths not multiples of 4
+    ((64, 260, 36), 12, "f32"),      # skinny kernels, ragged columns
+    ((1, 1, 1), 1, "f32"),           # one class: loss 0
+    ((5, 3), 3, "f32"),              # no hidden layer
+    ((128, 10), 300, "f32"),
+    ((784, 128, 10), 7, "f32"),
+    ((4100, 64, 8), 16, "f32"),      # skinny, many K splits
+    ((33, 70, 17, 10), 37, "bf16"),
+    ((100, 31, 7), 5, "bf16"),
+    ((72, 200, 1000), 48, "bf16"),
+]
+
+
+@pytest.mark.parametrize("dims,B,precision", EDGE_CASES)
+def test_edge_shapes(torch_dev, dims, B, precision):
+    torch, dev = torch_dev
+    _announce(f"edge dims={dims} B={B} {precision}")
+    Ws = synth.make_weights(dims, "glorot", seed=sum(dims) + B)
+    x, t, _ = synth.make_batch(B, dims[0], dims[-1], "normal", seed=B, step=len(dims))
+    lr = 0.05
+    net = make_net(dims, B, precision, Ws, dev)
+    xd, td = P.to_dev([x, t], dev)
+    loss, dws, dl, masks = P.gpu_grads(net, xd, td)
+    ref = P.oracle_step(x, t, Ws, lr, dims, precision, masks)
+    P.check_masks(ref, B, dims, precision, str(dims))
+    if dims[-1] == 1:
+        assert loss == 0.0 and np.all(dl == 0.0)
+    P.check_grads(loss, dws, dl, ref, precision, str(dims))
+    loss2, W_new, masks2 = P.gpu_train(net, xd, td, lr)
+    ref2 = P.oracle_step(x, t, Ws, lr, dims, precision, masks2)
+    P.check_update(loss2, W_new, Ws, ref2, precision, str(dims))
+    net.close()
+
+
+@pytest.mark.parametrize("dims,B,precision", [((784, 128, 10), 32, "f32"),
+                                              ((1024, 4096, 4096, 1000), 4096, "f32"),
+                                              ((1024, 4096, 4096, 1000), 4096, "bf16")])
+def test_zero_weights_loss_is_log_classes(torch_dev, dims, B, precision):
+    """P1 on the GPU: zero weights give loss = ln C, dlogits = (1/C - t)/B,
+    zero gradients, and an unchanged W after a step."""
+    torch, dev = torch_dev
+    _announce(f"zero weights dims={dims} B={B} {precision}")
+    Ws = [np.zeros((dims[l], dims[l + 1]), np.float32) for l in range(len(dims) - 1)]
+    x, t, _ = synth.make_batch(B, dims[0], dims[-1], "normal", seed=3)
+    net = make_net(dims, B, precision, Ws, dev)
+    xd, td = P.to_dev([x, t], dev)
+    loss, dws, dl, _ = P.gpu_grads(net, xd, td)
+    C = dims[-1]
+    assert abs(loss - math.log(C)) <= 1e-6 * math.log(C)
+    np.testing.assert_allclose(dl, (1.0 / C - t) / B, rtol=1e-6, atol=1e-12)
+    assert np.max(np.abs(dl.astype(np.float64).sum(1))) <= 2 * C * 2.0 ** -24 / B
+    for d in dws:
+        assert np.all(d == 0)
+    net.train_step(xd, td, 0.1)
+    for w in net.read_params():
+        assert torch.all(w == 0)
+    net.close()
+
+
+# -------------------------------------------------------------- invariants --
+
+@pytest.mark.parametrize("name", ["mnist_b1024", "wide_f32", "skinny_b8"])
+def test_determinism(torch_dev, name):
+    """P9: two steps from the same state are bitwise identical (fixed-order
+    reductions, integer tickets, no float atomics)."""
+    torch, dev = torch_dev
+    w = synth.WORKLOADS[name]
+    Ws = synth.workload_weights(w)
+    x, t, _ = synth.workload_batch(w, 0)
+    xd, td = P.to_dev([x, t], dev)
+    out = []
+    for rep in range(2):
+        _announce(f"determinism {name} rep {rep}")
+        net = make_net(w.dims, w.batch, w.precision, Ws, dev)
+        loss, dws, dl, _ = P.gpu_grads(net, xd, td)
+        loss2 = net.train_step(xd, td, w.lr)
+        W_new = [a.cpu().numpy() for a in net.read_params()]
+        out.append((loss, dws, dl, loss2, W_new))
+        net.close()
+    a, b = out
+    assert a[0] == b[0] and a[3] == b[3]
+    for u, v in zip(a[1] + [a[2]] + a[4], b[1] + [b[2]] + b[4]):
+        assert np.array_equal(u, v)
+
+
+def test_dlogits_rows_sum_to_zero(torch_dev):
+    """P2 on the GPU: row sums of dlogits vanish to float32 rounding."""
+    torch, dev = torch_dev
+    w = synth.WORKLOADS["wide_f32"]
+    dims, B = (256, 512, 1000), 512
+    Ws = synth.make_weights(dims, "kaiming", seed=4)
+    x, t, _ = synth.make_batch(B, dims[0], dims[-1], "normal", seed=5)
+    net = make_net(dims, B, "f32", Ws, dev)
+    _, _, dl, _ = P.gpu_grads(net, *P.to_dev([x, t], dev))
+    C = dims[-1]
+    assert np.max(np.abs(dl.astype(np.float64).sum(1))) <= 2 * C * 2.0 ** -24 / B * 4
+    del w
+    net.close()
+
+
+def test_softmax_shift_and_overflow(torch_dev):
+    """P4 on the GPU: logits of size ~1000 (large weights) give finite loss
+    and dlogits matching the oracle."""
+    torch, dev = torch_dev
+    dims, B = (16, 24, 10), 8
+    Ws = [a * 300 for a in synth.make_weights(dims, "glorot", seed=6)]
+    x, t, _ = synth.make_batch(B, dims[0], dims[-1], "normal", seed=7)
+    net = make_net(dims, B, "f32", Ws, dev)
+    loss, dws, dl, masks = P.gpu_grads(net, *P.to_dev([x, t], dev))
+    ref = P.oracle_step(x, t, Ws, 0.1, dims, "f32", masks)
+    assert np.isfinite(loss) and np.all(np.isfinite(dl))
+    P.check_grads(loss, dws, dl, ref, "f32", "overflow")
+    net.close()
+
+
+def test_dense_soft_labels(torch_dev):
+    """Labels are dense rows; non-one-hot rows follow the same definition."""
+    torch, dev = torch_dev
+    dims, B = (40, 52, 12), 20
+    Ws = synth.make_weights(dims, "glorot", seed=8)
+    x, _, _ = synth.make_batch(B, dims[0], dims[-1], "normal", seed=9)
+    t = np.random.default_rng(10).uniform(0, 1, (B, dims[-1])).astype(np.float32)
+    net = make_net(dims, B, "f32", Ws, dev)
+    loss, dws, dl, masks = P.gpu_grads(net, *P.to_dev([x, t], dev))
+    ref = P.oracle_step(x, t, Ws, 0.1, dims, "f32", masks)
+    P.check_grads(loss, dws, dl, ref, "f32", "soft labels")
+    net.close()
+
+
+# ------------------------------------------------------------ error paths --
+
+def test_errors_leave_state_unchanged(torch_dev):
+    from mlp_gemm_softmax_amd import binding
+    torch, dev = torch_dev
+    dims, B = (16, 8, 4), 4
+    Ws = synth.make_weights(dims, "glorot", seed=11)
+    net = binding.Mlp(dims, B, "f32", device=str(dev))
+    x, t, _ = synth.make_batch(B, dims[0], dims[-1], "normal", seed=12)
+    xd, td = P.to_dev([x, t], dev)
+    with pytest.raises(binding.MlpError) as e:       # weights never set
+        net.train_step(xd, td, 0.1)
+    assert e.value.status == binding.MLP_ERR_STATE
+    net.set_params(P.to_dev(Ws, dev))
+    for bad_lr in (float("nan"), float("inf")):
+        with pytest.raises(binding.MlpError) as e:
+            net.train_step(xd, td, bad_lr)
+        assert e.value.status == binding.MLP_ERR_ARG
+    with pytest.raises(binding.MlpError) as e:
+        net.read_state(binding.STATE_MASK, 0)
+    assert e.value.status == binding.MLP_ERR_ARG
+    lib = binding.lib()
+    misaligned = ctypes.c_void_p(xd.data_ptr() + 4)
+    assert lib.mlp_train_step(net._h, misaligned, ctypes_ptr(td), 0.1, None) == binding.MLP_ERR_ARG
+    for g, w in zip(net.read_params(), Ws):
+        np.testing.assert_array_equal(g.cpu().numpy(), w)
+    net.close()
+
+
+def ctypes_ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def test_profile_slots(torch_dev):
+    torch, dev = torch_dev
+    w = synth.WORKLOADS["mnist_b32"]
+    net = make_net(w.dims, w.batch, "f32", synth.workload_weights(w), dev)
+    xd, td = P.to_dev(synth.workload_batch(w)[:2], dev)
+    net.profile(True)
+    for _ in range(3):
+        net.train_step(xd, td, w.lr)
+    rows = net.profile_read()
+    assert len(rows) == 2 + 1 + 1 + 2
+    assert all(r["launches"] == 3 and r["total_ms"] > 0 for r in rows)
+    assert rows[0]["flops"] == 2 * 32 * 784 * 128
+    net.close()
