@@ -59,13 +59,45 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
                      : rem * (per + 1) + (xcd - rem) * per + slot;
 }
 
-// Last-arriving-workgroup pattern used by every cross-workgroup reduction:
-// each workgroup stores its partial result, executes __threadfence() (an
-// agent-scope release: dirty L2 lines are written back so the other XCDs can
-// see them), and takes an unsigned integer ticket with atomicAdd.  The
-// workgroup that draws the last ticket executes __threadfence() again (an
-// agent-scope acquire: stale L1/L2 lines are invalidated), reads every
-// partial with ordinary loads and adds them in a fixed order.  No
-// floating-point atomics are used anywhere.
+// Cross-workgroup reductions (split-K partials, row losses) use the
+// last-arriving-workgroup pattern without an L2-writeback fence:
+//   writer: store the partial with device-scope stores (sc1: acknowledged only
+//           once visible to every XCD), wait for the acknowledgements, then
+//           take an unsigned integer ticket with atomicAdd;
+//   reader: the workgroup that draws the last ticket reads every partial with
+//           device-scope loads (sc1: never served from a stale cache line) and
+//           adds them in a fixed order.
+// An agent-scope __threadfence() would write back the whole L2 of the XCD on
+// every workgroup, which serialises across the chip.  No floating-point
+// atomics are used anywhere.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_coherent(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until this thread's stores are acknowledged (and keep the compiler
+// from moving memory operations across the wait).
+__device__ __forceinline__ void wait_stores() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Every thread calls this after its coherent stores; returns true in all
+// threads of the workgroup that took the last of `expected` tickets, and
+// resets the counter for the next launch.
+__device__ __forceinline__ bool last_arrival(unsigned* ticket, unsigned expected, int* s_flag) {
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned old = atomicAdd(ticket, 1u);
+        const int last = old == expected - 1;
+        if (last) atomicExch(ticket, 0u);
+        *s_flag = last;
+    }
+    __syncthreads();
+    return *s_flag != 0;
+}
 
 }  // namespace mlp

@@ -29,7 +29,6 @@ template <int R, int VEC>
 struct KLoad {
     static constexpr int PER = R * kBK / (kThreads * VEC);
     static_assert(PER >= 1, "tile too small for the loader");
-    static constexpr int WORDS = VEC == 8 ? PER * 4 : (PER + 1) / 2;
     uint32_t v[VEC == 8 ? PER * 4 : PER];
 
     __device__ __forceinline__ void load(const bf16_t* __restrict__ g, int64_t ld, int r0,
@@ -120,7 +119,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int row, int col, 
 }
 
 template <class S, Layout LAY, int VEC, Epi EPI>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p) {
+__global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
     constexpr int BM = S::BM, BN = S::BN, FM = S::FM, FN = S::FN;
     __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * kLDK];
     __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * kLDK];
@@ -206,6 +205,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p) {
     const int col_w = n0 + wn * S::WN + (lane & 31);
 
     if (p.splits > 1) {
+        // Deterministic split-K (see the float32 kernel).
         float* part = p.partials + (int64_t)split * p.M * p.N;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -215,21 +215,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p) {
                 for (int r = 0; r < 16; ++r) {
                     const int row = row_w + i * 32 + 8 * (r >> 2) + (r & 3);
                     const int col = col_w + j * 32;
-                    if (row < p.M && col < p.N) part[(int64_t)row * p.N + col] = acc[i][j][r];
+                    if (row < p.M && col < p.N) store_coherent(part + (int64_t)row * p.N + col, acc[i][j][r]);
                 }
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) {
-            const unsigned old = atomicAdd(&p.tickets[tile], 1u);
-            const int last = old == (unsigned)(p.splits - 1);
-            if (last) atomicExch(&p.tickets[tile], 0u);
-            s_last = last;
-        }
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();   // acquire: the other splits' partials are visible
-        // Sum split by split (t = 0..S-1) so each element sees the same order;
-        // all loads of one split are independent and overlap.
+        if (!last_arrival(&p.tickets[tile], (unsigned)p.splits, &s_last)) return;
         float16v sum[FM][FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -248,7 +236,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmParams p) {
                         const int row = row_w + i * 32 + 8 * (r >> 2) + (r & 3);
                         const int col = col_w + j * 32;
                         float v = acc[i][j][r];
-                        if (t != split && row < p.M && col < p.N) v = q[(int64_t)row * p.N + col];
+                        if (t != split && row < p.M && col < p.N)
+                            v = load_coherent(q + (int64_t)row * p.N + col);
                         sum[i][j][r] += v;
                     }
         }

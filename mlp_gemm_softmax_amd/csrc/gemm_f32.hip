@@ -5,12 +5,15 @@
 // gfx950 matrix cores: v_mfma_f32_32x32x2f32, 64 flop/clk per SIMD.
 //
 // Workgroup: 256 threads = 4 wavefronts, tile BM x BN, K staged 32 at a time.
-// LDS holds both operand tiles k-contiguous ([row][k], row stride 36 floats,
-// so 8 consecutive rows of a 16-byte access fall on 8 disjoint 4-bank groups).
-// Each wave reads one float4 per MFMA operand: lanes 0-31 take k = 8c..8c+3,
-// lanes 32-63 take k = 8c+4..8c+7, and MFMA j (j = 0..3) multiplies component
-// j, so four MFMAs cover eight k.  Both operands use the same k map, which is
-// all the reduction needs.
+// Each operand tile keeps its global orientation in LDS, so global->LDS is a
+// straight 16-byte copy whichever way the operand is stored:
+//   k-contiguous operand (row r, k):  LDS [r][k], row stride 36 floats;
+//   r-contiguous operand (k, row r):  LDS [k][r], row stride R+4 floats.
+// For an MFMA both supply the same k map: over a chunk of 8 k, lanes 0-31
+// hold k = 8c..8c+3 and lanes 32-63 hold k = 8c+4..8c+7 of row lane%32, and
+// MFMA q (q = 0..3) takes the q-th of those four values.  A k-contiguous tile
+// delivers the four values in one 16-byte LDS read, an r-contiguous tile in
+// four 4-byte reads (consecutive lanes -> consecutive banks).
 #include "kernels.hpp"
 
 namespace mlp {
@@ -18,7 +21,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBK = 32;
-constexpr int kLDK = kBK + 4;
 
 template <int BM_, int BN_, int WM_, int WN_>
 struct Shape {
@@ -28,78 +30,74 @@ struct Shape {
     static_assert((BM / WM) * (BN / WN) == 4, "four waves per workgroup");
 };
 
-// Tile of an operand stored k-contiguous (global row r at g + r*ld).
-template <int R, int VEC>
-struct KLoad {
-    static constexpr int PER = R * kBK / (kThreads * VEC);
+// Operand tile of R rows x kBK k.  KC: stored k-contiguous (element (r,k) at
+// g + r*ld + k), else r-contiguous (at g + k*ld + r).  VEC: 4 = 16-byte global
+// loads (the contiguous extent and ld are multiples of 4), 1 = 4-byte loads.
+template <int R, bool KC, int VEC>
+struct Tile {
+    static constexpr int LD = KC ? kBK + 4 : R + 4;          // LDS row stride (floats)
+    static constexpr int ELEMS = KC ? R * LD : kBK * LD;     // LDS floats per stage
+    static constexpr int CONT = KC ? kBK : R;                // contiguous extent per line
+    static constexpr int PER = R * kBK / (kThreads * VEC);   // global accesses per thread
     static_assert(PER >= 1, "tile too small for the loader");
     float v[PER * VEC];
 
-    __device__ __forceinline__ void load(const float* __restrict__ g, int64_t ld, int r0,
-                                         int rmax, int k0, int kmax, int tid) {
+    // (line, offset) of access i: a line is a k-row (r-contiguous) or an r-row.
+    __device__ __forceinline__ static void where(int tid, int i, int& line, int& off) {
+        const int idx = tid + kThreads * i;
+        line = idx / (CONT / VEC);
+        off = (idx % (CONT / VEC)) * VEC;
+    }
+
+    __device__ __forceinline__ void load(const float* __restrict__ g, int64_t ld, int r0, int rmax,
+                                         int k0, int kmax, int tid) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int idx = tid + kThreads * i;
+            int line, off;
+            where(tid, i, line, off);
+            const int r = KC ? r0 + line : r0 + off;
+            const int k = KC ? k0 + off : k0 + line;
+            const bool ok = r < rmax && k < kmax;
+            const float* src = KC ? g + (int64_t)r * ld + k : g + (int64_t)k * ld + r;
             if constexpr (VEC == 4) {
-                const int row = idx / (kBK / 4), kq = idx % (kBK / 4);
-                const int r = r0 + row, k = k0 + 4 * kq;
                 float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (r < rmax && k < kmax)
-                    x = *reinterpret_cast<const float4*>(g + (int64_t)r * ld + k);
+                if (ok) x = *reinterpret_cast<const float4*>(src);
                 v[4 * i + 0] = x.x;
                 v[4 * i + 1] = x.y;
                 v[4 * i + 2] = x.z;
                 v[4 * i + 3] = x.w;
             } else {
-                const int row = idx / kBK, kk = idx % kBK;
-                const int r = r0 + row, k = k0 + kk;
-                v[i] = (r < rmax && k < kmax) ? g[(int64_t)r * ld + k] : 0.f;
+                v[i] = ok ? *src : 0.f;
             }
         }
     }
+
     __device__ __forceinline__ void store(float* s, int tid) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int idx = tid + kThreads * i;
-            if constexpr (VEC == 4) {
-                const int row = idx / (kBK / 4), kq = idx % (kBK / 4);
-                *reinterpret_cast<float4*>(s + row * kLDK + 4 * kq) =
+            int line, off;
+            where(tid, i, line, off);
+            if constexpr (VEC == 4)
+                *reinterpret_cast<float4*>(s + line * LD + off) =
                     make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-            } else {
-                const int row = idx / kBK, kk = idx % kBK;
-                s[row * kLDK + kk] = v[i];
-            }
+            else
+                s[line * LD + off] = v[i];
         }
     }
-};
 
-// Tile of an operand stored row-contiguous along r (element (r,k) at
-// g + k*ld + r).  Consecutive lanes read consecutive r (coalesced), each lane
-// gathers KPT consecutive k and writes them as float4s along k, so the
-// transpose into the k-contiguous LDS layout costs no extra pass.
-template <int R>
-struct MNLoad {
-    static constexpr int KG = kThreads / R;
-    static constexpr int KPT = kBK / KG;
-    static_assert(KPT % 4 == 0, "k per thread must fill float4s");
-    float v[KPT];
-
-    __device__ __forceinline__ void load(const float* __restrict__ g, int64_t ld, int r0,
-                                         int rmax, int k0, int kmax, int tid) {
-        const int r = r0 + tid % R, grp = tid / R;
-        const bool rok = r < rmax;
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int k = k0 + grp * KPT + i;
-            v[i] = (rok && k < kmax) ? g[(int64_t)k * ld + r] : 0.f;
+    // The four k-values of MFMA chunk c for tile row `row`, lane half h.
+    __device__ __forceinline__ static float4v read(const float* s, int row, int c, int h) {
+        const int k = 8 * c + 4 * h;
+        if constexpr (KC) {
+            return *reinterpret_cast<const float4v*>(s + row * LD + k);
+        } else {
+            float4v r;
+            r[0] = s[(k + 0) * LD + row];
+            r[1] = s[(k + 1) * LD + row];
+            r[2] = s[(k + 2) * LD + row];
+            r[3] = s[(k + 3) * LD + row];
+            return r;
         }
-    }
-    __device__ __forceinline__ void store(float* s, int tid) const {
-        const int r = tid % R, grp = tid / R;
-#pragma unroll
-        for (int q = 0; q < KPT / 4; ++q)
-            *reinterpret_cast<float4*>(s + r * kLDK + grp * KPT + 4 * q) =
-                make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
     }
 };
 
@@ -124,10 +122,12 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int row, int col, 
 }
 
 template <class S, Layout LAY, int VEC, Epi EPI>
-__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
+__global__ __launch_bounds__(kThreads, 2) void gemm_f32_kernel(GemmParams p) {
     constexpr int BM = S::BM, BN = S::BN, FM = S::FM, FN = S::FN;
-    __shared__ __attribute__((aligned(16))) float sA[2][BM * kLDK];
-    __shared__ __attribute__((aligned(16))) float sB[2][BN * kLDK];
+    using TA = Tile<BM, LAY != Layout::TN, VEC>;
+    using TB = Tile<BN, LAY == Layout::NT, VEC>;
+    __shared__ __attribute__((aligned(16))) float sA[2][TA::ELEMS];
+    __shared__ __attribute__((aligned(16))) float sB[2][TB::ELEMS];
     __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -156,11 +156,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
 
     const float* A = static_cast<const float*>(p.A);
     const float* B = static_cast<const float*>(p.B);
-
-    using ALoad = typename std::conditional<LAY == Layout::TN, MNLoad<BM>, KLoad<BM, VEC>>::type;
-    using BLoad = typename std::conditional<LAY == Layout::NT, KLoad<BN, VEC>, MNLoad<BN>>::type;
-    ALoad la;
-    BLoad lb;
+    TA la;
+    TB lb;
 
     float16v acc[FM][FN];
 #pragma unroll
@@ -169,6 +166,10 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int arow = wm * S::WM + (lane & 31);
+    const int brow = wn * S::WN + (lane & 31);
+    const int half = lane >> 5;
 
     if (nk > 0) {
         la.load(A, p.lda, m0, p.M, kbeg, kend, tid);
@@ -183,17 +184,13 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
                 la.load(A, p.lda, m0, p.M, kbeg + (kt + 1) * kBK, kend, tid);
                 lb.load(B, p.ldb, n0, p.N, kbeg + (kt + 1) * kBK, kend, tid);
             }
-            const float* a_base = sA[cur] + (wm * S::WM + (lane & 31)) * kLDK + 4 * (lane >> 5);
-            const float* b_base = sB[cur] + (wn * S::WN + (lane & 31)) * kLDK + 4 * (lane >> 5);
 #pragma unroll
             for (int c = 0; c < kBK / 8; ++c) {
                 float4v a[FM], b[FN];
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    a[i] = *reinterpret_cast<const float4v*>(a_base + i * 32 * kLDK + 8 * c);
+                for (int i = 0; i < FM; ++i) a[i] = TA::read(sA[cur], arow + 32 * i, c, half);
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    b[j] = *reinterpret_cast<const float4v*>(b_base + j * 32 * kLDK + 8 * c);
+                for (int j = 0; j < FN; ++j) b[j] = TB::read(sB[cur], brow + 32 * j, c, half);
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -213,13 +210,13 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
 
     // Accumulator element r of block (i, j) sits at
     //   row = 8*(r/4) + 4*(lane/32) + r%4,  col = lane%32   within the block.
-    const int row_w = m0 + wm * S::WM + 4 * (lane >> 5);
+    const int row_w = m0 + wm * S::WM + 4 * half;
     const int col_w = n0 + wn * S::WN + (lane & 31);
 
     if (p.splits > 1) {
         // Deterministic split-K: every split stores its partial tile; the
         // workgroup that takes the last ticket sums the partials in split
-        // order 0..S-1 and applies the epilogue.  Integer ticket only.
+        // order 0..S-1 and applies the epilogue.
         float* part = p.partials + (int64_t)split * p.M * p.N;
 #pragma unroll
         for (int i = 0; i < FM; ++i)
@@ -229,47 +226,31 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmParams p) {
                 for (int r = 0; r < 16; ++r) {
                     const int row = row_w + i * 32 + 8 * (r >> 2) + (r & 3);
                     const int col = col_w + j * 32;
-                    if (row < p.M && col < p.N) part[(int64_t)row * p.N + col] = acc[i][j][r];
+                    if (row < p.M && col < p.N) store_coherent(part + (int64_t)row * p.N + col, acc[i][j][r]);
                 }
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) {
-            const unsigned old = atomicAdd(&p.tickets[tile], 1u);
-            const int last = old == (unsigned)(p.splits - 1);
-            if (last) atomicExch(&p.tickets[tile], 0u);
-            s_last = last;
-        }
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();   // acquire: the other splits' partials are visible
-        // Sum split by split (t = 0..S-1) so each element sees the same order;
-        // all loads of one split are independent and overlap.
-        float16v sum[FM][FN];
+        if (!last_arrival(&p.tickets[tile], (unsigned)p.splits, &s_last)) return;
+        // One 32x32 block at a time: its S x 16 loads are independent.
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
+            for (int j = 0; j < FN; ++j) {
+                float16v sum;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sum[i][j][r] = 0.f;
-        for (int t = 0; t < p.splits; ++t) {
-            const float* q = p.partials + (int64_t)t * p.M * p.N;
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
+                for (int r = 0; r < 16; ++r) sum[r] = 0.f;
+                for (int t = 0; t < p.splits; ++t) {
+                    const float* q = p.partials + (int64_t)t * p.M * p.N;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int row = row_w + i * 32 + 8 * (r >> 2) + (r & 3);
                         const int col = col_w + j * 32;
                         float v = acc[i][j][r];
-                        if (t != split && row < p.M && col < p.N) v = q[(int64_t)row * p.N + col];
-                        sum[i][j][r] += v;
+                        if (t != split && row < p.M && col < p.N)
+                            v = load_coherent(q + (int64_t)row * p.N + col);
+                        sum[r] += v;
                     }
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = sum[i][j];
+                }
+                acc[i][j] = sum;
+            }
     }
 
 #pragma unroll
@@ -290,29 +271,24 @@ hipError_t go(const GemmParams& p, int grid, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <class S, Layout LAY, Epi EPI>
+hipError_t go_vec(const GemmLaunch& L, const GemmParams& p, hipStream_t st) {
+    return L.vec == 4 ? go<S, LAY, 4, EPI>(p, L.grid, st) : go<S, LAY, 1, EPI>(p, L.grid, st);
+}
+
 template <class S>
 hipError_t dispatch_shape(const GemmLaunch& L, const GemmParams& p, hipStream_t st) {
-    const bool v4 = L.vec == 4;
     switch (L.layout) {
     case Layout::NN:
-        if (L.epi == Epi::ReluMask)
-            return v4 ? go<S, Layout::NN, 4, Epi::ReluMask>(p, L.grid, st)
-                      : go<S, Layout::NN, 1, Epi::ReluMask>(p, L.grid, st);
-        if (L.epi == Epi::Store)
-            return v4 ? go<S, Layout::NN, 4, Epi::Store>(p, L.grid, st)
-                      : go<S, Layout::NN, 1, Epi::Store>(p, L.grid, st);
+        if (L.epi == Epi::ReluMask) return go_vec<S, Layout::NN, Epi::ReluMask>(L, p, st);
+        if (L.epi == Epi::Store) return go_vec<S, Layout::NN, Epi::Store>(L, p, st);
         break;
     case Layout::NT:
-        if (L.epi == Epi::MaskMul)
-            return v4 ? go<S, Layout::NT, 4, Epi::MaskMul>(p, L.grid, st)
-                      : go<S, Layout::NT, 1, Epi::MaskMul>(p, L.grid, st);
-        if (L.epi == Epi::Store)
-            return v4 ? go<S, Layout::NT, 4, Epi::Store>(p, L.grid, st)
-                      : go<S, Layout::NT, 1, Epi::Store>(p, L.grid, st);
+        if (L.epi == Epi::MaskMul) return go_vec<S, Layout::NT, Epi::MaskMul>(L, p, st);
         break;
     case Layout::TN:
-        if (L.epi == Epi::Sgd) return go<S, Layout::TN, 1, Epi::Sgd>(p, L.grid, st);
-        if (L.epi == Epi::Grad) return go<S, Layout::TN, 1, Epi::Grad>(p, L.grid, st);
+        if (L.epi == Epi::Sgd) return go_vec<S, Layout::TN, Epi::Sgd>(L, p, st);
+        if (L.epi == Epi::Grad) return go_vec<S, Layout::TN, Epi::Grad>(L, p, st);
         break;
     }
     return hipErrorInvalidValue;

@@ -76,6 +76,7 @@ struct SkinnyLaunch {
     int waves;       // waves per workgroup
 };
 hipError_t launch_skinny(const SkinnyLaunch& L, const SkinnyParams& p, hipStream_t s);
+int skinny_tn_rows();   // rows of W per dW+SGD workgroup
 
 // ---- softmax cross-entropy -------------------------------------------------
 struct XentParams {

@@ -168,20 +168,21 @@ GemmPlan plan_gemm(int M, int N, int K, bool bf16, bool kvec_ok) {
 }
 
 SkinnyPlan plan_skinny_nn(int N, int K, int B) {
+    (void)B;
     SkinnyPlan s;
-    const int ncb = (N + 255) / 256;
-    // waves of a workgroup split its K chunk; their partial columns meet in
-    // LDS ((waves-1) * B * 1 KiB), kept under 64 KiB
-    s.waves = B <= 8 ? 8 : 4;
-    const int target = 512;
-    int sp = std::max(1, std::min((target + ncb - 1) / ncb, K / 64));
+    // 64 output columns per workgroup of 16 waves; K splits only while the
+    // grid still fits one workgroup per CU (a partial second round of
+    // workgroups would double the kernel time).
+    const int ncg = (N + 63) / 64;
+    s.waves = 16;
+    int sp = std::max(1, std::min(256 / ncg, K / 256));
     int kchunk = (K + sp - 1) / sp;
-    kchunk = (kchunk + 3) / 4 * 4;
+    kchunk = (kchunk + 15) / 16 * 16;
     sp = (K + kchunk - 1) / kchunk;
     s.splits = sp;
-    s.kchunk = kchunk;
-    s.grid = ncb * sp;
-    s.tickets = ncb;
+    s.kchunk = sp > 1 ? kchunk : K;
+    s.grid = ncg * sp;
+    s.tickets = ncg;
     return s;
 }
 
@@ -504,17 +505,20 @@ size_t plan_and_carve(mlp_ctx* c, char* base) {
                 max_partial = std::max(max_partial, (size_t)c->sfwd[l].splits * B * dout);
                 max_tickets = std::max(max_tickets, (size_t)c->sfwd[l].tickets);
             }
-            c->sdx[l].grid = (din + 15) / 16;
-            c->sdw[l].grid = ((dout + 1023) / 1024) * ((din + 15) / 16);
+            c->sdx[l].grid = (din + 31) / 32;
+            c->sdw[l].grid = ((dout + 1023) / 1024) * ((din + skinny_tn_rows() - 1) / skinny_tn_rows());
             continue;
         }
         const int vq = c->bf16 ? 8 : 4;
-        // forward NN: A = a_l [B][din] (k-contiguous, K = din)
-        c->fwd[l] = plan_gemm(B, dout, din, c->bf16, din % vq == 0);
+        // 16-byte loads need the layer widths (every leading dimension and
+        // contiguous run of the three products) to be multiples of the vector.
+        const bool wide = din % vq == 0 && dout % vq == 0;
+        // forward NN: A = a_l [B][din] (k-contiguous, K = din), B = W [din][dout]
+        c->fwd[l] = plan_gemm(B, dout, din, c->bf16, wide);
         // dX NT: A = G [B][dout], B = W [din][dout] (both k-contiguous, K = dout)
-        c->dx[l] = plan_gemm(B, din, dout, c->bf16, dout % vq == 0);
-        // dW TN: M = din, N = dout, K = B
-        c->dw[l] = plan_gemm(din, dout, B, c->bf16, true);
+        c->dx[l] = plan_gemm(B, din, dout, c->bf16, wide);
+        // dW TN: A = a_l [B][din], B = G [B][dout]: M = din, N = dout, K = B
+        c->dw[l] = plan_gemm(din, dout, B, c->bf16, wide);
         for (const GemmPlan* g : {&c->fwd[l], &c->dx[l], &c->dw[l]}) {
             if (g->splits > 1) {
                 int bm, bn;

@@ -1,133 +1,137 @@
 // Skinny-batch (B <= 16) float32 kernels.  With a handful of rows every
-// product of the step is a pass over a weight matrix, so these kernels are
+// product of the step is one pass over a weight matrix, so these kernels are
 // shaped for HBM streaming rather than for the matrix cores' peak:
 //
-//   skinny_nn  out[b][n] = sum_k x[b][k] W[k][n]          forward, W row-streamed
-//   skinny_nt  out[b][k] = mask[b][k] * sum_n G[b][n] W[k][n]   dX (MFMA 16x16x4)
-//   skinny_tn  W[k][n]  -= lr * sum_b a[b][k] G[b][n]     dW + SGD, one read+write of W
+//   skinny_nn  out[b][n] = sum_k x[b][k] W[k][n]               forward
+//   skinny_nt  out[b][k] = mask[b][k] * sum_n G[b][n] W[k][n]   dX
+//   skinny_tn  W[k][n]  -= lr * sum_b a[b][k] G[b][n]          dW + SGD
 //
-// All reductions have a fixed order: k-splits inside a workgroup are summed
-// through LDS in wave order, splits across workgroups through partial buffers
-// that the last workgroup (integer ticket) adds up in split order.
-// Requires every width and K to be a multiple of 4 (float4 rows).
+// skinny_nn and skinny_nt reduce inside v_mfma_f32_16x16x4f32 (the batch is
+// the MFMA's 16-wide M or N side, rows >= B are zero), so every 16-byte load
+// of W feeds four MFMAs and no cross-lane reduction is spent on K.  skinny_tn
+// is a rank-B update streamed row by row: W is read once and written once.
+// All reductions have a fixed order: the waves of a workgroup meet in LDS in
+// wave order, and K splits across workgroups go through partial buffers that
+// the last workgroup (integer ticket) adds in split order.
+// Every width and K must be a multiple of 4 (float4 rows).
 #include "kernels.hpp"
 
 namespace mlp {
 namespace {
 
-constexpr int kCols = 4 * kWave;   // columns per wave in the row-streaming kernels
+__device__ __forceinline__ float4v ld4(const float* p) { return *reinterpret_cast<const float4v*>(p); }
 
 // ---------------------------------------------------------------------------
-// Forward: each lane owns 4 consecutive output columns for all batch rows;
-// the waves of a workgroup take interleaved groups of 4 rows of W from the
-// workgroup's K chunk; grid = column blocks x K splits.
-template <int MB, int NW, Epi EPI>
+// Forward.  A workgroup of NW waves owns 64 output columns n0..n0+63 and one
+// K chunk; wave w takes the w-th contiguous slice of the chunk, 16 rows at a
+// time.  Inside a 16-row block starting at k, MFMA step i (0..3) and k-lane
+// group g (0..3) stand for row k + 4g + i, so lane (j = lane%16, g) loads
+// W[k+4g+i][n0+4j .. n0+4j+3] for step i, and x[m = lane%16][k+4g .. k+4g+3]
+// once for the block.  MFMA q (0..3) of step i multiplies component q of the
+// W row: output column n0 + 4j + q.
+template <int NW, Epi EPI>
 __global__ __launch_bounds__(NW * kWave) void skinny_nn(SkinnyParams p) {
-    extern __shared__ float4 red[];   // [NW-1][MB][kWave] partial columns
+    __shared__ float4v red[NW - 1][4][kWave];
     __shared__ int s_last;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int ncb = (p.N + kCols - 1) / kCols;
-    const int id = blockIdx.x;
-    const int cb = id % ncb, split = id / ncb;
-    const int n = cb * kCols + 4 * lane;
+    const int j = lane & 15, g = lane >> 4;
+    const int ncg = (p.N + 63) / 64;
+    const int cg = blockIdx.x % ncg, split = blockIdx.x / ncg;
+    const int n = cg * 64 + 4 * j;
     const bool nok = n < p.N;
+    const bool mok = j < p.MB;
     const int kbeg = split * p.kchunk;
     const int kend = min(p.K, kbeg + p.kchunk);
+    // this wave's slice of the chunk, in whole 16-row blocks
+    const int blocks = (kend - kbeg + 15) / 16;
+    const int per = (blocks + NW - 1) / NW;
+    const int kw0 = kbeg + wave * per * 16;
+    const int kw1 = min(kend, kw0 + per * 16);
 
-    float4 acc[MB];
+    float4v acc[4];
 #pragma unroll
-    for (int b = 0; b < MB; ++b) acc[b] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q = 0; q < 4; ++q) acc[q] = {0.f, 0.f, 0.f, 0.f};
 
-    const float* __restrict__ W = p.B;
-    const float* __restrict__ X = p.A;
-    for (int k = kbeg + 4 * wave; k < kend; k += 4 * NW) {
-        float4 w[4];
+    const float* __restrict__ W = p.B + n;
+    const float* __restrict__ X = p.A + (int64_t)j * p.K;
+    for (int k = kw0; k < kw1; k += 16) {
+        const int kr = k + 4 * g;              // this lane group's 4 rows
+        float4v w[4];
+        float4v xv = {0.f, 0.f, 0.f, 0.f};
+        const bool rok = kr < kw1;             // K is a multiple of 4
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            w[r] = nok ? *reinterpret_cast<const float4*>(W + (int64_t)(k + r) * p.N + n)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int b = 0; b < MB; ++b) {
-            if (b < p.MB) {
-                const float4 xv = *reinterpret_cast<const float4*>(X + (int64_t)b * p.K + k);
-                acc[b].x += xv.x * w[0].x; acc[b].y += xv.x * w[0].y;
-                acc[b].z += xv.x * w[0].z; acc[b].w += xv.x * w[0].w;
-                acc[b].x += xv.y * w[1].x; acc[b].y += xv.y * w[1].y;
-                acc[b].z += xv.y * w[1].z; acc[b].w += xv.y * w[1].w;
-                acc[b].x += xv.z * w[2].x; acc[b].y += xv.z * w[2].y;
-                acc[b].z += xv.z * w[2].z; acc[b].w += xv.z * w[2].w;
-                acc[b].x += xv.w * w[3].x; acc[b].y += xv.w * w[3].y;
-                acc[b].z += xv.w * w[3].z; acc[b].w += xv.w * w[3].w;
-            }
+        for (int i = 0; i < 4; ++i) {
+            w[i] = {0.f, 0.f, 0.f, 0.f};
+            if (rok && nok) w[i] = ld4(W + (int64_t)(kr + i) * p.N);
         }
+        if (rok && mok) xv = ld4(X + kr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[i], w[i][q], acc[q], 0, 0, 0);
     }
 
-    // Sum the waves' partial columns in wave order 0..NW-1.
+    // acc[q][r] = out[m = 4g + r][n0 + 4j + q]; sum the waves in order 0..NW-1.
     if (wave > 0) {
 #pragma unroll
-        for (int b = 0; b < MB; ++b) red[((wave - 1) * MB + b) * kWave + lane] = acc[b];
+        for (int q = 0; q < 4; ++q) red[wave - 1][q][lane] = acc[q];
     }
     __syncthreads();
-    if (wave == 0) {
-        for (int w = 1; w < NW; ++w)
+    if (wave != 0) {
+        if (p.splits == 1) return;
+    } else {
+        for (int w = 0; w < NW - 1; ++w)
 #pragma unroll
-            for (int b = 0; b < MB; ++b) {
-                const float4 o = red[((w - 1) * MB + b) * kWave + lane];
-                acc[b].x += o.x; acc[b].y += o.y; acc[b].z += o.z; acc[b].w += o.w;
-            }
+            for (int q = 0; q < 4; ++q) acc[q] += red[w][q][lane];
     }
 
     if (p.splits > 1) {
         if (wave == 0 && nok) {
 #pragma unroll
-            for (int b = 0; b < MB; ++b)
-                if (b < p.MB)
-                    *reinterpret_cast<float4*>(p.partials + ((int64_t)split * p.MB + b) * p.N + n) = acc[b];
-        }
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const unsigned old = atomicAdd(&p.tickets[cb], 1u);
-            const int last = old == (unsigned)(p.splits - 1);
-            if (last) atomicExch(&p.tickets[cb], 0u);
-            s_last = last;
-        }
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();
-        // acquire done; add the splits in order t = 0..S-1
-        if (wave == 0 && nok) {
-            float4 sum[MB];
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * g + r;
+                if (m < p.MB) {
+                    float* dst = p.partials + ((int64_t)split * p.MB + m) * p.N + n;
 #pragma unroll
-            for (int b = 0; b < MB; ++b) sum[b] = make_float4(0.f, 0.f, 0.f, 0.f);
-            for (int t = 0; t < p.splits; ++t) {
-#pragma unroll
-                for (int b = 0; b < MB; ++b) {
-                    if (b < p.MB) {
-                        const float4 o = t == split ? acc[b]
-                            : *reinterpret_cast<const float4*>(p.partials + ((int64_t)t * p.MB + b) * p.N + n);
-                        sum[b].x += o.x; sum[b].y += o.y; sum[b].z += o.z; sum[b].w += o.w;
-                    }
+                    for (int q = 0; q < 4; ++q) store_coherent(dst + q, acc[q][r]);
                 }
             }
-#pragma unroll
-            for (int b = 0; b < MB; ++b) acc[b] = sum[b];
         }
+        if (!last_arrival(&p.tickets[cg], (unsigned)p.splits, &s_last)) return;
+        if (wave != 0) return;
+        float4v sum[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum[q] = {0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < p.splits; ++t) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * g + r;
+                const bool ok = m < p.MB && nok;
+                const float* src = p.partials + ((int64_t)t * p.MB + m) * p.N + n;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    sum[q][r] += (t == split || !ok) ? acc[q][r] : load_coherent(src + q);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = sum[q];
     }
 
-    if (wave == 0 && nok) {
+    if (nok) {
 #pragma unroll
-        for (int b = 0; b < MB; ++b) {
-            if (b >= p.MB) break;
-            float4 v = acc[b];
-            const int64_t o = (int64_t)b * p.N + n;
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * g + r;
+            if (m >= p.MB) continue;
+            const int64_t o = (int64_t)m * p.N + n;
+            float4 v = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
             if constexpr (EPI == Epi::ReluMask) {
-                uchar4 m;
-                m.x = v.x > 0.f; m.y = v.y > 0.f; m.z = v.z > 0.f; m.w = v.w > 0.f;
-                v.x = m.x ? v.x : 0.f; v.y = m.y ? v.y : 0.f;
-                v.z = m.z ? v.z : 0.f; v.w = m.w ? v.w : 0.f;
-                *reinterpret_cast<uchar4*>(p.mask + o) = m;
+                uchar4 mk;
+                mk.x = v.x > 0.f; mk.y = v.y > 0.f; mk.z = v.z > 0.f; mk.w = v.w > 0.f;
+                v.x = mk.x ? v.x : 0.f; v.y = mk.y ? v.y : 0.f;
+                v.z = mk.z ? v.z : 0.f; v.w = mk.w ? v.w : 0.f;
+                *reinterpret_cast<uchar4*>(p.mask + o) = mk;
             }
             *reinterpret_cast<float4*>(p.C + o) = v;
         }
@@ -136,52 +140,69 @@ __global__ __launch_bounds__(NW * kWave) void skinny_nn(SkinnyParams p) {
 
 // ---------------------------------------------------------------------------
 // dX: out[b][k] = mask[b][k] * sum_n G[b][n] W[k][n], W stored [Kout][N].
-// v_mfma_f32_16x16x4f32 with A = 16 rows of W and B = G^T (16 batch columns,
-// the ones >= B zero): lane l supplies W[k0 + l%16][n + 4(l/16) + q] and
-// G[l%16][n + 4(l/16) + q] to MFMA q, so one float4 of each feeds four MFMAs
-// and the reduction over n happens inside the matrix core.  A workgroup of
-// 4 waves covers 16 rows of W; wave w takes the w-th quarter of n.
-__global__ __launch_bounds__(256) void skinny_nt(SkinnyParams p) {
-    __shared__ float4 red[3][kWave];
+// A workgroup of NW waves covers RG*16 rows of W; wave w takes the w-th slice
+// of n.  MFMA: A = 16 rows of W, B = G^T (16 batch columns, zero past B);
+// lane (i = lane%16, g) supplies W[k0 + i][c + q] and G[i][c + q], with
+// c = n + 4g, to MFMA q, so one float4 of each feeds four MFMAs.
+template <int NW, int RG>
+__global__ __launch_bounds__(NW * kWave) void skinny_nt(SkinnyParams p) {
+    __shared__ float4v red[NW - 1][RG][kWave];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int k0 = blockIdx.x * 16;
+    const int k0 = blockIdx.x * 16 * RG;
     const int i = lane & 15, g = lane >> 4;
-    const int krow = k0 + i;
-    const bool rok = krow < p.K;
     const bool bok = i < p.MB;
-    // quarter of the n range, in multiples of 16
-    const int nq = ((p.N + 63) / 64) * 16;
+    const int nq = ((p.N + 16 * NW - 1) / (16 * NW)) * 16;   // slice, multiple of 16
     const int nbeg = wave * nq;
     const int nend = min(p.N, nbeg + nq);
 
-    float4v acc = {0.f, 0.f, 0.f, 0.f};
-    const float* __restrict__ Wr = p.A + (int64_t)krow * p.N;
+    float4v acc[RG];
+    const float* __restrict__ Wr[RG];
+    bool rok[RG];
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+        acc[r] = {0.f, 0.f, 0.f, 0.f};
+        const int krow = k0 + 16 * r + i;
+        rok[r] = krow < p.K;
+        Wr[r] = p.A + (int64_t)krow * p.N;
+    }
     const float* __restrict__ Gr = p.B + (int64_t)i * p.N;
+#pragma unroll 4
     for (int n = nbeg; n < nend; n += 16) {
         const int c = n + 4 * g;
-        float4v w = {0.f, 0.f, 0.f, 0.f}, gv = {0.f, 0.f, 0.f, 0.f};
-        if (c < nend) {
-            if (rok) w = *reinterpret_cast<const float4v*>(Wr + c);
-            if (bok) gv = *reinterpret_cast<const float4v*>(Gr + c);
+        const bool cok = c < nend;             // N is a multiple of 4
+        float4v gv = {0.f, 0.f, 0.f, 0.f};
+        if (cok && bok) gv = ld4(Gr + c);
+        float4v w[RG];
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            w[r] = {0.f, 0.f, 0.f, 0.f};
+            if (cok && rok[r]) w[r] = ld4(Wr[r] + c);
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(w[q], gv[q], acc, 0, 0, 0);
+        for (int r = 0; r < RG; ++r)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(w[r][q], gv[q], acc[r], 0, 0, 0);
     }
-    if (wave > 0) red[wave - 1][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    if (wave > 0) {
+#pragma unroll
+        for (int r = 0; r < RG; ++r) red[wave - 1][r][lane] = acc[r];
+    }
     __syncthreads();
     if (wave != 0) return;
+    for (int w = 0; w < NW - 1; ++w)
 #pragma unroll
-    for (int w = 0; w < 3; ++w) {
-        const float4 o = red[w][lane];
-        acc[0] += o.x; acc[1] += o.y; acc[2] += o.z; acc[3] += o.w;
-    }
-    // acc[r] = out[b = lane%16][k = k0 + 4*(lane/16) + r]
+        for (int r = 0; r < RG; ++r) acc[r] += red[w][r][lane];
+    // acc[r][e] = out[b = lane%16][k = k0 + 16r + 4*(lane/16) + e]
     const int b = lane & 15;
-    const int k = k0 + 4 * (lane >> 4);
-    if (b < p.MB && k < p.K) {
+    if (b >= p.MB) return;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+        const int k = k0 + 16 * r + 4 * g;
+        if (k >= p.K) continue;
         const int64_t o = (int64_t)b * p.K + k;
-        float4 v = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        float4 v = make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
         if (p.mask) {
             const uchar4 m = *reinterpret_cast<const uchar4*>(p.mask + o);
             v.x = m.x ? v.x : 0.f; v.y = m.y ? v.y : 0.f;
@@ -193,10 +214,12 @@ __global__ __launch_bounds__(256) void skinny_nt(SkinnyParams p) {
 
 // ---------------------------------------------------------------------------
 // dW + SGD: W[k][n] -= lr * sum_b a[b][k] G[b][n] (or store the gradient).
-// Each lane keeps G[0..B)[n..n+3] in registers and walks ROWS rows of W, so W
-// is read once and written once.  The per-row a[b][k] are staged in LDS.
+// Each lane keeps G[0..B)[n..n+3] in registers and walks ROWS rows of W in
+// chunks of 8 (the next chunk's loads are issued before the current chunk is
+// updated); the per-row a[b][k] come from LDS.
 template <int MB, int ROWS, Epi EPI>
 __global__ __launch_bounds__(256) void skinny_tn(SkinnyParams p) {
+    constexpr int CH = 8;
     __shared__ float sa[ROWS][MB];
     const int ncb = (p.N + 4 * 256 - 1) / (4 * 256);
     const int cb = blockIdx.x % ncb, rb = blockIdx.x / ncb;
@@ -208,78 +231,80 @@ __global__ __launch_bounds__(256) void skinny_tn(SkinnyParams p) {
     }
     __syncthreads();
     if (n >= p.N) return;
-    float4 gv[MB];
+    float4v gv[MB];
 #pragma unroll
-    for (int b = 0; b < MB; ++b)
-        gv[b] = b < p.MB ? *reinterpret_cast<const float4*>(p.B + (int64_t)b * p.N + n)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
-    const int rows = min(ROWS, p.K - k0);
-    float4 w[ROWS];
-    if constexpr (EPI == Epi::Sgd) {
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r)
-            if (r < rows) w[r] = *reinterpret_cast<const float4*>(p.C + (int64_t)(k0 + r) * p.N + n);
+    for (int b = 0; b < MB; ++b) {
+        gv[b] = {0.f, 0.f, 0.f, 0.f};
+        if (b < p.MB) gv[b] = ld4(p.B + (int64_t)b * p.N + n);
     }
+    const int rows = min(ROWS, p.K - k0);
+    float* base = p.C + (int64_t)k0 * p.N + n;
+    float4v w[2][CH];
+    auto load_chunk = [&](int buf, int c0) {
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-        if (r >= rows) break;
-        float4 d = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int r = 0; r < CH; ++r)
+            if (c0 + r < rows) w[buf][r] = __builtin_nontemporal_load(
+                reinterpret_cast<const float4v*>(base + (int64_t)(c0 + r) * p.N));
+    };
+    if constexpr (EPI == Epi::Sgd) load_chunk(0, 0);
 #pragma unroll
-        for (int b = 0; b < MB; ++b) {
-            const float a = sa[r][b];
-            d.x += a * gv[b].x; d.y += a * gv[b].y; d.z += a * gv[b].z; d.w += a * gv[b].w;
-        }
-        const int64_t o = (int64_t)(k0 + r) * p.N + n;
+    for (int c0 = 0, buf = 0; c0 < ROWS; c0 += CH, buf ^= 1) {
+        if (c0 >= rows) break;
         if constexpr (EPI == Epi::Sgd) {
-            float4 v = w[r];
-            v.x -= p.lr * d.x; v.y -= p.lr * d.y; v.z -= p.lr * d.z; v.w -= p.lr * d.w;
-            *reinterpret_cast<float4*>(p.C + o) = v;
-        } else {
-            *reinterpret_cast<float4*>(p.C + o) = d;
+            if (c0 + CH < rows) load_chunk(buf ^ 1, c0 + CH);
+        }
+#pragma unroll
+        for (int r = 0; r < CH; ++r) {
+            const int rr = c0 + r;
+            if (rr >= rows) break;
+            float4v d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int b = 0; b < MB; ++b) d += sa[rr][b] * gv[b];
+            float* dst = base + (int64_t)rr * p.N;
+            if constexpr (EPI == Epi::Sgd) {
+                const float4v v = w[buf][r] - p.lr * d;
+                __builtin_nontemporal_store(v, reinterpret_cast<float4v*>(dst));
+            } else {
+                *reinterpret_cast<float4v*>(dst) = d;
+            }
         }
     }
 }
 
+// rows of W per dW workgroup
+constexpr int kTnRows = 32;
+
 template <int MB>
-hipError_t go_mb(const SkinnyLaunch& L, const SkinnyParams& p, hipStream_t s) {
-    switch (L.layout) {
-    case Layout::NN: {
-        const size_t lds = (size_t)(L.waves - 1) * MB * kWave * sizeof(float4);
-#define MLP_NN(NWV)                                                                              \
-    if (L.waves == NWV) {                                                                        \
-        if (L.epi == Epi::ReluMask)                                                              \
-            hipLaunchKernelGGL((skinny_nn<MB, NWV, Epi::ReluMask>), dim3(L.grid), dim3(NWV * 64), \
-                               lds, s, p);                                                       \
-        else                                                                                     \
-            hipLaunchKernelGGL((skinny_nn<MB, NWV, Epi::Store>), dim3(L.grid), dim3(NWV * 64),    \
-                               lds, s, p);                                                       \
-        return hipGetLastError();                                                                \
-    }
-        MLP_NN(4)
-        MLP_NN(8)
-#undef MLP_NN
-        return hipErrorInvalidValue;
-    }
-    case Layout::NT:
-        hipLaunchKernelGGL(skinny_nt, dim3(L.grid), dim3(256), 0, s, p);
-        return hipGetLastError();
-    case Layout::TN:
-        if (L.epi == Epi::Sgd)
-            hipLaunchKernelGGL((skinny_tn<MB, 16, Epi::Sgd>), dim3(L.grid), dim3(256), 0, s, p);
-        else
-            hipLaunchKernelGGL((skinny_tn<MB, 16, Epi::Grad>), dim3(L.grid), dim3(256), 0, s, p);
-        return hipGetLastError();
-    }
-    return hipErrorInvalidValue;
+hipError_t go_tn(const SkinnyLaunch& L, const SkinnyParams& p, hipStream_t s) {
+    if (L.epi == Epi::Sgd)
+        hipLaunchKernelGGL((skinny_tn<MB, kTnRows, Epi::Sgd>), dim3(L.grid), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((skinny_tn<MB, kTnRows, Epi::Grad>), dim3(L.grid), dim3(256), 0, s, p);
+    return hipGetLastError();
 }
 
 }  // namespace
 
+int skinny_tn_rows() { return kTnRows; }
+
 hipError_t launch_skinny(const SkinnyLaunch& L, const SkinnyParams& p, hipStream_t s) {
-    if (p.MB <= 2) return go_mb<2>(L, p, s);
-    if (p.MB <= 4) return go_mb<4>(L, p, s);
-    if (p.MB <= 8) return go_mb<8>(L, p, s);
-    if (p.MB <= 16) return go_mb<16>(L, p, s);
+    if (p.MB < 1 || p.MB > 16) return hipErrorInvalidValue;
+    switch (L.layout) {
+    case Layout::NN:
+        if (L.waves != 16) return hipErrorInvalidValue;
+        if (L.epi == Epi::ReluMask)
+            hipLaunchKernelGGL((skinny_nn<16, Epi::ReluMask>), dim3(L.grid), dim3(16 * 64), 0, s, p);
+        else
+            hipLaunchKernelGGL((skinny_nn<16, Epi::Store>), dim3(L.grid), dim3(16 * 64), 0, s, p);
+        return hipGetLastError();
+    case Layout::NT:
+        hipLaunchKernelGGL((skinny_nt<8, 2>), dim3(L.grid), dim3(8 * 64), 0, s, p);
+        return hipGetLastError();
+    case Layout::TN:
+        if (p.MB <= 4) return go_tn<4>(L, p, s);
+        if (p.MB <= 8) return go_tn<8>(L, p, s);
+        return go_tn<16>(L, p, s);
+    }
     return hipErrorInvalidValue;
 }
 

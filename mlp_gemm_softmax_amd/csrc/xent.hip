@@ -1,12 +1,15 @@
 // Row-wise softmax cross-entropy against dense labels (the README's
 // cross_entropy_loss(logits, labels), "Example" section) in one kernel: the
-// reduction archetype.  One wavefront per row; per row b
+// reduction archetype.  Per row b
 //   mu = max_c z,  S = sum_c exp(z - mu),  lse = mu + log S,
 //   s = sum_c t,   loss_b = s*lse - sum_c t*z,
-//   dlogits = (exp(z - mu)/S * s - t) / B,
-// with max and sums taken by xor-butterfly shuffles across the 64 lanes.
-// Mean loss: every workgroup stores its rows' losses, takes an integer ticket,
-// and the last workgroup sums all B row losses in a fixed order.
+//   dlogits = (exp(z - mu)/S * s - t) / B.
+// Narrow rows (C <= 32) take one lane per row, so a wavefront handles 64 rows
+// and no cross-lane reduction is needed; wider rows take one wavefront per
+// row, with max and sums by xor-butterfly shuffles across the 64 lanes.
+// Mean loss: row losses are stored with device-scope stores, each workgroup
+// takes an integer ticket, and the last one sums all B row losses in a fixed
+// order (at most 256 workgroups draw tickets, bounding atomic contention).
 #include <math.h>
 
 #include "kernels.hpp"
@@ -14,47 +17,76 @@
 namespace mlp {
 namespace {
 
-constexpr int kRows = 4;           // rows (wavefronts) per workgroup
-constexpr int kThreads = kRows * kWave;
+constexpr int kThreads = 256;
+constexpr int kMaxGroups = 256;
 
 __device__ void finish_mean(const XentParams& p) {
-    // Called by the last workgroup only: fixed-order sum of row losses.
+    // Last workgroup only: fixed-order sum of the row losses.
     const int tid = threadIdx.x;
     float s = 0.f;
-    for (int b = tid; b < p.B; b += kThreads) s += p.rowloss[b];
+    for (int b = tid; b < p.B; b += kThreads) s += load_coherent(p.rowloss + b);
     s = wave_sum(s);
-    __shared__ float part[kRows];
+    __shared__ float part[kThreads / kWave];
     if ((tid & 63) == 0) part[tid >> 6] = s;
     __syncthreads();
     if (tid == 0) {
         float tot = 0.f;
-        for (int w = 0; w < kRows; ++w) tot += part[w];
+        for (int w = 0; w < kThreads / kWave; ++w) tot += part[w];
         *p.loss = tot * p.inv_b;
     }
 }
 
-__device__ void take_ticket_and_finish(const XentParams& p) {
+// One lane per row, C <= CMAX.
+template <int CMAX>
+__global__ __launch_bounds__(kThreads) void xent_lane(XentParams p) {
     __shared__ int s_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned old = atomicAdd(p.ticket, 1u);
-        const int last = old == gridDim.x - 1;
-        if (last) atomicExch(p.ticket, 0u);
-        s_last = last;
+    const int row = blockIdx.x * kThreads + threadIdx.x;
+    if (row < p.B) {
+        const float* z = p.logits + (int64_t)row * p.C;
+        const float* t = p.labels + (int64_t)row * p.C;
+        float zv[CMAX], tv[CMAX];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < CMAX; ++c) {
+            const bool ok = c < p.C;
+            zv[c] = ok ? z[c] : -INFINITY;
+            tv[c] = ok ? t[c] : 0.f;
+            mx = fmaxf(mx, zv[c]);
+        }
+        float se = 0.f, st = 0.f, stz = 0.f;
+#pragma unroll
+        for (int c = 0; c < CMAX; ++c) {
+            if (c < p.C) {
+                st += tv[c];
+                stz += tv[c] * zv[c];
+                zv[c] = expf(zv[c] - mx);
+                se += zv[c];
+            }
+        }
+        const float lse = mx + logf(se);
+        float* d = p.dlogits + (int64_t)row * p.C;
+        bf16_t* db = p.dlogits_b ? p.dlogits_b + (int64_t)row * p.C : nullptr;
+#pragma unroll
+        for (int c = 0; c < CMAX; ++c) {
+            if (c < p.C) {
+                const float g = (zv[c] / se * st - tv[c]) * p.inv_b;
+                d[c] = g;
+                if (db) db[c] = f32_to_bf16(g);
+            }
+        }
+        store_coherent(p.rowloss + row, st * lse - stz);
     }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    finish_mean(p);
+    if (last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
 }
 
-// Whole row in registers: C <= 64 * VPT.  Reads logits and labels once.
+// One wavefront per row, whole row in registers (C <= 64 * VPT); rows are
+// strided over the grid's wavefronts.
 template <int VPT>
-__global__ __launch_bounds__(kThreads) void xent_regs(XentParams p) {
+__global__ __launch_bounds__(kThreads) void xent_wave(XentParams p) {
+    __shared__ int s_last;
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * kRows + (threadIdx.x >> 6);
-    if (row < p.B) {
+    const int waves = gridDim.x * (kThreads / kWave);
+    for (int row = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6); row < p.B; row += waves) {
         const float* z = p.logits + (int64_t)row * p.C;
         const float* t = p.labels + (int64_t)row * p.C;
         float zv[VPT], tv[VPT];
@@ -94,17 +126,18 @@ __global__ __launch_bounds__(kThreads) void xent_regs(XentParams p) {
                 if (db) db[c] = f32_to_bf16(g);
             }
         }
-        if (lane == 0) p.rowloss[row] = st * lse - stz;
+        if (lane == 0) store_coherent(p.rowloss + row, st * lse - stz);
     }
-    take_ticket_and_finish(p);
+    if (last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
 }
 
 // Any C: running (max, sum) per lane in one sweep, merged across lanes, then
 // a second sweep writes dlogits.
 __global__ __launch_bounds__(kThreads) void xent_stream(XentParams p) {
+    __shared__ int s_last;
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * kRows + (threadIdx.x >> 6);
-    if (row < p.B) {
+    const int waves = gridDim.x * (kThreads / kWave);
+    for (int row = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6); row < p.B; row += waves) {
         const float* z = p.logits + (int64_t)row * p.C;
         const float* t = p.labels + (int64_t)row * p.C;
         float m = -INFINITY, se = 0.f, st = 0.f, stz = 0.f;
@@ -131,25 +164,35 @@ __global__ __launch_bounds__(kThreads) void xent_stream(XentParams p) {
             d[c] = g;
             if (db) db[c] = f32_to_bf16(g);
         }
-        if (lane == 0) p.rowloss[row] = st * lse - stz;
+        if (lane == 0) store_coherent(p.rowloss + row, st * lse - stz);
     }
-    take_ticket_and_finish(p);
+    if (last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
 }
 
 }  // namespace
 
 hipError_t launch_xent(const XentParams& p, int* grid_out, hipStream_t s) {
-    const int grid = (p.B + kRows - 1) / kRows;
+    int grid;
+    if (p.C <= 32) {
+        grid = (p.B + kThreads - 1) / kThreads;
+        if (p.C <= 8) hipLaunchKernelGGL(xent_lane<8>, dim3(grid), dim3(kThreads), 0, s, p);
+        else if (p.C <= 16) hipLaunchKernelGGL(xent_lane<16>, dim3(grid), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL(xent_lane<32>, dim3(grid), dim3(kThreads), 0, s, p);
+    } else {
+        const int rows_per_group = kThreads / kWave;
+        grid = (p.B + rows_per_group - 1) / rows_per_group;
+        if (grid > kMaxGroups) grid = kMaxGroups;
+        const int vpt = (p.C + kWave - 1) / kWave;
+        if (vpt <= 1) hipLaunchKernelGGL(xent_wave<1>, dim3(grid), dim3(kThreads), 0, s, p);
+        else if (vpt <= 2) hipLaunchKernelGGL(xent_wave<2>, dim3(grid), dim3(kThreads), 0, s, p);
+        else if (vpt <= 4) hipLaunchKernelGGL(xent_wave<4>, dim3(grid), dim3(kThreads), 0, s, p);
+        else if (vpt <= 8) hipLaunchKernelGGL(xent_wave<8>, dim3(grid), dim3(kThreads), 0, s, p);
+        else if (vpt <= 16) hipLaunchKernelGGL(xent_wave<16>, dim3(grid), dim3(kThreads), 0, s, p);
+        else if (vpt <= 32) hipLaunchKernelGGL(xent_wave<32>, dim3(grid), dim3(kThreads), 0, s, p);
+        else if (vpt <= 64) hipLaunchKernelGGL(xent_wave<64>, dim3(grid), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL(xent_stream, dim3(grid), dim3(kThreads), 0, s, p);
+    }
     if (grid_out) *grid_out = grid;
-    const int vpt = (p.C + kWave - 1) / kWave;
-    if (vpt <= 1) hipLaunchKernelGGL(xent_regs<1>, dim3(grid), dim3(kThreads), 0, s, p);
-    else if (vpt <= 2) hipLaunchKernelGGL(xent_regs<2>, dim3(grid), dim3(kThreads), 0, s, p);
-    else if (vpt <= 4) hipLaunchKernelGGL(xent_regs<4>, dim3(grid), dim3(kThreads), 0, s, p);
-    else if (vpt <= 8) hipLaunchKernelGGL(xent_regs<8>, dim3(grid), dim3(kThreads), 0, s, p);
-    else if (vpt <= 16) hipLaunchKernelGGL(xent_regs<16>, dim3(grid), dim3(kThreads), 0, s, p);
-    else if (vpt <= 32) hipLaunchKernelGGL(xent_regs<32>, dim3(grid), dim3(kThreads), 0, s, p);
-    else if (vpt <= 64) hipLaunchKernelGGL(xent_regs<64>, dim3(grid), dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL(xent_stream, dim3(grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
