@@ -4,9 +4,16 @@
 // epilogues still see the float32 accumulator (the ReLU mask is taken from
 // it), and outputs are rounded to bf16 only where a later GEMM consumes them.
 //
-// LDS tiles are k-contiguous bf16 [row][k] with a 72-element (144-byte) row
-// stride; each MFMA operand is one 16-byte read per lane: lanes 0-31 take
-// k = 16c..16c+7 and lanes 32-63 take k = 16c+8..16c+15 of row lane%32.
+// Operand tiles keep their global orientation in LDS (16-byte copies):
+//   k-contiguous operand: LDS [r][k], row stride 72 bf16; an MFMA operand is
+//     one 16-byte read: lanes 0-31 take k = 16c..16c+7 and lanes 32-63 take
+//     k = 16c+8..16c+15 of row lane%32;
+//   r-contiguous operand: LDS [k][r], row stride R+16 bf16; the same eight
+//     k-values per lane come from two ds_read_b64_tr_b16 transpose reads.
+//     Within each 16-lane group that instruction hands lane i element i%4 of
+//     the 8-byte chunks addressed by lanes 4e+i/4 (e = 0..3); pointing lane s
+//     at row kb + s/4, columns m0 + 4(s%4) therefore gives lane i the four
+//     values k = kb..kb+3 of row m0 + i.
 #include "kernels.hpp"
 
 namespace mlp {
@@ -14,7 +21,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBK = 64;
-constexpr int kLDK = kBK + 8;     // bf16 elements per LDS row
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
 
 template <int BM_, int BN_, int WM_, int WN_>
 struct Shape {
@@ -24,77 +33,74 @@ struct Shape {
     static_assert((BM / WM) * (BN / WN) == 4, "four waves per workgroup");
 };
 
-// k-contiguous operand; VEC = 8 loads 16 bytes (8 bf16) per access.
-template <int R, int VEC>
-struct KLoad {
+// Operand tile of R rows x kBK k in bf16.  KC: stored k-contiguous (element
+// (r,k) at g + r*ld + k), else r-contiguous (at g + k*ld + r).  VEC: 8 =
+// 16-byte global loads (contiguous extent and ld multiples of 8), 1 = 2-byte.
+template <int R, bool KC, int VEC>
+struct Tile {
+    static constexpr int LD = KC ? kBK + 8 : R + 16;         // LDS row stride (bf16)
+    static constexpr int ELEMS = KC ? R * LD : kBK * LD;     // LDS bf16 per stage
+    static constexpr int CONT = KC ? kBK : R;
     static constexpr int PER = R * kBK / (kThreads * VEC);
     static_assert(PER >= 1, "tile too small for the loader");
     uint32_t v[VEC == 8 ? PER * 4 : PER];
 
-    __device__ __forceinline__ void load(const bf16_t* __restrict__ g, int64_t ld, int r0,
-                                         int rmax, int k0, int kmax, int tid) {
+    __device__ __forceinline__ static void where(int tid, int i, int& line, int& off) {
+        const int idx = tid + kThreads * i;
+        line = idx / (CONT / VEC);
+        off = (idx % (CONT / VEC)) * VEC;
+    }
+
+    __device__ __forceinline__ void load(const bf16_t* __restrict__ g, int64_t ld, int r0, int rmax,
+                                         int k0, int kmax, int tid) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int idx = tid + kThreads * i;
+            int line, off;
+            where(tid, i, line, off);
+            const int r = KC ? r0 + line : r0 + off;
+            const int k = KC ? k0 + off : k0 + line;
+            const bool ok = r < rmax && k < kmax;
+            const bf16_t* src = KC ? g + (int64_t)r * ld + k : g + (int64_t)k * ld + r;
             if constexpr (VEC == 8) {
-                const int row = idx / (kBK / 8), kq = idx % (kBK / 8);
-                const int r = r0 + row, k = k0 + 8 * kq;
                 uint4 x = make_uint4(0u, 0u, 0u, 0u);
-                if (r < rmax && k < kmax) x = *reinterpret_cast<const uint4*>(g + (int64_t)r * ld + k);
+                if (ok) x = *reinterpret_cast<const uint4*>(src);
                 v[4 * i + 0] = x.x;
                 v[4 * i + 1] = x.y;
                 v[4 * i + 2] = x.z;
                 v[4 * i + 3] = x.w;
             } else {
-                const int row = idx / kBK, kk = idx % kBK;
-                const int r = r0 + row, k = k0 + kk;
-                v[i] = (r < rmax && k < kmax) ? (uint32_t)g[(int64_t)r * ld + k] : 0u;
+                v[i] = ok ? (uint32_t)*src : 0u;
             }
         }
     }
+
     __device__ __forceinline__ void store(bf16_t* s, int tid) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int idx = tid + kThreads * i;
-            if constexpr (VEC == 8) {
-                const int row = idx / (kBK / 8), kq = idx % (kBK / 8);
-                *reinterpret_cast<uint4*>(s + row * kLDK + 8 * kq) =
+            int line, off;
+            where(tid, i, line, off);
+            if constexpr (VEC == 8)
+                *reinterpret_cast<uint4*>(s + line * LD + off) =
                     make_uint4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-            } else {
-                const int row = idx / kBK, kk = idx % kBK;
-                s[row * kLDK + kk] = (bf16_t)v[i];
-            }
+            else
+                s[line * LD + off] = (bf16_t)v[i];
         }
     }
-};
 
-// r-contiguous operand (element (r,k) at g + k*ld + r): lanes along r, each
-// gathers KPT consecutive k into packed pairs and writes 16-byte runs along k.
-template <int R>
-struct MNLoad {
-    static constexpr int KG = kThreads / R;
-    static constexpr int KPT = kBK / KG;
-    static_assert(KPT % 8 == 0, "k per thread must fill 16-byte runs");
-    uint32_t v[KPT / 2];
-
-    __device__ __forceinline__ void load(const bf16_t* __restrict__ g, int64_t ld, int r0,
-                                         int rmax, int k0, int kmax, int tid) {
-        const int r = r0 + tid % R, grp = tid / R;
-        const bool rok = r < rmax;
-#pragma unroll
-        for (int i = 0; i < KPT / 2; ++i) {
-            const int k = k0 + grp * KPT + 2 * i;
-            const uint32_t lo = (rok && k < kmax) ? (uint32_t)g[(int64_t)k * ld + r] : 0u;
-            const uint32_t hi = (rok && k + 1 < kmax) ? (uint32_t)g[(int64_t)(k + 1) * ld + r] : 0u;
-            v[i] = lo | (hi << 16);
+    // Eight k-values (16c + 8*(lane/32) + 0..7) of tile row base + lane%32.
+    __device__ __forceinline__ static bf16x8v read(const bf16_t* s, int base, int c, int lane) {
+        const int kb = 16 * c + 8 * (lane >> 5);
+        if constexpr (KC) {
+            return *reinterpret_cast<const bf16x8v*>(s + (base + (lane & 31)) * LD + kb);
+        } else {
+            const int sl = lane & 15;
+            const int col = base + 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+            const bf16_t* p0 = s + (kb + (sl >> 2)) * LD + col;
+            const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)p0);
+            const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(p0 + 4 * LD));
+            const short8v both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            return __builtin_bit_cast(bf16x8v, both);
         }
-    }
-    __device__ __forceinline__ void store(bf16_t* s, int tid) const {
-        const int r = tid % R, grp = tid / R;
-#pragma unroll
-        for (int q = 0; q < KPT / 8; ++q)
-            *reinterpret_cast<uint4*>(s + r * kLDK + grp * KPT + 8 * q) =
-                make_uint4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
     }
 };
 
@@ -121,8 +127,10 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int row, int col, 
 template <class S, Layout LAY, int VEC, Epi EPI>
 __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
     constexpr int BM = S::BM, BN = S::BN, FM = S::FM, FN = S::FN;
-    __shared__ __attribute__((aligned(16))) bf16_t sA[2][BM * kLDK];
-    __shared__ __attribute__((aligned(16))) bf16_t sB[2][BN * kLDK];
+    using TA = Tile<BM, LAY != Layout::TN, VEC>;
+    using TB = Tile<BN, LAY == Layout::NT, VEC>;
+    __shared__ __attribute__((aligned(16))) bf16_t sA[2][TA::ELEMS];
+    __shared__ __attribute__((aligned(16))) bf16_t sB[2][TB::ELEMS];
     __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -149,11 +157,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
 
     const bf16_t* A = static_cast<const bf16_t*>(p.A);
     const bf16_t* B = static_cast<const bf16_t*>(p.B);
-
-    using ALoad = typename std::conditional<LAY == Layout::TN, MNLoad<BM>, KLoad<BM, VEC>>::type;
-    using BLoad = typename std::conditional<LAY == Layout::NT, KLoad<BN, VEC>, MNLoad<BN>>::type;
-    ALoad la;
-    BLoad lb;
+    TA la;
+    TB lb;
 
     float16v acc[FM][FN];
 #pragma unroll
@@ -176,17 +181,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
                 la.load(A, p.lda, m0, p.M, kbeg + (kt + 1) * kBK, kend, tid);
                 lb.load(B, p.ldb, n0, p.N, kbeg + (kt + 1) * kBK, kend, tid);
             }
-            const bf16_t* a_base = sA[cur] + (wm * S::WM + (lane & 31)) * kLDK + 8 * (lane >> 5);
-            const bf16_t* b_base = sB[cur] + (wn * S::WN + (lane & 31)) * kLDK + 8 * (lane >> 5);
 #pragma unroll
             for (int c = 0; c < kBK / 16; ++c) {
                 bf16x8v a[FM], b[FN];
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    a[i] = *reinterpret_cast<const bf16x8v*>(a_base + i * 32 * kLDK + 16 * c);
+                for (int i = 0; i < FM; ++i) a[i] = TA::read(sA[cur], wm * S::WM + 32 * i, c, lane);
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    b[j] = *reinterpret_cast<const bf16x8v*>(b_base + j * 32 * kLDK + 16 * c);
+                for (int j = 0; j < FN; ++j) b[j] = TB::read(sB[cur], wn * S::WN + 32 * j, c, lane);
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -218,19 +219,15 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
                     if (row < p.M && col < p.N) store_coherent(part + (int64_t)row * p.N + col, acc[i][j][r]);
                 }
         if (!last_arrival(&p.tickets[tile], (unsigned)p.splits, &s_last)) return;
-        float16v sum[FM][FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
+            for (int j = 0; j < FN; ++j) {
+                float16v sum;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sum[i][j][r] = 0.f;
-        for (int t = 0; t < p.splits; ++t) {
-            const float* q = p.partials + (int64_t)t * p.M * p.N;
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
+                for (int r = 0; r < 16; ++r) sum[r] = 0.f;
+                for (int t = 0; t < p.splits; ++t) {
+                    const float* q = p.partials + (int64_t)t * p.M * p.N;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int row = row_w + i * 32 + 8 * (r >> 2) + (r & 3);
@@ -238,13 +235,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
                         float v = acc[i][j][r];
                         if (t != split && row < p.M && col < p.N)
                             v = load_coherent(q + (int64_t)row * p.N + col);
-                        sum[i][j][r] += v;
+                        sum[r] += v;
                     }
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j) acc[i][j] = sum[i][j];
+                }
+                acc[i][j] = sum;
+            }
     }
 
 #pragma unroll
@@ -265,29 +260,24 @@ hipError_t go(const GemmParams& p, int grid, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <class S, Layout LAY, Epi EPI>
+hipError_t go_vec(const GemmLaunch& L, const GemmParams& p, hipStream_t st) {
+    return L.vec == 8 ? go<S, LAY, 8, EPI>(p, L.grid, st) : go<S, LAY, 1, EPI>(p, L.grid, st);
+}
+
 template <class S>
 hipError_t dispatch_shape(const GemmLaunch& L, const GemmParams& p, hipStream_t st) {
-    const bool v8 = L.vec == 8;
     switch (L.layout) {
     case Layout::NN:
-        if (L.epi == Epi::ReluMask)
-            return v8 ? go<S, Layout::NN, 8, Epi::ReluMask>(p, L.grid, st)
-                      : go<S, Layout::NN, 1, Epi::ReluMask>(p, L.grid, st);
-        if (L.epi == Epi::Store)
-            return v8 ? go<S, Layout::NN, 8, Epi::Store>(p, L.grid, st)
-                      : go<S, Layout::NN, 1, Epi::Store>(p, L.grid, st);
+        if (L.epi == Epi::ReluMask) return go_vec<S, Layout::NN, Epi::ReluMask>(L, p, st);
+        if (L.epi == Epi::Store) return go_vec<S, Layout::NN, Epi::Store>(L, p, st);
         break;
     case Layout::NT:
-        if (L.epi == Epi::MaskMul)
-            return v8 ? go<S, Layout::NT, 8, Epi::MaskMul>(p, L.grid, st)
-                      : go<S, Layout::NT, 1, Epi::MaskMul>(p, L.grid, st);
-        if (L.epi == Epi::Store)
-            return v8 ? go<S, Layout::NT, 8, Epi::Store>(p, L.grid, st)
-                      : go<S, Layout::NT, 1, Epi::Store>(p, L.grid, st);
+        if (L.epi == Epi::MaskMul) return go_vec<S, Layout::NT, Epi::MaskMul>(L, p, st);
         break;
     case Layout::TN:
-        if (L.epi == Epi::Sgd) return go<S, Layout::TN, 1, Epi::Sgd>(p, L.grid, st);
-        if (L.epi == Epi::Grad) return go<S, Layout::TN, 1, Epi::Grad>(p, L.grid, st);
+        if (L.epi == Epi::Sgd) return go_vec<S, Layout::TN, Epi::Sgd>(L, p, st);
+        if (L.epi == Epi::Grad) return go_vec<S, Layout::TN, Epi::Grad>(L, p, st);
         break;
     }
     return hipErrorInvalidValue;

@@ -92,6 +92,28 @@ struct XentParams {
 };
 hipError_t launch_xent(const XentParams& p, int* grid_out, hipStream_t s);
 
+// ---- fused output layer for C <= 32 (logits, softmax-CE, dX, dW + SGD) -----
+struct HeadParams {
+    const float* A;        // a_{L-1} [B][H]
+    float* W;              // W_L [H][C], updated in place unless dW is set
+    const float* labels;   // [B][C]
+    const uint8_t* mask;   // m_{L-1} [B][H]
+    float* logits;         // [B][C] or null
+    float* dlogits;        // [B][C]
+    float* G;              // dZ_{L-1} [B][H]
+    float* dW;             // [H][C] gradient output (no update) or null
+    float* partials;       // [ceil(B/RB)][H][C]
+    float* rowloss;        // [B]
+    float* loss;           // scalar mean loss
+    unsigned* ticket;      // zeroed counter
+    int B, H, C, CP, RB;   // CP = C | 1 (LDS row stride of W), RB rows per workgroup
+    float lr, inv_b;
+};
+size_t head_lds_bytes(int H, int C, int RB);
+int head_max_lds();          // dynamic LDS the head kernel may use
+hipError_t head_prepare();   // raise the kernel's dynamic-LDS limit once
+hipError_t launch_head(const HeadParams& p, hipStream_t s);
+
 // ---- f32 -> bf16 cast -----------------------------------------------------
 hipError_t launch_cast_bf16(const float* src, bf16_t* dst, size_t n, hipStream_t s);
 // ---- bf16 -> f32 widen (state read-back) -----------------------------------

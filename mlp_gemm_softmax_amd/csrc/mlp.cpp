@@ -91,6 +91,8 @@ struct mlp_ctx {
     int B = 0;
     bool bf16 = false;
     bool skinny = false;
+    bool head = false;      // fused output layer (C <= 32, f32)
+    int head_rb = 0;        // batch rows per head workgroup
     hipStream_t stream = nullptr;
 
     // workspace buffers
@@ -202,16 +204,25 @@ void build_slots(mlp_ctx* c) {
     };
     const char* kind = c->skinny ? "skinny" : (c->bf16 ? "mfma_bf16" : "mfma_f32");
     if (c->bf16) add("cast_x_bf16", 0, (double)B * c->dims[0] * 6);
-    for (int l = 0; l < L; ++l) {
+    const int C = c->dims[L];
+    const int Lf = c->head ? L - 1 : L;   // layers whose forward is a plain GEMM
+    for (int l = 0; l < Lf; ++l) {
         const double M = B, N = c->dims[l + 1], K = c->dims[l];
         const bool last = l == L - 1;
         const double out = last ? M * N * 4 : M * N * (e + 1);
         add(std::string(kind) + "_nn_" + (last ? "store" : "relu_mask") + "_l" + std::to_string(l),
             2 * M * N * K, M * K * e + K * N * e + out);
     }
-    const int C = c->dims[L];
-    add("softmax_xent", 0, (double)B * C * (12 + (c->bf16 ? 2 : 0)) + B * 4.0);
-    for (int l = L - 1; l >= 0; --l) {
+    int top = L - 1;
+    if (c->head) {
+        const double H = c->dims[L - 1];
+        add("head_logits_xent_dx_sgd_l" + std::to_string(L - 1), 6.0 * B * H * C,
+            B * H * 4 + H * C * 8 + B * C * 12 + B * H * 5 + B * 4.0);
+        top = L - 2;
+    } else {
+        add("softmax_xent", 0, (double)B * C * (12 + (c->bf16 ? 2 : 0)) + B * 4.0);
+    }
+    for (int l = top; l >= 0; --l) {
         const double din = c->dims[l], dout = c->dims[l + 1];
         if (l > 0)
             add(std::string(kind) + "_nt_mask_l" + std::to_string(l), 2.0 * B * din * dout,
@@ -327,8 +338,9 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
     } else {
         a_prev = x;
     }
-    // ---- forward
-    for (int l = 0; l < L; ++l) {
+    // ---- forward (with the fused head the last layer's matmul is in the head)
+    const bool use_head = c->head && mode != Mode::Forward;
+    for (int l = 0; l < (use_head ? L - 1 : L); ++l) {
         const int K = c->dims[l], N = c->dims[l + 1];
         const bool last = l == L - 1;
         const void* Wop = c->bf16 ? (const void*)c->Wb[l] : (const void*)c->W[l];
@@ -353,26 +365,59 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
 
     // ---- loss
     const int C = c->dims[L];
-    r.run(slot++, [&] {
-        XentParams xp;
-        xp.logits = c->logits;
-        xp.labels = labels;
-        xp.dlogits = c->dlogits;
-        xp.dlogits_b = c->bf16 ? c->dlogits_b : nullptr;
-        xp.rowloss = c->rowloss;
-        xp.loss = loss_dev ? loss_dev : c->loss_slot;
-        xp.ticket = c->xent_ticket;
-        xp.B = B;
-        xp.C = C;
-        xp.inv_b = 1.0f / (float)B;
-        return launch_xent(xp, nullptr, c->stream);
-    });
+    if (use_head) {
+        const int H = c->dims[L - 1];
+        r.run(slot++, [&] {
+            HeadParams hp;
+            hp.A = (const float*)c->act[L - 1];
+            hp.W = c->W[L - 1];
+            hp.labels = labels;
+            hp.mask = c->mask[L - 1];
+            hp.logits = c->logits;
+            hp.dlogits = c->dlogits;
+            hp.G = (float*)c->dz[0];
+            hp.dW = mode == Mode::Grads ? dw_out[L - 1] : nullptr;
+            hp.partials = c->partials;
+            hp.rowloss = c->rowloss;
+            hp.loss = loss_dev ? loss_dev : c->loss_slot;
+            hp.ticket = c->tickets;
+            hp.B = B;
+            hp.H = H;
+            hp.C = C;
+            hp.CP = C | 1;
+            hp.RB = c->head_rb;
+            hp.lr = lr;
+            hp.inv_b = 1.0f / (float)B;
+            return launch_head(hp, c->stream);
+        });
+    } else {
+        r.run(slot++, [&] {
+            XentParams xp;
+            xp.logits = c->logits;
+            xp.labels = labels;
+            xp.dlogits = c->dlogits;
+            xp.dlogits_b = c->bf16 ? c->dlogits_b : nullptr;
+            xp.rowloss = c->rowloss;
+            xp.loss = loss_dev ? loss_dev : c->loss_slot;
+            xp.ticket = c->xent_ticket;
+            xp.B = B;
+            xp.C = C;
+            xp.inv_b = 1.0f / (float)B;
+            return launch_xent(xp, nullptr, c->stream);
+        });
+    }
     if (mode == Mode::Forward) return r.err;
 
     // ---- backward
     const void* G = c->bf16 ? (const void*)c->dlogits_b : (const void*)c->dlogits;
     int pp = 0;
-    for (int l = L - 1; l >= 0; --l) {
+    int top = L - 1;
+    if (use_head) {           // the head produced G_{L-1} in dz[0] and updated W_{L-1}
+        G = c->dz[0];
+        pp = 1;
+        top = L - 2;
+    }
+    for (int l = top; l >= 0; --l) {
         const int din = c->dims[l], dout = c->dims[l + 1];
         const void* Wop = c->bf16 ? (const void*)c->Wb[l] : (const void*)c->W[l];
         const void* Gnext = nullptr;
@@ -488,6 +533,18 @@ mlp_status validate(const mlp_config* cfg, mlp_ctx* tmp) {
     bool all4 = true;
     for (int i = 0; i <= tmp->L; ++i) all4 = all4 && (tmp->dims[i] % 4 == 0);
     tmp->skinny = !tmp->bf16 && tmp->B <= kSkinnyMaxBatch && all4;
+    // Fused output layer: float32, a hidden layer below it, C <= 32, and W_L
+    // plus a block of at least 8 activation rows fitting the head's LDS.
+    tmp->head = false;
+    if (!tmp->bf16 && tmp->L >= 2 && tmp->dims[tmp->L] <= 32) {
+        const int H = tmp->dims[tmp->L - 1], C = tmp->dims[tmp->L];
+        for (int rb = 64; rb >= 8; rb /= 2)
+            if (head_lds_bytes(H, C, rb) <= (size_t)head_max_lds()) {
+                tmp->head = true;
+                tmp->head_rb = std::min(rb, tmp->B);
+                break;
+            }
+    }
     return MLP_OK;
 }
 
@@ -532,6 +589,10 @@ size_t plan_and_carve(mlp_ctx* c, char* base) {
         if (c->fwd[l].splits > 1) max_partial = std::max(max_partial, (size_t)c->fwd[l].splits * B * dout);
         if (c->dx[l].splits > 1) max_partial = std::max(max_partial, (size_t)c->dx[l].splits * B * din);
         if (c->dw[l].splits > 1) max_partial = std::max(max_partial, (size_t)c->dw[l].splits * din * dout);
+    }
+    if (c->head) {
+        const size_t nblk = (size_t)(B + c->head_rb - 1) / c->head_rb;
+        max_partial = std::max(max_partial, nblk * c->dims[L - 1] * c->dims[L]);
     }
     int max_hidden = 1;
     for (int l = 1; l < L; ++l) max_hidden = std::max(max_hidden, c->dims[l]);
@@ -629,6 +690,14 @@ mlp_status mlp_create(const mlp_config* cfg, void* workspace, size_t bytes, mlp_
     }
     plan_and_carve(c, (char*)workspace);
     build_slots(c);
+    if (c->head) {
+        const hipError_t he = head_prepare();
+        if (he != hipSuccess) {
+            set_err(nullptr, MLP_ERR_HIP, "head kernel set-up: %s", hipGetErrorString(he));
+            delete c;
+            return MLP_ERR_HIP;
+        }
+    }
     const hipError_t e = hipMemsetAsync(c->tickets, 0, tickets_bytes(c), c->stream);
     if (e != hipSuccess) {
         set_err(nullptr, MLP_ERR_HIP, "zeroing counters: %s", hipGetErrorString(e));

@@ -53,19 +53,32 @@ __global__ __launch_bounds__(NW * kWave) void skinny_nn(SkinnyParams p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = {0.f, 0.f, 0.f, 0.f};
 
-    const float* __restrict__ W = p.B + n;
-    const float* __restrict__ X = p.A + (int64_t)j * p.K;
-    for (int k = kw0; k < kw1; k += 16) {
+    // Loads are branch-free: lanes past N or past the slice read a valid
+    // address (the matrix base) and zero the value.  The next block's loads
+    // are issued before the current block's MFMAs, so memory latency overlaps
+    // the matrix-core work.
+    const float* __restrict__ W = p.B;
+    const float* __restrict__ X = p.A + (int64_t)(mok ? j : 0) * p.K;
+    const float4v zero = {0.f, 0.f, 0.f, 0.f};
+    float4v w[4], xv, wn[4], xn;
+    auto fetch = [&](int k, float4v* wd, float4v& xd) {
         const int kr = k + 4 * g;              // this lane group's 4 rows
-        float4v w[4];
-        float4v xv = {0.f, 0.f, 0.f, 0.f};
         const bool rok = kr < kw1;             // K is a multiple of 4
+        const bool ok = rok && nok;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            w[i] = {0.f, 0.f, 0.f, 0.f};
-            if (rok && nok) w[i] = ld4(W + (int64_t)(kr + i) * p.N);
+            const float4v v = ld4(ok ? W + (int64_t)(kr + i) * p.N + n : W);
+            wd[i] = ok ? v : zero;
         }
-        if (rok && mok) xv = ld4(X + kr);
+        const float4v v = ld4(rok ? X + kr : X);
+        xd = (rok && mok) ? v : zero;
+    };
+    if (kw0 < kw1) fetch(kw0, wn, xn);
+    for (int k = kw0; k < kw1; k += 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = wn[i];
+        xv = xn;
+        if (k + 16 < kw1) fetch(k + 16, wn, xn);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -142,8 +155,8 @@ __global__ __launch_bounds__(NW * kWave) void skinny_nn(SkinnyParams p) {
 // dX: out[b][k] = mask[b][k] * sum_n G[b][n] W[k][n], W stored [Kout][N].
 // A workgroup of NW waves covers RG*16 rows of W; wave w takes the w-th slice
 // of n.  MFMA: A = 16 rows of W, B = G^T (16 batch columns, zero past B);
-// lane (i = lane%16, g) supplies W[k0 + i][c + q] and G[i][c + q], with
-// c = n + 4g, to MFMA q, so one float4 of each feeds four MFMAs.
+// lane (i = lane%16, g) supplies W[k0 + i][c + q] and G[i][c + q] to MFMA q
+// for its float4 at column c, so one float4 of each feeds four MFMAs.
 template <int NW, int RG>
 __global__ __launch_bounds__(NW * kWave) void skinny_nt(SkinnyParams p) {
     __shared__ float4v red[NW - 1][RG][kWave];
@@ -152,7 +165,7 @@ __global__ __launch_bounds__(NW * kWave) void skinny_nt(SkinnyParams p) {
     const int k0 = blockIdx.x * 16 * RG;
     const int i = lane & 15, g = lane >> 4;
     const bool bok = i < p.MB;
-    const int nq = ((p.N + 16 * NW - 1) / (16 * NW)) * 16;   // slice, multiple of 16
+    const int nq = ((p.N + 32 * NW - 1) / (32 * NW)) * 32;   // slice, multiple of 32
     const int nbeg = wave * nq;
     const int nend = min(p.N, nbeg + nq);
 
@@ -166,24 +179,44 @@ __global__ __launch_bounds__(NW * kWave) void skinny_nt(SkinnyParams p) {
         rok[r] = krow < p.K;
         Wr[r] = p.A + (int64_t)krow * p.N;
     }
-    const float* __restrict__ Gr = p.B + (int64_t)i * p.N;
-#pragma unroll 4
-    for (int n = nbeg; n < nend; n += 16) {
-        const int c = n + 4 * g;
-        const bool cok = c < nend;             // N is a multiple of 4
-        float4v gv = {0.f, 0.f, 0.f, 0.f};
-        if (cok && bok) gv = ld4(Gr + c);
-        float4v w[RG];
+    const float* __restrict__ Gr = p.B + (int64_t)(bok ? i : 0) * p.N;
+    // 32 n per step: lane group g takes n + 8g .. n + 8g + 7 (two float4s),
+    // so the four groups read whole 128-byte lines of each W row.  Loads are
+    // branch-free (out-of-range lanes read the row start and zero the value)
+    // and the next step's loads are issued before this step's MFMAs.
+    const float4v zero = {0.f, 0.f, 0.f, 0.f};
+    float4v gv[2], w[RG][2], gn[2], wn[RG][2];
+    auto fetch = [&](int n, float4v* gd, float4v (*wd)[2]) {
+        const int c = n + 8 * g;
 #pragma unroll
-        for (int r = 0; r < RG; ++r) {
-            w[r] = {0.f, 0.f, 0.f, 0.f};
-            if (cok && rok[r]) w[r] = ld4(Wr[r] + c);
+        for (int h = 0; h < 2; ++h) {
+            const bool cok = c + 4 * h < nend;  // N is a multiple of 4
+            const float4v v = ld4(cok ? Gr + c + 4 * h : Gr);
+            gd[h] = (cok && bok) ? v : zero;
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                const bool ok = cok && rok[r];
+                const float4v x = ld4(ok ? Wr[r] + c + 4 * h : p.A);
+                wd[r][h] = ok ? x : zero;
+            }
         }
+    };
+    if (nbeg < nend) fetch(nbeg, gn, wn);
+    for (int n = nbeg; n < nend; n += 32) {
 #pragma unroll
-        for (int r = 0; r < RG; ++r)
+        for (int h = 0; h < 2; ++h) {
+            gv[h] = gn[h];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(w[r][q], gv[q], acc[r], 0, 0, 0);
+            for (int r = 0; r < RG; ++r) w[r][h] = wn[r][h];
+        }
+        if (n + 32 < nend) fetch(n + 32, gn, wn);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < RG; ++r)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(w[r][h][q], gv[h][q], acc[r], 0, 0, 0);
     }
     if (wave > 0) {
 #pragma unroll

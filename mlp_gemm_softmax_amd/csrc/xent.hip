@@ -23,8 +23,18 @@ constexpr int kMaxGroups = 256;
 __device__ void finish_mean(const XentParams& p) {
     // Last workgroup only: fixed-order sum of the row losses.
     const int tid = threadIdx.x;
+    // loads of 8 rows in flight before they are added (row order kept)
     float s = 0.f;
-    for (int b = tid; b < p.B; b += kThreads) s += load_coherent(p.rowloss + b);
+    for (int b0 = tid; b0 < p.B; b0 += 8 * kThreads) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int b = b0 + u * kThreads;
+            v[u] = b < p.B ? load_coherent(p.rowloss + b) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+    }
     s = wave_sum(s);
     __shared__ float part[kThreads / kWave];
     if ((tid & 63) == 0) part[tid >> 6] = s;
@@ -131,6 +141,79 @@ __global__ __launch_bounds__(kThreads) void xent_wave(XentParams p) {
     if (last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
 }
 
+// One workgroup per row, for few wide rows (B small, C large): the row is
+// spread over 256 lanes (VPT values each); max and sums go through the
+// wavefront butterflies and then LDS in wave order.
+template <int VPT>
+__global__ __launch_bounds__(kThreads) void xent_group(XentParams p) {
+    __shared__ int s_last;
+    __shared__ float red[3][kThreads / kWave];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = blockIdx.x;
+    const float* z = p.logits + (int64_t)row * p.C;
+    const float* t = p.labels + (int64_t)row * p.C;
+    float zv[VPT], tv[VPT];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int c = tid + kThreads * i;
+        const bool ok = c < p.C;
+        zv[i] = ok ? z[c] : -INFINITY;
+        tv[i] = ok ? t[c] : 0.f;
+        mx = fmaxf(mx, zv[i]);
+    }
+    mx = wave_max(mx);
+    if (lane == 0) red[0][wave] = mx;
+    __syncthreads();
+    mx = red[0][0];
+#pragma unroll
+    for (int w = 1; w < kThreads / kWave; ++w) mx = fmaxf(mx, red[0][w]);
+    float se = 0.f, st = 0.f, stz = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int c = tid + kThreads * i;
+        if (c < p.C) {
+            st += tv[i];
+            stz += tv[i] * zv[i];
+            zv[i] = expf(zv[i] - mx);
+            se += zv[i];
+        }
+    }
+    se = wave_sum(se);
+    st = wave_sum(st);
+    stz = wave_sum(stz);
+    __syncthreads();
+    if (lane == 0) {
+        red[0][wave] = se;
+        red[1][wave] = st;
+        red[2][wave] = stz;
+    }
+    __syncthreads();
+    se = red[0][0];
+    st = red[1][0];
+    stz = red[2][0];
+#pragma unroll
+    for (int w = 1; w < kThreads / kWave; ++w) {
+        se += red[0][w];
+        st += red[1][w];
+        stz += red[2][w];
+    }
+    const float lse = mx + logf(se);
+    float* d = p.dlogits + (int64_t)row * p.C;
+    bf16_t* db = p.dlogits_b ? p.dlogits_b + (int64_t)row * p.C : nullptr;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+        const int c = tid + kThreads * i;
+        if (c < p.C) {
+            const float g = (zv[i] / se * st - tv[i]) * p.inv_b;
+            d[c] = g;
+            if (db) db[c] = f32_to_bf16(g);
+        }
+    }
+    if (tid == 0) store_coherent(p.rowloss + row, st * lse - stz);
+    if (last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
+}
+
 // Any C: running (max, sum) per lane in one sweep, merged across lanes, then
 // a second sweep writes dlogits.
 __global__ __launch_bounds__(kThreads) void xent_stream(XentParams p) {
@@ -178,6 +261,13 @@ hipError_t launch_xent(const XentParams& p, int* grid_out, hipStream_t s) {
         if (p.C <= 8) hipLaunchKernelGGL(xent_lane<8>, dim3(grid), dim3(kThreads), 0, s, p);
         else if (p.C <= 16) hipLaunchKernelGGL(xent_lane<16>, dim3(grid), dim3(kThreads), 0, s, p);
         else hipLaunchKernelGGL(xent_lane<32>, dim3(grid), dim3(kThreads), 0, s, p);
+    } else if (p.B <= 64 && p.C >= 512 && p.C <= 32 * kThreads) {
+        grid = p.B;
+        const int vpt = (p.C + kThreads - 1) / kThreads;
+        if (vpt <= 4) hipLaunchKernelGGL(xent_group<4>, dim3(grid), dim3(kThreads), 0, s, p);
+        else if (vpt <= 8) hipLaunchKernelGGL(xent_group<8>, dim3(grid), dim3(kThreads), 0, s, p);
+        else if (vpt <= 16) hipLaunchKernelGGL(xent_group<16>, dim3(grid), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL(xent_group<32>, dim3(grid), dim3(kThreads), 0, s, p);
     } else {
         const int rows_per_group = kThreads / kWave;
         grid = (p.B + rows_per_group - 1) / rows_per_group;

@@ -350,7 +350,10 @@ def test_profile_slots(torch_dev):
     for _ in range(3):
         net.train_step(xd, td, w.lr)
     rows = net.profile_read()
-    assert len(rows) == 2 + 1 + 1 + 2
+    # 784->128->10: hidden forward GEMM, the fused output layer (logits, CE,
+    # dX, dW + SGD of the last layer), dW + SGD of the first layer
+    assert [r["name"] for r in rows] == ["mfma_f32_nn_relu_mask_l0", "head_logits_xent_dx_sgd_l1",
+                                         "mfma_f32_tn_sgd_l0"]
     assert all(r["launches"] == 3 and r["total_ms"] > 0 for r in rows)
     assert rows[0]["flops"] == 2 * 32 * 784 * 128
     net.close()
