@@ -156,9 +156,6 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_f32_kernel(GemmParams p) {
 
     const float* A = static_cast<const float*>(p.A);
     const float* B = static_cast<const float*>(p.B);
-    TA la;
-    TB lb;
-
     float16v acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -171,6 +168,26 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_f32_kernel(GemmParams p) {
     const int brow = wn * S::WN + (lane & 31);
     const int half = lane >> 5;
 
+    auto compute = [&](const float* a_s, const float* b_s) {
+#pragma unroll
+        for (int c = 0; c < kBK / 8; ++c) {
+            float4v a[FM], b[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) a[i] = TA::read(a_s, arow + 32 * i, c, half);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) b[j] = TB::read(b_s, brow + 32 * j, c, half);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][q], b[j][q], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    TA la;
+    TB lb;
     if (nk > 0) {
         la.load(A, p.lda, m0, p.M, kbeg, kend, tid);
         lb.load(B, p.ldb, n0, p.N, kbeg, kend, tid);
@@ -184,22 +201,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_f32_kernel(GemmParams p) {
                 la.load(A, p.lda, m0, p.M, kbeg + (kt + 1) * kBK, kend, tid);
                 lb.load(B, p.ldb, n0, p.N, kbeg + (kt + 1) * kBK, kend, tid);
             }
-#pragma unroll
-            for (int c = 0; c < kBK / 8; ++c) {
-                float4v a[FM], b[FN];
-#pragma unroll
-                for (int i = 0; i < FM; ++i) a[i] = TA::read(sA[cur], arow + 32 * i, c, half);
-#pragma unroll
-                for (int j = 0; j < FN; ++j) b[j] = TB::read(sB[cur], brow + 32 * j, c, half);
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int i = 0; i < FM; ++i)
-#pragma unroll
-                        for (int j = 0; j < FN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][q], b[j][q],
-                                                                            acc[i][j], 0, 0, 0);
-            }
+            compute(sA[cur], sB[cur]);
             if (more) {
                 la.store(sA[cur ^ 1], tid);
                 lb.store(sB[cur ^ 1], tid);
@@ -229,7 +231,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_f32_kernel(GemmParams p) {
                     if (row < p.M && col < p.N) store_coherent(part + (int64_t)row * p.N + col, acc[i][j][r]);
                 }
         if (!last_arrival(&p.tickets[tile], (unsigned)p.splits, &s_last)) return;
-        // One 32x32 block at a time: its S x 16 loads are independent.
+        // One 32x32 block at a time; the loads of TU splits are in flight
+        // together, then added in split order.
+        constexpr int TU = FM * FN >= 4 ? 1 : 4 / (FM * FN);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -237,17 +241,25 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_f32_kernel(GemmParams p) {
                 float16v sum;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sum[r] = 0.f;
-                for (int t = 0; t < p.splits; ++t) {
-                    const float* q = p.partials + (int64_t)t * p.M * p.N;
+                for (int t0 = 0; t0 < p.splits; t0 += TU) {
+                    float16v v[TU];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = row_w + i * 32 + 8 * (r >> 2) + (r & 3);
-                        const int col = col_w + j * 32;
-                        float v = acc[i][j][r];
-                        if (t != split && row < p.M && col < p.N)
-                            v = load_coherent(q + (int64_t)row * p.N + col);
-                        sum[r] += v;
+                    for (int u = 0; u < TU; ++u) {
+                        const int t = t0 + u;
+                        const float* q = p.partials + (int64_t)t * p.M * p.N;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int row = row_w + i * 32 + 8 * (r >> 2) + (r & 3);
+                            const int col = col_w + j * 32;
+                            float x = 0.f;
+                            if (t == split) x = acc[i][j][r];
+                            else if (t < p.splits && row < p.M && col < p.N)
+                                x = load_coherent(q + (int64_t)row * p.N + col);
+                            v[u][r] = x;
+                        }
                     }
+#pragma unroll
+                    for (int u = 0; u < TU; ++u) sum += v[u];
                 }
                 acc[i][j] = sum;
             }

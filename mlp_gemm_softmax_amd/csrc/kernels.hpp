@@ -55,6 +55,12 @@ struct GemmLaunch {
 
 hipError_t launch_gemm(const GemmLaunch& L, const GemmParams& p, hipStream_t s);
 
+// Small float32 products: one 32x32 tile per workgroup, K split across its
+// `waves` waves and reduced in LDS (no split-K across workgroups).  Uses
+// L.layout, L.epi, L.vec and L.grid = ceil(M/32) * ceil(N/32).
+int gemm_small_waves(int M, int N, int K);
+hipError_t launch_gemm_small(const GemmLaunch& L, const GemmParams& p, int waves, hipStream_t s);
+
 // ---- skinny batch (B <= 16) float32 kernels ------------------------------
 struct SkinnyParams {
     const float* A;   // NN: x [MB][K] ; NT: W [Kout][N] ; TN: a [MB][K]

@@ -65,6 +65,7 @@ struct GemmPlan {
     TileCfg cfg;
     int splits = 1, kchunk = 0, tiles_m = 1, tiles_n = 1, grid = 1;
     int vec = 1;
+    int small_waves = 0;    // > 0: the small-product kernel with this many waves
 };
 
 struct SkinnyPlan {
@@ -156,6 +157,16 @@ GemmPlan plan_gemm(int M, int N, int K, bool bf16, bool kvec_ok) {
     g.tiles_n = (N + bn - 1) / bn;
     const int nt = g.tiles_m * g.tiles_n;
     const int bk = bf16 ? 64 : 32;
+    const int t32 = ((M + 31) / 32) * ((N + 31) / 32);
+    if (!bf16 && nt < 256 && t32 <= 1024) {
+        // Under-filled product: K split inside the workgroup, no partials.
+        g.small_waves = gemm_small_waves(M, N, K);
+        g.splits = 1;
+        g.kchunk = std::max(K, 1);
+        g.grid = t32;
+        g.vec = kvec_ok ? 4 : 1;
+        return g;
+    }
     const int target = 512;
     const int kmin = bf16 ? 256 : 128;
     int s = std::max(1, std::min((target + nt - 1) / nt, K / kmin));
@@ -296,6 +307,7 @@ hipError_t run_gemm(mlp_ctx* c, const GemmPlan& g, Layout lay, Epi epi, const vo
     p.tickets = c->tickets;
     p.tiles_m = g.tiles_m;
     p.tiles_n = g.tiles_n;
+    if (g.small_waves > 0) return launch_gemm_small(L, p, g.small_waves, c->stream);
     return launch_gemm(L, p, c->stream);
 }
 

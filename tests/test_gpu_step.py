@@ -42,6 +42,8 @@ EXACT_CASES = [
     ((784, 128, 16), 32, "f32", 2),          # the README MLP's widths, 32x128 tiles
     ((256, 520, 64), 8, "f32", 2),           # skinny-batch kernels, ragged columns
     ((1024, 1100, 260), 16, "f32", 1),       # skinny-batch with K splits
+    ((320, 2080, 40), 512, "f32", 1),        # tiled NN with split-K, ragged N
+    ((2080, 1040, 40), 512, "f32", 1),       # tiled TN and NT with split-K, ragged tiles
     ((200, 300, 36), 64, "bf16", 1),
     ((120, 136, 24), 256, "bf16", 1),
 ]
