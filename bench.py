@@ -41,7 +41,41 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--profile-steps", type=int, default=None,
                     help="steps of the per-launch event pass (default: --steps)")
+    ap.add_argument("--summarize", metavar="DIR", default=None,
+                    help="no GPU work: turn the rocprofv3 runs collected under DIR "
+                         "(bench_W.log, trace_W/, fetch_W/, write_W/) into profiles/W.md and "
+                         "profiles/traffic.json for --workload")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="before timing, copy a buffer of this many MiB once (a plain copy of "
+                         "known size, for scaling hardware byte counters)")
     return ap.parse_args()
+
+
+def source_digest():
+    """sha256 over the HIP/C++ sources of the library (kernel identity)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "mlp_gemm_softmax_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter runs
+    (profiles/traffic.json), or None when absent or when the kernel sources
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_digest() or rec.get("kernel") != kernel:
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def roofline(rows, precision, steps):
@@ -93,8 +127,119 @@ def cpu_baseline(w, budget_s):
                       f"{cores}), {el:.1f} s"}
 
 
+# ---------------------------------------------------------------- profiles --
+
+TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace_{w} -o {w} -- "
+             "python3 bench.py --workload {w} --steps {s} --warmup {wu} --no-cpu-baseline")
+PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d OUT/{d}_{w} -o {w} -- python3 bench.py "
+           "--workload {w} --steps 2 --warmup 1 --profile-steps 1 --no-cpu-baseline --calib-copy-mb 256")
+
+
+def _csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _bench_log(path):
+    slots, line = [], None
+    with open(path) as f:
+        for ln in f:
+            if ln.startswith("[bench] per-launch"):
+                body = ln.split(":", 1)[1]
+                for item in body.split(","):
+                    name, val = item.strip().rsplit("=", 1)
+                    slots.append((name, float(val) * 1e3))
+            elif ln.startswith("{"):
+                line = json.loads(ln)
+    return slots, line
+
+
+def _short(name):
+    import re
+    name = name.replace("void mlp::(anonymous namespace)::", "").replace("mlp::(anonymous namespace)::", "")
+    return re.sub(r"\((mlp::)?\w+Params\)$", "", name)
+
+
+def _per_slot(dispatches, n_slots, steps):
+    """Average a per-dispatch value by slot over the last `steps` whole steps."""
+    mine = [d for d in dispatches if "mlp::" in d[0]]
+    tail = mine[-n_slots * steps:]
+    names = [tail[i][0] for i in range(n_slots)]
+    avg = [sum(tail[k * n_slots + i][1] for k in range(steps)) / steps for i in range(n_slots)]
+    return names, avg
+
+
+def summarize(outdir, w, steps, warmup):
+    slots, line = _bench_log(os.path.join(outdir, f"bench_{w}.log"))
+    n = len(slots)
+    trace = _csv(os.path.join(outdir, f"trace_{w}", f"{w}_kernel_trace.csv"))
+    trace.sort(key=lambda r: int(r["Dispatch_Id"]))
+    disp = [(r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in trace]
+    full_steps = sum(1 for d in disp if "mlp::" in d[0]) // n
+    names, trace_us = _per_slot(disp, n, max(1, full_steps - 1))
+    stats = _csv(os.path.join(outdir, f"trace_{w}", f"{w}_kernel_stats.csv"))
+
+    counters, scale = {}, {}
+    for cname, d in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        rows = _csv(os.path.join(outdir, f"{d}_{w}", f"{w}_counter_collection.csv"))
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        vals = [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows if r["Counter_Name"] == cname]
+        copies = [v for k, v in vals if "copyBuffer" in k]
+        scale[cname] = (256 * 1024) / max(copies)          # KiB the 256 MiB copy moved / counted
+        _, per = _per_slot(vals, n, 2)
+        counters[cname] = [v * scale[cname] * 1024 for v in per]   # bytes per launch
+
+    roof = line["roofline"]
+    dom = [i for i, (nm, _) in enumerate(slots) if nm == roof["kernel"]][0]
+    lines = [f"# rocprofv3 summary: workload `{w}`", "",
+             f"Kernel source digest (sha256 of mlp_gemm_softmax_amd/csrc/*): `{source_digest()}`", "",
+             "Commands (repository root on one MI355X; OUT is the output folder):", "",
+             "```", TRACE_CMD.format(w=w, s=steps, wu=warmup),
+             PMC_CMD.format(c="FETCH_SIZE", d="fetch", w=w),
+             PMC_CMD.format(c="WRITE_SIZE", d="write", w=w), "```", "",
+             f"bench: {line['value']} steps/s, {line['ms_per_step']} ms/step, "
+             f"{line['achieved_tflops']} TFLOP/s; dominant kernel `{roof['kernel']}` "
+             f"{roof['achieved']} {roof['unit']} = {roof['frac']:.4f} of {roof['peak']} ({roof['bound']})", "",
+             "## Per launch slot (one training step)", "",
+             "HBM bytes are the FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch) scaled by what "
+             f"they read for a 256 MiB device-to-device copy (x{scale['FETCH_SIZE']:.3f} fetch, "
+             f"x{scale['WRITE_SIZE']:.3f} write).", "",
+             "| slot | kernel | HIP-event avg us | trace avg us | fetch MB | write MB |",
+             "|---|---|---|---|---|---|"]
+    for i, (nm, ev) in enumerate(slots):
+        kn = _short(names[i])
+        lines.append(f"| {nm} | `{kn}` | {ev:.2f} | {trace_us[i]:.2f} | "
+                     f"{counters['FETCH_SIZE'][i] / 1e6:.2f} | {counters['WRITE_SIZE'][i] / 1e6:.2f} |")
+    lines += ["", "## kernel_stats (whole run)", "", "| kernel | calls | avg us | % |", "|---|---|---|---|"]
+    for r in stats[:12]:
+        kn = _short(r["Name"])[:90]
+        lines.append(f"| `{kn}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"{w}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(tpath) as f:
+            allrec = json.load(f)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[w] = {"kernel": roof["kernel"], "source_sha": source_digest(),
+                 "bytes_per_launch": round(counters["FETCH_SIZE"][dom] + counters["WRITE_SIZE"][dom]),
+                 "fetch_bytes": round(counters["FETCH_SIZE"][dom]),
+                 "write_bytes": round(counters["WRITE_SIZE"][dom]),
+                 "algorithmic_bytes": roof["algorithmic_bytes"],
+                 "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"]}
+    with open(tpath, "w") as f:
+        json.dump(allrec, f, indent=1, sort_keys=True)
+    print(f"wrote profiles/{w}.md and profiles/traffic.json[{w}]")
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize, args.workload, args.steps, args.warmup)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the path has no multi-GPU mode)", file=sys.stderr)
@@ -116,6 +261,13 @@ def main():
         x, t, _ = synth.workload_batch(w, s)
         batches.append((torch.from_numpy(x).to(dev), torch.from_numpy(t).to(dev)))
     loss_dev = torch.zeros(1, dtype=torch.float32, device=dev)
+    if args.calib_copy_mb > 0:
+        src = torch.ones(args.calib_copy_mb << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     torch.cuda.synchronize()
 
     def run(k, offset=0):
@@ -140,6 +292,7 @@ def main():
     rows = net.profile_read()
     net.profile(False)
     roof = roofline(rows, w.precision, pk)
+    roof["traffic"] = recorded_traffic(w.name, roof["kernel"])
     print("[bench] per-launch (ms avg): " + ", ".join(
         f"{r['name']}={r['total_ms'] / max(r['launches'], 1):.4f}" for r in rows),
         file=sys.stderr, flush=True)
