@@ -84,6 +84,12 @@ __device__ __forceinline__ void wait_stores() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Wait until this thread's outstanding vector-memory loads have landed (also
+// the loads that write LDS directly).
+__device__ __forceinline__ void wait_loads() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // Every thread calls this after its coherent stores; returns true in all
 // threads of the workgroup that took the last of `expected` tickets, and
 // resets the counter for the next launch.

@@ -292,6 +292,7 @@ hipError_t launch_gemm_bf16(const GemmLaunch& L, const GemmParams& p, hipStream_
     case TileCfg::T32x128: return dispatch_shape<Shape<32, 128, 32, 32>>(L, p, st);
     case TileCfg::T128x32: return dispatch_shape<Shape<128, 32, 32, 32>>(L, p, st);
     case TileCfg::T128x64: return dispatch_shape<Shape<128, 64, 64, 32>>(L, p, st);
+    default: break;
     }
     return hipErrorInvalidValue;
 }

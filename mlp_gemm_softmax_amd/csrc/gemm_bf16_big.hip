@@ -1,0 +1,366 @@
+// bf16-operand MFMA GEMM with 256 x 256 workgroup tiles for the large
+// products of the bf16 fast path (float32 accumulate, same layouts and
+// epilogues as the 128-wide bf16 kernel; one workgroup per output tile, no
+// K split).
+//
+// Why a second kernel: at 128 x 128 tiles the LDS traffic per MFMA flop
+// (fragment reads plus tile writes) exceeds what one CU's LDS delivers while
+// the matrix cores run at full rate, and the L2 -> CU operand traffic per
+// flop is twice that of a 256 x 256 tile.  Here
+//   - 4 waves, each owning a 128 x 128 sub-tile (16 accumulators of 32 x 32,
+//     v_mfma_f32_32x32x16_bf16), so every LDS fragment feeds 4 MFMAs;
+//   - operands go from global memory straight into LDS with
+//     buffer_load_dwordx4 ... lds (no staging registers, no ds_write); lanes
+//     whose element lies outside the matrix get an offset past the buffer's
+//     size, which the hardware turns into zeros;
+//   - two 64-deep k stages (2 x 64 KB of LDS, four static arrays): the loads
+//     of stage k+1 are in flight while stage k is multiplied; one barrier per
+//     stage;
+//   - bank-conflict-free layouts by XOR swizzles (the direct loads write 1 KB
+//     contiguous per wave instruction, so rows cannot be padded):
+//       k-contiguous operand: LDS row r (128 B = 64 k) holds 16-byte chunk j
+//         of the global row at chunk slot j ^ ((r >> 1) & 7); an MFMA operand
+//         is one ds_read_b128 per lane;
+//       r-contiguous operand: LDS k-row (512 B = 256 r) holds the 64-byte
+//         segment s (32 r) at slot s ^ (k & 3); an MFMA operand is two
+//         ds_read_b64_tr_b16 per lane (transpose reads, as in the 128-wide
+//         kernel), the four k-rows one read touches landing in distinct banks.
+#include "kernels.hpp"
+
+namespace mlp {
+namespace {
+
+constexpr int kT = 256;                  // tile rows and columns
+constexpr int kBK = 64;                  // k per stage
+constexpr int kThreads = 256;            // 4 waves, 2 x 2, 128 x 128 each
+constexpr int kOpBytes = kT * kBK * 2;   // one operand tile: 32 KB
+constexpr unsigned kOob = 0x80000000u;   // buffer offset that reads as zero
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Per-lane source offsets of one operand tile's 8 direct-load instructions
+// (this wave's share of 32 KB), relative to the tile's first k.
+template <bool KC>
+struct Loader {
+    unsigned off[8];   // element offset of the row (KC) or column (MN) part, or kOob outside the matrix
+    int kk[8];         // k of this lane's chunk within the stage
+
+    __device__ __forceinline__ void init(int64_t ld, int r0, int rmax, int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int q = wave * 8 + i;
+            if constexpr (KC) {
+                const int r = 8 * q + (lane >> 3);
+                const int j = (lane & 7) ^ ((r >> 1) & 7);
+                kk[i] = 8 * j;
+                off[i] = r0 + r < rmax ? (unsigned)((int64_t)(r0 + r) * ld) : kOob;
+            } else {
+                const int k = 2 * q + (lane >> 5);
+                const int p = lane & 31;
+                const int col = (((p >> 2) ^ (k & 3)) << 5) + 8 * (p & 3);
+                kk[i] = k;
+                off[i] = r0 + col < rmax ? (unsigned)(r0 + col) : kOob;
+            }
+        }
+    }
+
+    // Issue the 8 loads of stage k0 into `dst` (this operand's 32 KB tile).
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0, int kmax,
+                                          char* dst, int wave) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            unsigned o = kOob;
+            const int k = k0 + kk[i];
+            if (off[i] != kOob && k < kmax)
+                o = 2u * (KC ? off[i] + (unsigned)k : (unsigned)((int64_t)k * ld) + off[i]);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (wave * 8 + i) * 1024), 16, o, 0, 0, 0);
+        }
+    }
+};
+
+// Eight k-values (16c + 8*(lane/32) + 0..7) of tile row `base` + lane%32.
+template <bool KC>
+__device__ __forceinline__ bf16x8v frag(const char* s, int base, int c, int lane) {
+    if constexpr (KC) {
+        const int r = base + (lane & 31);
+        const int j = (2 * c + (lane >> 5)) ^ ((r >> 1) & 7);
+        return *reinterpret_cast<const bf16x8v*>(s + r * 128 + j * 16);
+    } else {
+        const int sl = lane & 15;
+        const int k = 16 * c + 8 * (lane >> 5) + (sl >> 2);
+        const int seg = (base >> 5) ^ (k & 3);
+        const char* p0 = s + k * 512 + seg * 64 + 32 * ((lane >> 4) & 1) + 8 * (sl & 3);
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)p0);
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(p0 + 4 * 512));
+        const short8v both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8v, both);
+    }
+}
+
+// Fused epilogue on four consecutive columns col..col+3 of one row (the
+// column count is a multiple of 8, so all four are inside or all outside).
+// `pre` is what epilogue_load fetched for the same place.
+struct Pre {
+    float4v w;        // Sgd: the f32 master weights
+    uint32_t m;       // MaskMul: four mask bytes
+};
+
+template <Epi EPI>
+__device__ __forceinline__ Pre epilogue_load(const GemmParams& p, int row, int col) {
+    Pre pre{};
+    const int64_t o = (int64_t)row * p.ldc + col;
+    if constexpr (EPI == Epi::Sgd) pre.w = *reinterpret_cast<const float4v*>(p.C + o);
+    if constexpr (EPI == Epi::MaskMul) pre.m = *reinterpret_cast<const uint32_t*>(p.mask + o);
+    return pre;
+}
+
+__device__ __forceinline__ uint2 pack_bf16x4(float4v v) {
+    return make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                      (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+}
+
+template <Epi EPI>
+__device__ __forceinline__ void epilogue4(const GemmParams& p, int row, int col, float4v v, const Pre& pre) {
+    const int64_t o = (int64_t)row * p.ldc + col;
+    if constexpr (EPI == Epi::Store || EPI == Epi::Grad) {
+        *reinterpret_cast<float4v*>(p.C + o) = v;
+    } else if constexpr (EPI == Epi::ReluMask) {
+        uint32_t m = 0;
+        float4v a;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const bool pos = v[c] > 0.f;
+            a[c] = pos ? v[c] : 0.f;
+            m |= (pos ? 1u : 0u) << (8 * c);
+        }
+        if (p.Cb) *reinterpret_cast<uint2*>(p.Cb + o) = pack_bf16x4(a);
+        else *reinterpret_cast<float4v*>(p.C + o) = a;
+        *reinterpret_cast<uint32_t*>(p.mask + o) = m;
+    } else if constexpr (EPI == Epi::MaskMul) {
+        float4v g;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) g[c] = ((pre.m >> (8 * c)) & 0xffu) ? v[c] : 0.f;
+        if (p.Cb) *reinterpret_cast<uint2*>(p.Cb + o) = pack_bf16x4(g);
+        else *reinterpret_cast<float4v*>(p.C + o) = g;
+    } else if constexpr (EPI == Epi::Sgd) {
+        float4v w;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) w[c] = pre.w[c] - p.lr * v[c];
+        *reinterpret_cast<float4v*>(p.C + o) = w;
+        if (p.Cb) *reinterpret_cast<uint2*>(p.Cb + o) = pack_bf16x4(w);
+    }
+}
+
+// Bytes from the first element to one past the last of a row-major matrix
+// with `rows` rows of `cols` used elements and leading dimension ld.
+__device__ __forceinline__ unsigned extent_bytes(int rows, int cols, int64_t ld) {
+    return (unsigned)(2 * ((int64_t)(rows - 1) * ld + cols));
+}
+
+// One k stage on LDS buffer (ca, cb); (na, nb) holds the next stage.
+// Chunks 0-2 multiply while the following chunk's fragments are read; then,
+// once this thread's loads of the next stage have landed and every wave has
+// passed the barrier, the loads of the stage after next go out into the
+// buffer just finished, and chunk 3 multiplies while chunk 0 of the next
+// stage is read.  The buffers are distinct LDS arrays known at compile time,
+// so the compiler's wait counting sees that reads of one buffer do not depend
+// on the direct loads in flight into the other.
+template <bool AKC, bool BKC>
+__device__ __forceinline__ void stage(float16v (&acc)[4][4], bf16x8v (&a)[2][4], bf16x8v (&b)[2][4],
+                                      char* ca, char* cb, const char* na, const char* nb,
+                                      const Loader<AKC>& la, const Loader<BKC>& lb,
+                                      __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                      const GemmParams& p, int kload, int kend, int wm, int wn,
+                                      int wave, int lane) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        const int f = c & 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[f ^ 1][i] = frag<AKC>(ca, wm * 128 + 32 * i, c + 1, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[f ^ 1][j] = frag<BKC>(cb, wn * 128 + 32 * j, c + 1, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[f][i], b[f][j], acc[i][j], 0, 0, 0);
+        // one fragment read after each MFMA
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_loads();
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[0][i] = frag<AKC>(na, wm * 128 + 32 * i, 0, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[0][j] = frag<BKC>(nb, wn * 128 + 32 * j, 0, lane);
+    la.issue(ra, p.lda, kload, kend, ca, wave);
+    lb.issue(rb, p.ldb, kload, kend, cb, wave);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][i], b[1][j], acc[i][j], 0, 0, 0);
+    // the fragment reads first (one after each MFMA), then the direct loads,
+    // so that no LDS read is ordered after a load into LDS
+#pragma unroll
+    for (int u = 0; u < 12; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <Layout LAY, Epi EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p) {
+    constexpr bool AKC = LAY != Layout::TN;   // A stored [M][K]
+    constexpr bool BKC = LAY == Layout::NT;   // B stored [N][K]
+    __shared__ __attribute__((aligned(16))) char sa0[kOpBytes], sb0[kOpBytes], sa1[kOpBytes], sb1[kOpBytes];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const int tile = xcd_remap(blockIdx.x, gridDim.x);
+    int tm, tn;
+    {
+        constexpr int GROUP = 8;
+        const int width = GROUP * p.tiles_n;
+        const int first = (tile / width) * GROUP;
+        const int gs = min(p.tiles_m - first, GROUP);
+        const int in = tile % width;
+        tm = first + in % gs;
+        tn = in / gs;
+    }
+    const int m0 = tm * kT, n0 = tn * kT;
+    const int kbeg = 0, kend = p.K;
+    const int nk = (p.K + kBK - 1) / kBK;
+
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(p.A), (short)0, AKC ? extent_bytes(p.M, p.K, p.lda) : extent_bytes(p.K, p.M, p.lda),
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(p.B), (short)0, BKC ? extent_bytes(p.N, p.K, p.ldb) : extent_bytes(p.K, p.N, p.ldb),
+        0x00020000);
+    Loader<AKC> la;
+    Loader<BKC> lb;
+    la.init(p.lda, m0, p.M, wave, lane);
+    lb.init(p.ldb, n0, p.N, wave, lane);
+
+    float16v acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    if (nk > 0) {
+        // Stage t lives in buffer t & 1; stages past the end load as zeros
+        // and are never multiplied.
+        la.issue(ra, p.lda, kbeg, kend, sa0, wave);
+        lb.issue(rb, p.ldb, kbeg, kend, sb0, wave);
+        wait_loads();
+        __syncthreads();
+        la.issue(ra, p.lda, kbeg + kBK, kend, sa1, wave);
+        lb.issue(rb, p.ldb, kbeg + kBK, kend, sb1, wave);
+        bf16x8v a[2][4], b[2][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[0][i] = frag<AKC>(sa0, wm * 128 + 32 * i, 0, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[0][j] = frag<BKC>(sb0, wn * 128 + 32 * j, 0, lane);
+        // Stages in pairs (buffer 0, buffer 1); an odd count multiplies one
+        // all-zero stage at the end, which adds exact zeros.
+        for (int kt = 0; kt < nk; kt += 2) {
+            stage<AKC, BKC>(acc, a, b, sa0, sb0, sa1, sb1, la, lb, ra, rb, p, kbeg + (kt + 2) * kBK, kend, wm,
+                            wn, wave, lane);
+            stage<AKC, BKC>(acc, a, b, sa1, sb1, sa0, sb0, la, lb, ra, rb, p, kbeg + (kt + 3) * kBK, kend, wm,
+                            wn, wave, lane);
+        }
+        // the zero-filling loads of the stages past the end
+        wait_loads();
+    }
+
+    // Epilogue.  Each wave stages its 128 x 128 accumulators through LDS, 32
+    // rows at a time (row stride 132 floats), and reads them back row-major:
+    // lane l takes float4 q of row 2q + l/32, columns 4(l%32)..+3, so every
+    // global access is a coalesced 16-byte (f32) or 8-byte (bf16) vector.
+    __syncthreads();   // every wave is done with the stage buffers
+    float* st = reinterpret_cast<float*>(wave == 0 ? sa0 : wave == 1 ? sb0 : wave == 2 ? sa1 : sb1);
+    constexpr int SP = 132;
+    const int rbase = m0 + wm * 128 + (lane >> 5);
+    const int col = n0 + wn * 128 + 4 * (lane & 31);
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                st[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * SP + 32 * j + (lane & 31)] = acc[i][j][r];
+        float4v v[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            v[q] = *reinterpret_cast<const float4v*>(st + (2 * q + (lane >> 5)) * SP + 4 * (lane & 31));
+        const int row0 = rbase + 32 * i;
+        Pre pre[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            if (row0 + 2 * q < p.M && col < p.N) pre[q] = epilogue_load<EPI>(p, row0 + 2 * q, col);
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            if (row0 + 2 * q < p.M && col < p.N) epilogue4<EPI>(p, row0 + 2 * q, col, v[q], pre[q]);
+    }
+}
+
+template <Layout LAY, Epi EPI>
+hipError_t go(const GemmParams& p, int grid, hipStream_t st) {
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<LAY, EPI>), dim3(grid), dim3(kThreads), 0, st, p);
+    return hipGetLastError();
+}
+
+
+}  // namespace
+
+bool gemm_bf16_big_fits(Layout lay, int M, int N, int K, int64_t lda, int64_t ldb) {
+    // 16-byte direct loads: contiguous extents and leading dimensions in
+    // multiples of 8 elements; buffer offsets below 2^31 bytes.
+    const bool akc = lay != Layout::TN, bkc = lay == Layout::NT;
+    const int acont = akc ? K : M, bcont = bkc ? K : N;
+    if (acont % 8 || bcont % 8 || lda % 8 || ldb % 8) return false;
+    const int64_t arows = akc ? M : K, brows = bkc ? N : K;
+    return 2 * arows * lda < (int64_t)kOob && 2 * brows * ldb < (int64_t)kOob;
+}
+
+hipError_t gemm_bf16_big_prepare() { return hipSuccess; }
+
+hipError_t launch_gemm_bf16_big(const GemmLaunch& L, const GemmParams& p, hipStream_t st) {
+    if (p.splits != 1 || L.grid != p.tiles_m * p.tiles_n) return hipErrorInvalidValue;
+    switch (L.layout) {
+    case Layout::NN:
+        if (L.epi == Epi::ReluMask) return go<Layout::NN, Epi::ReluMask>(p, L.grid, st);
+        if (L.epi == Epi::Store) return go<Layout::NN, Epi::Store>(p, L.grid, st);
+        break;
+    case Layout::NT:
+        if (L.epi == Epi::MaskMul) return go<Layout::NT, Epi::MaskMul>(p, L.grid, st);
+        break;
+    case Layout::TN:
+        if (L.epi == Epi::Sgd) return go<Layout::TN, Epi::Sgd>(p, L.grid, st);
+        if (L.epi == Epi::Grad) return go<Layout::TN, Epi::Grad>(p, L.grid, st);
+        break;
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mlp

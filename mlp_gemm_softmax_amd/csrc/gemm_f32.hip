@@ -315,6 +315,7 @@ hipError_t launch_gemm_f32(const GemmLaunch& L, const GemmParams& p, hipStream_t
     case TileCfg::T32x128: return dispatch_shape<Shape<32, 128, 32, 32>>(L, p, st);
     case TileCfg::T128x32: return dispatch_shape<Shape<128, 32, 32, 32>>(L, p, st);
     case TileCfg::T128x64: return dispatch_shape<Shape<128, 64, 64, 32>>(L, p, st);
+    default: break;
     }
     return hipErrorInvalidValue;
 }

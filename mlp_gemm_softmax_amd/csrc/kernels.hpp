@@ -41,7 +41,9 @@ struct GemmParams {
 };
 
 // Tile configurations of the MFMA GEMM (workgroup tile BM x BN, 4 waves).
-enum class TileCfg : int { T128x128 = 0, T64x64 = 1, T32x128 = 2, T128x32 = 3, T128x64 = 4 };
+// T256x256 is the bf16-only large-tile kernel (direct-to-LDS loads).
+enum class TileCfg : int { T128x128 = 0, T64x64 = 1, T32x128 = 2, T128x32 = 3, T128x64 = 4,
+                           T256x256 = 5 };
 void tile_shape(TileCfg cfg, int* bm, int* bn);
 
 struct GemmLaunch {
@@ -54,6 +56,12 @@ struct GemmLaunch {
 };
 
 hipError_t launch_gemm(const GemmLaunch& L, const GemmParams& p, hipStream_t s);
+
+// Large-tile bf16 kernel: whether its 16-byte direct loads suit the operands,
+// the one-time raise of its dynamic-LDS limit, and the launch.
+bool gemm_bf16_big_fits(Layout lay, int M, int N, int K, int64_t lda, int64_t ldb);
+hipError_t gemm_bf16_big_prepare();
+hipError_t launch_gemm_bf16_big(const GemmLaunch& L, const GemmParams& p, hipStream_t s);
 
 // Small float32 products: one 32x32 tile per workgroup, K split across its
 // `waves` waves and reduced in LDS (no split-K across workgroups).  Uses

@@ -35,6 +35,7 @@ hipError_t launch_gemm_f32(const GemmLaunch& L, const GemmParams& p, hipStream_t
 hipError_t launch_gemm_bf16(const GemmLaunch& L, const GemmParams& p, hipStream_t st);
 
 hipError_t launch_gemm(const GemmLaunch& L, const GemmParams& p, hipStream_t st) {
+    if (L.cfg == TileCfg::T256x256) return launch_gemm_bf16_big(L, p, st);
     return L.bf16 ? launch_gemm_bf16(L, p, st) : launch_gemm_f32(L, p, st);
 }
 
@@ -45,6 +46,7 @@ void tile_shape(TileCfg cfg, int* bm, int* bn) {
     case TileCfg::T32x128: *bm = 32; *bn = 128; return;
     case TileCfg::T128x32: *bm = 128; *bn = 32; return;
     case TileCfg::T128x64: *bm = 128; *bn = 64; return;
+    case TileCfg::T256x256: *bm = 256; *bn = 256; return;
     }
     *bm = *bn = 0;
 }
@@ -62,7 +64,7 @@ constexpr size_t kAlign = 256;
 thread_local std::string g_create_error;
 
 struct GemmPlan {
-    TileCfg cfg;
+    TileCfg cfg = TileCfg::T128x128;
     int splits = 1, kchunk = 0, tiles_m = 1, tiles_n = 1, grid = 1;
     int vec = 1;
     int small_waves = 0;    // > 0: the small-product kernel with this many waves
@@ -143,9 +145,21 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // ------------------------------------------------------------------ plans --
 
-GemmPlan plan_gemm(int M, int N, int K, bool bf16, bool kvec_ok) {
+GemmPlan plan_gemm(int M, int N, int K, bool bf16, bool kvec_ok, bool big_ok) {
     GemmPlan g;
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    if (bf16 && big_ok && tiles(256, 256) >= 128) {
+        // Large bf16 products: 256 x 256 tiles, one workgroup per CU and no K
+        // split (the partial round trip costs more than the idle CUs).
+        g.cfg = TileCfg::T256x256;
+        g.tiles_m = (M + 255) / 256;
+        g.tiles_n = (N + 255) / 256;
+        g.splits = 1;
+        g.kchunk = std::max(K, 1);
+        g.grid = g.tiles_m * g.tiles_n;
+        g.vec = 8;
+        return g;
+    }
     if (M <= 32) g.cfg = TileCfg::T32x128;
     else if (N <= 32) g.cfg = TileCfg::T128x32;
     else if (tiles(128, 128) >= 240) g.cfg = TileCfg::T128x128;
@@ -178,6 +192,14 @@ GemmPlan plan_gemm(int M, int N, int K, bool bf16, bool kvec_ok) {
     g.grid = nt * g.splits;
     g.vec = kvec_ok ? (bf16 ? 8 : 4) : 1;
     return g;
+}
+
+// Split-K partial floats a plan needs: [splits][M][N], or whole padded tiles
+// for the large-tile kernel.
+size_t partial_elems(const GemmPlan& g, int M, int N) {
+    if (g.splits <= 1) return 0;
+    if (g.cfg == TileCfg::T256x256) return (size_t)g.splits * g.tiles_m * 256 * g.tiles_n * 256;
+    return (size_t)g.splits * M * N;
 }
 
 SkinnyPlan plan_skinny_nn(int N, int K, int B) {
@@ -583,11 +605,11 @@ size_t plan_and_carve(mlp_ctx* c, char* base) {
         // contiguous run of the three products) to be multiples of the vector.
         const bool wide = din % vq == 0 && dout % vq == 0;
         // forward NN: A = a_l [B][din] (k-contiguous, K = din), B = W [din][dout]
-        c->fwd[l] = plan_gemm(B, dout, din, c->bf16, wide);
+        c->fwd[l] = plan_gemm(B, dout, din, c->bf16, wide, gemm_bf16_big_fits(Layout::NN, B, dout, din, din, dout));
         // dX NT: A = G [B][dout], B = W [din][dout] (both k-contiguous, K = dout)
-        c->dx[l] = plan_gemm(B, din, dout, c->bf16, wide);
+        c->dx[l] = plan_gemm(B, din, dout, c->bf16, wide, gemm_bf16_big_fits(Layout::NT, B, din, dout, dout, dout));
         // dW TN: A = a_l [B][din], B = G [B][dout]: M = din, N = dout, K = B
-        c->dw[l] = plan_gemm(din, dout, B, c->bf16, wide);
+        c->dw[l] = plan_gemm(din, dout, B, c->bf16, wide, gemm_bf16_big_fits(Layout::TN, din, dout, B, din, dout));
         for (const GemmPlan* g : {&c->fwd[l], &c->dx[l], &c->dw[l]}) {
             if (g->splits > 1) {
                 int bm, bn;
@@ -598,9 +620,9 @@ size_t plan_and_carve(mlp_ctx* c, char* base) {
                 max_tickets = std::max(max_tickets, (size_t)g->tiles_m * g->tiles_n);
             }
         }
-        if (c->fwd[l].splits > 1) max_partial = std::max(max_partial, (size_t)c->fwd[l].splits * B * dout);
-        if (c->dx[l].splits > 1) max_partial = std::max(max_partial, (size_t)c->dx[l].splits * B * din);
-        if (c->dw[l].splits > 1) max_partial = std::max(max_partial, (size_t)c->dw[l].splits * din * dout);
+        max_partial = std::max(max_partial, partial_elems(c->fwd[l], B, dout));
+        max_partial = std::max(max_partial, partial_elems(c->dx[l], B, din));
+        max_partial = std::max(max_partial, partial_elems(c->dw[l], din, dout));
     }
     if (c->head) {
         const size_t nblk = (size_t)(B + c->head_rb - 1) / c->head_rb;
@@ -702,6 +724,17 @@ mlp_status mlp_create(const mlp_config* cfg, void* workspace, size_t bytes, mlp_
     }
     plan_and_carve(c, (char*)workspace);
     build_slots(c);
+    bool big = false;
+    for (int l = 0; l < c->L; ++l)
+        for (const GemmPlan* g : {&c->fwd[l], &c->dx[l], &c->dw[l]}) big = big || g->cfg == TileCfg::T256x256;
+    if (big) {
+        const hipError_t he = gemm_bf16_big_prepare();
+        if (he != hipSuccess) {
+            set_err(nullptr, MLP_ERR_HIP, "large-tile GEMM set-up: %s", hipGetErrorString(he));
+            delete c;
+            return MLP_ERR_HIP;
+        }
+    }
     if (c->head) {
         const hipError_t he = head_prepare();
         if (he != hipSuccess) {

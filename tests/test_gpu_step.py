@@ -46,6 +46,8 @@ EXACT_CASES = [
     ((2080, 1040, 40), 512, "f32", 1),       # tiled TN and NT with split-K, ragged tiles
     ((200, 300, 36), 64, "bf16", 1),
     ((120, 136, 24), 256, "bf16", 1),
+    ((256, 4096, 40), 2048, "bf16", 1),      # 256-wide bf16 tiles, no split (forward)
+    ((2056, 4096, 1024), 2048, "bf16", 1),   # 256-wide bf16 tiles in all three layouts, ragged K and M
 ]
 
 
