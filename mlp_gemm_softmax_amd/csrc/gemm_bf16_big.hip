@@ -1,7 +1,6 @@
 // bf16-operand MFMA GEMM with 256 x 256 workgroup tiles for the large
 // products of the bf16 fast path (float32 accumulate, same layouts and
-// epilogues as the 128-wide bf16 kernel; one workgroup per output tile, no
-// K split).
+// epilogues as the 128-wide bf16 kernel, K split in up to 4 parts).
 //
 // Why a second kernel: at 128 x 128 tiles the LDS traffic per MFMA flop
 // (fragment reads plus tile writes) exceeds what one CU's LDS delivers while
@@ -35,6 +34,7 @@ constexpr int kBK = 64;                  // k per stage
 constexpr int kThreads = 256;            // 4 waves, 2 x 2, 128 x 128 each
 constexpr int kOpBytes = kT * kBK * 2;   // one operand tile: 32 KB
 constexpr unsigned kOob = 0x80000000u;   // buffer offset that reads as zero
+constexpr int kMaxSplits = 4;            // K splits the reduction handles
 
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
@@ -210,14 +210,14 @@ __device__ __forceinline__ void stage(float16v (&acc)[4][4], bf16x8v (&a)[2][4],
     // the fragment reads first (one after each MFMA), then the direct loads,
     // so that no LDS read is ordered after a load into LDS
 #pragma unroll
-    for (int u = 0; u < 12; ++u) {
+    for (int u = 0; u < 6; ++u) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -227,12 +227,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
     constexpr bool AKC = LAY != Layout::TN;   // A stored [M][K]
     constexpr bool BKC = LAY == Layout::NT;   // B stored [N][K]
     __shared__ __attribute__((aligned(16))) char sa0[kOpBytes], sb0[kOpBytes], sa1[kOpBytes], sb1[kOpBytes];
+    __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
-    const int tile = xcd_remap(blockIdx.x, gridDim.x);
+    // Split-major order: the workgroups that share an XCD (consecutive ids)
+    // work on the same k range of neighbouring tiles and share operands in L2.
+    const int ntile = p.tiles_m * p.tiles_n;
+    const int id = xcd_remap(blockIdx.x, gridDim.x);
+    const int split = id / ntile;
+    const int tile = id % ntile;
     int tm, tn;
     {
         constexpr int GROUP = 8;
@@ -244,8 +250,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
         tn = in / gs;
     }
     const int m0 = tm * kT, n0 = tn * kT;
-    const int kbeg = 0, kend = p.K;
-    const int nk = (p.K + kBK - 1) / kBK;
+    const int kbeg = split * p.kchunk;
+    const int kend = min(p.K, kbeg + p.kchunk);
+    const int nk = kend > kbeg ? (kend - kbeg + kBK - 1) / kBK : 0;
 
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(p.A), (short)0, AKC ? extent_bytes(p.M, p.K, p.lda) : extent_bytes(p.K, p.M, p.lda),
@@ -301,6 +308,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
     constexpr int SP = 132;
     const int rbase = m0 + wm * 128 + (lane >> 5);
     const int col = n0 + wn * 128 + 4 * (lane & 31);
+    // Split-K partials, per (tile, split) 256 x 256 floats in the order
+    // [wave][i][q][component][lane]: the thread that writes a value in one
+    // split reads the same place in the others, and every access is a
+    // contiguous 256-byte wave store or load.
+    constexpr int64_t kPart = (int64_t)kT * kT;
+    float* mypart = p.partials + (int64_t)tile * p.splits * kPart + wave * 16384 + lane;
 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -313,6 +326,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
 #pragma unroll
         for (int q = 0; q < 16; ++q)
             v[q] = *reinterpret_cast<const float4v*>(st + (2 * q + (lane >> 5)) * SP + 4 * (lane & 31));
+        if (p.splits > 1) {
+            float* dst = mypart + split * kPart + i * 4096;
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) store_coherent(dst + (q * 4 + c) * 64, v[q][c]);
+            continue;
+        }
         const int row0 = rbase + 32 * i;
         Pre pre[16];
 #pragma unroll
@@ -321,6 +342,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
 #pragma unroll
         for (int q = 0; q < 16; ++q)
             if (row0 + 2 * q < p.M && col < p.N) epilogue4<EPI>(p, row0 + 2 * q, col, v[q], pre[q]);
+    }
+    if (p.splits == 1) return;
+
+    // Deterministic split-K: the workgroup that takes the tile's last integer
+    // ticket adds the partials of all splits, its own included, in split
+    // order.  The loads of every split for half a row block (up to 128 per
+    // thread) are issued before the first add.
+    if (!last_arrival(&p.tickets[tile], (unsigned)p.splits, &s_last)) return;
+    for (int h = 0; h < 8; ++h) {
+        const int i = h >> 1, q0 = (h & 1) * 8;
+        const float* src = mypart + i * 4096 + q0 * 256;
+        float x[kMaxSplits][8][4];
+        // unconditional loads (splits past the last re-read it and are
+        // dropped below), so that none waits behind a branch
+#pragma unroll
+        for (int t = 0; t < kMaxSplits; ++t) {
+            const float* st_t = src + min(t, p.splits - 1) * kPart;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) x[t][u][c] = load_coherent(st_t + (u * 4 + c) * 64);
+        }
+        const int row0 = rbase + 32 * i + 2 * q0;
+        Pre pre[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (row0 + 2 * u < p.M && col < p.N) pre[u] = epilogue_load<EPI>(p, row0 + 2 * u, col);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            float4v sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < kMaxSplits; ++t)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) sum[c] += t < p.splits ? x[t][u][c] : 0.f;
+            if (row0 + 2 * u < p.M && col < p.N) epilogue4<EPI>(p, row0 + 2 * u, col, sum, pre[u]);
+        }
     }
 }
 
@@ -346,7 +403,8 @@ bool gemm_bf16_big_fits(Layout lay, int M, int N, int K, int64_t lda, int64_t ld
 hipError_t gemm_bf16_big_prepare() { return hipSuccess; }
 
 hipError_t launch_gemm_bf16_big(const GemmLaunch& L, const GemmParams& p, hipStream_t st) {
-    if (p.splits != 1 || L.grid != p.tiles_m * p.tiles_n) return hipErrorInvalidValue;
+    if (p.splits < 1 || p.splits > kMaxSplits || L.grid != p.tiles_m * p.tiles_n * p.splits)
+        return hipErrorInvalidValue;
     switch (L.layout) {
     case Layout::NN:
         if (L.epi == Epi::ReluMask) return go<Layout::NN, Epi::ReluMask>(p, L.grid, st);

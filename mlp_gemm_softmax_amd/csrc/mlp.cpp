@@ -148,17 +148,26 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 GemmPlan plan_gemm(int M, int N, int K, bool bf16, bool kvec_ok, bool big_ok) {
     GemmPlan g;
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    if (bf16 && big_ok && tiles(256, 256) >= 128) {
-        // Large bf16 products: 256 x 256 tiles, one workgroup per CU and no K
-        // split (the partial round trip costs more than the idle CUs).
-        g.cfg = TileCfg::T256x256;
-        g.tiles_m = (M + 255) / 256;
-        g.tiles_n = (N + 255) / 256;
-        g.splits = 1;
-        g.kchunk = std::max(K, 1);
-        g.grid = g.tiles_m * g.tiles_n;
-        g.vec = 8;
-        return g;
+    if (bf16 && big_ok) {
+        // Large bf16 products: 256 x 256 tiles, one workgroup per CU; K is
+        // split (up to 4 ways, at least 512 deep) while the tiles fill fewer
+        // than half the CUs.
+        const int nt = tiles(256, 256);
+        int s = 1;
+        if (nt < 128) s = std::max(1, std::min({4, (256 + nt - 1) / nt, K / 512}));
+        if (nt * s >= 128) {
+            int kchunk = (K + s - 1) / s;
+            kchunk = (kchunk + 63) / 64 * 64;
+            s = (K + kchunk - 1) / kchunk;
+            g.cfg = TileCfg::T256x256;
+            g.tiles_m = (M + 255) / 256;
+            g.tiles_n = (N + 255) / 256;
+            g.splits = s;
+            g.kchunk = s > 1 ? kchunk : std::max(K, 1);
+            g.grid = nt * s;
+            g.vec = 8;
+            return g;
+        }
     }
     if (M <= 32) g.cfg = TileCfg::T32x128;
     else if (N <= 32) g.cfg = TileCfg::T128x32;

@@ -47,7 +47,8 @@ EXACT_CASES = [
     ((200, 300, 36), 64, "bf16", 1),
     ((120, 136, 24), 256, "bf16", 1),
     ((256, 4096, 40), 2048, "bf16", 1),      # 256-wide bf16 tiles, no split (forward)
-    ((2056, 4096, 1024), 2048, "bf16", 1),   # 256-wide bf16 tiles in all three layouts, ragged K and M
+    ((2056, 4096, 1024), 2048, "bf16", 1),   # 256-wide bf16 tiles in all three layouts, ragged K and M, 4-way K split
+    ((2056, 2048, 1024), 2048, "bf16", 1),   # 256-wide bf16 tiles, 2- and 4-way K splits
 ]
 
 
