@@ -82,12 +82,15 @@ struct SkinnyParams {
     int splits, kchunk;
     float* partials;
     unsigned* tickets;
+    const float* act;  // NT with fused update: a [MB][K] of the layer's input
+    float* wout;       // NT with fused update: W (Sgd, in place) or dW (Grad)
 };
 struct SkinnyLaunch {
     Layout layout;
     Epi epi;
     int grid;
     int waves;       // waves per workgroup
+    bool fused_update = false;   // NT: also apply the layer's dW (+ SGD) in the same pass
 };
 hipError_t launch_skinny(const SkinnyLaunch& L, const SkinnyParams& p, hipStream_t s);
 int skinny_tn_rows();   // rows of W per dW+SGD workgroup

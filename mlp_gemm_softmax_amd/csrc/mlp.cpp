@@ -266,6 +266,12 @@ void build_slots(mlp_ctx* c) {
     }
     for (int l = top; l >= 0; --l) {
         const double din = c->dims[l], dout = c->dims[l + 1];
+        if (l > 0 && c->skinny) {
+            // dX and dW + SGD in one pass over W: W read and written once
+            add(std::string(kind) + "_nt_mask_sgd_l" + std::to_string(l), 4.0 * B * din * dout,
+                8.0 * din * dout + 4.0 * B * dout + 4.0 * B * din + B * din * 5.0);
+            continue;
+        }
         if (l > 0)
             add(std::string(kind) + "_nt_mask_l" + std::to_string(l), 2.0 * B * din * dout,
                 B * dout * e + din * dout * e + B * din * (1 + e));
@@ -464,25 +470,45 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
         const int din = c->dims[l], dout = c->dims[l + 1];
         const void* Wop = c->bf16 ? (const void*)c->Wb[l] : (const void*)c->W[l];
         const void* Gnext = nullptr;
+        const bool grads = mode == Mode::Grads;
+        if (l > 0 && c->skinny) {
+            // one pass over W_l: G_{l-1} (from the old W_l) and the update
+            void* out = c->dz[pp];
+            pp ^= 1;
+            r.run(slot++, [&] {
+                SkinnyLaunch sl;
+                sl.layout = Layout::NT;
+                sl.epi = grads ? Epi::Grad : Epi::Sgd;
+                sl.grid = c->sdx[l].grid;
+                sl.waves = 8;
+                sl.fused_update = true;
+                SkinnyParams sp{};
+                sp.A = c->W[l];
+                sp.B = (const float*)G;
+                sp.MB = B;
+                sp.K = din;
+                sp.N = dout;
+                sp.C = (float*)out;
+                sp.mask = c->mask[l];
+                sp.lr = lr;
+                sp.act = (const float*)c->act[l];
+                sp.wout = grads ? dw_out[l] : c->W[l];
+                return launch_skinny(sl, sp, c->stream);
+            });
+            G = out;
+            continue;
+        }
         if (l > 0) {
             void* out = c->dz[pp];
             pp ^= 1;
-            if (c->skinny) {
-                r.run(slot++, [&] {
-                    return run_skinny(c, c->sdx[l], Layout::NT, Epi::MaskMul, (const float*)Wop,
-                                      (const float*)G, din, dout, (float*)out, c->mask[l], 0.f);
-                });
-            } else {
-                r.run(slot++, [&] {
-                    return run_gemm(c, c->dx[l], Layout::NT, Epi::MaskMul, G, dout, Wop, dout, B, din,
-                                    dout, c->bf16 ? nullptr : (float*)out,
-                                    c->bf16 ? (bf16_t*)out : nullptr, c->mask[l], 0.f);
-                });
-            }
+            r.run(slot++, [&] {
+                return run_gemm(c, c->dx[l], Layout::NT, Epi::MaskMul, G, dout, Wop, dout, B, din, dout,
+                                c->bf16 ? nullptr : (float*)out, c->bf16 ? (bf16_t*)out : nullptr, c->mask[l],
+                                0.f);
+            });
             Gnext = out;
         }
         const void* a_in = l == 0 ? (c->bf16 ? (const void*)c->xb : (const void*)x) : c->act[l];
-        const bool grads = mode == Mode::Grads;
         float* Wdst = grads ? dw_out[l] : c->W[l];
         bf16_t* Wbdst = (!grads && c->bf16) ? c->Wb[l] : nullptr;
         if (c->skinny) {

@@ -3,10 +3,12 @@
 // shaped for HBM streaming rather than for the matrix cores' peak:
 //
 //   skinny_nn  out[b][n] = sum_k x[b][k] W[k][n]               forward
-//   skinny_nt  out[b][k] = mask[b][k] * sum_n G[b][n] W[k][n]   dX
-//   skinny_tn  W[k][n]  -= lr * sum_b a[b][k] G[b][n]          dW + SGD
+//   skinny_ntu out[b][k] = mask[b][k] * sum_n G[b][n] W[k][n]   dX, and
+//              W[k][n] -= lr * sum_b a[b][k] G[b][n]           its dW + SGD,
+//              in one pass over W (hidden layers)
+//   skinny_tn  W[k][n]  -= lr * sum_b a[b][k] G[b][n]          dW + SGD (first layer)
 //
-// skinny_nn and skinny_nt reduce inside v_mfma_f32_16x16x4f32 (the batch is
+// skinny_nn and skinny_ntu reduce inside v_mfma_f32_16x16x4f32 (the batch is
 // the MFMA's 16-wide M or N side, rows >= B are zero), so every 16-byte load
 // of W feeds four MFMAs and no cross-lane reduction is spent on K.  skinny_tn
 // is a rank-B update streamed row by row: W is read once and written once.
@@ -152,13 +154,26 @@ __global__ __launch_bounds__(NW * kWave) void skinny_nn(SkinnyParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dX: out[b][k] = mask[b][k] * sum_n G[b][n] W[k][n], W stored [Kout][N].
+// dX and dW + SGD of one layer in a single pass over W (which both read):
+//   out[b][k] = mask[b][k] * sum_n G[b][n] W[k][n]      (the old W)
+//   W[k][n]  -= lr * sum_b a[b][k] G[b][n]              (or store the gradient)
 // A workgroup of NW waves covers RG*16 rows of W; wave w takes the w-th slice
-// of n.  MFMA: A = 16 rows of W, B = G^T (16 batch columns, zero past B);
-// lane (i = lane%16, g) supplies W[k0 + i][c + q] and G[i][c + q] to MFMA q
-// for its float4 at column c, so one float4 of each feeds four MFMAs.
-template <int NW, int RG>
-__global__ __launch_bounds__(NW * kWave) void skinny_nt(SkinnyParams p) {
+// of the columns, 32 at a time: lane group g takes columns n + 16h + 4g .. +3
+// (h = 0, 1).  The dX MFMA has A = 16 rows of W and B = G^T (16 batch
+// columns, zero past B): lane (i = lane%16, g) supplies W[k0 + i][c + q] and
+// G[i][c + q] to MFMA q for its float4 at column c, so one float4 of each
+// feeds four MFMAs; the waves' sums meet in LDS in wave order.  The update
+// of those four elements comes from v_mfma_f32_16x16x4f32 as well: with
+// A[m][j] = G[4s + j][n + 16h + m] and B[j][c] = a[4s + j][k0 + 16r + c], the
+// 16x16 result D[m][c] = sum_j G a is dW^T of a 16 x 16 block, and lane
+// (i, g) holds D[4g + e][i] = dW[k0 + 16r + i][n + 16h + 4g + e], exactly the
+// float4 of W it loaded.  So each element of W is read once, feeds the dX
+// reduction, and is written once, by the same lane.  Loads and stores of W
+// are ordinary (cached): one instruction covers 64 bytes of each of 16 rows,
+// and the L2 merges the two halves of every 128-byte line before it goes to
+// HBM (non-temporal stores of half lines measured at half the bandwidth).
+template <int NW, int RG, int S, Epi EPI>
+__global__ __launch_bounds__(NW * kWave) void skinny_ntu(SkinnyParams p) {
     __shared__ float4v red[NW - 1][RG][kWave];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -171,52 +186,79 @@ __global__ __launch_bounds__(NW * kWave) void skinny_nt(SkinnyParams p) {
 
     float4v acc[RG];
     const float* __restrict__ Wr[RG];
+    float* __restrict__ Or[RG];
     bool rok[RG];
+    float av[RG][S];   // a[4s + g][k0 + 16r + i]
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
         acc[r] = {0.f, 0.f, 0.f, 0.f};
         const int krow = k0 + 16 * r + i;
         rok[r] = krow < p.K;
         Wr[r] = p.A + (int64_t)krow * p.N;
+        Or[r] = p.wout + (int64_t)krow * p.N;
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            const int b = 4 * t + g;
+            av[r][t] = (rok[r] && b < p.MB) ? p.act[(int64_t)b * p.K + krow] : 0.f;
+        }
     }
     const float* __restrict__ Gr = p.B + (int64_t)(bok ? i : 0) * p.N;
-    // 32 n per step: lane group g takes n + 8g .. n + 8g + 7 (two float4s),
-    // so the four groups read whole 128-byte lines of each W row.  Loads are
-    // branch-free (out-of-range lanes read the row start and zero the value)
-    // and the next step's loads are issued before this step's MFMAs.
     const float4v zero = {0.f, 0.f, 0.f, 0.f};
-    float4v gv[2], w[RG][2], gn[2], wn[RG][2];
-    auto fetch = [&](int n, float4v* gd, float4v (*wd)[2]) {
-        const int c = n + 8 * g;
+    // gv: G[i][cols] for the dX MFMA; gu: G[4s + g][n + 16h + i] for the update
+    float4v gv[2], w[RG][2], gvn[2], wn[RG][2];
+    float gu[2][S], gun[2][S];
+    auto fetch = [&](int n, float4v* gd, float4v (*wd)[2], float (*ud)[S]) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const bool cok = c + 4 * h < nend;  // N is a multiple of 4
-            const float4v v = ld4(cok ? Gr + c + 4 * h : Gr);
+            const int c = n + 16 * h + 4 * g;
+            const bool cok = c < nend;   // N is a multiple of 4
+            const float4v v = ld4(cok ? Gr + c : Gr);
             gd[h] = (cok && bok) ? v : zero;
 #pragma unroll
             for (int r = 0; r < RG; ++r) {
                 const bool ok = cok && rok[r];
-                const float4v x = ld4(ok ? Wr[r] + c + 4 * h : p.A);
+                const float4v x = ld4(ok ? Wr[r] + c : p.A);
                 wd[r][h] = ok ? x : zero;
+            }
+            const int cu = n + 16 * h + i;
+#pragma unroll
+            for (int t = 0; t < S; ++t) {
+                const int b = 4 * t + g;
+                const bool ok = cu < nend && b < p.MB;
+                const float x = p.B[ok ? (int64_t)b * p.N + cu : 0];
+                ud[h][t] = ok ? x : 0.f;
             }
         }
     };
-    if (nbeg < nend) fetch(nbeg, gn, wn);
+    if (nbeg < nend) fetch(nbeg, gvn, wn, gun);
     for (int n = nbeg; n < nend; n += 32) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            gv[h] = gn[h];
+            gv[h] = gvn[h];
 #pragma unroll
             for (int r = 0; r < RG; ++r) w[r][h] = wn[r][h];
+#pragma unroll
+            for (int t = 0; t < S; ++t) gu[h][t] = gun[h][t];
         }
-        if (n + 32 < nend) fetch(n + 32, gn, wn);
+        if (n + 32 < nend) fetch(n + 32, gvn, wn, gun);
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h) {
+            const int c = n + 16 * h + 4 * g;
 #pragma unroll
-            for (int r = 0; r < RG; ++r)
+            for (int r = 0; r < RG; ++r) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     acc[r] = __builtin_amdgcn_mfma_f32_16x16x4f32(w[r][h][q], gv[h][q], acc[r], 0, 0, 0);
+                float4v d = zero;
+#pragma unroll
+                for (int t = 0; t < S; ++t) d = __builtin_amdgcn_mfma_f32_16x16x4f32(gu[h][t], av[r][t], d, 0, 0, 0);
+                if (c < nend && rok[r]) {
+                    float4v* dst = reinterpret_cast<float4v*>(Or[r] + c);
+                    if constexpr (EPI == Epi::Sgd) *dst = w[r][h] - p.lr * d;
+                    else *dst = d;
+                }
+            }
+        }
     }
     if (wave > 0) {
 #pragma unroll
@@ -224,9 +266,9 @@ __global__ __launch_bounds__(NW * kWave) void skinny_nt(SkinnyParams p) {
     }
     __syncthreads();
     if (wave != 0) return;
-    for (int w = 0; w < NW - 1; ++w)
+    for (int v = 0; v < NW - 1; ++v)
 #pragma unroll
-        for (int r = 0; r < RG; ++r) acc[r] += red[w][r][lane];
+        for (int r = 0; r < RG; ++r) acc[r] += red[v][r][lane];
     // acc[r][e] = out[b = lane%16][k = k0 + 16r + 4*(lane/16) + e]
     const int b = lane & 15;
     if (b >= p.MB) return;
@@ -331,8 +373,19 @@ hipError_t launch_skinny(const SkinnyLaunch& L, const SkinnyParams& p, hipStream
             hipLaunchKernelGGL((skinny_nn<16, Epi::Store>), dim3(L.grid), dim3(16 * 64), 0, s, p);
         return hipGetLastError();
     case Layout::NT:
-        hipLaunchKernelGGL((skinny_nt<8, 2>), dim3(L.grid), dim3(8 * 64), 0, s, p);
-        return hipGetLastError();
+        if (L.fused_update) {
+            if (L.epi == Epi::Sgd) {
+                if (p.MB <= 4) hipLaunchKernelGGL((skinny_ntu<8, 2, 1, Epi::Sgd>), dim3(L.grid), dim3(8 * 64), 0, s, p);
+                else if (p.MB <= 8) hipLaunchKernelGGL((skinny_ntu<8, 2, 2, Epi::Sgd>), dim3(L.grid), dim3(8 * 64), 0, s, p);
+                else hipLaunchKernelGGL((skinny_ntu<8, 2, 4, Epi::Sgd>), dim3(L.grid), dim3(8 * 64), 0, s, p);
+            } else {
+                if (p.MB <= 4) hipLaunchKernelGGL((skinny_ntu<8, 2, 1, Epi::Grad>), dim3(L.grid), dim3(8 * 64), 0, s, p);
+                else if (p.MB <= 8) hipLaunchKernelGGL((skinny_ntu<8, 2, 2, Epi::Grad>), dim3(L.grid), dim3(8 * 64), 0, s, p);
+                else hipLaunchKernelGGL((skinny_ntu<8, 2, 4, Epi::Grad>), dim3(L.grid), dim3(8 * 64), 0, s, p);
+            }
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
     case Layout::TN:
         if (p.MB <= 4) return go_tn<4>(L, p, s);
         if (p.MB <= 8) return go_tn<8>(L, p, s);
