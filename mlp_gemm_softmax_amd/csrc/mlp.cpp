@@ -214,9 +214,9 @@ size_t partial_elems(const GemmPlan& g, int M, int N) {
 SkinnyPlan plan_skinny_nn(int N, int K, int B) {
     (void)B;
     SkinnyPlan s;
-    // 64 output columns per workgroup of 16 waves; K splits only while the
-    // grid still fits one workgroup per CU (a partial second round of
-    // workgroups would double the kernel time).
+    // 64 output columns per workgroup of 16 waves (one such workgroup per
+    // CU); K splits only while the grid still fits one round of workgroups
+    // (measured: 8-wave workgroups with deeper splits stream no faster).
     const int ncg = (N + 63) / 64;
     s.waves = 16;
     int sp = std::max(1, std::min(256 / ncg, K / 256));

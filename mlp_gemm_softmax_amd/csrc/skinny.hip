@@ -116,19 +116,33 @@ __global__ __launch_bounds__(NW * kWave) void skinny_nn(SkinnyParams p) {
         }
         if (!last_arrival(&p.tickets[cg], (unsigned)p.splits, &s_last)) return;
         if (wave != 0) return;
+        // Add every split's partial, this workgroup's own included, in split
+        // order.  Four splits' loads are issued at a time, unconditionally
+        // (clamped in-range addresses; the extra ones are dropped), so that
+        // none waits behind a branch.
         float4v sum[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) sum[q] = {0.f, 0.f, 0.f, 0.f};
-        for (int t = 0; t < p.splits; ++t) {
+        const int nc = nok ? n : 0;
+        for (int t0 = 0; t0 < p.splits; t0 += 4) {
+            float x[4][4][4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = 4 * g + r;
-                const bool ok = m < p.MB && nok;
-                const float* src = p.partials + ((int64_t)t * p.MB + m) * p.N + n;
+            for (int u = 0; u < 4; ++u) {
+                const int t = min(t0 + u, p.splits - 1);
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    sum[q][r] += (t == split || !ok) ? acc[q][r] : load_coherent(src + q);
+                for (int r = 0; r < 4; ++r) {
+                    const int m = min(4 * g + r, p.MB - 1);
+                    const float* src = p.partials + ((int64_t)t * p.MB + m) * p.N + nc;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) x[u][r][q] = load_coherent(src + q);
+                }
             }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) sum[q][r] += t0 + u < p.splits ? x[u][r][q] : 0.f;
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[q] = sum[q];
@@ -366,11 +380,19 @@ hipError_t launch_skinny(const SkinnyLaunch& L, const SkinnyParams& p, hipStream
     if (p.MB < 1 || p.MB > 16) return hipErrorInvalidValue;
     switch (L.layout) {
     case Layout::NN:
-        if (L.waves != 16) return hipErrorInvalidValue;
-        if (L.epi == Epi::ReluMask)
-            hipLaunchKernelGGL((skinny_nn<16, Epi::ReluMask>), dim3(L.grid), dim3(16 * 64), 0, s, p);
-        else
-            hipLaunchKernelGGL((skinny_nn<16, Epi::Store>), dim3(L.grid), dim3(16 * 64), 0, s, p);
+        if (L.waves == 8) {
+            if (L.epi == Epi::ReluMask)
+                hipLaunchKernelGGL((skinny_nn<8, Epi::ReluMask>), dim3(L.grid), dim3(8 * 64), 0, s, p);
+            else
+                hipLaunchKernelGGL((skinny_nn<8, Epi::Store>), dim3(L.grid), dim3(8 * 64), 0, s, p);
+        } else if (L.waves == 16) {
+            if (L.epi == Epi::ReluMask)
+                hipLaunchKernelGGL((skinny_nn<16, Epi::ReluMask>), dim3(L.grid), dim3(16 * 64), 0, s, p);
+            else
+                hipLaunchKernelGGL((skinny_nn<16, Epi::Store>), dim3(L.grid), dim3(16 * 64), 0, s, p);
+        } else {
+            return hipErrorInvalidValue;
+        }
         return hipGetLastError();
     case Layout::NT:
         if (L.fused_update) {
