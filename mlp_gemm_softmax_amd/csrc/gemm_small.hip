@@ -24,19 +24,26 @@ constexpr int kDepth = 8;   // chunks of 8 k in flight per wave
 // The four k-values of chunk c (k = k0 + 4h + 0..3) for row r of an operand.
 // KC: element (r, k) at g + r*ld + k (16-byte load when VEC == 4);
 // otherwise at g + k*ld + r (four 4-byte loads, coalesced across lanes).
+// Rows and k past the matrix are read from clamped in-range addresses and
+// the values are used as they are: rows past M or N only reach outputs that
+// are never stored, and the k tail is zeroed where the chunk is multiplied.
+// Keeping the loads free of selects and branches lets the loads of all
+// chunks stay in flight together.
 template <bool KC, int VEC>
 __device__ __forceinline__ float4v load_op(const float* __restrict__ g, int64_t ld, int r, int rmax,
                                            int k, int kmax) {
-    float4v v = {0.f, 0.f, 0.f, 0.f};
-    if (r >= rmax) return v;
+    const int64_t rc = r < rmax ? r : rmax - 1;
     if constexpr (KC && VEC == 4) {
-        if (k < kmax) v = *reinterpret_cast<const float4v*>(g + (int64_t)r * ld + k);
+        return *reinterpret_cast<const float4v*>(g + rc * ld + (k < kmax ? k : 0));   // kmax % 4 == 0
     } else {
+        float4v v;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (k + q < kmax) v[q] = KC ? g[(int64_t)r * ld + k + q] : g[(int64_t)(k + q) * ld + r];
+        for (int q = 0; q < 4; ++q) {
+            const int64_t kc = k + q < kmax ? k + q : kmax - 1;
+            v[q] = KC ? g[rc * ld + kc] : g[kc * ld + rc];
+        }
+        return v;
     }
-    return v;
 }
 
 template <Epi EPI>
@@ -80,10 +87,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmParams p) {
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
     float4v qa[kDepth], qb[kDepth];
+    if (c0 < c1) {
+        // chunks past this wave's slice load a clamped chunk and are never used
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-        const int k = 8 * (c0 + d) + 4 * h;
-        if (c0 + d < c1) {
+        for (int d = 0; d < kDepth; ++d) {
+            const int k = 8 * min(c0 + d, c1 - 1) + 4 * h;
             qa[d] = load_op<AKC, VEC>(A, p.lda, ra, p.M, k, p.K);
             qb[d] = load_op<BKC, VEC>(B, p.ldb, rb, p.N, k, p.K);
         }
@@ -92,7 +100,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmParams p) {
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
             if (c + d < c1) {
-                const float4v a = qa[d], b = qb[d];
+                float4v a = qa[d], b = qb[d];
+                if (8 * (c + d) + 8 > p.K) {   // the chunk holding the k tail
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const bool kok = 8 * (c + d) + 4 * h + q < p.K;
+                        a[q] = kok ? a[q] : 0.f;
+                        b[q] = kok ? b[q] : 0.f;
+                    }
+                }
                 const int cn = c + d + kDepth;
                 if (cn < c1) {
                     const int k = 8 * cn + 4 * h;
@@ -122,15 +138,116 @@ __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmParams p) {
     }
 }
 
+// The same scheme with 32 x 16 tiles on v_mfma_f32_16x16x4f32, twice as many
+// workgroups for the same product (the f32 matrix-core time of one CU, not
+// latency, bounds a 32 x 32 tile of a K = 784 product).  A chunk is 16 k:
+// lane (i = lane%16, g = lane/16) loads k = k0 + 4g .. +3 of A rows
+// m0 + i and m0 + 16 + i and of B column n0 + i, and MFMA q (0..3) takes
+// component q of each, so one 16-byte (or four coalesced 4-byte) load feeds
+// four MFMAs.  Result lane l holds rows 4(l/16)..+3 of column l%16.
+template <bool KC, int VEC>
+__device__ __forceinline__ float4v load_op16(const float* __restrict__ g, int64_t ld, int r, int rmax, int k,
+                                             int kmax) {
+    const int64_t rc = r < rmax ? r : rmax - 1;
+    if constexpr (KC && VEC == 4) {
+        return *reinterpret_cast<const float4v*>(g + rc * ld + (k < kmax ? k : 0));   // kmax % 4 == 0
+    } else {
+        float4v v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int64_t kc = k + q < kmax ? k + q : kmax - 1;
+            v[q] = KC ? g[rc * ld + kc] : g[kc * ld + rc];
+        }
+        return v;
+    }
+}
+
 template <int NW, Layout LAY, int VEC, Epi EPI>
-hipError_t go(const GemmParams& p, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_small_kernel<NW, LAY, VEC, EPI>), dim3(grid), dim3(NW * 64), 0, st, p);
+__global__ __launch_bounds__(NW * 64) void gemm_small16_kernel(GemmParams p) {
+    constexpr bool AKC = LAY != Layout::TN;   // A stored [M][K]
+    constexpr bool BKC = LAY == Layout::NT;   // B stored [N][K]
+    constexpr int D = kDepth / 2;             // chunks of 16 k in flight per wave
+    __shared__ float4v red[NW][2][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tiles_n = (p.N + 15) / 16;
+    const int id = xcd_remap(blockIdx.x, gridDim.x);
+    const int m0 = (id / tiles_n) * 32, n0 = (id % tiles_n) * 16;
+    const int i = lane & 15, g = lane >> 4;
+
+    const int chunks = (p.K + 15) / 16;
+    const int per = (chunks + NW - 1) / NW;
+    const int c0 = wave * per, c1 = min(chunks, c0 + per);
+
+    const float* A = static_cast<const float*>(p.A);
+    const float* B = static_cast<const float*>(p.B);
+    float4v acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    float4v qa[D][2], qb[D];
+    auto fetch = [&](int d, int c) {
+        const int k = 16 * c + 4 * g;
+        qa[d][0] = load_op16<AKC, VEC>(A, p.lda, m0 + i, p.M, k, p.K);
+        qa[d][1] = load_op16<AKC, VEC>(A, p.lda, m0 + 16 + i, p.M, k, p.K);
+        qb[d] = load_op16<BKC, VEC>(B, p.ldb, n0 + i, p.N, k, p.K);
+    };
+    if (c0 < c1) {
+        // chunks past this wave's slice load a clamped chunk and are never used
+#pragma unroll
+        for (int d = 0; d < D; ++d) fetch(d, min(c0 + d, c1 - 1));
+    }
+    for (int c = c0; c < c1; c += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (c + d < c1) {
+                float4v a0 = qa[d][0], a1 = qa[d][1], b = qb[d];
+                if (16 * (c + d) + 16 > p.K) {   // the chunk holding the k tail
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const bool kok = 16 * (c + d) + 4 * g + q < p.K;
+                        a0[q] = kok ? a0[q] : 0.f;
+                        a1[q] = kok ? a1[q] : 0.f;
+                        b[q] = kok ? b[q] : 0.f;
+                    }
+                }
+                if (c + d + D < c1) fetch(d, c + d + D);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[q], b[q], acc[0], 0, 0, 0);
+                    acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[q], b[q], acc[1], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    red[wave][0][lane] = acc[0];
+    red[wave][1][lane] = acc[1];
+    __syncthreads();
+    // 512 outputs: thread t < 128 takes row block t/64 and lane position t%64
+    // and adds the waves' float4s in wave order 0..NW-1.
+    if (threadIdx.x < 128) {
+        const int rbk = threadIdx.x >> 6, l = threadIdx.x & 63;
+        float4v v = red[0][rbk][l];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += red[w][rbk][l];
+        const int col = n0 + (l & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = m0 + 16 * rbk + 4 * (l >> 4) + e;
+            if (row < p.M && col < p.N) epilogue<EPI>(p, row, col, v[e]);
+        }
+    }
+}
+
+template <int NW, Layout LAY, int VEC, Epi EPI>
+hipError_t go(const GemmParams& p, int grid, bool t16, hipStream_t st) {
+    if (t16) hipLaunchKernelGGL((gemm_small16_kernel<NW, LAY, VEC, EPI>), dim3(grid), dim3(NW * 64), 0, st, p);
+    else hipLaunchKernelGGL((gemm_small_kernel<NW, LAY, VEC, EPI>), dim3(grid), dim3(NW * 64), 0, st, p);
     return hipGetLastError();
 }
 
 template <int NW, Layout LAY, Epi EPI>
 hipError_t go_vec(const GemmLaunch& L, const GemmParams& p, hipStream_t st) {
-    return L.vec == 4 ? go<NW, LAY, 4, EPI>(p, L.grid, st) : go<NW, LAY, 1, EPI>(p, L.grid, st);
+    const bool t16 = L.cfg == TileCfg::T32x16;
+    return L.vec == 4 ? go<NW, LAY, 4, EPI>(p, L.grid, t16, st) : go<NW, LAY, 1, EPI>(p, L.grid, t16, st);
 }
 
 template <int NW>

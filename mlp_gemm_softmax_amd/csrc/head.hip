@@ -5,10 +5,12 @@
 //
 // Each workgroup (16 waves) owns RB batch rows; W_L [H][C] and the rows'
 // activations, labels and masks are staged in LDS.  Per workgroup:
-//   logits[b][c] = sum_h a[b][h] W[h][c]                (fixed order)
+//   logits[b][c] = sum_h a[b][h] W[h][c]
 //   lane-per-row softmax-CE -> dlogits, row loss         (as the CE kernel)
 //   G[b][h] = mask[b][h] * sum_c dlogits[b][c] W[h][c]   (old W)
 //   P_blk[h][c] = sum_{b in block} a[b][h] dlogits[b][c] (partial dW)
+// The three products run as 16x16 blocks on v_mfma_f32_16x16x4f32 with
+// operands read from LDS (zero past the edges), one wave per block.
 // The workgroup that draws the last integer ticket adds the partials in block
 // order, applies W -= lr * dW (or stores dW) and averages the row losses in
 // row order.  Every other workgroup has finished reading W before it takes
@@ -23,6 +25,7 @@ namespace mlp {
 namespace {
 
 constexpr int kThreads = 1024;
+constexpr int kU = 8;   // staging loads in flight per thread
 
 __global__ __launch_bounds__(kThreads) void head_kernel(HeadParams p) {
     extern __shared__ float lds[];
@@ -35,37 +38,84 @@ __global__ __launch_bounds__(kThreads) void head_kernel(HeadParams p) {
     float* sT = sZ + RB * C;          // [RB][C]  labels
     uint8_t* sM = (uint8_t*)(sT + RB * C);   // [RB][H] mask
     const int tid = threadIdx.x;
-    const int blk = blockIdx.x;
-    const int row0 = blk * RB;
+    const int blk_id = blockIdx.x;
+    const int row0 = blk_id * RB;
     const int rows = min(RB, p.B - row0);
 
-    // Stage everything the block reads once, all loads in flight together.
-    for (int e = tid; e < H * C; e += kThreads) sW[(e / C) * CP + e % C] = p.W[e];
-    for (int e = tid; e < rows * H; e += kThreads) {
-        sA[(e / H) * HS + e % H] = p.A[(int64_t)row0 * H + e];
-        sM[e] = p.mask[(int64_t)row0 * H + e];
+    // Stage everything the block reads once.  Loads go out kU at a time per
+    // thread from clamped (in-range) addresses before any is stored, so the
+    // staging costs one memory round trip rather than one per element.
+    {
+        const float* gA = p.A + (int64_t)row0 * H;
+        const uint8_t* gM = p.mask + (int64_t)row0 * H;
+        const float* gT = p.labels + (int64_t)row0 * C;
+        const int nA = rows * H, nW = H * C, nT = rows * C;
+        for (int e0 = tid; e0 < nA; e0 += kU * kThreads) {
+            float a[kU];
+            uint8_t m[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int e = min(e0 + u * kThreads, nA - 1);
+                a[u] = gA[e];
+                m[u] = gM[e];
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int e = e0 + u * kThreads;
+                if (e < nA) {
+                    sA[(e / H) * HS + e % H] = a[u];
+                    sM[e] = m[u];
+                }
+            }
+        }
+        for (int e0 = tid; e0 < nW; e0 += kU * kThreads) {
+            float w[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) w[u] = p.W[min(e0 + u * kThreads, nW - 1)];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int e = e0 + u * kThreads;
+                if (e < nW) sW[(e / C) * CP + e % C] = w[u];
+            }
+        }
+        for (int e0 = tid; e0 < nT; e0 += kU * kThreads) {
+            float t[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) t[u] = gT[min(e0 + u * kThreads, nT - 1)];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int e = e0 + u * kThreads;
+                if (e < nT) sT[e] = t[u];
+            }
+        }
     }
-    for (int e = tid; e < rows * C; e += kThreads) sT[e] = p.labels[(int64_t)row0 * C + e];
     __syncthreads();
 
-    // logits; four interleaved partial sums (h mod 4) combined in fixed order
-    for (int e = tid; e < rows * C; e += kThreads) {
-        const int b = e / C, c = e % C;
-        const float* a = sA + b * HS;
-        const float* w = sW + c;
-        float z0 = 0.f, z1 = 0.f, z2 = 0.f, z3 = 0.f;
-        int h = 0;
-#pragma unroll 4
-        for (; h + 4 <= H; h += 4) {
-            z0 += a[h] * w[h * CP];
-            z1 += a[h + 1] * w[(h + 1) * CP];
-            z2 += a[h + 2] * w[(h + 2) * CP];
-            z3 += a[h + 3] * w[(h + 3) * CP];
+    // logits Z = A W: 16x16 output blocks on v_mfma_f32_16x16x4f32 (the
+    // K = H sum runs inside the matrix core, 4 h per step), one wave per
+    // block.  Operand lanes: A[m = l%16][k = l/16], B[k = l/16][n = l%16];
+    // result lane l holds rows 4(l/16)..+3 of column l%16.
+    const int lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lk = lane >> 4;
+    const int RBb = (rows + 15) / 16, CB = (C + 15) / 16, HB = (H + 15) / 16;
+    for (int blk = wave; blk < RBb * CB; blk += kThreads / kWave) {
+        const int b0 = (blk / CB) * 16, c0 = (blk % CB) * 16;
+        const int ba = b0 + li, cb = c0 + li;
+        float4v acc = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < H; k0 += 4) {
+            const int k = k0 + lk;
+            const float av = (ba < rows && k < H) ? sA[ba * HS + k] : 0.f;
+            const float wv = (cb < C && k < H) ? sW[k * CP + cb] : 0.f;
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wv, acc, 0, 0, 0);
         }
-        for (; h < H; ++h) z0 += a[h] * w[h * CP];
-        const float z = (z0 + z1) + (z2 + z3);
-        sZ[b * C + c] = z;
-        if (p.logits) p.logits[(int64_t)(row0 + b) * C + c] = z;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int bb = b0 + 4 * lk + e;
+            if (bb < rows && cb < C) {
+                sZ[bb * C + cb] = acc[e];
+                if (p.logits) p.logits[(int64_t)(row0 + bb) * C + cb] = acc[e];
+            }
+        }
     }
     __syncthreads();
 
@@ -93,44 +143,43 @@ __global__ __launch_bounds__(kThreads) void head_kernel(HeadParams p) {
     }
     __syncthreads();
 
-    // dX of the last layer through the ReLU mask (four outputs per pass)
-    for (int e0 = tid; e0 < rows * H; e0 += 4 * kThreads) {
-        float g[4];
-        int eo[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int e = e0 + u * kThreads;
-            eo[u] = e;
-            g[u] = 0.f;
-            if (e < rows * H) {
-                const float* z = sZ + (e / H) * C;
-                const float* w = sW + (e % H) * CP;
-                for (int c = 0; c < C; ++c) g[u] += z[c] * w[c];
-            }
+    // dX of the last layer through the ReLU mask: G = (dZ W^T) . m, blocks
+    // of 16 rows x 16 h with K = C on the matrix core.
+    for (int blk = wave; blk < RBb * HB; blk += kThreads / kWave) {
+        const int b0 = (blk / HB) * 16, h0 = (blk % HB) * 16;
+        const int ba = b0 + li, hb = h0 + li;
+        float4v acc = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < C; k0 += 4) {
+            const int k = k0 + lk;
+            const float zv = (ba < rows && k < C) ? sZ[ba * C + k] : 0.f;
+            const float wv = (hb < H && k < C) ? sW[hb * CP + k] : 0.f;
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(zv, wv, acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (eo[u] < rows * H) {
-                p.G[(int64_t)row0 * H + eo[u]] = sM[eo[u]] ? g[u] : 0.f;
-            }
+        for (int e = 0; e < 4; ++e) {
+            const int bb = b0 + 4 * lk + e;
+            if (bb < rows && hb < H) p.G[(int64_t)(row0 + bb) * H + hb] = sM[bb * H + hb] ? acc[e] : 0.f;
         }
     }
 
-    // partial dW over this block's rows; four interleaved partial sums
-    float* part = p.partials + (int64_t)blk * H * C;
-    for (int e = tid; e < H * C; e += kThreads) {
-        const int h = e / C, c = e % C;
-        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-        int b = 0;
-#pragma unroll 4
-        for (; b + 4 <= rows; b += 4) {
-            s0 += sA[b * HS + h] * sZ[b * C + c];
-            s1 += sA[(b + 1) * HS + h] * sZ[(b + 1) * C + c];
-            s2 += sA[(b + 2) * HS + h] * sZ[(b + 2) * C + c];
-            s3 += sA[(b + 3) * HS + h] * sZ[(b + 3) * C + c];
+    // partial dW over this block's rows: P = A^T dZ, blocks of 16 h x 16
+    // classes with K = the block's rows.
+    float* part = p.partials + (int64_t)blk_id * H * C;
+    for (int blk = wave; blk < HB * CB; blk += kThreads / kWave) {
+        const int h0 = (blk / CB) * 16, c0 = (blk % CB) * 16;
+        const int ha = h0 + li, cb = c0 + li;
+        float4v acc = {0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < rows; k0 += 4) {
+            const int k = k0 + lk;
+            const float av = (ha < H && k < rows) ? sA[k * HS + ha] : 0.f;
+            const float zv = (cb < C && k < rows) ? sZ[k * C + cb] : 0.f;
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, zv, acc, 0, 0, 0);
         }
-        for (; b < rows; ++b) s0 += sA[b * HS + h] * sZ[b * C + c];
-        store_coherent(part + e, (s0 + s1) + (s2 + s3));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int hh = h0 + 4 * lk + e;
+            if (hh < H && cb < C) store_coherent(part + hh * C + cb, acc[e]);
+        }
     }
 
     if (!last_arrival(p.ticket, gridDim.x, &s_last)) return;
@@ -138,16 +187,18 @@ __global__ __launch_bounds__(kThreads) void head_kernel(HeadParams p) {
     // dW in block order, then the update (or the stored gradient).  The loads
     // of up to 8 blocks are issued before any is added, so the reduction costs
     // a few memory round trips rather than one per block.
+    // The loads of 16 blocks' partials are issued, unconditionally from
+    // clamped addresses (extra ones dropped), before any is added.
     const int nblk = gridDim.x;
     for (int e = tid; e < H * C; e += kThreads) {
         float s = 0.f;
-        for (int k0 = 0; k0 < nblk; k0 += 8) {
-            float v[8];
+        for (int k0 = 0; k0 < nblk; k0 += 16) {
+            float v[16];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                v[u] = k0 + u < nblk ? load_coherent(p.partials + (int64_t)(k0 + u) * H * C + e) : 0.f;
+            for (int u = 0; u < 16; ++u)
+                v[u] = load_coherent(p.partials + (int64_t)min(k0 + u, nblk - 1) * H * C + e);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) s += v[u];
+            for (int u = 0; u < 16; ++u) s += k0 + u < nblk ? v[u] : 0.f;
         }
         if (p.dW) p.dW[e] = s;
         else p.W[e] = sW[(e / C) * CP + e % C] - p.lr * s;
@@ -157,12 +208,9 @@ __global__ __launch_bounds__(kThreads) void head_kernel(HeadParams p) {
     for (int b0 = tid; b0 < p.B; b0 += 4 * kThreads) {
         float v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int b = b0 + u * kThreads;
-            v[u] = b < p.B ? load_coherent(p.rowloss + b) : 0.f;
-        }
+        for (int u = 0; u < 4; ++u) v[u] = load_coherent(p.rowloss + min(b0 + u * kThreads, p.B - 1));
 #pragma unroll
-        for (int u = 0; u < 4; ++u) s += v[u];
+        for (int u = 0; u < 4; ++u) s += b0 + u * kThreads < p.B ? v[u] : 0.f;
     }
     s = wave_sum(s);
     __shared__ float part_sum[kThreads / kWave];

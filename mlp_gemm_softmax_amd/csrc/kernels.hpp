@@ -42,8 +42,9 @@ struct GemmParams {
 
 // Tile configurations of the MFMA GEMM (workgroup tile BM x BN, 4 waves).
 // T256x256 is the bf16-only large-tile kernel (direct-to-LDS loads).
+// T32x32 / T32x16 are the small-product kernel's tiles (one per workgroup).
 enum class TileCfg : int { T128x128 = 0, T64x64 = 1, T32x128 = 2, T128x32 = 3, T128x64 = 4,
-                           T256x256 = 5 };
+                           T256x256 = 5, T32x32 = 6, T32x16 = 7 };
 void tile_shape(TileCfg cfg, int* bm, int* bn);
 
 struct GemmLaunch {
@@ -63,9 +64,10 @@ bool gemm_bf16_big_fits(Layout lay, int M, int N, int K, int64_t lda, int64_t ld
 hipError_t gemm_bf16_big_prepare();
 hipError_t launch_gemm_bf16_big(const GemmLaunch& L, const GemmParams& p, hipStream_t s);
 
-// Small float32 products: one 32x32 tile per workgroup, K split across its
-// `waves` waves and reduced in LDS (no split-K across workgroups).  Uses
-// L.layout, L.epi, L.vec and L.grid = ceil(M/32) * ceil(N/32).
+// Small float32 products: one 32x32 (L.cfg == T32x32) or 32x16 (T32x16)
+// tile per workgroup, K split across its `waves` waves and reduced in LDS (no
+// split-K across workgroups).  Uses L.layout, L.epi, L.vec, L.cfg and
+// L.grid = ceil(M/32) * ceil(N/32 or 16).
 int gemm_small_waves(int M, int N, int K);
 hipError_t launch_gemm_small(const GemmLaunch& L, const GemmParams& p, int waves, hipStream_t s);
 

@@ -47,6 +47,8 @@ void tile_shape(TileCfg cfg, int* bm, int* bn) {
     case TileCfg::T128x32: *bm = 128; *bn = 32; return;
     case TileCfg::T128x64: *bm = 128; *bn = 64; return;
     case TileCfg::T256x256: *bm = 256; *bn = 256; return;
+    case TileCfg::T32x32: *bm = 32; *bn = 32; return;
+    case TileCfg::T32x16: *bm = 32; *bn = 16; return;
     }
     *bm = *bn = 0;
 }
@@ -182,11 +184,14 @@ GemmPlan plan_gemm(int M, int N, int K, bool bf16, bool kvec_ok, bool big_ok) {
     const int bk = bf16 ? 64 : 32;
     const int t32 = ((M + 31) / 32) * ((N + 31) / 32);
     if (!bf16 && nt < 256 && t32 <= 1024) {
-        // Under-filled product: K split inside the workgroup, no partials.
+        // Under-filled product: K split inside the workgroup, no partials;
+        // 32 x 16 tiles while 32 x 32 ones would leave CUs idle.
         g.small_waves = gemm_small_waves(M, N, K);
         g.splits = 1;
         g.kchunk = std::max(K, 1);
-        g.grid = t32;
+        const int t16 = ((M + 31) / 32) * ((N + 15) / 16);
+        g.cfg = t32 < 256 ? TileCfg::T32x16 : TileCfg::T32x32;
+        g.grid = t32 < 256 ? t16 : t32;
         g.vec = kvec_ok ? 4 : 1;
         return g;
     }
