@@ -25,11 +25,14 @@ namespace mlp {
 namespace {
 
 constexpr int kThreads = 1024;
+constexpr int kNumWaves = kThreads / kWave;
 constexpr int kU = 8;   // staging loads in flight per thread
 
 __global__ __launch_bounds__(kThreads) void head_kernel(HeadParams p) {
     extern __shared__ float lds[];
     __shared__ int s_last;
+    __shared__ float4v s_red[kNumWaves][kWave];   // K-split partial logits
+    __shared__ float s_part[kNumWaves];
     const int H = p.H, C = p.C, CP = p.CP, RB = p.RB;
     const int HS = H | 1;             // odd LDS row stride: rows land on distinct banks
     float* sW = lds;                  // [H][CP]
@@ -92,54 +95,86 @@ __global__ __launch_bounds__(kThreads) void head_kernel(HeadParams p) {
     __syncthreads();
 
     // logits Z = A W: 16x16 output blocks on v_mfma_f32_16x16x4f32 (the
-    // K = H sum runs inside the matrix core, 4 h per step), one wave per
-    // block.  Operand lanes: A[m = l%16][k = l/16], B[k = l/16][n = l%16];
-    // result lane l holds rows 4(l/16)..+3 of column l%16.
+    // K = H sum runs inside the matrix core, 4 h per step).  Operand lanes:
+    // A[m = l%16][k = l/16], B[k = l/16][n = l%16]; the result lane l holds
+    // rows 4(l/16)..+3 of column l%16.  The waves split each block's K range
+    // into KS parts, whose sums meet in LDS and are added in part order.
     const int lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lk = lane >> 4;
     const int RBb = (rows + 15) / 16, CB = (C + 15) / 16, HB = (H + 15) / 16;
-    for (int blk = wave; blk < RBb * CB; blk += kThreads / kWave) {
-        const int b0 = (blk / CB) * 16, c0 = (blk % CB) * 16;
-        const int ba = b0 + li, cb = c0 + li;
-        float4v acc = {0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < H; k0 += 4) {
-            const int k = k0 + lk;
-            const float av = (ba < rows && k < H) ? sA[ba * HS + k] : 0.f;
-            const float wv = (cb < C && k < H) ? sW[k * CP + cb] : 0.f;
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wv, acc, 0, 0, 0);
+    {
+        const int nb = RBb * CB;                       // <= 8 (RB <= 64, C <= 32)
+        const int KS = kNumWaves / nb >= 1 ? kNumWaves / nb : 1;
+        const int kpart = ((H + 4 * KS - 1) / (4 * KS)) * 4;
+        if (wave < nb * KS) {
+            const int blk = wave % nb, part = wave / nb;
+            const int b0 = (blk / CB) * 16, c0 = (blk % CB) * 16;
+            const int ba = b0 + li, cb = c0 + li;
+            float4v acc = {0.f, 0.f, 0.f, 0.f};
+            const int kb = part * kpart, ke = min(H, kb + kpart);
+            for (int k0 = kb; k0 < ke; k0 += 4) {
+                const int k = k0 + lk;
+                const float av = (ba < rows && k < ke) ? sA[ba * HS + k] : 0.f;
+                const float wv = (cb < C && k < ke) ? sW[k * CP + cb] : 0.f;
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wv, acc, 0, 0, 0);
+            }
+            s_red[wave][lane] = acc;
         }
+        __syncthreads();
+        if (wave < nb) {
+            const int blk = wave;
+            const int b0 = (blk / CB) * 16, c0 = (blk % CB) * 16;
+            const int cb = c0 + li;
+            float4v z = s_red[blk][lane];
+            for (int part = 1; part < KS; ++part) z += s_red[part * nb + blk][lane];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int bb = b0 + 4 * lk + e;
-            if (bb < rows && cb < C) {
-                sZ[bb * C + cb] = acc[e];
-                if (p.logits) p.logits[(int64_t)(row0 + bb) * C + cb] = acc[e];
+            for (int e = 0; e < 4; ++e) {
+                const int bb = b0 + 4 * lk + e;
+                if (bb < rows && cb < C) {
+                    sZ[bb * C + cb] = z[e];
+                    if (p.logits) p.logits[(int64_t)(row0 + bb) * C + cb] = z[e];
+                }
             }
         }
     }
     __syncthreads();
 
-    // softmax cross-entropy, one lane per row
-    if (tid < rows) {
-        const int b = tid, row = row0 + b;
-        const float* t = sT + b * C;
-        float* z = sZ + b * C;
-        float mx = -INFINITY;
-        for (int c = 0; c < C; ++c) mx = fmaxf(mx, z[c]);
-        float se = 0.f, st = 0.f, stz = 0.f;
-        for (int c = 0; c < C; ++c) {
-            const float tc = t[c];
-            st += tc;
-            stz += tc * z[c];
-            se += expf(z[c] - mx);
+    // softmax cross-entropy, 16 lanes per row (classes j and j + 16 of the
+    // row on lane j); max and sums by a fixed xor butterfly inside the
+    // 16-lane group.
+    {
+        const int b = tid >> 4, j = tid & 15;
+        if (b < rows) {
+            const int row = row0 + b;
+            const float* t = sT + b * C;
+            float* z = sZ + b * C;
+            const bool v0 = j < C, v1 = j + 16 < C;
+            const float z0 = v0 ? z[j] : -INFINITY, z1 = v1 ? z[j + 16] : -INFINITY;
+            const float t0 = v0 ? t[j] : 0.f, t1 = v1 ? t[j + 16] : 0.f;
+            float mx = fmaxf(z0, z1);
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+            const float e0 = v0 ? expf(z0 - mx) : 0.f, e1 = v1 ? expf(z1 - mx) : 0.f;
+            float se = e0 + e1, st = t0 + t1, stz = (v0 ? t0 * z0 : 0.f) + (v1 ? t1 * z1 : 0.f);
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1) {
+                se += __shfl_xor(se, o, 16);
+                st += __shfl_xor(st, o, 16);
+                stz += __shfl_xor(stz, o, 16);
+            }
+            const float lse = mx + logf(se);
+            if (v0) {
+                const float g = (e0 / se * st - t0) * p.inv_b;
+                z[j] = g;
+                p.dlogits[(int64_t)row * C + j] = g;
+            }
+            if (v1) {
+                const float g = (e1 / se * st - t1) * p.inv_b;
+                z[j + 16] = g;
+                p.dlogits[(int64_t)row * C + j + 16] = g;
+            }
+            if (j == 0) store_coherent(p.rowloss + row, st * lse - stz);
         }
-        const float lse = mx + logf(se);
-        for (int c = 0; c < C; ++c) {
-            const float g = (expf(z[c] - mx) / se * st - t[c]) * p.inv_b;
-            z[c] = g;
-            p.dlogits[(int64_t)row * C + c] = g;
-        }
-        store_coherent(p.rowloss + row, st * lse - stz);
     }
     __syncthreads();
 
@@ -187,8 +222,13 @@ __global__ __launch_bounds__(kThreads) void head_kernel(HeadParams p) {
     // dW in block order, then the update (or the stored gradient).  The loads
     // of up to 8 blocks are issued before any is added, so the reduction costs
     // a few memory round trips rather than one per block.
-    // The loads of 16 blocks' partials are issued, unconditionally from
-    // clamped addresses (extra ones dropped), before any is added.
+    // The row losses' loads go out first (kept in registers), then the loads
+    // of 16 blocks' partials at a time, unconditionally from clamped
+    // addresses (extra ones dropped), before any is added.
+    float lv[4];
+    const int nl = (p.B + kThreads - 1) / kThreads;   // row losses per thread (<= 4 kept)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) lv[u] = load_coherent(p.rowloss + min(tid + u * kThreads, p.B - 1));
     const int nblk = gridDim.x;
     for (int e = tid; e < H * C; e += kThreads) {
         float s = 0.f;
@@ -203,22 +243,17 @@ __global__ __launch_bounds__(kThreads) void head_kernel(HeadParams p) {
         if (p.dW) p.dW[e] = s;
         else p.W[e] = sW[(e / C) * CP + e % C] - p.lr * s;
     }
-    // mean loss in row order
+    // mean loss in a fixed order: per thread, a wave butterfly, waves in order
     float s = 0.f;
-    for (int b0 = tid; b0 < p.B; b0 += 4 * kThreads) {
-        float v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = load_coherent(p.rowloss + min(b0 + u * kThreads, p.B - 1));
-#pragma unroll
-        for (int u = 0; u < 4; ++u) s += b0 + u * kThreads < p.B ? v[u] : 0.f;
-    }
+    for (int u = 0; u < 4; ++u) s += u < nl && tid + u * kThreads < p.B ? lv[u] : 0.f;
+    for (int b = tid + 4 * kThreads; b < p.B; b += kThreads) s += load_coherent(p.rowloss + b);
     s = wave_sum(s);
-    __shared__ float part_sum[kThreads / kWave];
-    if ((tid & 63) == 0) part_sum[tid >> 6] = s;
+    if ((tid & 63) == 0) s_part[tid >> 6] = s;
     __syncthreads();
     if (tid == 0) {
         float tot = 0.f;
-        for (int w = 0; w < kThreads / kWave; ++w) tot += part_sum[w];
+        for (int w = 0; w < kNumWaves; ++w) tot += s_part[w];
         *p.loss = tot * p.inv_b;
     }
 }
