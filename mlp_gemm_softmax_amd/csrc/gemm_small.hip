@@ -15,6 +15,7 @@
 // chunk c, lanes 0-31 hold k = 8c..8c+3 and lanes 32-63 hold k = 8c+4..8c+7,
 // and MFMA q (0..3) takes the q-th of those four values.
 #include "kernels.hpp"
+#include "tail.hpp"
 
 namespace mlp {
 namespace {
@@ -162,16 +163,28 @@ __device__ __forceinline__ float4v load_op16(const float* __restrict__ g, int64_
     }
 }
 
-template <int NW, Layout LAY, int VEC, Epi EPI>
-__global__ __launch_bounds__(NW * 64) void gemm_small16_kernel(GemmParams p) {
+// With TAIL, the first tail_jobs(t.H) workgroups run the fused output
+// layer's tail jobs (tail.hpp) instead of tiles.
+template <int NW, Layout LAY, int VEC, Epi EPI, bool TAIL>
+__global__ __launch_bounds__(NW * 64) void gemm_small16_kernel(GemmParams p, TailParams t) {
     constexpr bool AKC = LAY != Layout::TN;   // A stored [M][K]
     constexpr bool BKC = LAY == Layout::NT;   // B stored [N][K]
     constexpr int D = kDepth / 2;             // chunks of 16 k in flight per wave
     __shared__ float4v red[NW][2][64];
+    int bid = blockIdx.x, nb = gridDim.x;
+    if constexpr (TAIL) {
+        const int jobs = tail_jobs(t.H);
+        if (bid < jobs) {
+            tail_job<NW>(t, bid, &red[0][0][0]);
+            return;
+        }
+        bid -= jobs;
+        nb -= jobs;
+    }
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int tiles_n = (p.N + 15) / 16;
-    const int id = xcd_remap(blockIdx.x, gridDim.x);
+    const int id = xcd_remap(bid, nb);
     const int m0 = (id / tiles_n) * 32, n0 = (id % tiles_n) * 16;
     const int i = lane & 15, g = lane >> 4;
 
@@ -239,9 +252,29 @@ __global__ __launch_bounds__(NW * 64) void gemm_small16_kernel(GemmParams p) {
 
 template <int NW, Layout LAY, int VEC, Epi EPI>
 hipError_t go(const GemmParams& p, int grid, bool t16, hipStream_t st) {
-    if (t16) hipLaunchKernelGGL((gemm_small16_kernel<NW, LAY, VEC, EPI>), dim3(grid), dim3(NW * 64), 0, st, p);
-    else hipLaunchKernelGGL((gemm_small_kernel<NW, LAY, VEC, EPI>), dim3(grid), dim3(NW * 64), 0, st, p);
+    const TailParams none{};
+    if (t16)
+        hipLaunchKernelGGL((gemm_small16_kernel<NW, LAY, VEC, EPI, false>), dim3(grid), dim3(NW * 64), 0, st, p,
+                           none);
+    else
+        hipLaunchKernelGGL((gemm_small_kernel<NW, LAY, VEC, EPI>), dim3(grid), dim3(NW * 64), 0, st, p);
     return hipGetLastError();
+}
+
+template <int NW, int VEC, Epi EPI>
+hipError_t go_tail(const GemmParams& p, int grid, const TailParams& t, hipStream_t st) {
+    hipLaunchKernelGGL((gemm_small16_kernel<NW, Layout::TN, VEC, EPI, true>), dim3(grid + tail_jobs(t.H)),
+                       dim3(NW * 64), 0, st, p, t);
+    return hipGetLastError();
+}
+
+template <int NW>
+hipError_t dispatch_tail(const GemmLaunch& L, const GemmParams& p, const TailParams& t, hipStream_t st) {
+    if (L.epi == Epi::Sgd)
+        return L.vec == 4 ? go_tail<NW, 4, Epi::Sgd>(p, L.grid, t, st) : go_tail<NW, 1, Epi::Sgd>(p, L.grid, t, st);
+    if (L.epi == Epi::Grad)
+        return L.vec == 4 ? go_tail<NW, 4, Epi::Grad>(p, L.grid, t, st) : go_tail<NW, 1, Epi::Grad>(p, L.grid, t, st);
+    return hipErrorInvalidValue;
 }
 
 template <int NW, Layout LAY, Epi EPI>
@@ -280,6 +313,17 @@ int gemm_small_waves(int M, int N, int K) {
     for (int nw : {4, 8, 16})
         if ((chunks + nw - 1) / nw <= kDepth) return nw;
     return 16;
+}
+
+hipError_t launch_gemm_small_tail(const GemmLaunch& L, const GemmParams& p, int waves, const TailParams& t,
+                                  hipStream_t st) {
+    if (L.bf16 || p.Cb || L.cfg != TileCfg::T32x16 || L.layout != Layout::TN) return hipErrorInvalidValue;
+    switch (waves) {
+    case 4: return dispatch_tail<4>(L, p, t, st);
+    case 8: return dispatch_tail<8>(L, p, t, st);
+    case 16: return dispatch_tail<16>(L, p, t, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_small(const GemmLaunch& L, const GemmParams& p, int waves, hipStream_t st) {

@@ -1,25 +1,23 @@
 // Fused output layer for narrow class counts (C <= 32): one launch does the
-// last matmul, the softmax cross-entropy, the dX of the last layer and its
-// dW + SGD (README "Example": logits = matmul(h, w2) feeding
-// cross_entropy_loss; the backward that autodiff derives for them).
+// last matmul, the softmax cross-entropy and the dX of the last layer
+// (README "Example": logits = matmul(h, w2) feeding cross_entropy_loss; the
+// backward that autodiff derives for them).  dW of the last layer, its SGD
+// update and the mean loss follow in the tail (tail.hpp), which rides along
+// with the last launch of the step.
 //
 // Each workgroup (16 waves) owns RB batch rows; W_L [H][C] and the rows'
 // activations, labels and masks are staged in LDS.  Per workgroup:
 //   logits[b][c] = sum_h a[b][h] W[h][c]
-//   lane-per-row softmax-CE -> dlogits, row loss         (as the CE kernel)
-//   G[b][h] = mask[b][h] * sum_c dlogits[b][c] W[h][c]   (old W)
-//   P_blk[h][c] = sum_{b in block} a[b][h] dlogits[b][c] (partial dW)
-// The three products run as 16x16 blocks on v_mfma_f32_16x16x4f32 with
-// operands read from LDS (zero past the edges), one wave per block.
-// The workgroup that draws the last integer ticket adds the partials in block
-// order, applies W -= lr * dW (or stores dW) and averages the row losses in
-// row order.  Every other workgroup has finished reading W before it takes
-// its ticket, so the in-place update is safe.  For small batches this
-// replaces five launches (logits GEMM, CE, dX GEMM, dW GEMM and the loss
-// mean) whose run time is dominated by launch and memory latency.
+//   softmax-CE, 16 lanes per row -> dlogits, row loss
+//   G[b][h] = mask[b][h] * sum_c dlogits[b][c] W[h][c]
+// The two products run as 16x16 blocks on v_mfma_f32_16x16x4f32 with
+// operands read from LDS (zero past the edges).  For small batches this
+// replaces the logits GEMM, the CE kernel and the dX GEMM, whose run time is
+// dominated by launch and memory latency.
 #include <math.h>
 
 #include "kernels.hpp"
+#include "tail.hpp"
 
 namespace mlp {
 namespace {
@@ -30,9 +28,7 @@ constexpr int kU = 8;   // staging loads in flight per thread
 
 __global__ __launch_bounds__(kThreads) void head_kernel(HeadParams p) {
     extern __shared__ float lds[];
-    __shared__ int s_last;
     __shared__ float4v s_red[kNumWaves][kWave];   // K-split partial logits
-    __shared__ float s_part[kNumWaves];
     const int H = p.H, C = p.C, CP = p.CP, RB = p.RB;
     const int HS = H | 1;             // odd LDS row stride: rows land on distinct banks
     float* sW = lds;                  // [H][CP]
@@ -41,8 +37,7 @@ __global__ __launch_bounds__(kThreads) void head_kernel(HeadParams p) {
     float* sT = sZ + RB * C;          // [RB][C]  labels
     uint8_t* sM = (uint8_t*)(sT + RB * C);   // [RB][H] mask
     const int tid = threadIdx.x;
-    const int blk_id = blockIdx.x;
-    const int row0 = blk_id * RB;
+    const int row0 = blockIdx.x * RB;
     const int rows = min(RB, p.B - row0);
 
     // Stage everything the block reads once.  Loads go out kU at a time per
@@ -173,7 +168,7 @@ __global__ __launch_bounds__(kThreads) void head_kernel(HeadParams p) {
                 z[j + 16] = g;
                 p.dlogits[(int64_t)row * C + j + 16] = g;
             }
-            if (j == 0) store_coherent(p.rowloss + row, st * lse - stz);
+            if (j == 0) p.rowloss[row] = st * lse - stz;
         }
     }
     __syncthreads();
@@ -196,69 +191,19 @@ __global__ __launch_bounds__(kThreads) void head_kernel(HeadParams p) {
             if (bb < rows && hb < H) p.G[(int64_t)(row0 + bb) * H + hb] = sM[bb * H + hb] ? acc[e] : 0.f;
         }
     }
+}
 
-    // partial dW over this block's rows: P = A^T dZ, blocks of 16 h x 16
-    // classes with K = the block's rows.
-    float* part = p.partials + (int64_t)blk_id * H * C;
-    for (int blk = wave; blk < HB * CB; blk += kThreads / kWave) {
-        const int h0 = (blk / CB) * 16, c0 = (blk % CB) * 16;
-        const int ha = h0 + li, cb = c0 + li;
-        float4v acc = {0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < rows; k0 += 4) {
-            const int k = k0 + lk;
-            const float av = (ha < H && k < rows) ? sA[k * HS + ha] : 0.f;
-            const float zv = (cb < C && k < rows) ? sZ[k * C + cb] : 0.f;
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, zv, acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int hh = h0 + 4 * lk + e;
-            if (hh < H && cb < C) store_coherent(part + hh * C + cb, acc[e]);
-        }
-    }
-
-    if (!last_arrival(p.ticket, gridDim.x, &s_last)) return;
-
-    // dW in block order, then the update (or the stored gradient).  The loads
-    // of up to 8 blocks are issued before any is added, so the reduction costs
-    // a few memory round trips rather than one per block.
-    // The row losses' loads go out first (kept in registers), then the loads
-    // of 16 blocks' partials at a time, unconditionally from clamped
-    // addresses (extra ones dropped), before any is added.
-    float lv[4];
-    const int nl = (p.B + kThreads - 1) / kThreads;   // row losses per thread (<= 4 kept)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) lv[u] = load_coherent(p.rowloss + min(tid + u * kThreads, p.B - 1));
-    const int nblk = gridDim.x;
-    for (int e = tid; e < H * C; e += kThreads) {
-        float s = 0.f;
-        for (int k0 = 0; k0 < nblk; k0 += 16) {
-            float v[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-                v[u] = load_coherent(p.partials + (int64_t)min(k0 + u, nblk - 1) * H * C + e);
-#pragma unroll
-            for (int u = 0; u < 16; ++u) s += k0 + u < nblk ? v[u] : 0.f;
-        }
-        if (p.dW) p.dW[e] = s;
-        else p.W[e] = sW[(e / C) * CP + e % C] - p.lr * s;
-    }
-    // mean loss in a fixed order: per thread, a wave butterfly, waves in order
-    float s = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) s += u < nl && tid + u * kThreads < p.B ? lv[u] : 0.f;
-    for (int b = tid + 4 * kThreads; b < p.B; b += kThreads) s += load_coherent(p.rowloss + b);
-    s = wave_sum(s);
-    if ((tid & 63) == 0) s_part[tid >> 6] = s;
-    __syncthreads();
-    if (tid == 0) {
-        float tot = 0.f;
-        for (int w = 0; w < kNumWaves; ++w) tot += s_part[w];
-        *p.loss = tot * p.inv_b;
-    }
+__global__ __launch_bounds__(kThreads) void tail_kernel(TailParams t) {
+    __shared__ float4v red[kNumWaves * 2 * kWave];
+    tail_job<kNumWaves>(t, blockIdx.x, red);
 }
 
 }  // namespace
+
+hipError_t launch_tail(const TailParams& t, hipStream_t s) {
+    hipLaunchKernelGGL(tail_kernel, dim3(tail_jobs(t.H)), dim3(kThreads), 0, s, t);
+    return hipGetLastError();
+}
 
 size_t head_lds_bytes(int H, int C, int RB) {
     const int CP = C | 1, HS = H | 1;

@@ -111,27 +111,44 @@ struct XentParams {
 };
 hipError_t launch_xent(const XentParams& p, int* grid_out, hipStream_t s);
 
-// ---- fused output layer for C <= 32 (logits, softmax-CE, dX, dW + SGD) -----
+// ---- fused output layer for C <= 32 (logits, softmax-CE, dX) --------------
 struct HeadParams {
     const float* A;        // a_{L-1} [B][H]
-    float* W;              // W_L [H][C], updated in place unless dW is set
+    const float* W;        // W_L [H][C] (read; updated later by the tail)
     const float* labels;   // [B][C]
     const uint8_t* mask;   // m_{L-1} [B][H]
     float* logits;         // [B][C] or null
     float* dlogits;        // [B][C]
     float* G;              // dZ_{L-1} [B][H]
-    float* dW;             // [H][C] gradient output (no update) or null
-    float* partials;       // [ceil(B/RB)][H][C]
     float* rowloss;        // [B]
-    float* loss;           // scalar mean loss
-    unsigned* ticket;      // zeroed counter
     int B, H, C, CP, RB;   // CP = C | 1 (LDS row stride of W), RB rows per workgroup
-    float lr, inv_b;
+    float inv_b;
 };
 size_t head_lds_bytes(int H, int C, int RB);
 int head_max_lds();          // dynamic LDS the head kernel may use
 hipError_t head_prepare();   // raise the kernel's dynamic-LDS limit once
 hipError_t launch_head(const HeadParams& p, hipStream_t s);
+
+// ---- tail of the fused output layer: dW_L (+ SGD) and the mean loss ------
+// Runs after the head, either as extra workgroups of the last small-product
+// launch of the step (gemm_small, T32x16) or on its own.  Job j < ceil(H/16)
+// owns rows 16j..16j+15 of dW_L (K = B on the matrix core, no cross-
+// workgroup reduction); job ceil(H/16) adds the row losses.
+struct TailParams {
+    const float* A;        // a_{L-1} [B][H]
+    const float* dZ;       // dlogits [B][C]
+    float* W;              // W_L [H][C], updated in place unless dW is set
+    float* dW;             // gradient output or null
+    const float* rowloss;  // [B]
+    float* loss;           // scalar mean loss
+    int B, H, C;
+    float lr, inv_b;
+};
+__host__ __device__ inline int tail_jobs(int H) { return (H + 15) / 16 + 1; }
+hipError_t launch_tail(const TailParams& t, hipStream_t s);
+// The last small-product dW launch with the tail's jobs as extra workgroups.
+hipError_t launch_gemm_small_tail(const GemmLaunch& L, const GemmParams& p, int waves, const TailParams& t,
+                                  hipStream_t s);
 
 // ---- f32 -> bf16 cast -----------------------------------------------------
 hipError_t launch_cast_bf16(const float* src, bf16_t* dst, size_t n, hipStream_t s);

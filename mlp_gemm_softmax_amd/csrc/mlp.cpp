@@ -237,6 +237,12 @@ SkinnyPlan plan_skinny_nn(int N, int K, int B) {
 
 double es(bool bf16) { return bf16 ? 2.0 : 4.0; }
 
+// Whether the fused output layer's tail can ride along with the first
+// layer's dW launch (the 32 x 16 small-product kernel), else it runs alone.
+bool tail_fused(const mlp_ctx* c) {
+    return c->head && !c->skinny && c->dw[0].small_waves > 0 && c->dw[0].cfg == TileCfg::T32x16;
+}
+
 // Slot names and algorithmic work, in launch order.
 void build_slots(mlp_ctx* c) {
     c->slots.clear();
@@ -261,13 +267,16 @@ void build_slots(mlp_ctx* c) {
             2 * M * N * K, M * K * e + K * N * e + out);
     }
     int top = L - 1;
+    double tail_flops = 0, tail_bytes = 0;
+    std::string tail_name;
     if (c->head) {
         const double H = c->dims[L - 1];
-        add("head_logits_xent_dx_sgd_l" + std::to_string(L - 1), 6.0 * B * H * C,
-            B * H * 4 + H * C * 8 + B * C * 12 + B * H * 5 + B * 4.0);
+        add("head_logits_xent_dx_l" + std::to_string(L - 1), 4.0 * B * H * C,
+            B * H * 4 + H * C * 4 + B * C * 12 + B * H * 5 + B * 4.0);
         top = L - 2;
-    } else {
-        add("softmax_xent", 0, (double)B * C * (12 + (c->bf16 ? 2 : 0)) + B * 4.0);
+        tail_flops = 2.0 * B * H * C;
+        tail_bytes = B * H * 4 + B * C * 4 + H * C * 8 + B * 4.0;
+        tail_name = "tail_dw_sgd_loss_l" + std::to_string(L - 1);
     }
     for (int l = top; l >= 0; --l) {
         const double din = c->dims[l], dout = c->dims[l + 1];
@@ -280,9 +289,13 @@ void build_slots(mlp_ctx* c) {
         if (l > 0)
             add(std::string(kind) + "_nt_mask_l" + std::to_string(l), 2.0 * B * din * dout,
                 B * dout * e + din * dout * e + B * din * (1 + e));
-        add(std::string(kind) + "_tn_sgd_l" + std::to_string(l), 2.0 * B * din * dout,
-            B * din * e + B * dout * e + din * dout * (8 + (c->bf16 ? 2 : 0)));
+        const double f = 2.0 * B * din * dout, b = B * din * e + B * dout * e + din * dout * (8 + (c->bf16 ? 2 : 0));
+        if (l == 0 && c->head && tail_fused(c))
+            add(std::string(kind) + "_tn_sgd_l0+" + tail_name, f + tail_flops, b + tail_bytes);
+        else
+            add(std::string(kind) + "_tn_sgd_l" + std::to_string(l), f, b);
     }
+    if (c->head && !tail_fused(c)) add(tail_name, tail_flops, tail_bytes);
 }
 
 // ---------------------------------------------------------------- launches --
@@ -322,7 +335,7 @@ struct Runner {
 
 hipError_t run_gemm(mlp_ctx* c, const GemmPlan& g, Layout lay, Epi epi, const void* A, int64_t lda,
                     const void* Bm, int64_t ldb, int M, int N, int K, float* C, bf16_t* Cb,
-                    uint8_t* mask, float lr) {
+                    uint8_t* mask, float lr, const TailParams* tail = nullptr) {
     GemmLaunch L;
     L.layout = lay;
     L.epi = epi;
@@ -349,9 +362,11 @@ hipError_t run_gemm(mlp_ctx* c, const GemmPlan& g, Layout lay, Epi epi, const vo
     p.tickets = c->tickets;
     p.tiles_m = g.tiles_m;
     p.tiles_n = g.tiles_n;
+    if (tail) return launch_gemm_small_tail(L, p, g.small_waves, *tail, c->stream);
     if (g.small_waves > 0) return launch_gemm_small(L, p, g.small_waves, c->stream);
     return launch_gemm(L, p, c->stream);
 }
+
 
 hipError_t run_skinny(mlp_ctx* c, const SkinnyPlan& s, Layout lay, Epi epi, const float* A,
                       const float* Bm, int K, int N, float* C, uint8_t* mask, float lr) {
@@ -430,17 +445,12 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
             hp.logits = c->logits;
             hp.dlogits = c->dlogits;
             hp.G = (float*)c->dz[0];
-            hp.dW = mode == Mode::Grads ? dw_out[L - 1] : nullptr;
-            hp.partials = c->partials;
             hp.rowloss = c->rowloss;
-            hp.loss = loss_dev ? loss_dev : c->loss_slot;
-            hp.ticket = c->tickets;
             hp.B = B;
             hp.H = H;
             hp.C = C;
             hp.CP = C | 1;
             hp.RB = c->head_rb;
-            hp.lr = lr;
             hp.inv_b = 1.0f / (float)B;
             return launch_head(hp, c->stream);
         });
@@ -463,6 +473,21 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
     if (mode == Mode::Forward) return r.err;
 
     // ---- backward
+    TailParams tp{};
+    if (use_head) {
+        tp.A = (const float*)c->act[L - 1];
+        tp.dZ = c->dlogits;
+        tp.W = c->W[L - 1];
+        tp.dW = mode == Mode::Grads ? dw_out[L - 1] : nullptr;
+        tp.rowloss = c->rowloss;
+        tp.loss = loss_dev ? loss_dev : c->loss_slot;
+        tp.B = B;
+        tp.H = c->dims[L - 1];
+        tp.C = C;
+        tp.lr = lr;
+        tp.inv_b = 1.0f / (float)B;
+    }
+    const bool fuse_tail = use_head && tail_fused(c);
     const void* G = c->bf16 ? (const void*)c->dlogits_b : (const void*)c->dlogits;
     int pp = 0;
     int top = L - 1;
@@ -524,11 +549,12 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
         } else {
             r.run(slot++, [&] {
                 return run_gemm(c, c->dw[l], Layout::TN, grads ? Epi::Grad : Epi::Sgd, a_in, din, G, dout,
-                                din, dout, B, Wdst, Wbdst, nullptr, lr);
+                                din, dout, B, Wdst, Wbdst, nullptr, lr, (l == 0 && fuse_tail) ? &tp : nullptr);
             });
         }
         G = Gnext;
     }
+    if (use_head && !fuse_tail) r.run(slot++, [&] { return launch_tail(tp, c->stream); });
     return r.err;
 }
 
@@ -663,10 +689,6 @@ size_t plan_and_carve(mlp_ctx* c, char* base) {
         max_partial = std::max(max_partial, partial_elems(c->fwd[l], B, dout));
         max_partial = std::max(max_partial, partial_elems(c->dx[l], B, din));
         max_partial = std::max(max_partial, partial_elems(c->dw[l], din, dout));
-    }
-    if (c->head) {
-        const size_t nblk = (size_t)(B + c->head_rb - 1) / c->head_rb;
-        max_partial = std::max(max_partial, nblk * c->dims[L - 1] * c->dims[L]);
     }
     int max_hidden = 1;
     for (int l = 1; l < L; ++l) max_hidden = std::max(max_hidden, c->dims[l]);

@@ -132,9 +132,21 @@ def _exact_everywhere(x, t, Ws, bf16):
     return True
 
 
+def loss_sum_bound(rowloss):
+    """Largest error of a float32 sum of the (integer) row losses in any order,
+    before the exact division by B = 2^k: zero while every partial sum stays
+    below 2^24, else the classical bound (B - 1) * 2^-24 * sum |l_b|."""
+    s = float(np.sum(np.abs(np.asarray(rowloss, np.float64))))
+    if s < 2.0 ** 24:
+        return 0.0
+    return (len(rowloss) - 1) * 2.0 ** -24 * s
+
+
 def integer_problem(dims, B, seed, xmax=2, wmax=2, gap=50, bf16=False):
     """Integer-valued x and weights for which every product, partial sum,
-    softmax and loss of the step is exact in float32 (and in bf16 operands):
+    softmax and row loss of the step is exact in float32 (and in bf16
+    operands; the mean of the row losses is exact only while their sum stays
+    below 2^24, see loss_sum_bound):
     the last layer's column 0 beats every other column by gap * sum(a) >= 110
     per row, so softmax is exactly one-hot in float32 and dlogits =
     (e_0 - t)/B.  B must be a power of two."""

@@ -44,6 +44,8 @@ EXACT_CASES = [
     ((1024, 1100, 260), 16, "f32", 1),       # skinny-batch with K splits
     ((320, 2080, 40), 512, "f32", 1),        # tiled NN with split-K, ragged N
     ((2080, 1040, 40), 512, "f32", 1),       # tiled TN and NT with split-K, ragged tiles
+    ((64, 32, 8), 8, "f32", 2),              # fused output layer with skinny kernels, tail on its own
+    ((512, 2048, 16), 1024, "f32", 1),       # fused output layer with tiled GEMMs, tail on its own
     ((200, 300, 36), 64, "bf16", 1),
     ((120, 136, 24), 256, "bf16", 1),
     ((256, 4096, 40), 2048, "bf16", 1),      # 256-wide bf16 tiles, no split (forward)
@@ -52,11 +54,22 @@ EXACT_CASES = [
 ]
 
 
+def _check_exact_loss(loss, ref, B):
+    """The mean loss: bitwise while the row-loss sum is representable, else
+    within the summation bound of that sum (the division by B = 2^k is exact)."""
+    bound = P.loss_sum_bound(ref["rowloss"]) / B
+    if bound == 0.0:
+        assert np.float32(loss) == np.float32(ref["loss"])
+    else:
+        assert abs(float(loss) - ref["loss"]) <= bound + float(np.spacing(np.float32(ref["loss"])))
+
+
 @pytest.mark.parametrize("dims,B,precision,vmax", EXACT_CASES)
 def test_exact_integer_step_is_bitwise(torch_dev, dims, B, precision, vmax):
-    """P7: integer operands make every product, sum, softmax and update exact,
-    so the GPU must equal the float32-rounded oracle bit for bit, whatever
-    its tiling, split-K or summation order."""
+    """P7: integer operands make every product, sum, softmax, row loss and
+    update exact, so the GPU must equal the float32-rounded oracle bit for
+    bit, whatever its tiling, split-K or summation order (the mean loss too,
+    while the row losses sum below 2^24)."""
     torch, dev = torch_dev
     _announce(f"exact dims={dims} B={B} {precision}")
     x, t, Ws = P.integer_problem(dims, B, seed=len(dims) * 1000 + B, xmax=vmax, wmax=vmax,
@@ -67,7 +80,7 @@ def test_exact_integer_step_is_bitwise(torch_dev, dims, B, precision, vmax):
     xd, td = P.to_dev([x, t], dev)
     loss, dws, dl, masks = P.gpu_grads(net, xd, td)
     logits, _ = net.forward(xd)
-    assert np.float32(loss) == np.float32(ref["loss"])
+    _check_exact_loss(loss, ref, B)
     np.testing.assert_array_equal(logits.cpu().numpy(), ref["fwd"]["logits"].astype(np.float32))
     np.testing.assert_array_equal(dl, ref["dlogits"].astype(np.float32))
     for m_gpu, m_ref in zip(masks, ref["fwd"]["m"]):
@@ -75,7 +88,7 @@ def test_exact_integer_step_is_bitwise(torch_dev, dims, B, precision, vmax):
     for g, r in zip(dws, ref["dW"]):
         np.testing.assert_array_equal(g, r.astype(np.float32))
     loss2, W_new, _ = P.gpu_train(net, xd, td, lr)
-    assert np.float32(loss2) == np.float32(ref["loss"])
+    _check_exact_loss(loss2, ref, B)
     for g, r in zip(W_new, ref["W_new"]):
         np.testing.assert_array_equal(g, r.astype(np.float32))
     net.close()
@@ -356,9 +369,10 @@ def test_profile_slots(torch_dev):
         net.train_step(xd, td, w.lr)
     rows = net.profile_read()
     # 784->128->10: hidden forward GEMM, the fused output layer (logits, CE,
-    # dX, dW + SGD of the last layer), dW + SGD of the first layer
-    assert [r["name"] for r in rows] == ["mfma_f32_nn_relu_mask_l0", "head_logits_xent_dx_sgd_l1",
-                                         "mfma_f32_tn_sgd_l0"]
+    # dX), dW + SGD of the first layer with the output layer's dW + SGD and
+    # mean loss riding along
+    assert [r["name"] for r in rows] == ["mfma_f32_nn_relu_mask_l0", "head_logits_xent_dx_l1",
+                                         "mfma_f32_tn_sgd_l0+tail_dw_sgd_loss_l1"]
     assert all(r["launches"] == 3 and r["total_ms"] > 0 for r in rows)
     assert rows[0]["flops"] == 2 * 32 * 784 * 128
     net.close()
