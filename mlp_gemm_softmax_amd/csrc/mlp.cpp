@@ -277,6 +277,8 @@ void build_slots(mlp_ctx* c) {
         tail_flops = 2.0 * B * H * C;
         tail_bytes = B * H * 4 + B * C * 4 + H * C * 8 + B * 4.0;
         tail_name = "tail_dw_sgd_loss_l" + std::to_string(L - 1);
+    } else {
+        add("softmax_xent", 0, (double)B * C * (12 + (c->bf16 ? 2 : 0)) + B * 4.0);
     }
     for (int l = top; l >= 0; --l) {
         const double din = c->dims[l], dout = c->dims[l + 1];

@@ -376,3 +376,17 @@ def test_profile_slots(torch_dev):
     assert all(r["launches"] == 3 and r["total_ms"] > 0 for r in rows)
     assert rows[0]["flops"] == 2 * 32 * 784 * 128
     net.close()
+    # without the fused output layer (C > 32): one slot per launch, in order
+    dims, B = (16, 8, 40), 64
+    rng = np.random.default_rng(5)
+    Ws = [(rng.standard_normal((dims[l], dims[l + 1])) * 0.3).astype(np.float32) for l in range(2)]
+    net = make_net(dims, B, "f32", Ws, dev)
+    x = rng.standard_normal((B, dims[0])).astype(np.float32)
+    t = np.eye(dims[-1], dtype=np.float32)[rng.integers(0, dims[-1], B)]
+    xd, td = P.to_dev([x, t], dev)
+    net.profile(True)
+    net.train_step(xd, td, 0.1)
+    names = [r["name"] for r in net.profile_read()]
+    assert names == ["mfma_f32_nn_relu_mask_l0", "mfma_f32_nn_store_l1", "softmax_xent",
+                     "mfma_f32_nt_mask_l1", "mfma_f32_tn_sgd_l1", "mfma_f32_tn_sgd_l0"], names
+    net.close()
