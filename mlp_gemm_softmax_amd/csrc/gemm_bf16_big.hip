@@ -1,6 +1,8 @@
 // bf16-operand MFMA GEMM with 256 x 256 workgroup tiles for the large
 // products of the bf16 fast path (float32 accumulate, same layouts and
-// epilogues as the 128-wide bf16 kernel, K split in up to 4 parts).
+// epilogues as the 128-wide bf16 kernel; with the K split in up to 4 parts
+// the partial sums go to memory and a separate all-CU kernel adds them and
+// applies the epilogue).
 //
 // Why a second kernel: at 128 x 128 tiles the LDS traffic per MFMA flop
 // (fragment reads plus tile writes) exceeds what one CU's LDS delivers while
@@ -24,6 +26,7 @@
 //         segment s (32 r) at slot s ^ (k & 3); an MFMA operand is two
 //         ds_read_b64_tr_b16 per lane (transpose reads, as in the 128-wide
 //         kernel), the four k-rows one read touches landing in distinct banks.
+#include "epilogue4.hpp"
 #include "kernels.hpp"
 
 namespace mlp {
@@ -96,60 +99,6 @@ __device__ __forceinline__ bf16x8v frag(const char* s, int base, int c, int lane
         const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(p0 + 4 * 512));
         const short8v both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         return __builtin_bit_cast(bf16x8v, both);
-    }
-}
-
-// Fused epilogue on four consecutive columns col..col+3 of one row (the
-// column count is a multiple of 8, so all four are inside or all outside).
-// `pre` is what epilogue_load fetched for the same place.
-struct Pre {
-    float4v w;        // Sgd: the f32 master weights
-    uint32_t m;       // MaskMul: four mask bytes
-};
-
-template <Epi EPI>
-__device__ __forceinline__ Pre epilogue_load(const GemmParams& p, int row, int col) {
-    Pre pre{};
-    const int64_t o = (int64_t)row * p.ldc + col;
-    if constexpr (EPI == Epi::Sgd) pre.w = *reinterpret_cast<const float4v*>(p.C + o);
-    if constexpr (EPI == Epi::MaskMul) pre.m = *reinterpret_cast<const uint32_t*>(p.mask + o);
-    return pre;
-}
-
-__device__ __forceinline__ uint2 pack_bf16x4(float4v v) {
-    return make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                      (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
-}
-
-template <Epi EPI>
-__device__ __forceinline__ void epilogue4(const GemmParams& p, int row, int col, float4v v, const Pre& pre) {
-    const int64_t o = (int64_t)row * p.ldc + col;
-    if constexpr (EPI == Epi::Store || EPI == Epi::Grad) {
-        *reinterpret_cast<float4v*>(p.C + o) = v;
-    } else if constexpr (EPI == Epi::ReluMask) {
-        uint32_t m = 0;
-        float4v a;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const bool pos = v[c] > 0.f;
-            a[c] = pos ? v[c] : 0.f;
-            m |= (pos ? 1u : 0u) << (8 * c);
-        }
-        if (p.Cb) *reinterpret_cast<uint2*>(p.Cb + o) = pack_bf16x4(a);
-        else *reinterpret_cast<float4v*>(p.C + o) = a;
-        *reinterpret_cast<uint32_t*>(p.mask + o) = m;
-    } else if constexpr (EPI == Epi::MaskMul) {
-        float4v g;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) g[c] = ((pre.m >> (8 * c)) & 0xffu) ? v[c] : 0.f;
-        if (p.Cb) *reinterpret_cast<uint2*>(p.Cb + o) = pack_bf16x4(g);
-        else *reinterpret_cast<float4v*>(p.C + o) = g;
-    } else if constexpr (EPI == Epi::Sgd) {
-        float4v w;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) w[c] = pre.w[c] - p.lr * v[c];
-        *reinterpret_cast<float4v*>(p.C + o) = w;
-        if (p.Cb) *reinterpret_cast<uint2*>(p.Cb + o) = pack_bf16x4(w);
     }
 }
 
@@ -227,7 +176,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
     constexpr bool AKC = LAY != Layout::TN;   // A stored [M][K]
     constexpr bool BKC = LAY == Layout::NT;   // B stored [N][K]
     __shared__ __attribute__((aligned(16))) char sa0[kOpBytes], sb0[kOpBytes], sa1[kOpBytes], sb1[kOpBytes];
-    __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -308,13 +256,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
     constexpr int SP = 132;
     const int rbase = m0 + wm * 128 + (lane >> 5);
     const int col = n0 + wn * 128 + 4 * (lane & 31);
-    // Split-K partials, per (tile, split) 256 x 256 floats in the order
-    // [wave][i][q][component][lane]: the thread that writes a value in one
-    // split reads the same place in the others, and every access is a
-    // contiguous 256-byte wave store or load.
-    constexpr int64_t kPart = (int64_t)kT * kT;
-    float* mypart = p.partials + (int64_t)tile * p.splits * kPart + wave * 16384 + lane;
-
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -326,15 +267,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
 #pragma unroll
         for (int q = 0; q < 16; ++q)
             v[q] = *reinterpret_cast<const float4v*>(st + (2 * q + (lane >> 5)) * SP + 4 * (lane & 31));
+        const int row0 = rbase + 32 * i;
         if (p.splits > 1) {
-            float* dst = mypart + split * kPart + i * 4096;
+            // K split: this split's sums go to partials [split][M][N]; the
+            // split-K epilogue kernel adds them in split order
+            float* part = p.partials + (int64_t)split * p.M * p.N;
 #pragma unroll
             for (int q = 0; q < 16; ++q)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) store_coherent(dst + (q * 4 + c) * 64, v[q][c]);
+                if (row0 + 2 * q < p.M && col < p.N)
+                    *reinterpret_cast<float4v*>(part + (int64_t)(row0 + 2 * q) * p.N + col) = v[q];
             continue;
         }
-        const int row0 = rbase + 32 * i;
         Pre pre[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q)
@@ -343,48 +286,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
         for (int q = 0; q < 16; ++q)
             if (row0 + 2 * q < p.M && col < p.N) epilogue4<EPI>(p, row0 + 2 * q, col, v[q], pre[q]);
     }
-    if (p.splits == 1) return;
-
-    // Deterministic split-K: the workgroup that takes the tile's last integer
-    // ticket adds the partials of all splits, its own included, in split
-    // order.  The loads of every split for half a row block (up to 128 per
-    // thread) are issued before the first add.
-    if (!last_arrival(&p.tickets[tile], (unsigned)p.splits, &s_last)) return;
-    for (int h = 0; h < 8; ++h) {
-        const int i = h >> 1, q0 = (h & 1) * 8;
-        const float* src = mypart + i * 4096 + q0 * 256;
-        float x[kMaxSplits][8][4];
-        // unconditional loads (splits past the last re-read it and are
-        // dropped below), so that none waits behind a branch
-#pragma unroll
-        for (int t = 0; t < kMaxSplits; ++t) {
-            const float* st_t = src + min(t, p.splits - 1) * kPart;
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) x[t][u][c] = load_coherent(st_t + (u * 4 + c) * 64);
-        }
-        const int row0 = rbase + 32 * i + 2 * q0;
-        Pre pre[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (row0 + 2 * u < p.M && col < p.N) pre[u] = epilogue_load<EPI>(p, row0 + 2 * u, col);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            float4v sum = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int t = 0; t < kMaxSplits; ++t)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) sum[c] += t < p.splits ? x[t][u][c] : 0.f;
-            if (row0 + 2 * u < p.M && col < p.N) epilogue4<EPI>(p, row0 + 2 * u, col, sum, pre[u]);
-        }
-    }
 }
 
 template <Layout LAY, Epi EPI>
 hipError_t go(const GemmParams& p, int grid, hipStream_t st) {
     hipLaunchKernelGGL((gemm_bf16_big_kernel<LAY, EPI>), dim3(grid), dim3(kThreads), 0, st, p);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && p.splits > 1) e = launch_splitk_epilogue(p, EPI, st);
+    return e;
 }
 
 

@@ -63,6 +63,9 @@ hipError_t launch_gemm(const GemmLaunch& L, const GemmParams& p, hipStream_t s);
 bool gemm_bf16_big_fits(Layout lay, int M, int N, int K, int64_t lda, int64_t ldb);
 hipError_t gemm_bf16_big_prepare();
 hipError_t launch_gemm_bf16_big(const GemmLaunch& L, const GemmParams& p, hipStream_t s);
+// Adds the K splits' partials [splits][M][N] in split order and applies the
+// epilogue (used by the large-tile kernel when it splits K).
+hipError_t launch_splitk_epilogue(const GemmParams& p, Epi epi, hipStream_t s);
 
 // Small float32 products: one 32x32 (L.cfg == T32x32) or 32x16 (T32x16)
 // tile per workgroup, K split across its `waves` waves and reduced in LDS (no
