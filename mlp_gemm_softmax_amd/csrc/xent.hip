@@ -90,23 +90,45 @@ __global__ __launch_bounds__(kThreads) void xent_lane(XentParams p) {
 }
 
 // One wavefront per row, whole row in registers (C <= 64 * VPT); rows are
-// strided over the grid's wavefronts.
+// strided over the grid's wavefronts, and the next row's logits and labels
+// are loaded (from a clamped in-range row, unconditionally) before the
+// current row is reduced, so each wave pays one memory round trip rather
+// than one per row.
 template <int VPT>
 __global__ __launch_bounds__(kThreads) void xent_wave(XentParams p) {
     __shared__ int s_last;
     const int lane = threadIdx.x & 63;
     const int waves = gridDim.x * (kThreads / kWave);
-    for (int row = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6); row < p.B; row += waves) {
-        const float* z = p.logits + (int64_t)row * p.C;
-        const float* t = p.labels + (int64_t)row * p.C;
+    float zn[VPT], tn[VPT];
+    auto fetch = [&](int row) {
+        const float* z = p.logits + (int64_t)min(row, p.B - 1) * p.C;
+        const float* t = p.labels + (int64_t)min(row, p.B - 1) * p.C;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int c = min(lane + kWave * i, p.C - 1);
+            zn[i] = z[c];
+            tn[i] = t[c];
+        }
+    };
+    // wide rows (VPT > 16) are not double-buffered: the registers would spill
+    constexpr bool kAhead = VPT <= 16;
+    int row = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
+    if (kAhead && row < p.B) fetch(row);
+    for (; row < p.B; row += waves) {
+        if (!kAhead) fetch(row);
         float zv[VPT], tv[VPT];
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            zv[i] = zn[i];
+            tv[i] = tn[i];
+        }
+        if (kAhead && row + waves < p.B) fetch(row + waves);
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
-            const int c = lane + kWave * i;
-            const bool ok = c < p.C;
-            zv[i] = ok ? z[c] : -INFINITY;
-            tv[i] = ok ? t[c] : 0.f;
+            const bool ok = lane + kWave * i < p.C;
+            zv[i] = ok ? zv[i] : -INFINITY;
+            tv[i] = ok ? tv[i] : 0.f;
             mx = fmaxf(mx, zv[i]);
         }
         mx = wave_max(mx);
