@@ -61,31 +61,39 @@ __global__ __launch_bounds__(NW * kWave) void skinny_nn(SkinnyParams p) {
     // the matrix-core work.
     const float* __restrict__ W = p.B;
     const float* __restrict__ X = p.A + (int64_t)(mok ? j : 0) * p.K;
+    // Two blocks are in flight ahead of the one being multiplied.  Loads use
+    // clamped in-range addresses; values past the slice or past N are zeroed
+    // where they are multiplied.
     const float4v zero = {0.f, 0.f, 0.f, 0.f};
-    float4v w[4], xv, wn[4], xn;
+    constexpr int kAhead = 2;
+    float4v wq[kAhead][4], xq[kAhead];
     auto fetch = [&](int k, float4v* wd, float4v& xd) {
-        const int kr = k + 4 * g;              // this lane group's 4 rows
-        const bool rok = kr < kw1;             // K is a multiple of 4
-        const bool ok = rok && nok;
+        const int kr = min(k + 4 * g, kw1 - 4);   // this lane group's 4 rows (K is a multiple of 4)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4v v = ld4(ok ? W + (int64_t)(kr + i) * p.N + n : W);
-            wd[i] = ok ? v : zero;
-        }
-        const float4v v = ld4(rok ? X + kr : X);
-        xd = (rok && mok) ? v : zero;
+        for (int i = 0; i < 4; ++i) wd[i] = ld4(W + (int64_t)(kr + i) * p.N + (nok ? n : 0));
+        xd = ld4(X + kr);
     };
-    if (kw0 < kw1) fetch(kw0, wn, xn);
-    for (int k = kw0; k < kw1; k += 16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = wn[i];
-        xv = xn;
-        if (k + 16 < kw1) fetch(k + 16, wn, xn);
+    for (int a = 0; a < kAhead; ++a)
+        if (kw0 + 16 * a < kw1) fetch(kw0 + 16 * a, wq[a], xq[a]);
+    for (int k = kw0; k < kw1; k += 16 * kAhead) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int a = 0; a < kAhead; ++a) {
+            const int kb = k + 16 * a;
+            if (kb < kw1) {
+                const bool ok = kb + 4 * g < kw1;
+                float4v w[4], xv;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[i], w[i][q], acc[q], 0, 0, 0);
+                for (int i = 0; i < 4; ++i) w[i] = (ok && nok) ? wq[a][i] : zero;
+                xv = (ok && mok) ? xq[a] : zero;
+                if (kb + 16 * kAhead < kw1) fetch(kb + 16 * kAhead, wq[a], xq[a]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[i], w[i][q], acc[q], 0, 0, 0);
+            }
+        }
     }
 
     // acc[q][r] = out[m = 4g + r][n0 + 4j + q]; sum the waves in order 0..NW-1.
