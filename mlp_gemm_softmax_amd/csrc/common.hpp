@@ -78,6 +78,14 @@ __device__ __forceinline__ float load_coherent(const float* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ void store_coherent(uint8_t* p, uint8_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint8_t load_coherent(const uint8_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Wait until this thread's stores are acknowledged (and keep the compiler
 // from moving memory operations across the wait).
 __device__ __forceinline__ void wait_stores() {

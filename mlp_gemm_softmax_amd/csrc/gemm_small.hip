@@ -15,6 +15,7 @@
 // chunk c, lanes 0-31 hold k = 8c..8c+3 and lanes 32-63 hold k = 8c+4..8c+7,
 // and MFMA q (0..3) takes the q-th of those four values.
 #include "kernels.hpp"
+#include "head_body.hpp"
 #include "tail.hpp"
 
 namespace mlp {
@@ -164,13 +165,20 @@ __device__ __forceinline__ float4v load_op16(const float* __restrict__ g, int64_
 }
 
 // With TAIL, the first tail_jobs(t.H) workgroups run the fused output
-// layer's tail jobs (tail.hpp) instead of tiles.
-template <int NW, Layout LAY, int VEC, Epi EPI, bool TAIL>
-__global__ __launch_bounds__(NW * 64) void gemm_small16_kernel(GemmParams p, TailParams t) {
+// layer's tail jobs (tail.hpp) instead of tiles.  With HEAD (forward of the
+// last hidden layer, ReluMask, 16 waves), the activations and masks go out
+// with device-scope stores, and the workgroup that finishes the last column
+// tile of a 32-row block (integer ticket per row block) runs the output
+// layer's head for those rows (head_body.hpp) with dynamic LDS.
+template <int NW, Layout LAY, int VEC, Epi EPI, bool TAIL, bool HEAD>
+__global__ __launch_bounds__(NW * 64) void gemm_small16_kernel(GemmParams p, TailParams t, HeadParams hp) {
     constexpr bool AKC = LAY != Layout::TN;   // A stored [M][K]
     constexpr bool BKC = LAY == Layout::NT;   // B stored [N][K]
     constexpr int D = kDepth / 2;             // chunks of 16 k in flight per wave
+    static_assert(!HEAD || (NW == kHeadWaves && EPI == Epi::ReluMask && LAY == Layout::NN), "head layout");
     __shared__ float4v red[NW][2][64];
+    __shared__ int s_last;
+    extern __shared__ float head_lds[];
     int bid = blockIdx.x, nb = gridDim.x;
     if constexpr (TAIL) {
         const int jobs = tail_jobs(t.H);
@@ -245,17 +253,31 @@ __global__ __launch_bounds__(NW * 64) void gemm_small16_kernel(GemmParams p, Tai
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int row = m0 + 16 * rbk + 4 * (l >> 4) + e;
-            if (row < p.M && col < p.N) epilogue<EPI>(p, row, col, v[e]);
+            if (row < p.M && col < p.N) {
+                if constexpr (HEAD) {
+                    const int64_t o = (int64_t)row * p.ldc + col;
+                    const bool pos = v[e] > 0.f;
+                    store_coherent(p.C + o, pos ? v[e] : 0.f);
+                    store_coherent(p.mask + o, (uint8_t)(pos ? 1 : 0));
+                } else {
+                    epilogue<EPI>(p, row, col, v[e]);
+                }
+            }
         }
+    }
+    if constexpr (HEAD) {
+        if (!last_arrival(&p.tickets[m0 / 32], (unsigned)tiles_n, &s_last)) return;
+        head_block<true>(hp, m0, head_lds, reinterpret_cast<float4v(*)[kWave]>(&red[0][0][0]));
     }
 }
 
 template <int NW, Layout LAY, int VEC, Epi EPI>
 hipError_t go(const GemmParams& p, int grid, bool t16, hipStream_t st) {
     const TailParams none{};
+    const HeadParams nohead{};
     if (t16)
-        hipLaunchKernelGGL((gemm_small16_kernel<NW, LAY, VEC, EPI, false>), dim3(grid), dim3(NW * 64), 0, st, p,
-                           none);
+        hipLaunchKernelGGL((gemm_small16_kernel<NW, LAY, VEC, EPI, false, false>), dim3(grid), dim3(NW * 64), 0, st,
+                           p, none, nohead);
     else
         hipLaunchKernelGGL((gemm_small_kernel<NW, LAY, VEC, EPI>), dim3(grid), dim3(NW * 64), 0, st, p);
     return hipGetLastError();
@@ -263,8 +285,9 @@ hipError_t go(const GemmParams& p, int grid, bool t16, hipStream_t st) {
 
 template <int NW, int VEC, Epi EPI>
 hipError_t go_tail(const GemmParams& p, int grid, const TailParams& t, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_small16_kernel<NW, Layout::TN, VEC, EPI, true>), dim3(grid + tail_jobs(t.H)),
-                       dim3(NW * 64), 0, st, p, t);
+    const HeadParams nohead{};
+    hipLaunchKernelGGL((gemm_small16_kernel<NW, Layout::TN, VEC, EPI, true, false>), dim3(grid + tail_jobs(t.H)),
+                       dim3(NW * 64), 0, st, p, t, nohead);
     return hipGetLastError();
 }
 
@@ -313,6 +336,22 @@ int gemm_small_waves(int M, int N, int K) {
     for (int nw : {4, 8, 16})
         if ((chunks + nw - 1) / nw <= kDepth) return nw;
     return 16;
+}
+
+hipError_t launch_gemm_small_head(const GemmLaunch& L, const GemmParams& p, const HeadParams& hp,
+                                  hipStream_t st) {
+    if (L.bf16 || p.Cb || L.cfg != TileCfg::T32x16 || L.layout != Layout::NN || L.epi != Epi::ReluMask ||
+        hp.RB != 32 || !p.tickets)
+        return hipErrorInvalidValue;
+    const TailParams none{};
+    const size_t lds = head_lds_bytes(hp.H, hp.C, hp.RB);
+    if (L.vec == 4)
+        hipLaunchKernelGGL((gemm_small16_kernel<kHeadWaves, Layout::NN, 4, Epi::ReluMask, false, true>),
+                           dim3(L.grid), dim3(kHeadThreads), lds, st, p, none, hp);
+    else
+        hipLaunchKernelGGL((gemm_small16_kernel<kHeadWaves, Layout::NN, 1, Epi::ReluMask, false, true>),
+                           dim3(L.grid), dim3(kHeadThreads), lds, st, p, none, hp);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm_small_tail(const GemmLaunch& L, const GemmParams& p, int waves, const TailParams& t,

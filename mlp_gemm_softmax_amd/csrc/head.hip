@@ -1,207 +1,34 @@
-// Fused output layer for narrow class counts (C <= 32): one launch does the
-// last matmul, the softmax cross-entropy and the dX of the last layer
-// (README "Example": logits = matmul(h, w2) feeding cross_entropy_loss; the
-// backward that autodiff derives for them).  dW of the last layer, its SGD
-// update and the mean loss follow in the tail (tail.hpp), which rides along
-// with the last launch of the step.
-//
-// Each workgroup (16 waves) owns RB batch rows; W_L [H][C] and the rows'
-// activations, labels and masks are staged in LDS.  Per workgroup:
-//   logits[b][c] = sum_h a[b][h] W[h][c]
-//   softmax-CE, 16 lanes per row -> dlogits, row loss
-//   G[b][h] = mask[b][h] * sum_c dlogits[b][c] W[h][c]
-// The two products run as 16x16 blocks on v_mfma_f32_16x16x4f32 with
-// operands read from LDS (zero past the edges).  For small batches this
-// replaces the logits GEMM, the CE kernel and the dX GEMM, whose run time is
+// Fused output layer for narrow class counts (C <= 32): the stand-alone head
+// kernel (one workgroup of 16 waves per RB batch rows runs head_block, see
+// head_body.hpp: logits, softmax-CE and the dX of the last layer) and the
+// stand-alone tail kernel (tail.hpp: dW + SGD of the last layer and the mean
+// loss).  Both usually ride along with neighbouring launches instead: the
+// head with the last hidden layer's forward, the tail with the first layer's
+// dW.  For small batches this replaces the logits GEMM, the CE kernel, the
+// dX and dW GEMMs of the last layer and the loss mean, whose run time is
 // dominated by launch and memory latency.
-#include <math.h>
-
 #include "kernels.hpp"
+#include "head_body.hpp"
 #include "tail.hpp"
 
 namespace mlp {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kNumWaves = kThreads / kWave;
-constexpr int kU = 8;   // staging loads in flight per thread
-
-__global__ __launch_bounds__(kThreads) void head_kernel(HeadParams p) {
+__global__ __launch_bounds__(kHeadThreads) void head_kernel(HeadParams p) {
     extern __shared__ float lds[];
-    __shared__ float4v s_red[kNumWaves][kWave];   // K-split partial logits
-    const int H = p.H, C = p.C, CP = p.CP, RB = p.RB;
-    const int HS = H | 1;             // odd LDS row stride: rows land on distinct banks
-    float* sW = lds;                  // [H][CP]
-    float* sA = sW + H * CP;          // [RB][HS]
-    float* sZ = sA + RB * HS;         // [RB][C]  logits, then dlogits
-    float* sT = sZ + RB * C;          // [RB][C]  labels
-    uint8_t* sM = (uint8_t*)(sT + RB * C);   // [RB][H] mask
-    const int tid = threadIdx.x;
-    const int row0 = blockIdx.x * RB;
-    const int rows = min(RB, p.B - row0);
-
-    // Stage everything the block reads once.  Loads go out kU at a time per
-    // thread from clamped (in-range) addresses before any is stored, so the
-    // staging costs one memory round trip rather than one per element.
-    {
-        const float* gA = p.A + (int64_t)row0 * H;
-        const uint8_t* gM = p.mask + (int64_t)row0 * H;
-        const float* gT = p.labels + (int64_t)row0 * C;
-        const int nA = rows * H, nW = H * C, nT = rows * C;
-        for (int e0 = tid; e0 < nA; e0 += kU * kThreads) {
-            float a[kU];
-            uint8_t m[kU];
-#pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                const int e = min(e0 + u * kThreads, nA - 1);
-                a[u] = gA[e];
-                m[u] = gM[e];
-            }
-#pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                const int e = e0 + u * kThreads;
-                if (e < nA) {
-                    sA[(e / H) * HS + e % H] = a[u];
-                    sM[e] = m[u];
-                }
-            }
-        }
-        for (int e0 = tid; e0 < nW; e0 += kU * kThreads) {
-            float w[kU];
-#pragma unroll
-            for (int u = 0; u < kU; ++u) w[u] = p.W[min(e0 + u * kThreads, nW - 1)];
-#pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                const int e = e0 + u * kThreads;
-                if (e < nW) sW[(e / C) * CP + e % C] = w[u];
-            }
-        }
-        for (int e0 = tid; e0 < nT; e0 += kU * kThreads) {
-            float t[kU];
-#pragma unroll
-            for (int u = 0; u < kU; ++u) t[u] = gT[min(e0 + u * kThreads, nT - 1)];
-#pragma unroll
-            for (int u = 0; u < kU; ++u) {
-                const int e = e0 + u * kThreads;
-                if (e < nT) sT[e] = t[u];
-            }
-        }
-    }
-    __syncthreads();
-
-    // logits Z = A W: 16x16 output blocks on v_mfma_f32_16x16x4f32 (the
-    // K = H sum runs inside the matrix core, 4 h per step).  Operand lanes:
-    // A[m = l%16][k = l/16], B[k = l/16][n = l%16]; the result lane l holds
-    // rows 4(l/16)..+3 of column l%16.  The waves split each block's K range
-    // into KS parts, whose sums meet in LDS and are added in part order.
-    const int lane = tid & 63, wave = tid >> 6;
-    const int li = lane & 15, lk = lane >> 4;
-    const int RBb = (rows + 15) / 16, CB = (C + 15) / 16, HB = (H + 15) / 16;
-    {
-        const int nb = RBb * CB;                       // <= 8 (RB <= 64, C <= 32)
-        const int KS = kNumWaves / nb >= 1 ? kNumWaves / nb : 1;
-        const int kpart = ((H + 4 * KS - 1) / (4 * KS)) * 4;
-        if (wave < nb * KS) {
-            const int blk = wave % nb, part = wave / nb;
-            const int b0 = (blk / CB) * 16, c0 = (blk % CB) * 16;
-            const int ba = b0 + li, cb = c0 + li;
-            float4v acc = {0.f, 0.f, 0.f, 0.f};
-            const int kb = part * kpart, ke = min(H, kb + kpart);
-            for (int k0 = kb; k0 < ke; k0 += 4) {
-                const int k = k0 + lk;
-                const float av = (ba < rows && k < ke) ? sA[ba * HS + k] : 0.f;
-                const float wv = (cb < C && k < ke) ? sW[k * CP + cb] : 0.f;
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wv, acc, 0, 0, 0);
-            }
-            s_red[wave][lane] = acc;
-        }
-        __syncthreads();
-        if (wave < nb) {
-            const int blk = wave;
-            const int b0 = (blk / CB) * 16, c0 = (blk % CB) * 16;
-            const int cb = c0 + li;
-            float4v z = s_red[blk][lane];
-            for (int part = 1; part < KS; ++part) z += s_red[part * nb + blk][lane];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int bb = b0 + 4 * lk + e;
-                if (bb < rows && cb < C) {
-                    sZ[bb * C + cb] = z[e];
-                    if (p.logits) p.logits[(int64_t)(row0 + bb) * C + cb] = z[e];
-                }
-            }
-        }
-    }
-    __syncthreads();
-
-    // softmax cross-entropy, 16 lanes per row (classes j and j + 16 of the
-    // row on lane j); max and sums by a fixed xor butterfly inside the
-    // 16-lane group.
-    {
-        const int b = tid >> 4, j = tid & 15;
-        if (b < rows) {
-            const int row = row0 + b;
-            const float* t = sT + b * C;
-            float* z = sZ + b * C;
-            const bool v0 = j < C, v1 = j + 16 < C;
-            const float z0 = v0 ? z[j] : -INFINITY, z1 = v1 ? z[j + 16] : -INFINITY;
-            const float t0 = v0 ? t[j] : 0.f, t1 = v1 ? t[j + 16] : 0.f;
-            float mx = fmaxf(z0, z1);
-#pragma unroll
-            for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
-            const float e0 = v0 ? expf(z0 - mx) : 0.f, e1 = v1 ? expf(z1 - mx) : 0.f;
-            float se = e0 + e1, st = t0 + t1, stz = (v0 ? t0 * z0 : 0.f) + (v1 ? t1 * z1 : 0.f);
-#pragma unroll
-            for (int o = 8; o >= 1; o >>= 1) {
-                se += __shfl_xor(se, o, 16);
-                st += __shfl_xor(st, o, 16);
-                stz += __shfl_xor(stz, o, 16);
-            }
-            const float lse = mx + logf(se);
-            if (v0) {
-                const float g = (e0 / se * st - t0) * p.inv_b;
-                z[j] = g;
-                p.dlogits[(int64_t)row * C + j] = g;
-            }
-            if (v1) {
-                const float g = (e1 / se * st - t1) * p.inv_b;
-                z[j + 16] = g;
-                p.dlogits[(int64_t)row * C + j + 16] = g;
-            }
-            if (j == 0) p.rowloss[row] = st * lse - stz;
-        }
-    }
-    __syncthreads();
-
-    // dX of the last layer through the ReLU mask: G = (dZ W^T) . m, blocks
-    // of 16 rows x 16 h with K = C on the matrix core.
-    for (int blk = wave; blk < RBb * HB; blk += kThreads / kWave) {
-        const int b0 = (blk / HB) * 16, h0 = (blk % HB) * 16;
-        const int ba = b0 + li, hb = h0 + li;
-        float4v acc = {0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < C; k0 += 4) {
-            const int k = k0 + lk;
-            const float zv = (ba < rows && k < C) ? sZ[ba * C + k] : 0.f;
-            const float wv = (hb < H && k < C) ? sW[hb * CP + k] : 0.f;
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(zv, wv, acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int bb = b0 + 4 * lk + e;
-            if (bb < rows && hb < H) p.G[(int64_t)(row0 + bb) * H + hb] = sM[bb * H + hb] ? acc[e] : 0.f;
-        }
-    }
+    __shared__ float4v s_red[kHeadWaves][kWave];   // K-split partial logits
+    head_block<false>(p, blockIdx.x * p.RB, lds, s_red);
 }
 
-__global__ __launch_bounds__(kThreads) void tail_kernel(TailParams t) {
-    __shared__ float4v red[kNumWaves * 2 * kWave];
-    tail_job<kNumWaves>(t, blockIdx.x, red);
+__global__ __launch_bounds__(kHeadThreads) void tail_kernel(TailParams t) {
+    __shared__ float4v red[kHeadWaves * 2 * kWave];
+    tail_job<kHeadWaves>(t, blockIdx.x, red);
 }
 
 }  // namespace
 
 hipError_t launch_tail(const TailParams& t, hipStream_t s) {
-    hipLaunchKernelGGL(tail_kernel, dim3(tail_jobs(t.H)), dim3(kThreads), 0, s, t);
+    hipLaunchKernelGGL(tail_kernel, dim3(tail_jobs(t.H)), dim3(kHeadThreads), 0, s, t);
     return hipGetLastError();
 }
 
@@ -219,7 +46,7 @@ hipError_t head_prepare() {
 
 hipError_t launch_head(const HeadParams& p, hipStream_t s) {
     const int grid = (p.B + p.RB - 1) / p.RB;
-    hipLaunchKernelGGL(head_kernel, dim3(grid), dim3(kThreads), head_lds_bytes(p.H, p.C, p.RB), s, p);
+    hipLaunchKernelGGL(head_kernel, dim3(grid), dim3(kHeadThreads), head_lds_bytes(p.H, p.C, p.RB), s, p);
     return hipGetLastError();
 }
 

@@ -149,6 +149,10 @@ struct TailParams {
 };
 __host__ __device__ inline int tail_jobs(int H) { return (H + 15) / 16 + 1; }
 hipError_t launch_tail(const TailParams& t, hipStream_t s);
+// The last hidden layer's small-product forward (32 x 16 tiles, 16 waves)
+// with the head run by the workgroup finishing each 32-row block (hp.RB =
+// 32; p.tickets: one zeroed counter per row block).
+hipError_t launch_gemm_small_head(const GemmLaunch& L, const GemmParams& p, const HeadParams& hp, hipStream_t s);
 // The last small-product dW launch with the tail's jobs as extra workgroups.
 hipError_t launch_gemm_small_tail(const GemmLaunch& L, const GemmParams& p, int waves, const TailParams& t,
                                   hipStream_t s);

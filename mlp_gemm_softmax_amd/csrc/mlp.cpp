@@ -243,6 +243,16 @@ bool tail_fused(const mlp_ctx* c) {
     return c->head && !c->skinny && c->dw[0].small_waves > 0 && c->dw[0].cfg == TileCfg::T32x16;
 }
 
+// Whether the output layer's head runs inside the last hidden layer's
+// forward launch (32 x 16 small-product tiles with 16 waves; the workgroup
+// finishing a 32-row block runs the head for it), else in a launch of its own.
+bool head_fused(const mlp_ctx* c) {
+    if (!c->head || c->skinny || c->L < 2) return false;
+    const GemmPlan& g = c->fwd[c->L - 2];
+    return g.small_waves == 16 && g.cfg == TileCfg::T32x16 &&
+           head_lds_bytes(c->dims[c->L - 1], c->dims[c->L], 32) <= 64 * 1024;
+}
+
 // Slot names and algorithmic work, in launch order.
 void build_slots(mlp_ctx* c) {
     c->slots.clear();
@@ -271,8 +281,16 @@ void build_slots(mlp_ctx* c) {
     std::string tail_name;
     if (c->head) {
         const double H = c->dims[L - 1];
-        add("head_logits_xent_dx_l" + std::to_string(L - 1), 4.0 * B * H * C,
-            B * H * 4 + H * C * 4 + B * C * 12 + B * H * 5 + B * 4.0);
+        const std::string hn = "head_logits_xent_dx_l" + std::to_string(L - 1);
+        const double hf = 4.0 * B * H * C, hb = B * H * 4 + H * C * 4 + B * C * 12 + B * H * 5 + B * 4.0;
+        if (head_fused(c)) {   // merge into the last hidden layer's forward slot
+            Slot& f = c->slots.back();
+            f.name += "+" + hn;
+            f.flops += hf;
+            f.bytes += hb;
+        } else {
+            add(hn, hf, hb);
+        }
         top = L - 2;
         tail_flops = 2.0 * B * H * C;
         tail_bytes = B * H * 4 + B * C * 4 + H * C * 8 + B * 4.0;
@@ -411,6 +429,26 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
     }
     // ---- forward (with the fused head the last layer's matmul is in the head)
     const bool use_head = c->head && mode != Mode::Forward;
+    const bool fuse_head = use_head && head_fused(c);
+    const int C = c->dims[L];
+    auto head_params = [&](int RB) {
+        HeadParams hp;
+        hp.A = (const float*)c->act[L - 1];
+        hp.W = c->W[L - 1];
+        hp.labels = labels;
+        hp.mask = c->mask[L - 1];
+        hp.logits = c->logits;
+        hp.dlogits = c->dlogits;
+        hp.G = (float*)c->dz[0];
+        hp.rowloss = c->rowloss;
+        hp.B = B;
+        hp.H = c->dims[L - 1];
+        hp.C = C;
+        hp.CP = C | 1;
+        hp.RB = RB;
+        hp.inv_b = 1.0f / (float)B;
+        return hp;
+    };
     for (int l = 0; l < (use_head ? L - 1 : L); ++l) {
         const int K = c->dims[l], N = c->dims[l + 1];
         const bool last = l == L - 1;
@@ -421,6 +459,32 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
                                   (const float*)a_prev, (const float*)Wop, K, N,
                                   last ? c->logits : (float*)c->act[l + 1],
                                   last ? nullptr : c->mask[l + 1], 0.f);
+            });
+        } else if (fuse_head && l == L - 2) {
+            r.run(slot++, [&] {
+                const GemmPlan& g = c->fwd[l];
+                GemmLaunch gl;
+                gl.layout = Layout::NN;
+                gl.epi = Epi::ReluMask;
+                gl.bf16 = false;
+                gl.cfg = g.cfg;
+                gl.vec = g.vec;
+                gl.grid = g.grid;
+                GemmParams gp{};
+                gp.A = a_prev;
+                gp.B = Wop;
+                gp.lda = K;
+                gp.ldb = N;
+                gp.M = B;
+                gp.N = N;
+                gp.K = K;
+                gp.C = (float*)c->act[l + 1];
+                gp.mask = c->mask[l + 1];
+                gp.ldc = N;
+                gp.splits = 1;
+                gp.kchunk = K;
+                gp.tickets = c->tickets;
+                return launch_gemm_small_head(gl, gp, head_params(32), c->stream);
             });
         } else {
             r.run(slot++, [&] {
@@ -435,27 +499,8 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
     if (mode == Mode::Forward && !labels) return r.err;
 
     // ---- loss
-    const int C = c->dims[L];
     if (use_head) {
-        const int H = c->dims[L - 1];
-        r.run(slot++, [&] {
-            HeadParams hp;
-            hp.A = (const float*)c->act[L - 1];
-            hp.W = c->W[L - 1];
-            hp.labels = labels;
-            hp.mask = c->mask[L - 1];
-            hp.logits = c->logits;
-            hp.dlogits = c->dlogits;
-            hp.G = (float*)c->dz[0];
-            hp.rowloss = c->rowloss;
-            hp.B = B;
-            hp.H = H;
-            hp.C = C;
-            hp.CP = C | 1;
-            hp.RB = c->head_rb;
-            hp.inv_b = 1.0f / (float)B;
-            return launch_head(hp, c->stream);
-        });
+        if (!fuse_head) r.run(slot++, [&] { return launch_head(head_params(c->head_rb), c->stream); });
     } else {
         r.run(slot++, [&] {
             XentParams xp;
@@ -691,6 +736,15 @@ size_t plan_and_carve(mlp_ctx* c, char* base) {
         max_partial = std::max(max_partial, partial_elems(c->fwd[l], B, dout));
         max_partial = std::max(max_partial, partial_elems(c->dx[l], B, din));
         max_partial = std::max(max_partial, partial_elems(c->dw[l], din, dout));
+    }
+    if (c->head && !c->skinny && L >= 2) {
+        // the head rides along with the last hidden layer's forward: that
+        // launch needs 16 waves and one ticket per 32-row block
+        GemmPlan& g = c->fwd[L - 2];
+        if (g.small_waves > 0 && g.cfg == TileCfg::T32x16 &&
+            head_lds_bytes(c->dims[L - 1], c->dims[L], 32) <= 64 * 1024)
+            g.small_waves = 16;
+        if (head_fused(c)) max_tickets = std::max(max_tickets, (size_t)(B + 31) / 32);
     }
     int max_hidden = 1;
     for (int l = 1; l < L; ++l) max_hidden = std::max(max_hidden, c->dims[l]);

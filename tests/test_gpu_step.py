@@ -368,13 +368,13 @@ def test_profile_slots(torch_dev):
     for _ in range(3):
         net.train_step(xd, td, w.lr)
     rows = net.profile_read()
-    # 784->128->10: hidden forward GEMM, the fused output layer (logits, CE,
-    # dX), dW + SGD of the first layer with the output layer's dW + SGD and
-    # mean loss riding along
-    assert [r["name"] for r in rows] == ["mfma_f32_nn_relu_mask_l0", "head_logits_xent_dx_l1",
+    # 784->128->10: the hidden forward GEMM with the fused output layer's head
+    # (logits, CE, dX) riding along, then dW + SGD of the first layer with the
+    # output layer's dW + SGD and mean loss riding along
+    assert [r["name"] for r in rows] == ["mfma_f32_nn_relu_mask_l0+head_logits_xent_dx_l1",
                                          "mfma_f32_tn_sgd_l0+tail_dw_sgd_loss_l1"]
     assert all(r["launches"] == 3 and r["total_ms"] > 0 for r in rows)
-    assert rows[0]["flops"] == 2 * 32 * 784 * 128
+    assert rows[0]["flops"] == 2 * 32 * 784 * 128 + 4 * 32 * 128 * 10   # forward + logits and dX
     net.close()
     # without the fused output layer (C > 32): one slot per launch, in order
     dims, B = (16, 8, 40), 64
