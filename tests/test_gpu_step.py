@@ -390,3 +390,40 @@ def test_profile_slots(torch_dev):
     assert names == ["mfma_f32_nn_relu_mask_l0", "mfma_f32_nn_store_l1", "softmax_xent",
                      "mfma_f32_nt_mask_l1", "mfma_f32_tn_sgd_l1", "mfma_f32_tn_sgd_l0"], names
     net.close()
+
+
+@pytest.mark.parametrize("name", ["mnist_b1024", "skinny_b8"])
+def test_graph_replay_matches_eager(torch_dev, name):
+    """A8: a captured training step (HIP graph via torch.cuda.graph) replays
+    bit for bit like the eager steps: the step enqueues only kernels (no
+    memsets, no host synchronisation) and every reduction has a fixed order.
+    Eager work and synchronisations run between the replays."""
+    from mlp_gemm_softmax_amd import binding
+    torch, dev = torch_dev
+    w = synth.WORKLOADS[name]
+    _announce(f"graph replay {name}")
+    Ws = synth.workload_weights(w)
+    x, t, _ = synth.workload_batch(w)
+    xd, td = P.to_dev([x, t], dev)
+    eager = make_net(w.dims, w.batch, "f32", Ws, dev)
+    s = torch.cuda.Stream(device=dev)
+    graphed = binding.Mlp(w.dims, w.batch, "f32", device=str(dev), stream=s)
+    graphed.set_params(P.to_dev(Ws, dev))
+    loss_e = torch.zeros(1, dtype=torch.float32, device=dev)
+    loss_g = torch.zeros(1, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        graphed.train_step_async(xd, td, w.lr, loss_g)
+    torch.cuda.synchronize()
+    for step in range(3):
+        eager.train_step_async(xd, td, w.lr, loss_e)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert loss_g.item() == loss_e.item(), f"step {step}: loss {loss_g.item()} vs {loss_e.item()}"
+        for l, (a, b) in enumerate(zip(graphed.read_params(), eager.read_params())):
+            assert torch.equal(a, b), f"step {step}: W{l} differs"
+        torch.cuda.synchronize()
+    eager.close()
+    graphed.close()
