@@ -156,17 +156,19 @@ __device__ __forceinline__ void stage(float16v (&acc)[4][4], bf16x8v (&a)[2][4],
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][i], b[1][j], acc[i][j], 0, 0, 0);
-    // the fragment reads first (one after each MFMA), then the direct loads,
-    // so that no LDS read is ordered after a load into LDS
+    // one fragment read and one direct load after each of the first 12
+    // MFMAs, the remaining loads after the last 4 (the reads target the
+    // other buffer, which the compiler's wait counting tells apart)
 #pragma unroll
-    for (int u = 0; u < 6; ++u) {
+    for (int u = 0; u < 12; ++u) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 4; ++u) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
 }
