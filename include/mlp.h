@@ -9,7 +9,12 @@
  * with the backward pass the framework's autodiff derives for it and a plain
  * SGD update (README "Contents": SGD sessions).  A step is a fixed sequence
  * of hand-written HIP kernels: MFMA GEMMs with fused ReLU/mask, mask-multiply
- * and SGD epilogues, and one row-wise softmax cross-entropy kernel.
+ * and SGD epilogues, and one row-wise softmax cross-entropy kernel.  For
+ * narrow outputs (float32, at most 32 classes) the last layer's products,
+ * the cross-entropy and the loss mean run inside the neighbouring GEMM
+ * launches, and for batches of at most 16 rows every product is one
+ * streaming pass over its weight matrix.  The step enqueues kernels only (no
+ * memsets, no host synchronisation), so it may be captured into a HIP graph.
  *
  * Two arithmetic contracts, following the split between a strict-f32 mode
  * and validated fast paths in the abstract of "Meganeura: Portable GPU
@@ -154,7 +159,8 @@ mlp_status mlp_profile_enable(mlp_ctx* ctx, int32_t enable);
 mlp_status mlp_profile_reset(mlp_ctx* ctx);
 /* Number of launch slots in one training step. */
 int32_t mlp_profile_slots(const mlp_ctx* ctx);
-/* Slot `idx`: kernel name (copied into `name`, NUL-terminated), total
+/* Slot `idx`: slot name (the launch's products, copied into `name`,
+ * NUL-terminated), total
  * milliseconds and launch count since the last reset, and the slot's
  * algorithmic flops and HBM bytes per launch. */
 mlp_status mlp_profile_read(mlp_ctx* ctx, int32_t idx, char* name, size_t name_len,
