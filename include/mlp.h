@@ -13,8 +13,9 @@
  * narrow outputs (float32, at most 32 classes) the last layer's products,
  * the cross-entropy and the loss mean run inside the neighbouring GEMM
  * launches, and for batches of at most 16 rows every product is one
- * streaming pass over its weight matrix.  The step enqueues kernels only (no
- * memsets, no host synchronisation), so it may be captured into a HIP graph.
+ * streaming pass over its weight matrix.  mlp_train_step_async enqueues
+ * kernels only (no memsets, no host synchronisation), so it may be captured
+ * into a HIP graph.
  *
  * Two arithmetic contracts, following the split between a strict-f32 mode
  * and validated fast paths in the abstract of "Meganeura: Portable GPU
