@@ -161,11 +161,32 @@ def _short(name):
     return re.sub(r"\((mlp::)?\w+Params\)$", "", name)
 
 
+# The only slot with a second dispatch is a split-K product: its epilogue
+# kernel follows the product's own launch in the same slot.
+_FOLLOWER = "splitk_epilogue_kernel"
+
+
 def _per_slot(dispatches, n_slots, steps):
-    """Average a per-dispatch value by slot over the last `steps` whole steps."""
-    mine = [d for d in dispatches if "mlp::" in d[0]]
-    tail = mine[-n_slots * steps:]
-    names = [tail[i][0] for i in range(n_slots)]
+    """Average a per-dispatch value by slot over the last `steps` whole steps.
+    Dispatches are grouped per slot: a split-K epilogue joins the launch
+    before it, and the group's value is the sum over its dispatches."""
+    groups = []
+    for name, val in dispatches:
+        if "mlp::" not in name:
+            continue
+        if _FOLLOWER in name and groups:
+            groups[-1][1] += val
+            groups[-1][2].append(name)
+        else:
+            groups.append([name, val, [name]])
+    if len(groups) < n_slots * steps:
+        raise SystemExit(f"trace holds {len(groups)} slot dispatch groups, expected {n_slots * steps}")
+    tail = groups[-n_slots * steps:]
+    for k in range(steps):   # every step must repeat the same kernel sequence
+        for i in range(n_slots):
+            if tail[k * n_slots + i][2] != tail[i][2]:
+                raise SystemExit(f"dispatch sequence differs between steps at slot {i}")
+    names = [" + ".join(_short(n) for n in tail[i][2]) for i in range(n_slots)]
     avg = [sum(tail[k * n_slots + i][1] for k in range(steps)) / steps for i in range(n_slots)]
     return names, avg
 
@@ -176,7 +197,7 @@ def summarize(outdir, w, steps, warmup):
     trace = _csv(os.path.join(outdir, f"trace_{w}", f"{w}_kernel_trace.csv"))
     trace.sort(key=lambda r: int(r["Dispatch_Id"]))
     disp = [(r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in trace]
-    full_steps = sum(1 for d in disp if "mlp::" in d[0]) // n
+    full_steps = sum(1 for d in disp if "mlp::" in d[0] and _FOLLOWER not in d[0]) // n
     names, trace_us = _per_slot(disp, n, max(1, full_steps - 1))
     stats = _csv(os.path.join(outdir, f"trace_{w}", f"{w}_kernel_stats.csv"))
 
@@ -208,7 +229,7 @@ def summarize(outdir, w, steps, warmup):
              "| slot | kernel | HIP-event avg us | trace avg us | fetch MB | write MB |",
              "|---|---|---|---|---|---|"]
     for i, (nm, ev) in enumerate(slots):
-        kn = _short(names[i])
+        kn = names[i]
         lines.append(f"| {nm} | `{kn}` | {ev:.2f} | {trace_us[i]:.2f} | "
                      f"{counters['FETCH_SIZE'][i] / 1e6:.2f} | {counters['WRITE_SIZE'][i] / 1e6:.2f} |")
     lines += ["", "## kernel_stats (whole run)", "", "| kernel | calls | avg us | % |", "|---|---|---|---|"]

@@ -24,9 +24,13 @@ __device__ __forceinline__ Pre epilogue_load(const GemmParams& p, int row, int c
     return pre;
 }
 
-__device__ __forceinline__ uint2 pack_bf16x4(float4v v) {
-    return make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                      (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x2v pack_bf16x4(float4v v) {
+    u32x2v r;
+    r[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    r[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    return r;
 }
 
 template <Epi EPI>
@@ -43,21 +47,25 @@ __device__ __forceinline__ void epilogue4(const GemmParams& p, int row, int col,
             a[c] = pos ? v[c] : 0.f;
             m |= (pos ? 1u : 0u) << (8 * c);
         }
-        if (p.Cb) *reinterpret_cast<uint2*>(p.Cb + o) = pack_bf16x4(a);
+        // the next launch reads the activations, so they stay cached; the
+        // mask is read only in the backward pass: streaming store
+        if (p.Cb) *reinterpret_cast<u32x2v*>(p.Cb + o) = pack_bf16x4(a);
         else *reinterpret_cast<float4v*>(p.C + o) = a;
-        *reinterpret_cast<uint32_t*>(p.mask + o) = m;
+        __builtin_nontemporal_store(m, reinterpret_cast<uint32_t*>(p.mask + o));
     } else if constexpr (EPI == Epi::MaskMul) {
         float4v g;
 #pragma unroll
         for (int c = 0; c < 4; ++c) g[c] = ((pre.m >> (8 * c)) & 0xffu) ? v[c] : 0.f;
-        if (p.Cb) *reinterpret_cast<uint2*>(p.Cb + o) = pack_bf16x4(g);
-        else *reinterpret_cast<float4v*>(p.C + o) = g;
+        // streaming stores: measured faster for the whole step although the
+        // next products read this gradient
+        if (p.Cb) __builtin_nontemporal_store(pack_bf16x4(g), reinterpret_cast<u32x2v*>(p.Cb + o));
+        else __builtin_nontemporal_store(g, reinterpret_cast<float4v*>(p.C + o));
     } else if constexpr (EPI == Epi::Sgd) {
         float4v w;
 #pragma unroll
         for (int c = 0; c < 4; ++c) w[c] = pre.w[c] - p.lr * v[c];
         *reinterpret_cast<float4v*>(p.C + o) = w;
-        if (p.Cb) *reinterpret_cast<uint2*>(p.Cb + o) = pack_bf16x4(w);
+        if (p.Cb) *reinterpret_cast<u32x2v*>(p.Cb + o) = pack_bf16x4(w);
     }
 }
 

@@ -253,11 +253,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
     // rows at a time (row stride 132 floats), and reads them back row-major:
     // lane l takes float4 q of row 2q + l/32, columns 4(l%32)..+3, so every
     // global access is a coalesced 16-byte (f32) or 8-byte (bf16) vector.
+    // The mask bytes of all four chunks (64 registers) are requested before
+    // the staging starts, so their latency is paid once; the SGD weights
+    // (256 registers for all chunks) are read chunk by chunk.
+    const int rbase = m0 + wm * 128 + (lane >> 5);
+    const int col = n0 + wn * 128 + 4 * (lane & 31);
+    constexpr bool kAllPre = EPI == Epi::MaskMul;
+    Pre pre[kAllPre ? 4 : 1][16];
+    if (kAllPre && p.splits == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                if (rbase + 32 * i + 2 * q < p.M && col < p.N)
+                    pre[i][q] = epilogue_load<EPI>(p, rbase + 32 * i + 2 * q, col);
+    }
     __syncthreads();   // every wave is done with the stage buffers
     float* st = reinterpret_cast<float*>(wave == 0 ? sa0 : wave == 1 ? sb0 : wave == 2 ? sa1 : sb1);
     constexpr int SP = 132;
-    const int rbase = m0 + wm * 128 + (lane >> 5);
-    const int col = n0 + wn * 128 + 4 * (lane & 31);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -280,13 +293,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
                     *reinterpret_cast<float4v*>(part + (int64_t)(row0 + 2 * q) * p.N + col) = v[q];
             continue;
         }
-        Pre pre[16];
+        Pre* pr = pre[kAllPre ? i : 0];
+        if constexpr (!kAllPre) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                if (row0 + 2 * q < p.M && col < p.N) pr[q] = epilogue_load<EPI>(p, row0 + 2 * q, col);
+        }
 #pragma unroll
         for (int q = 0; q < 16; ++q)
-            if (row0 + 2 * q < p.M && col < p.N) pre[q] = epilogue_load<EPI>(p, row0 + 2 * q, col);
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-            if (row0 + 2 * q < p.M && col < p.N) epilogue4<EPI>(p, row0 + 2 * q, col, v[q], pre[q]);
+            if (row0 + 2 * q < p.M && col < p.N) epilogue4<EPI>(p, row0 + 2 * q, col, v[q], pr[q]);
     }
 }
 
