@@ -306,10 +306,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
 }
 
 template <Layout LAY, Epi EPI>
-hipError_t go(const GemmParams& p, int grid, hipStream_t st) {
+hipError_t go(const GemmParams& p, int grid, bool reduce, hipStream_t st) {
     hipLaunchKernelGGL((gemm_bf16_big_kernel<LAY, EPI>), dim3(grid), dim3(kThreads), 0, st, p);
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess && p.splits > 1) e = launch_splitk_epilogue(p, EPI, st);
+    if (e == hipSuccess && p.splits > 1 && reduce) e = launch_splitk_epilogue(p, EPI, st);
     return e;
 }
 
@@ -328,20 +328,23 @@ bool gemm_bf16_big_fits(Layout lay, int M, int N, int K, int64_t lda, int64_t ld
 
 hipError_t gemm_bf16_big_prepare() { return hipSuccess; }
 
-hipError_t launch_gemm_bf16_big(const GemmLaunch& L, const GemmParams& p, hipStream_t st) {
+hipError_t launch_gemm_bf16_big(const GemmLaunch& L, const GemmParams& p, hipStream_t st, bool reduce) {
     if (p.splits < 1 || p.splits > kMaxSplits || L.grid != p.tiles_m * p.tiles_n * p.splits)
         return hipErrorInvalidValue;
+    // without the reduction only the raw partials of a split product are
+    // written; its epilogue must then be Store (the caller reduces them)
+    if (!reduce && p.splits > 1 && L.epi != Epi::Store) return hipErrorInvalidValue;
     switch (L.layout) {
     case Layout::NN:
-        if (L.epi == Epi::ReluMask) return go<Layout::NN, Epi::ReluMask>(p, L.grid, st);
-        if (L.epi == Epi::Store) return go<Layout::NN, Epi::Store>(p, L.grid, st);
+        if (L.epi == Epi::ReluMask) return go<Layout::NN, Epi::ReluMask>(p, L.grid, reduce, st);
+        if (L.epi == Epi::Store) return go<Layout::NN, Epi::Store>(p, L.grid, reduce, st);
         break;
     case Layout::NT:
-        if (L.epi == Epi::MaskMul) return go<Layout::NT, Epi::MaskMul>(p, L.grid, st);
+        if (L.epi == Epi::MaskMul) return go<Layout::NT, Epi::MaskMul>(p, L.grid, reduce, st);
         break;
     case Layout::TN:
-        if (L.epi == Epi::Sgd) return go<Layout::TN, Epi::Sgd>(p, L.grid, st);
-        if (L.epi == Epi::Grad) return go<Layout::TN, Epi::Grad>(p, L.grid, st);
+        if (L.epi == Epi::Sgd) return go<Layout::TN, Epi::Sgd>(p, L.grid, reduce, st);
+        if (L.epi == Epi::Grad) return go<Layout::TN, Epi::Grad>(p, L.grid, reduce, st);
         break;
     }
     return hipErrorInvalidValue;

@@ -62,7 +62,9 @@ hipError_t launch_gemm(const GemmLaunch& L, const GemmParams& p, hipStream_t s);
 // the one-time raise of its dynamic-LDS limit, and the launch.
 bool gemm_bf16_big_fits(Layout lay, int M, int N, int K, int64_t lda, int64_t ldb);
 hipError_t gemm_bf16_big_prepare();
-hipError_t launch_gemm_bf16_big(const GemmLaunch& L, const GemmParams& p, hipStream_t s);
+// With reduce = false a split product (Store epilogue only) leaves its sums
+// in p.partials for a later launch (launch_splitk_xent) to add.
+hipError_t launch_gemm_bf16_big(const GemmLaunch& L, const GemmParams& p, hipStream_t s, bool reduce = true);
 // Adds the K splits' partials [splits][M][N] in split order and applies the
 // epilogue (used by the large-tile kernel when it splits K).
 hipError_t launch_splitk_epilogue(const GemmParams& p, Epi epi, hipStream_t s);
@@ -113,6 +115,11 @@ struct XentParams {
     float inv_b;
 };
 hipError_t launch_xent(const XentParams& p, int* grid_out, hipStream_t s);
+// Split-K sum of the logits product's partials [splits][B][C] (split order),
+// logits store and softmax-CE in one launch; C % 4 == 0, C <= 1024, 2..4 splits.
+bool splitk_xent_fits(int C, int splits);
+hipError_t launch_splitk_xent(const XentParams& p, const float* partials, int splits, float* logits,
+                              hipStream_t s);
 
 // ---- fused output layer for C <= 32 (logits, softmax-CE, dX) --------------
 struct HeadParams {

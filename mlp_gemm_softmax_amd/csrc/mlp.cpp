@@ -253,6 +253,15 @@ bool head_fused(const mlp_ctx* c) {
            head_lds_bytes(c->dims[c->L - 1], c->dims[c->L], 32) <= 64 * 1024;
 }
 
+// Whether the softmax-CE launch also adds the split-K partials of the logits
+// product (large-tile bf16 forward split over K): the logits are then written
+// once, by the loss kernel, and not read back.
+bool xent_fused(const mlp_ctx* c) {
+    if (c->head || c->skinny) return false;
+    const GemmPlan& g = c->fwd[c->L - 1];
+    return g.cfg == TileCfg::T256x256 && g.splits > 1 && splitk_xent_fits(c->dims[c->L], g.splits);
+}
+
 // Slot names and algorithmic work, in launch order.
 void build_slots(mlp_ctx* c) {
     c->slots.clear();
@@ -269,12 +278,15 @@ void build_slots(mlp_ctx* c) {
     if (c->bf16) add("cast_x_bf16", 0, (double)B * c->dims[0] * 6);
     const int C = c->dims[L];
     const int Lf = c->head ? L - 1 : L;   // layers whose forward is a plain GEMM
+    const bool xf = xent_fused(c);
     for (int l = 0; l < Lf; ++l) {
         const double M = B, N = c->dims[l + 1], K = c->dims[l];
         const bool last = l == L - 1;
-        const double out = last ? M * N * 4 : M * N * (e + 1);
-        add(std::string(kind) + "_nn_" + (last ? "store" : "relu_mask") + "_l" + std::to_string(l),
-            2 * M * N * K, M * K * e + K * N * e + out);
+        // a product that leaves its split-K sums to the loss kernel has no
+        // compulsory output of its own
+        const double out = last ? (xf ? 0.0 : M * N * 4) : M * N * (e + 1);
+        const char* what = last ? (xf ? "partials" : "store") : "relu_mask";
+        add(std::string(kind) + "_nn_" + what + "_l" + std::to_string(l), 2 * M * N * K, M * K * e + K * N * e + out);
     }
     int top = L - 1;
     double tail_flops = 0, tail_bytes = 0;
@@ -296,7 +308,10 @@ void build_slots(mlp_ctx* c) {
         tail_bytes = B * H * 4 + B * C * 4 + H * C * 8 + B * 4.0;
         tail_name = "tail_dw_sgd_loss_l" + std::to_string(L - 1);
     } else {
-        add("softmax_xent", 0, (double)B * C * (12 + (c->bf16 ? 2 : 0)) + B * 4.0);
+        if (xf)   // labels in; logits, dlogits (+ bf16 copy) and row losses out
+            add("splitk_sum_softmax_xent", 0, (double)B * C * (12 + (c->bf16 ? 2 : 0)) + B * 4.0);
+        else      // logits and labels in; dlogits (+ bf16 copy) and row losses out
+            add("softmax_xent", 0, (double)B * C * (12 + (c->bf16 ? 2 : 0)) + B * 4.0);
     }
     for (int l = top; l >= 0; --l) {
         const double din = c->dims[l], dout = c->dims[l + 1];
@@ -355,7 +370,7 @@ struct Runner {
 
 hipError_t run_gemm(mlp_ctx* c, const GemmPlan& g, Layout lay, Epi epi, const void* A, int64_t lda,
                     const void* Bm, int64_t ldb, int M, int N, int K, float* C, bf16_t* Cb,
-                    uint8_t* mask, float lr, const TailParams* tail = nullptr) {
+                    uint8_t* mask, float lr, const TailParams* tail = nullptr, bool reduce = true) {
     GemmLaunch L;
     L.layout = lay;
     L.epi = epi;
@@ -384,6 +399,7 @@ hipError_t run_gemm(mlp_ctx* c, const GemmPlan& g, Layout lay, Epi epi, const vo
     p.tiles_n = g.tiles_n;
     if (tail) return launch_gemm_small_tail(L, p, g.small_waves, *tail, c->stream);
     if (g.small_waves > 0) return launch_gemm_small(L, p, g.small_waves, c->stream);
+    if (g.cfg == TileCfg::T256x256) return launch_gemm_bf16_big(L, p, c->stream, reduce);
     return launch_gemm(L, p, c->stream);
 }
 
@@ -487,11 +503,14 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
                 return launch_gemm_small_head(gl, gp, head_params(32), c->stream);
             });
         } else {
+            // with labels the loss kernel adds a split logits product's partials
+            const bool partials_only = last && labels && xent_fused(c);
             r.run(slot++, [&] {
                 float* Cf = last ? c->logits : (c->bf16 ? nullptr : (float*)c->act[l + 1]);
                 bf16_t* Cb = (!last && c->bf16) ? (bf16_t*)c->act[l + 1] : nullptr;
                 return run_gemm(c, c->fwd[l], Layout::NN, last ? Epi::Store : Epi::ReluMask, a_prev, K,
-                                Wop, N, B, N, K, Cf, Cb, last ? nullptr : c->mask[l + 1], 0.f);
+                                Wop, N, B, N, K, Cf, Cb, last ? nullptr : c->mask[l + 1], 0.f, nullptr,
+                                !partials_only);
             });
         }
         if (!last) a_prev = c->act[l + 1];
@@ -514,6 +533,7 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
             xp.B = B;
             xp.C = C;
             xp.inv_b = 1.0f / (float)B;
+            if (xent_fused(c)) return launch_splitk_xent(xp, c->partials, c->fwd[L - 1].splits, c->logits, c->stream);
             return launch_xent(xp, nullptr, c->stream);
         });
     }

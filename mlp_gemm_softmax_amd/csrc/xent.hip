@@ -12,6 +12,8 @@
 // order (at most 256 workgroups draw tickets, bounding atomic contention).
 #include <math.h>
 
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace mlp {
@@ -163,6 +165,97 @@ __global__ __launch_bounds__(kThreads) void xent_wave(XentParams p) {
     if (last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
 }
 
+// Split-K sum and softmax-CE in one pass, for an output layer whose logits
+// product was split over K: the partial sums [split][B][C] are added in split
+// order (the order of the split-K epilogue, so the logits are the same), the
+// logits are stored, and the row's loss and dlogits follow as in xent_wave.
+// One wavefront per row, lane l holding float4 columns 4(l + 64 i); the next
+// row's partials and labels are loaded before the current row is reduced.
+// C is a multiple of 4 and at most 256 * V4 <= 1024.
+constexpr int kMaxSplitsXent = 4;
+
+template <int V4>
+__global__ __launch_bounds__(kThreads) void splitk_xent_kernel(XentParams p, const float* __restrict__ partials,
+                                                                 int splits, float* __restrict__ logits) {
+    __shared__ int s_last;
+    const int lane = threadIdx.x & 63;
+    const int waves = gridDim.x * (kThreads / kWave);
+    const int64_t bc = (int64_t)p.B * p.C;
+    float4v zn[kMaxSplitsXent][V4], tn[V4];
+    auto fetch = [&](int row) {
+        const int64_t base = (int64_t)min(row, p.B - 1) * p.C;
+#pragma unroll
+        for (int i = 0; i < V4; ++i) {
+            const int c = min(4 * (lane + kWave * i), p.C - 4);
+#pragma unroll
+            for (int t = 0; t < kMaxSplitsXent; ++t)   // splits past the last re-read it
+                zn[t][i] = *reinterpret_cast<const float4v*>(partials + min(t, splits - 1) * bc + base + c);
+            tn[i] = *reinterpret_cast<const float4v*>(p.labels + base + c);
+        }
+    };
+    int row = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
+    if (row < p.B) fetch(row);
+    for (; row < p.B; row += waves) {
+        float4v zv[V4], tv[V4];
+#pragma unroll
+        for (int i = 0; i < V4; ++i) {
+            zv[i] = zn[0][i];
+#pragma unroll
+            for (int t = 1; t < kMaxSplitsXent; ++t)
+                if (t < splits) zv[i] += zn[t][i];
+            tv[i] = tn[i];
+        }
+        if (row + waves < p.B) fetch(row + waves);
+        const int64_t base = (int64_t)row * p.C;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < V4; ++i) {
+            const int c = 4 * (lane + kWave * i);
+            if (c < p.C) {
+                *reinterpret_cast<float4v*>(logits + base + c) = zv[i];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, zv[i][e]);
+            }
+        }
+        mx = wave_max(mx);
+        float se = 0.f, st = 0.f, stz = 0.f;
+#pragma unroll
+        for (int i = 0; i < V4; ++i) {
+            if (4 * (lane + kWave * i) < p.C) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    st += tv[i][e];
+                    stz += tv[i][e] * zv[i][e];
+                    zv[i][e] = expf(zv[i][e] - mx);
+                    se += zv[i][e];
+                }
+            }
+        }
+        se = wave_sum(se);
+        st = wave_sum(st);
+        stz = wave_sum(stz);
+        const float lse = mx + logf(se);
+#pragma unroll
+        for (int i = 0; i < V4; ++i) {
+            const int c = 4 * (lane + kWave * i);
+            if (c < p.C) {
+                float4v g;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) g[e] = (zv[i][e] / se * st - tv[i][e]) * p.inv_b;
+                *reinterpret_cast<float4v*>(p.dlogits + base + c) = g;
+                if (p.dlogits_b) {
+                    uint2 h;
+                    h.x = (uint32_t)f32_to_bf16(g[0]) | ((uint32_t)f32_to_bf16(g[1]) << 16);
+                    h.y = (uint32_t)f32_to_bf16(g[2]) | ((uint32_t)f32_to_bf16(g[3]) << 16);
+                    *reinterpret_cast<uint2*>(p.dlogits_b + base + c) = h;
+                }
+            }
+        }
+        if (lane == 0) store_coherent(p.rowloss + row, st * lse - stz);
+    }
+    if (last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
+}
+
 // One workgroup per row, for few wide rows (B small, C large): the row is
 // spread over 256 lanes (VPT values each); max and sums go through the
 // wavefront butterflies and then LDS in wave order.
@@ -305,6 +398,22 @@ hipError_t launch_xent(const XentParams& p, int* grid_out, hipStream_t s) {
         else hipLaunchKernelGGL(xent_stream, dim3(grid), dim3(kThreads), 0, s, p);
     }
     if (grid_out) *grid_out = grid;
+    return hipGetLastError();
+}
+
+bool splitk_xent_fits(int C, int splits) {
+    return C >= 4 && C % 4 == 0 && C <= 256 * 4 && splits >= 2 && splits <= kMaxSplitsXent;
+}
+
+hipError_t launch_splitk_xent(const XentParams& p, const float* partials, int splits, float* logits,
+                              hipStream_t s) {
+    if (!splitk_xent_fits(p.C, splits) || p.B < 1 || !partials || !logits) return hipErrorInvalidValue;
+    const int rows_per_group = kThreads / kWave;
+    const int grid = std::min((p.B + rows_per_group - 1) / rows_per_group, 2 * kMaxGroups);
+    const int v4 = (p.C + 4 * kWave - 1) / (4 * kWave);
+    if (v4 <= 1) hipLaunchKernelGGL(splitk_xent_kernel<1>, dim3(grid), dim3(kThreads), 0, s, p, partials, splits, logits);
+    else if (v4 <= 2) hipLaunchKernelGGL(splitk_xent_kernel<2>, dim3(grid), dim3(kThreads), 0, s, p, partials, splits, logits);
+    else hipLaunchKernelGGL(splitk_xent_kernel<4>, dim3(grid), dim3(kThreads), 0, s, p, partials, splits, logits);
     return hipGetLastError();
 }
 

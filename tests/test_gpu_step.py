@@ -258,7 +258,7 @@ def test_zero_weights_loss_is_log_classes(torch_dev, dims, B, precision):
 
 # -------------------------------------------------------------- invariants --
 
-@pytest.mark.parametrize("name", ["mnist_b1024", "wide_f32", "skinny_b8"])
+@pytest.mark.parametrize("name", ["mnist_b1024", "wide_f32", "wide_bf16", "skinny_b8"])
 def test_determinism(torch_dev, name):
     """P9: two steps from the same state are bitwise identical (fixed-order
     reductions, integer tickets, no float atomics)."""
@@ -280,6 +280,33 @@ def test_determinism(torch_dev, name):
     assert a[0] == b[0] and a[3] == b[3]
     for u, v in zip(a[1] + [a[2]] + a[4], b[1] + [b[2]] + b[4]):
         assert np.array_equal(u, v)
+
+
+def test_fused_splitk_loss_matches_forward(torch_dev):
+    """A bf16 logits product split over K hands its partial sums to the loss
+    kernel, which adds them in split order: the logits it stores equal, bit
+    for bit, those of a forward without labels (split-K epilogue launch), and
+    the loss and dlogits pass the oracle gates."""
+    from mlp_gemm_softmax_amd import binding
+    torch, dev = torch_dev
+    dims, B = (1024, 2048, 1000), 2048    # logits product 2048 x 1000, K = 2048: 32 tiles, 4 splits
+    _announce(f"fused split-K loss dims={dims} B={B}")
+    Ws = synth.make_weights(dims, "kaiming", seed=21)
+    x, t, _ = synth.make_batch(B, dims[0], dims[-1], "normal", seed=22)
+    net = make_net(dims, B, "bf16", Ws, dev)
+    xd, td = P.to_dev([x, t], dev)
+    plain, _ = net.forward(xd)
+    net.profile(True)
+    loss, dws, dl, masks = P.gpu_grads(net, xd, td)
+    names = [r["name"] for r in net.profile_read()]
+    assert names[2:4] == ["mfma_bf16_nn_partials_l1", "splitk_sum_softmax_xent"], names
+    fused = net.read_state(binding.STATE_LOGITS)
+    assert torch.equal(plain, fused)
+    fl, floss = net.forward(xd, td)
+    assert torch.equal(fl, plain) and floss == loss
+    ref = P.oracle_step(x, t, Ws, 0.0, dims, "bf16", masks)
+    P.check_grads(loss, dws, dl, ref, "bf16", "fused split-K loss")
+    net.close()
 
 
 def test_dlogits_rows_sum_to_zero(torch_dev):
