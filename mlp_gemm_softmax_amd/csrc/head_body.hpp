@@ -128,10 +128,7 @@ __device__ __forceinline__ void head_block(const HeadParams& p, int row0, float*
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int bb = b0 + 4 * lk + e;
-                if (bb < rows && cb < C) {
-                    sZ[bb * C + cb] = z[e];
-                    if (p.logits) p.logits[(int64_t)(row0 + bb) * C + cb] = z[e];
-                }
+                if (bb < rows && cb < C) sZ[bb * C + cb] = z[e];
             }
         }
     }
@@ -139,14 +136,19 @@ __device__ __forceinline__ void head_block(const HeadParams& p, int row0, float*
 
     // softmax cross-entropy, 16 lanes per row (classes j and j + 16 of the
     // row on lane j); max and sums by a fixed xor butterfly inside the
-    // 16-lane group.
+    // 16-lane group.  Only LDS is written before the next barrier (a barrier
+    // also waits for the thread's outstanding global stores): the logits,
+    // dlogits and row loss stay in this thread's registers and are stored
+    // after the last phase.
+    const int cb_row = tid >> 4, cj = tid & 15;
+    const bool cv0 = cb_row < rows && cj < C, cv1 = cb_row < rows && cj + 16 < C;
+    float cz0 = 0.f, cz1 = 0.f, cg0 = 0.f, cg1 = 0.f, closs = 0.f;
     {
-        const int b = tid >> 4, j = tid & 15;
+        const int b = cb_row, j = cj;
         if (b < rows) {
-            const int row = row0 + b;
             const float* t = sT + b * C;
             float* z = sZ + b * C;
-            const bool v0 = j < C, v1 = j + 16 < C;
+            const bool v0 = cv0, v1 = cv1;
             const float z0 = v0 ? z[j] : -INFINITY, z1 = v1 ? z[j + 16] : -INFINITY;
             const float t0 = v0 ? t[j] : 0.f, t1 = v1 ? t[j + 16] : 0.f;
             float mx = fmaxf(z0, z1);
@@ -161,17 +163,17 @@ __device__ __forceinline__ void head_block(const HeadParams& p, int row0, float*
                 stz += __shfl_xor(stz, o, 16);
             }
             const float lse = mx + logf(se);
+            cz0 = z0;
+            cz1 = z1;
             if (v0) {
-                const float g = (e0 / se * st - t0) * p.inv_b;
-                z[j] = g;
-                p.dlogits[(int64_t)row * C + j] = g;
+                cg0 = (e0 / se * st - t0) * p.inv_b;
+                z[j] = cg0;
             }
             if (v1) {
-                const float g = (e1 / se * st - t1) * p.inv_b;
-                z[j + 16] = g;
-                p.dlogits[(int64_t)row * C + j + 16] = g;
+                cg1 = (e1 / se * st - t1) * p.inv_b;
+                z[j + 16] = cg1;
             }
-            if (j == 0) p.rowloss[row] = st * lse - stz;
+            closs = st * lse - stz;
         }
     }
     __syncthreads();
@@ -194,6 +196,18 @@ __device__ __forceinline__ void head_block(const HeadParams& p, int row0, float*
             if (bb < rows && hb < H) p.G[(int64_t)(row0 + bb) * H + hb] = sM[bb * H + hb] ? acc[e] : 0.f;
         }
     }
+
+    // the softmax-CE phase's outputs
+    const int64_t o = (int64_t)(row0 + cb_row) * C + cj;
+    if (cv0) {
+        if (p.logits) p.logits[o] = cz0;
+        p.dlogits[o] = cg0;
+    }
+    if (cv1) {
+        if (p.logits) p.logits[o + 16] = cz1;
+        p.dlogits[o + 16] = cg1;
+    }
+    if (cb_row < rows && cj == 0) p.rowloss[row0 + cb_row] = closs;
 }
 
 }  // namespace mlp
