@@ -187,6 +187,60 @@ def sgd(weights: Sequence, grads: Sequence, lr: float) -> List[np.ndarray]:
     return [_f64(w) - float(lr) * _f64(g) for w, g in zip(weights, grads)]
 
 
+def adam(weights: Sequence, grads: Sequence, m: Sequence, v: Sequence, t: int, lr: float,
+         beta1: float, beta2: float, eps: float) -> Dict:
+    """Adam, step t >= 1 (Kingma and Ba, "Adam: A Method for Stochastic
+    Optimization", Algorithm 1; the pages name Adam among the optimizers a
+    session can carry, README "Contents", without restating it).  Per element:
+
+        m <- beta1 m + (1 - beta1) g
+        v <- beta2 v + (1 - beta2) g^2
+        W <- W - lr * (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+
+    Returns {"W_new", "m", "v"} (float64 lists); m = v = 0 before step 1."""
+    assert t >= 1
+    c1 = 1.0 - float(beta1) ** t
+    c2 = 1.0 - float(beta2) ** t
+    W_new, m_new, v_new = [], [], []
+    for w, g, m0, v0 in zip(weights, grads, m, v):
+        g = _f64(g)
+        m1 = beta1 * _f64(m0) + (1.0 - beta1) * g
+        v1 = beta2 * _f64(v0) + (1.0 - beta2) * g * g
+        W_new.append(_f64(w) - float(lr) * (m1 / c1) / (np.sqrt(v1 / c2) + eps))
+        m_new.append(m1)
+        v_new.append(v1)
+    return {"W_new": W_new, "m": m_new, "v": v_new}
+
+
+def laprop(weights: Sequence, grads: Sequence, m: Sequence, v: Sequence, t: int, lr: float,
+           beta1: float, beta2: float, eps: float) -> Dict:
+    """LaProp, step t >= 1 (Ziyin, Wang and Ueda, "LaProp: Separating Momentum
+    and Adaptivity in Adam", Algorithm 1; named beside Adam in the README
+    "Contents").  The gradient is divided by the bias-corrected root mean
+    square before it enters the momentum:
+
+        v <- beta2 v + (1 - beta2) g^2
+        m <- beta1 m + (1 - beta1) g / (sqrt(v / (1 - beta2^t)) + eps)
+        W <- W - lr * m / (1 - beta1^t)
+
+    Returns {"W_new", "m", "v"} (float64 lists); m = v = 0 before step 1."""
+    assert t >= 1
+    c1 = 1.0 - float(beta1) ** t
+    c2 = 1.0 - float(beta2) ** t
+    W_new, m_new, v_new = [], [], []
+    for w, g, m0, v0 in zip(weights, grads, m, v):
+        g = _f64(g)
+        v1 = beta2 * _f64(v0) + (1.0 - beta2) * g * g
+        m1 = beta1 * _f64(m0) + (1.0 - beta1) * g / (np.sqrt(v1 / c2) + eps)
+        W_new.append(_f64(w) - float(lr) * m1 / c1)
+        m_new.append(m1)
+        v_new.append(v1)
+    return {"W_new": W_new, "m": m_new, "v": v_new}
+
+
+OPTIMIZERS = {"adam": adam, "laprop": laprop}
+
+
 # --------------------------------------------------------------------------
 # One whole training step.
 # --------------------------------------------------------------------------

@@ -349,3 +349,121 @@ def test_pins_accept_the_oracle(golden):
                                   "no_mask", "updated_weights", "sgd_sign"])
 def test_pins_reject_planted_mistakes(golden, kind):
     assert not _pins_pass(_mutant(kind), golden)
+
+
+# ------------------------------------------------------ Adam / LaProp pins --
+# Closed forms derived by hand from the published update rules (scalar
+# sequences run through the oracle's per-element arithmetic as 1x1 layers),
+# plus scale invariance; mutants of each rule must fail at least one pin.
+
+def _run_opt(fn, gs, lr=0.1, b1=0.9, b2=0.999, eps=1e-8, w0=0.5):
+    """W after each step of a scalar gradient sequence (float64)."""
+    W = [np.array([[w0]])]
+    m = [np.zeros((1, 1))]
+    v = [np.zeros((1, 1))]
+    out = []
+    for t, g in enumerate(gs, start=1):
+        r = fn(W, [np.array([[g]])], m, v, t, lr, b1, b2, eps)
+        W, m, v = r["W_new"], r["m"], r["v"]
+        out.append(float(W[0][0, 0]))
+    return out
+
+
+def _opt_pins_pass(fn, name):
+    lr, b1, b2 = 0.1, 0.9, 0.999
+    ok = True
+    # first step, any gradient: bias-corrected moments are g and g^2, so the
+    # step is lr * g / (|g| + eps) for both rules
+    for g, eps in ((0.3, 1e-8), (-2.0, 0.5), (1e-9, 1e-8)):
+        w1 = _run_opt(fn, [g], lr, b1, b2, eps)[0]
+        ok &= abs((0.5 - w1) - lr * g / (abs(g) + eps)) < 1e-14
+    # constant gradient: the bias corrections cancel the (1 - beta^t) growth
+    # of both moments at every step
+    ws = _run_opt(fn, [0.7] * 5, lr, b1, b2, 0.25)
+    steps = np.diff([0.5] + ws)
+    ok &= np.allclose(steps, -lr * 0.7 / 0.95, rtol=0, atol=1e-13)
+    # +1 then -1 (eps = 0): v_hat_2 = 1 and m_hat_2 = -(1 - b1)/(1 + b1), so the
+    # second step moves W up by lr (1 - b1)/(1 + b1) for both rules
+    ws = _run_opt(fn, [1.0, -1.0], lr, b1, b2, 0.0)
+    ok &= abs((ws[1] - ws[0]) - lr * (1 - b1) / (1 + b1)) < 1e-14
+    # 2 then 1 (eps = 0): v_hat_2 = (4 b2 + 1)/(1 + b2);
+    #   Adam:   m_hat_2 = (2 b1 + 1)/(1 + b1),   step = -lr m_hat_2 / sqrt(v_hat_2)
+    #   LaProp: m_1 = 1 - b1, m_2 = b1 (1 - b1) + (1 - b1)/sqrt(v_hat_2),
+    #           step = -lr m_2 / (1 - b1^2) = -lr (b1 + 1/sqrt(v_hat_2)) / (1 + b1)
+    ws = _run_opt(fn, [2.0, 1.0], lr, b1, b2, 0.0)
+    vh = (4 * b2 + 1) / (1 + b2)
+    if name == "adam":
+        want = -lr * (2 * b1 + 1) / (1 + b1) / math.sqrt(vh)
+    else:
+        want = -lr * (b1 + 1 / math.sqrt(vh)) / (1 + b1)
+    ok &= abs((ws[1] - ws[0]) - want) < 1e-14
+    # eps = 0: multiplying every gradient by c > 0 leaves every step unchanged
+    r = _rng(77)
+    gs = r.standard_normal(6)
+    a = _run_opt(fn, list(gs), lr, b1, b2, 0.0)
+    b = _run_opt(fn, list(37.0 * gs), lr, b1, b2, 0.0)
+    ok &= np.allclose(a, b, rtol=0, atol=1e-13)
+    return bool(ok)
+
+
+@pytest.mark.parametrize("name", ["adam", "laprop"])
+def test_optimizer_pins(name):
+    assert _opt_pins_pass(O.OPTIMIZERS[name], name)
+
+
+def test_optimizers_on_matrices_match_elementwise_rule():
+    """The layer-wise update is the scalar rule applied to every element
+    (checked against the scalar runs above on a 3x4 matrix, two steps)."""
+    r = _rng(5)
+    W = [r.standard_normal((3, 4))]
+    g1, g2 = r.standard_normal((3, 4)), r.standard_normal((3, 4))
+    for name, fn in O.OPTIMIZERS.items():
+        z = [np.zeros((3, 4))]
+        s1 = fn(W, [g1], z, z, 1, 0.01, 0.9, 0.99, 1e-3)
+        s2 = fn(s1["W_new"], [g2], s1["m"], s1["v"], 2, 0.01, 0.9, 0.99, 1e-3)
+        for idx in np.ndindex(3, 4):
+            ws = _run_opt(fn, [g1[idx], g2[idx]], 0.01, 0.9, 0.99, 1e-3, w0=W[0][idx])
+            assert abs(s2["W_new"][0][idx] - ws[1]) < 1e-14, (name, idx)
+
+
+def _opt_mutant(name, kind):
+    def fn(weights, grads, m, v, t, lr, b1, b2, eps):
+        c1 = 1.0 - b1 ** t
+        c2 = 1.0 - b2 ** t
+        if kind == "no_bias_correction":
+            c1 = c2 = 1.0
+        if kind == "betas_swapped":
+            b1, b2 = b2, b1
+            c1, c2 = 1.0 - b1 ** t, 1.0 - b2 ** t
+        W_new, m_new, v_new = [], [], []
+        for w, g, m0, v0 in zip(weights, grads, m, v):
+            g = np.asarray(g, float)
+            if kind == "no_square":
+                v1 = b2 * np.asarray(v0) + (1 - b2) * np.abs(g)
+            else:
+                v1 = b2 * np.asarray(v0) + (1 - b2) * g * g
+            root = np.sqrt(v1 / c2) if kind != "no_sqrt" else v1 / c2
+            if name == "adam":
+                m1 = b1 * np.asarray(m0) + (1 - b1) * g
+                W_new.append(np.asarray(w) - lr * (m1 / c1) / (root + eps))
+            else:
+                m1 = b1 * np.asarray(m0) + (1 - b1) * g / (root + eps)
+                W_new.append(np.asarray(w) - lr * m1 / c1)
+            m_new.append(m1)
+            v_new.append(v1)
+        return {"W_new": W_new, "m": m_new, "v": v_new}
+    return fn
+
+
+@pytest.mark.parametrize("name", ["adam", "laprop"])
+@pytest.mark.parametrize("kind", ["no_bias_correction", "betas_swapped", "no_square", "no_sqrt"])
+def test_optimizer_pins_reject_planted_mistakes(name, kind):
+    assert _opt_pins_pass(_opt_mutant(name, "none"), name)   # the harness itself is faithful
+    assert not _opt_pins_pass(_opt_mutant(name, kind), name)
+
+
+def test_adam_and_laprop_differ():
+    """The two rules part ways as soon as the gradient scale changes."""
+    a = _run_opt(O.adam, [2.0, 1.0], eps=0.0)
+    b = _run_opt(O.laprop, [2.0, 1.0], eps=0.0)
+    assert abs(a[1] - b[1]) > 1e-3
