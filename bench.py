@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--optimizer", choices=["sgd", "adam", "laprop"], default="sgd",
+                    help="update rule of the step (Adam/LaProp: beta1 0.9, beta2 0.999, eps 1e-8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--profile-steps", type=int, default=None,
@@ -100,9 +102,10 @@ def roofline(rows, precision, steps):
             "algorithmic_bytes": dom["bytes"]}
 
 
-def cpu_baseline(w, budget_s):
+def cpu_baseline(w, budget_s, rule="sgd"):
     """The float64 oracle as it stands, on this host's cores, over a bounded
-    sample of the workload's steps."""
+    sample of the workload's steps (with the oracle's Adam/LaProp when the
+    step uses one)."""
     import numpy as np
     from mlp_gemm_softmax_amd import synth
     from oracle import mlp_oracle
@@ -112,10 +115,15 @@ def cpu_baseline(w, budget_s):
     except Exception:
         cores = len(os.sched_getaffinity(0))
     Ws = synth.workload_weights(w)
+    m = [np.zeros(a.shape) for a in Ws]
+    v = [np.zeros(a.shape) for a in Ws]
     n, t0 = 0, time.perf_counter()
     while True:
         x, t, _ = synth.workload_batch(w, n)
         r = mlp_oracle.train_step(x, t, Ws, w.lr)
+        if rule != "sgd":
+            u = mlp_oracle.OPTIMIZERS[rule](Ws, r["dW"], m, v, n + 1, w.lr, 0.9, 0.999, 1e-8)
+            r["W_new"], m, v = u["W_new"], u["m"], u["v"]
         Ws = [a.astype(np.float32) for a in r["W_new"]]
         n += 1
         el = time.perf_counter() - t0
@@ -123,7 +131,7 @@ def cpu_baseline(w, budget_s):
             break
     # batch generation is inside the loop; it is small next to the f64 step
     return {"value": round(n / el, 4), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n} consecutive training steps of {w.name} (float64 numpy, BLAS threads "
+            "sample": f"{n} consecutive training steps ({rule}) of {w.name} (float64 numpy, BLAS threads "
                       f"{cores}), {el:.1f} s"}
 
 
@@ -276,6 +284,8 @@ def main():
 
     net = binding.Mlp(w.dims, w.batch, w.precision, device="cuda:0")
     net.set_params([torch.from_numpy(a).to(dev) for a in synth.workload_weights(w)])
+    if args.optimizer != "sgd":
+        net.set_optimizer(args.optimizer, 0.9, 0.999, 1e-8)
     n_batches = w.steps if w.fresh_batch else 1
     batches = []
     for s in range(n_batches):
@@ -334,14 +344,15 @@ def main():
         "dtype": "bf16" if w.precision == "bf16" else "f32",
         "data": "synthetic (seeded; MNIST-shaped uniform [0,1) pixels or N(0,1) features, uniform class ids)",
         "config": {"workload": w.name, "dims": list(w.dims), "batch": w.batch, "lr": w.lr,
-                   "precision": w.precision, "fresh_batch_per_step": w.fresh_batch},
+                   "precision": w.precision, "fresh_batch_per_step": w.fresh_batch,
+                   "optimizer": args.optimizer},
         "achieved_tflops": round(flops * steps_per_s / 1e12, 4),
         "step_flops": flops,
         "final_loss": final_loss,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s, args.optimizer)
     net.close()
     print(json.dumps(out), flush=True)
 

@@ -75,6 +75,19 @@ typedef enum mlp_precision {
     MLP_BF16 = 1
 } mlp_precision;
 
+/* Update rule of a training step (README "Contents": Adam/LaProp moments are
+ * allocated only when requested; SGD sessions keep no optimizer state). */
+typedef enum mlp_optimizer {
+    MLP_OPT_SGD = 0,        /* W <- W - lr g */
+    MLP_OPT_ADAM = 1,       /* Kingma and Ba, "Adam: A Method for Stochastic Optimization",
+                               Algorithm 1: m <- b1 m + (1-b1) g, v <- b2 v + (1-b2) g^2,
+                               W <- W - lr (m/(1-b1^t)) / (sqrt(v/(1-b2^t)) + eps) */
+    MLP_OPT_LAPROP = 2      /* Ziyin, Wang and Ueda, "LaProp: Separating Momentum and
+                               Adaptivity in Adam", Algorithm 1: v <- b2 v + (1-b2) g^2,
+                               m <- b1 m + (1-b1) g / (sqrt(v/(1-b2^t)) + eps),
+                               W <- W - lr m/(1-b1^t) */
+} mlp_optimizer;
+
 /* What mlp_read_state copies out (debug-session reads, README "Debugging"). */
 typedef enum mlp_state_kind {
     MLP_STATE_ACT = 0,      /* a_l = relu(z_l), l = 1..n_layers-1: float32 [B, dims[l]]
@@ -128,9 +141,9 @@ mlp_status mlp_read_params(mlp_ctx* ctx, int32_t layer, float* dst);
 mlp_status mlp_forward(mlp_ctx* ctx, const float* x, float* logits,
                        const float* labels, float* loss);
 
-/* One training step: forward, mean softmax-CE, backward and
- * W_l <- W_l - lr * dW_l for every layer, all gradients taken at the
- * pre-update weights.  x: device float32 [B, d0]; labels: device float32
+/* One training step: forward, mean softmax-CE, backward and the update of
+ * every layer (W_l <- W_l - lr * dW_l, or the rule mlp_set_optimizer chose),
+ * all gradients taken at the pre-update weights.  x: device float32 [B, d0]; labels: device float32
  * [B, C]; lr: finite.  loss: host float or NULL; the call synchronises the
  * stream and writes the mean loss at the pre-update weights. */
 mlp_status mlp_train_step(mlp_ctx* ctx, const float* x, const float* labels,
@@ -147,6 +160,28 @@ mlp_status mlp_train_step_async(mlp_ctx* ctx, const float* x, const float* label
  * NULL.  loss: host float or NULL (the call synchronises when non-NULL). */
 mlp_status mlp_grads(mlp_ctx* ctx, const float* x, const float* labels,
                      float* const* dw, float* dlogits, float* loss);
+
+/* Device memory (bytes, a multiple of 256) that update rule `opt` keeps for
+ * this configuration: float32 first and second moments and a float32
+ * gradient buffer per weight.  0 for MLP_OPT_SGD, for an unknown rule and
+ * for an invalid configuration.  Host only. */
+size_t mlp_optimizer_bytes(const mlp_config* cfg, int32_t opt);
+
+/* Select the update rule of mlp_train_step / mlp_train_step_async (the
+ * default is MLP_OPT_SGD).  For Adam and LaProp, `state` is caller-owned
+ * device memory of at least mlp_optimizer_bytes(cfg, opt) bytes, 256-byte
+ * aligned, that must stay alive while the rule is in use; both moments are
+ * zeroed (enqueued on the context's stream) and the step count t restarts,
+ * so the next step has t = 1.  beta1, beta2 in [0, 1); eps finite and > 0.
+ * For SGD, state, bytes, beta1, beta2 and eps are ignored.  With an adaptive
+ * rule a step stores every dW_l into the state, then one more launch updates
+ * all layers; the step count is a launch argument, so such steps refuse
+ * (MLP_ERR_ARG) to be enqueued while the stream is being captured.  Errors:
+ * MLP_ERR_ARG (rule, betas, eps), MLP_ERR_WORKSPACE (state), MLP_ERR_STATE
+ * (poisoned context); nothing changes on an error.  Resets the per-launch
+ * timing (the launch sequence changes). */
+mlp_status mlp_set_optimizer(mlp_ctx* ctx, int32_t opt, float beta1, float beta2, float eps,
+                             void* state, size_t bytes);
 
 /* Copy an intermediate of the last step or forward to device memory `dst`
  * (see mlp_state_kind for shapes; `layer` is 1..n_layers-1 for ACT/MASK). */

@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(HERE, "libmlp.so")
 MLP_OK, MLP_ERR_ARG, MLP_ERR_SHAPE, MLP_ERR_WORKSPACE, MLP_ERR_HIP, MLP_ERR_STATE = range(6)
 MLP_F32, MLP_BF16 = 0, 1
 STATE_ACT, STATE_MASK, STATE_DLOGITS, STATE_LOGITS = range(4)
+OPT_SGD, OPT_ADAM, OPT_LAPROP = range(3)
+OPTIMIZERS = {"sgd": OPT_SGD, "adam": OPT_ADAM, "laprop": OPT_LAPROP}
 
 # Every entry point include/mlp.h declares: name -> (restype, argtypes).
 _c = ctypes
@@ -37,6 +39,9 @@ SIGNATURES = {
     "mlp_grads": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.POINTER(_c.c_void_p),
                              _c.c_void_p, _c.POINTER(_c.c_float)]),
     "mlp_read_state": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_int32, _c.c_void_p]),
+    "mlp_optimizer_bytes": (_c.c_size_t, [_c.c_void_p, _c.c_int32]),
+    "mlp_set_optimizer": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_float, _c.c_float, _c.c_float,
+                                     _c.c_void_p, _c.c_size_t]),
     "mlp_profile_enable": (_c.c_int, [_c.c_void_p, _c.c_int32]),
     "mlp_profile_reset": (_c.c_int, [_c.c_void_p]),
     "mlp_profile_slots": (_c.c_int32, [_c.c_void_p]),
@@ -160,6 +165,21 @@ class Mlp:
         for l, w in enumerate(weights):
             self._dev_f32(w, (self.dims[l], self.dims[l + 1]))
             self._check(lib().mlp_set_params(self._h, l, ctypes.c_void_p(w.data_ptr())))
+
+    def set_optimizer(self, rule: str = "sgd", beta1: float = 0.9, beta2: float = 0.999,
+                      eps: float = 1e-8):
+        """Update rule of later training steps; Adam/LaProp state (moments and a
+        gradient buffer) lives in a torch-owned device buffer kept here."""
+        opt = OPTIMIZERS[rule]
+        state, nbytes = None, 0
+        if opt != OPT_SGD:
+            nbytes = int(lib().mlp_optimizer_bytes(ctypes.byref(self._cfg), opt))
+            if nbytes == 0:
+                raise MlpError(MLP_ERR_ARG, "no optimizer state size for this configuration")
+            state = self.torch.empty(nbytes, dtype=self.torch.uint8, device=self.device)
+        ptr = ctypes.c_void_p(state.data_ptr()) if state is not None else None
+        self._check(lib().mlp_set_optimizer(self._h, opt, float(beta1), float(beta2), float(eps), ptr, nbytes))
+        self.opt_state = state
 
     def read_params(self) -> List:
         out = []

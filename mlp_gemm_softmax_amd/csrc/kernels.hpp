@@ -166,6 +166,31 @@ hipError_t launch_gemm_small_tail(const GemmLaunch& L, const GemmParams& p, int 
 
 // ---- f32 -> bf16 cast -----------------------------------------------------
 hipError_t launch_cast_bf16(const float* src, bf16_t* dst, size_t n, hipStream_t s);
+
+// ---- adaptive update rules (optim.hip) -------------------------------------
+constexpr int kOptAdam = 1;
+constexpr int kOptLaProp = 2;
+constexpr int kMaxOptTensors = 16;
+struct OptTensor {
+    float* W;          // f32 master [n]
+    bf16_t* Wb;        // bf16 operand copy [n] or null
+    const float* g;    // gradient [n]
+    float* m;          // first moment [n]
+    float* v;          // second moment [n]
+    int64_t n;
+};
+struct OptParams {
+    OptTensor t[kMaxOptTensors];
+    int first_block[kMaxOptTensors + 1];   // filled by launch_opt_update
+    int count;
+    int rule;                              // kOptAdam or kOptLaProp
+    float lr, b1, b2, om1, om2, eps;       // om = 1 - beta
+    float inv_c1, inv_c2;                  // 1 / (1 - beta^t)
+};
+// Every tensor's arrays are 16-byte aligned.
+hipError_t launch_opt_update(OptParams p, hipStream_t s);
+// Zero n floats (n % 4 == 0, 16-byte aligned) with a kernel.
+hipError_t launch_zero(float* p, size_t n, hipStream_t s);
 // ---- bf16 -> f32 widen (state read-back) -----------------------------------
 hipError_t launch_widen_bf16(const bf16_t* src, float* dst, size_t n, hipStream_t s);
 

@@ -59,6 +59,7 @@ using namespace mlp;
 namespace {
 
 constexpr int kMaxLayers = 16;
+static_assert(kMaxLayers <= kMaxOptTensors, "one update tensor per layer");
 constexpr int kMaxDim = 1 << 20;
 constexpr int kSkinnyMaxBatch = 16;
 constexpr size_t kAlign = 256;
@@ -122,6 +123,15 @@ struct mlp_ctx {
     unsigned params_set = 0;   // bit l: W_l written since creation / poisoning
     bool poisoned = false;
     std::string err;
+
+    // update rule of a training step: SGD (no state), or Adam / LaProp with
+    // moments and a gradient buffer in caller memory given to mlp_set_optimizer
+    int opt = MLP_OPT_SGD;
+    float opt_b1 = 0.f, opt_b2 = 0.f, opt_eps = 0.f;
+    int64_t opt_t = 0;                  // steps taken with the current moments
+    float* opt_m[kMaxLayers] = {};
+    float* opt_v[kMaxLayers] = {};
+    float* opt_g[kMaxLayers] = {};
 
     bool profiling = false;
     std::vector<Slot> slots;
@@ -275,6 +285,9 @@ void build_slots(mlp_ctx* c) {
         c->slots.push_back(s);
     };
     const char* kind = c->skinny ? "skinny" : (c->bf16 ? "mfma_bf16" : "mfma_f32");
+    // with an adaptive rule the dW launches store gradients and one more
+    // launch applies the update
+    const std::string upd = c->opt == MLP_OPT_SGD ? "sgd" : "grad";
     if (c->bf16) add("cast_x_bf16", 0, (double)B * c->dims[0] * 6);
     const int C = c->dims[L];
     const int Lf = c->head ? L - 1 : L;   // layers whose forward is a plain GEMM
@@ -306,7 +319,7 @@ void build_slots(mlp_ctx* c) {
         top = L - 2;
         tail_flops = 2.0 * B * H * C;
         tail_bytes = B * H * 4 + B * C * 4 + H * C * 8 + B * 4.0;
-        tail_name = "tail_dw_sgd_loss_l" + std::to_string(L - 1);
+        tail_name = "tail_dw_" + upd + "_loss_l" + std::to_string(L - 1);
     } else {
         if (xf)   // labels in; logits, dlogits (+ bf16 copy) and row losses out
             add("splitk_sum_softmax_xent", 0, (double)B * C * (12 + (c->bf16 ? 2 : 0)) + B * 4.0);
@@ -317,20 +330,27 @@ void build_slots(mlp_ctx* c) {
         const double din = c->dims[l], dout = c->dims[l + 1];
         if (l > 0 && c->skinny) {
             // dX and dW + SGD in one pass over W: W read and written once
-            add(std::string(kind) + "_nt_mask_sgd_l" + std::to_string(l), 4.0 * B * din * dout,
+            add(std::string(kind) + "_nt_mask_" + upd + "_l" + std::to_string(l), 4.0 * B * din * dout,
                 8.0 * din * dout + 4.0 * B * dout + 4.0 * B * din + B * din * 5.0);
             continue;
         }
         if (l > 0)
             add(std::string(kind) + "_nt_mask_l" + std::to_string(l), 2.0 * B * din * dout,
                 B * dout * e + din * dout * e + B * din * (1 + e));
-        const double f = 2.0 * B * din * dout, b = B * din * e + B * dout * e + din * dout * (8 + (c->bf16 ? 2 : 0));
+        const double wb = c->opt == MLP_OPT_SGD ? 8 + (c->bf16 ? 2 : 0) : 4;   // W in+out (+copy), or dW out
+        const double f = 2.0 * B * din * dout, b = B * din * e + B * dout * e + din * dout * wb;
         if (l == 0 && c->head && tail_fused(c))
-            add(std::string(kind) + "_tn_sgd_l0+" + tail_name, f + tail_flops, b + tail_bytes);
+            add(std::string(kind) + "_tn_" + upd + "_l0+" + tail_name, f + tail_flops, b + tail_bytes);
         else
-            add(std::string(kind) + "_tn_sgd_l" + std::to_string(l), f, b);
+            add(std::string(kind) + "_tn_" + upd + "_l" + std::to_string(l), f, b);
     }
     if (c->head && !tail_fused(c)) add(tail_name, tail_flops, tail_bytes);
+    if (c->opt != MLP_OPT_SGD) {
+        // per weight: g, m, v, W in; m, v, W (+ bf16 copy) out
+        double n = 0;
+        for (int l = 0; l < L; ++l) n += (double)c->dims[l] * c->dims[l + 1];
+        add(c->opt == MLP_OPT_ADAM ? "opt_update_adam" : "opt_update_laprop", 0, n * (28 + (c->bf16 ? 2 : 0)));
+    }
 }
 
 // ---------------------------------------------------------------- launches --
@@ -539,13 +559,16 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
     }
     if (mode == Mode::Forward) return r.err;
 
-    // ---- backward
+    // ---- backward (an adaptive rule stores the gradients and updates after)
+    const bool adaptive = mode == Mode::Train && c->opt != MLP_OPT_SGD;
+    const bool grads = mode == Mode::Grads || adaptive;
+    float* const* dwo = adaptive ? c->opt_g : dw_out;
     TailParams tp{};
     if (use_head) {
         tp.A = (const float*)c->act[L - 1];
         tp.dZ = c->dlogits;
         tp.W = c->W[L - 1];
-        tp.dW = mode == Mode::Grads ? dw_out[L - 1] : nullptr;
+        tp.dW = grads ? dwo[L - 1] : nullptr;
         tp.rowloss = c->rowloss;
         tp.loss = loss_dev ? loss_dev : c->loss_slot;
         tp.B = B;
@@ -567,7 +590,6 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
         const int din = c->dims[l], dout = c->dims[l + 1];
         const void* Wop = c->bf16 ? (const void*)c->Wb[l] : (const void*)c->W[l];
         const void* Gnext = nullptr;
-        const bool grads = mode == Mode::Grads;
         if (l > 0 && c->skinny) {
             // one pass over W_l: G_{l-1} (from the old W_l) and the update
             void* out = c->dz[pp];
@@ -589,7 +611,7 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
                 sp.mask = c->mask[l];
                 sp.lr = lr;
                 sp.act = (const float*)c->act[l];
-                sp.wout = grads ? dw_out[l] : c->W[l];
+                sp.wout = grads ? dwo[l] : c->W[l];
                 return launch_skinny(sl, sp, c->stream);
             });
             G = out;
@@ -606,7 +628,7 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
             Gnext = out;
         }
         const void* a_in = l == 0 ? (c->bf16 ? (const void*)c->xb : (const void*)x) : c->act[l];
-        float* Wdst = grads ? dw_out[l] : c->W[l];
+        float* Wdst = grads ? dwo[l] : c->W[l];
         bf16_t* Wbdst = (!grads && c->bf16) ? c->Wb[l] : nullptr;
         if (c->skinny) {
             r.run(slot++, [&] {
@@ -622,6 +644,31 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
         G = Gnext;
     }
     if (use_head && !fuse_tail) r.run(slot++, [&] { return launch_tail(tp, c->stream); });
+    if (adaptive) {
+        r.run(slot++, [&] {
+            OptParams op{};
+            op.count = L;
+            op.rule = c->opt == MLP_OPT_ADAM ? kOptAdam : kOptLaProp;
+            op.lr = lr;
+            op.b1 = c->opt_b1;
+            op.b2 = c->opt_b2;
+            op.om1 = (float)(1.0 - (double)c->opt_b1);
+            op.om2 = (float)(1.0 - (double)c->opt_b2);
+            op.eps = c->opt_eps;
+            op.inv_c1 = (float)(1.0 / (1.0 - std::pow((double)c->opt_b1, (double)c->opt_t)));
+            op.inv_c2 = (float)(1.0 / (1.0 - std::pow((double)c->opt_b2, (double)c->opt_t)));
+            for (int l = 0; l < L; ++l) {
+                OptTensor& t = op.t[l];
+                t.W = c->W[l];
+                t.Wb = c->bf16 ? c->Wb[l] : nullptr;
+                t.g = c->opt_g[l];
+                t.m = c->opt_m[l];
+                t.v = c->opt_v[l];
+                t.n = (int64_t)c->dims[l] * c->dims[l + 1];
+            }
+            return launch_opt_update(op, c->stream);
+        });
+    }
     return r.err;
 }
 
@@ -959,6 +1006,17 @@ mlp_status mlp_train_step_async(mlp_ctx* c, const float* x, const float* labels,
         return set_err(c, MLP_ERR_ARG, "labels must be a 16-byte aligned device pointer");
     if (!std::isfinite(lr)) return set_err(c, MLP_ERR_ARG, "lr must be finite");
     if (loss_dev && ((uintptr_t)loss_dev & 3u)) return set_err(c, MLP_ERR_ARG, "loss_dev must be 4-byte aligned");
+    if (c->opt != MLP_OPT_SGD) {
+        // the step count is a launch argument of the update: a captured
+        // graph would replay one step count forever
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        const hipError_t ce = hipStreamIsCapturing(c->stream, &cs);
+        if (ce != hipSuccess) return hip_fail(c, ce, "hipStreamIsCapturing");
+        if (cs != hipStreamCaptureStatusNone)
+            return set_err(c, MLP_ERR_ARG, "Adam/LaProp steps cannot be captured into a graph (the step count "
+                                           "is a launch argument)");
+        ++c->opt_t;
+    }
     const hipError_t e = enqueue(c, Mode::Train, x, labels, lr, nullptr, loss_dev);
     if (e != hipSuccess) return hip_fail(c, e, "mlp_train_step");
     return MLP_OK;
@@ -988,6 +1046,78 @@ mlp_status mlp_grads(mlp_ctx* c, const float* x, const float* labels, float* con
                            c->stream);
     if (e != hipSuccess) return hip_fail(c, e, "mlp_grads");
     if (loss) return read_loss(c, loss);
+    return MLP_OK;
+}
+
+// Device bytes of an adaptive rule's state: first and second moments and a
+// gradient buffer, float32 per weight, each array 256-byte aligned.
+static size_t optimizer_bytes(const mlp_ctx* c) {
+    size_t b = 0;
+    for (int l = 0; l < c->L; ++l) b += 3 * align_up((size_t)c->dims[l] * c->dims[l + 1] * 4, kAlign);
+    return b;
+}
+
+size_t mlp_optimizer_bytes(const mlp_config* cfg, int32_t opt) {
+    mlp_ctx tmp;
+    if (validate(cfg, &tmp) != MLP_OK) return 0;
+    if (opt == MLP_OPT_SGD) return 0;
+    if (opt != MLP_OPT_ADAM && opt != MLP_OPT_LAPROP) return 0;
+    return optimizer_bytes(&tmp);
+}
+
+mlp_status mlp_set_optimizer(mlp_ctx* c, int32_t opt, float beta1, float beta2, float eps, void* state,
+                             size_t bytes) {
+    if (!c) return MLP_ERR_ARG;
+    c->err.clear();
+    if (opt != MLP_OPT_SGD && opt != MLP_OPT_ADAM && opt != MLP_OPT_LAPROP)
+        return set_err(c, MLP_ERR_ARG, "unknown update rule %d", opt);
+    if (c->poisoned) return set_err(c, MLP_ERR_STATE, "context poisoned by an earlier HIP failure");
+    if (opt != MLP_OPT_SGD) {
+        if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f))
+            return set_err(c, MLP_ERR_ARG, "beta1 and beta2 must lie in [0, 1)");
+        if (!(eps > 0.f) || !std::isfinite(eps)) return set_err(c, MLP_ERR_ARG, "eps must be finite and > 0");
+        const size_t need = optimizer_bytes(c);
+        if (!state || ((uintptr_t)state % kAlign) != 0 || bytes < need)
+            return set_err(c, MLP_ERR_WORKSPACE, "optimizer state %p of %zu bytes: need %zu bytes, %zu-byte aligned",
+                           state, bytes, need, kAlign);
+    }
+    float* m[kMaxLayers] = {};
+    float* v[kMaxLayers] = {};
+    float* g[kMaxLayers] = {};
+    if (opt != MLP_OPT_SGD) {
+        char* p = (char*)state;
+        for (int l = 0; l < c->L; ++l) {
+            const size_t a = align_up((size_t)c->dims[l] * c->dims[l + 1] * 4, kAlign);
+            m[l] = (float*)p;
+            v[l] = (float*)(p + a);
+            g[l] = (float*)(p + 2 * a);
+            p += 3 * a;
+        }
+        // zero both moments (one contiguous range per layer)
+        for (int l = 0; l < c->L; ++l) {
+            const size_t a = align_up((size_t)c->dims[l] * c->dims[l + 1] * 4, kAlign);
+            const hipError_t e = launch_zero(m[l], 2 * a / 4, c->stream);
+            if (e != hipSuccess) return hip_fail(c, e, "zeroing the moments");
+        }
+    }
+    c->opt = opt;
+    c->opt_b1 = beta1;
+    c->opt_b2 = beta2;
+    c->opt_eps = eps;
+    c->opt_t = 0;
+    for (int l = 0; l < kMaxLayers; ++l) {
+        c->opt_m[l] = m[l];
+        c->opt_v[l] = v[l];
+        c->opt_g[l] = g[l];
+    }
+    // the launch sequence of a step changed: new slot names, fresh counts
+    collect_profile(c);
+    for (const Pending& pe : c->pending) {
+        hipEventDestroy(pe.beg);
+        hipEventDestroy(pe.end);
+    }
+    c->pending.clear();
+    build_slots(c);
     return MLP_OK;
 }
 

@@ -454,3 +454,134 @@ def test_graph_replay_matches_eager(torch_dev, name):
         torch.cuda.synchronize()
     eager.close()
     graphed.close()
+
+
+# ------------------------------------------------------------ Adam / LaProp --
+
+ADAPTIVE_CASES = [
+    # dims, B, precision, integer operands (exact first-step gradients)
+    ((200, 300, 36), 64, "f32", True),        # tiled GEMMs with split-K
+    ((784, 128, 10), 1024, "f32", False),     # fused output layer: head in the forward, tail in dW
+    ((64, 32, 8), 8, "f32", True),            # skinny kernels with the fused output layer
+    ((256, 520, 64), 8, "f32", False),        # skinny kernels, ragged columns
+    ((33, 70, 17, 10), 37, "f32", False),     # three layers, widths not multiples of 4
+    ((120, 136, 24), 256, "bf16", True),      # bf16 operands: the update refreshes the bf16 copy
+    ((1024, 2048, 1000), 2048, "bf16", False),  # large bf16 tiles, split-K logits into the loss
+]
+
+
+@pytest.mark.parametrize("rule", ["adam", "laprop"])
+@pytest.mark.parametrize("dims,B,precision,exact", ADAPTIVE_CASES)
+def test_adaptive_update_parity(torch_dev, rule, dims, B, precision, exact):
+    """Three Adam / LaProp steps against the oracle's rule applied to the
+    oracle's own gradients.  Before each step the GPU gradients (same
+    kernels, no update) pass the gradient gate; the weights after each step
+    must lie within the bound derived from that gate and the update rule."""
+    torch, dev = torch_dev
+    _announce(f"{rule} dims={dims} B={B} {precision}")
+    # small enough that three steps keep the loss away from 0 (the loss gate
+    # is relative, and a near-zero loss is a difference of near-equal terms)
+    lr, b1, b2, eps = 1e-3, 0.9, 0.999, 1e-8
+    if exact:
+        x, t, Ws = P.integer_problem(dims, B, seed=sum(dims), bf16=precision == "bf16")
+    else:
+        Ws = synth.make_weights(dims, "glorot", seed=sum(dims) + B)
+        x, t, _ = synth.make_batch(B, dims[0], dims[-1], "normal", seed=B, step=1)
+    net = make_net(dims, B, precision, Ws, dev)
+    net.set_optimizer(rule, b1, b2, eps)
+    xd, td = P.to_dev([x, t], dev)
+    W_ref = [np.asarray(w, np.float64) for w in Ws]
+    m = [np.zeros_like(w) for w in W_ref]
+    v = [np.zeros_like(w) for w in W_ref]
+    bound = P.AdaptiveBound(rule, lr, b1, b2, eps, [w.shape for w in W_ref])
+    for step in range(1, 4):
+        W_now = [w.cpu().numpy() for w in net.read_params()]
+        loss_g, dws, dl, masks = P.gpu_grads(net, xd, td)
+        ref = mlp_oracle.train_step(x, t, W_now, 0.0, kink_choice=masks,
+                                    kink_beta=mlp_oracle.kink_betas(dims, precision))
+        # after one step from an integer problem many pre-activations sit
+        # next to 0 (they were exactly 0): no cap on band adoptions there
+        P.check_masks(ref, B, dims, precision, f"{rule} step {step}", limit_band=not exact)
+        P.check_grads(loss_g, dws, dl, ref, precision, f"{rule} step {step}")
+        # the trajectory's own oracle gradients (at the oracle's weights)
+        rt = mlp_oracle.train_step(x, t, W_ref, 0.0, kink_choice=masks,
+                                   kink_beta=mlp_oracle.kink_betas(dims, precision))
+        dg = [P.GRAD_TOL[precision] * float(np.max(np.abs(g))) for g in rt["dW"]]
+        if exact and step == 1:
+            for a, r in zip(dws, rt["dW"]):
+                assert np.array_equal(np.asarray(a, np.float64), r)
+            dg = [0.0] * len(dg)
+        upd = mlp_oracle.OPTIMIZERS[rule](W_ref, rt["dW"], m, v, step, lr, b1, b2, eps)
+        loss = net.train_step(xd, td, lr)
+        assert loss == loss_g    # the loss of a step is the one of its gradients
+        W_gpu = [w.cpu().numpy() for w in net.read_params()]
+        bnd = bound.step(rt["dW"], dg, upd["W_new"], W_ref)
+        P.check_adaptive(W_gpu, upd["W_new"], bnd, f"{rule} {dims} step {step}")
+        W_ref, m, v = upd["W_new"], upd["m"], upd["v"]
+    net.close()
+
+
+def test_adaptive_then_sgd_matches_fresh_sgd(torch_dev):
+    """Switching back to SGD gives exactly the plain SGD step (same kernels
+    and order) from the same weights."""
+    torch, dev = torch_dev
+    dims, B = (96, 160, 130, 40), 128
+    Ws = synth.make_weights(dims, "glorot", seed=8)
+    x, t, _ = synth.make_batch(B, dims[0], dims[-1], "normal", seed=9)
+    xd, td = P.to_dev([x, t], dev)
+    a = make_net(dims, B, "f32", Ws, dev)
+    a.set_optimizer("adam")
+    a.train_step(xd, td, 0.01)
+    W_mid = [w.clone() for w in a.read_params()]
+    a.set_optimizer("sgd")
+    a.train_step(xd, td, 0.05)
+    b = make_net(dims, B, "f32", [w.cpu().numpy() for w in W_mid], dev)
+    b.train_step(xd, td, 0.05)
+    for u, w in zip(a.read_params(), b.read_params()):
+        assert torch.equal(u, w)
+    a.close()
+    b.close()
+
+
+def test_adaptive_profile_slots_and_errors(torch_dev):
+    """With Adam the dW launches store gradients and one update launch
+    follows; bad arguments are refused before anything is enqueued, and an
+    Adam step refuses stream capture."""
+    from mlp_gemm_softmax_amd import binding
+    torch, dev = torch_dev
+    dims, B = (16, 8, 40), 64
+    rng = np.random.default_rng(5)
+    Ws = [(rng.standard_normal((dims[l], dims[l + 1])) * 0.3).astype(np.float32) for l in range(2)]
+    net = make_net(dims, B, "f32", Ws, dev)
+    x = rng.standard_normal((B, dims[0])).astype(np.float32)
+    t = np.eye(dims[-1], dtype=np.float32)[rng.integers(0, dims[-1], B)]
+    xd, td = P.to_dev([x, t], dev)
+    L = binding.lib()
+    for args in [(binding.OPT_ADAM, 1.0, 0.999, 1e-8), (binding.OPT_ADAM, 0.9, -0.1, 1e-8),
+                 (binding.OPT_LAPROP, 0.9, 0.999, 0.0), (7, 0.9, 0.999, 1e-8)]:
+        st = L.mlp_set_optimizer(net._h, args[0], args[1], args[2], args[3], None, 0)
+        assert st == binding.MLP_ERR_ARG, args
+    st = L.mlp_set_optimizer(net._h, binding.OPT_ADAM, 0.9, 0.999, 1e-8, None, 0)
+    assert st == binding.MLP_ERR_WORKSPACE
+    net.set_optimizer("adam")
+    net.profile(True)
+    net.train_step(xd, td, 0.01)
+    names = [r["name"] for r in net.profile_read()]
+    assert names == ["mfma_f32_nn_relu_mask_l0", "mfma_f32_nn_store_l1", "softmax_xent",
+                     "mfma_f32_nt_mask_l1", "mfma_f32_tn_grad_l1", "mfma_f32_tn_grad_l0",
+                     "opt_update_adam"], names
+    net.profile(False)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        snet = binding.Mlp(dims, B, "f32", device=str(dev), stream=side)
+        snet.set_params(P.to_dev(Ws, dev))
+        snet.set_optimizer("adam")
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            with pytest.raises(binding.MlpError) as ei:
+                snet.train_step_async(xd, td, 0.01)
+        assert ei.value.status == binding.MLP_ERR_ARG
+    snet.close()
+    net.close()
