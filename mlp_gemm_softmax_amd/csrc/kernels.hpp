@@ -21,7 +21,17 @@ enum class Layout : int { NN = 0, NT = 1, TN = 2 };
 //   MaskMul  C = mask ? v : 0 (f32 or bf16)        (dX through the ReLU)
 //   Sgd      W = W - lr * v, optional bf16 copy    (dW + in-place update)
 //   Grad     C = v                                  (dW, no update)
-enum class Epi : int { Store = 0, ReluMask = 1, MaskMul = 2, Sgd = 3, Grad = 4 };
+//   Adapt    W, m, v <- Adam or LaProp step with g = v (skinny-batch kernels)
+enum class Epi : int { Store = 0, ReluMask = 1, MaskMul = 2, Sgd = 3, Grad = 4, Adapt = 5 };
+
+// Scalars of an adaptive update step (Adam or LaProp, see optim_rule.hpp).
+constexpr int kOptAdam = 1;
+constexpr int kOptLaProp = 2;
+struct OptScalars {
+    int rule;                              // kOptAdam or kOptLaProp
+    float lr, b1, b2, om1, om2, eps;       // om = 1 - beta
+    float inv_c1, inv_c2;                  // 1 / (1 - beta^t)
+};
 
 struct GemmParams {
     const void* A;       // float or bf16, per the kernel's precision
@@ -90,7 +100,10 @@ struct SkinnyParams {
     float* partials;
     unsigned* tickets;
     const float* act;  // NT with fused update: a [MB][K] of the layer's input
-    float* wout;       // NT with fused update: W (Sgd, in place) or dW (Grad)
+    float* wout;       // NT with fused update: W (Sgd/Adapt, in place) or dW (Grad)
+    float* m;          // Adapt: first and second moments, laid out as W
+    float* v;
+    OptScalars opt;    // Adapt: the step's scalars
 };
 struct SkinnyLaunch {
     Layout layout;
@@ -168,8 +181,6 @@ hipError_t launch_gemm_small_tail(const GemmLaunch& L, const GemmParams& p, int 
 hipError_t launch_cast_bf16(const float* src, bf16_t* dst, size_t n, hipStream_t s);
 
 // ---- adaptive update rules (optim.hip) -------------------------------------
-constexpr int kOptAdam = 1;
-constexpr int kOptLaProp = 2;
 constexpr int kMaxOptTensors = 16;
 struct OptTensor {
     float* W;          // f32 master [n]
@@ -183,9 +194,7 @@ struct OptParams {
     OptTensor t[kMaxOptTensors];
     int first_block[kMaxOptTensors + 1];   // filled by launch_opt_update
     int count;
-    int rule;                              // kOptAdam or kOptLaProp
-    float lr, b1, b2, om1, om2, eps;       // om = 1 - beta
-    float inv_c1, inv_c2;                  // 1 / (1 - beta^t)
+    OptScalars o;
 };
 // Every tensor's arrays are 16-byte aligned.
 hipError_t launch_opt_update(OptParams p, hipStream_t s);

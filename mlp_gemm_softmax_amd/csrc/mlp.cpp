@@ -263,6 +263,27 @@ bool head_fused(const mlp_ctx* c) {
            head_lds_bytes(c->dims[c->L - 1], c->dims[c->L], 32) <= 64 * 1024;
 }
 
+// The skinny-batch kernels apply an adaptive rule while W streams through
+// them; other layers store their gradients for the update launch.
+bool adapt_fused(const mlp_ctx* c, int l) {
+    if (c->opt == MLP_OPT_SGD || !c->skinny) return false;
+    return !(c->head && l == c->L - 1);   // the output layer's dW is the tail's
+}
+
+OptScalars opt_scalars(const mlp_ctx* c, float lr) {
+    OptScalars o{};
+    o.rule = c->opt == MLP_OPT_ADAM ? kOptAdam : kOptLaProp;
+    o.lr = lr;
+    o.b1 = c->opt_b1;
+    o.b2 = c->opt_b2;
+    o.om1 = (float)(1.0 - (double)c->opt_b1);
+    o.om2 = (float)(1.0 - (double)c->opt_b2);
+    o.eps = c->opt_eps;
+    o.inv_c1 = (float)(1.0 / (1.0 - std::pow((double)c->opt_b1, (double)c->opt_t)));
+    o.inv_c2 = (float)(1.0 / (1.0 - std::pow((double)c->opt_b2, (double)c->opt_t)));
+    return o;
+}
+
 // Whether the softmax-CE launch also adds the split-K partials of the logits
 // product (large-tile bf16 forward split over K): the logits are then written
 // once, by the loss kernel, and not read back.
@@ -288,6 +309,7 @@ void build_slots(mlp_ctx* c) {
     // with an adaptive rule the dW launches store gradients and one more
     // launch applies the update
     const std::string upd = c->opt == MLP_OPT_SGD ? "sgd" : "grad";
+    const std::string rule = c->opt == MLP_OPT_ADAM ? "adam" : "laprop";
     if (c->bf16) add("cast_x_bf16", 0, (double)B * c->dims[0] * 6);
     const int C = c->dims[L];
     const int Lf = c->head ? L - 1 : L;   // layers whose forward is a plain GEMM
@@ -330,26 +352,32 @@ void build_slots(mlp_ctx* c) {
         const double din = c->dims[l], dout = c->dims[l + 1];
         if (l > 0 && c->skinny) {
             // dX and dW + SGD in one pass over W: W read and written once
-            add(std::string(kind) + "_nt_mask_" + upd + "_l" + std::to_string(l), 4.0 * B * din * dout,
-                8.0 * din * dout + 4.0 * B * dout + 4.0 * B * din + B * din * 5.0);
+            // W read and written once; an adaptive rule also streams m and v
+            const double wb = adapt_fused(c, l) ? 24.0 : 8.0;
+            add(std::string(kind) + "_nt_mask_" + (adapt_fused(c, l) ? rule : upd) + "_l" + std::to_string(l),
+                4.0 * B * din * dout, wb * din * dout + 4.0 * B * dout + 4.0 * B * din + B * din * 5.0);
             continue;
         }
         if (l > 0)
             add(std::string(kind) + "_nt_mask_l" + std::to_string(l), 2.0 * B * din * dout,
                 B * dout * e + din * dout * e + B * din * (1 + e));
-        const double wb = c->opt == MLP_OPT_SGD ? 8 + (c->bf16 ? 2 : 0) : 4;   // W in+out (+copy), or dW out
+        // W in+out (+copy); dW out; or W, m, v in+out (rule applied here)
+        const double wb = c->opt == MLP_OPT_SGD ? 8 + (c->bf16 ? 2 : 0) : (adapt_fused(c, l) ? 24 : 4);
+        const std::string what = adapt_fused(c, l) ? rule : upd;
         const double f = 2.0 * B * din * dout, b = B * din * e + B * dout * e + din * dout * wb;
         if (l == 0 && c->head && tail_fused(c))
-            add(std::string(kind) + "_tn_" + upd + "_l0+" + tail_name, f + tail_flops, b + tail_bytes);
+            add(std::string(kind) + "_tn_" + what + "_l0+" + tail_name, f + tail_flops, b + tail_bytes);
         else
-            add(std::string(kind) + "_tn_" + upd + "_l" + std::to_string(l), f, b);
+            add(std::string(kind) + "_tn_" + what + "_l" + std::to_string(l), f, b);
     }
     if (c->head && !tail_fused(c)) add(tail_name, tail_flops, tail_bytes);
     if (c->opt != MLP_OPT_SGD) {
-        // per weight: g, m, v, W in; m, v, W (+ bf16 copy) out
+        // per weight of the layers not updated in their dW launch: g, m, v, W
+        // in; m, v, W (+ bf16 copy) out
         double n = 0;
-        for (int l = 0; l < L; ++l) n += (double)c->dims[l] * c->dims[l + 1];
-        add(c->opt == MLP_OPT_ADAM ? "opt_update_adam" : "opt_update_laprop", 0, n * (28 + (c->bf16 ? 2 : 0)));
+        for (int l = 0; l < L; ++l)
+            if (!adapt_fused(c, l)) n += (double)c->dims[l] * c->dims[l + 1];
+        if (n > 0) add("opt_update_" + rule, 0, n * (28 + (c->bf16 ? 2 : 0)));
     }
 }
 
@@ -425,7 +453,8 @@ hipError_t run_gemm(mlp_ctx* c, const GemmPlan& g, Layout lay, Epi epi, const vo
 
 
 hipError_t run_skinny(mlp_ctx* c, const SkinnyPlan& s, Layout lay, Epi epi, const float* A,
-                      const float* Bm, int K, int N, float* C, uint8_t* mask, float lr) {
+                      const float* Bm, int K, int N, float* C, uint8_t* mask, float lr,
+                      float* m = nullptr, float* v = nullptr, const OptScalars* opt = nullptr) {
     SkinnyLaunch L;
     L.layout = lay;
     L.epi = epi;
@@ -445,8 +474,14 @@ hipError_t run_skinny(mlp_ctx* c, const SkinnyPlan& s, Layout lay, Epi epi, cons
     p.kchunk = s.kchunk;
     p.partials = c->partials;
     p.tickets = c->tickets;
+    p.act = nullptr;
+    p.wout = nullptr;
+    p.m = m;
+    p.v = v;
+    p.opt = opt ? *opt : OptScalars{};
     return launch_skinny(L, p, c->stream);
 }
+
 
 enum class Mode { Forward, Train, Grads };
 
@@ -563,6 +598,7 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
     const bool adaptive = mode == Mode::Train && c->opt != MLP_OPT_SGD;
     const bool grads = mode == Mode::Grads || adaptive;
     float* const* dwo = adaptive ? c->opt_g : dw_out;
+    const OptScalars osc = adaptive ? opt_scalars(c, lr) : OptScalars{};
     TailParams tp{};
     if (use_head) {
         tp.A = (const float*)c->act[L - 1];
@@ -595,10 +631,11 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
             void* out = c->dz[pp];
             pp ^= 1;
             r.run(slot++, [&] {
+                const bool fu = adaptive && adapt_fused(c, l);
                 SkinnyLaunch sl;
                 sl.layout = Layout::NT;
-                sl.epi = grads ? Epi::Grad : Epi::Sgd;
-                sl.grid = c->sdx[l].grid;
+                sl.epi = fu ? Epi::Adapt : (grads ? Epi::Grad : Epi::Sgd);
+                sl.grid = fu ? (din + 15) / 16 : c->sdx[l].grid;
                 sl.waves = 8;
                 sl.fused_update = true;
                 SkinnyParams sp{};
@@ -611,7 +648,10 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
                 sp.mask = c->mask[l];
                 sp.lr = lr;
                 sp.act = (const float*)c->act[l];
-                sp.wout = grads ? dwo[l] : c->W[l];
+                sp.wout = (grads && !fu) ? dwo[l] : c->W[l];
+                sp.m = fu ? c->opt_m[l] : nullptr;
+                sp.v = fu ? c->opt_v[l] : nullptr;
+                sp.opt = osc;
                 return launch_skinny(sl, sp, c->stream);
             });
             G = out;
@@ -631,7 +671,11 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
         float* Wdst = grads ? dwo[l] : c->W[l];
         bf16_t* Wbdst = (!grads && c->bf16) ? c->Wb[l] : nullptr;
         if (c->skinny) {
+            const bool fu = adaptive && adapt_fused(c, l);
             r.run(slot++, [&] {
+                if (fu)
+                    return run_skinny(c, c->sdw[l], Layout::TN, Epi::Adapt, (const float*)a_in, (const float*)G,
+                                      din, dout, c->W[l], nullptr, lr, c->opt_m[l], c->opt_v[l], &osc);
                 return run_skinny(c, c->sdw[l], Layout::TN, grads ? Epi::Grad : Epi::Sgd,
                                   (const float*)a_in, (const float*)G, din, dout, Wdst, nullptr, lr);
             });
@@ -644,21 +688,15 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
         G = Gnext;
     }
     if (use_head && !fuse_tail) r.run(slot++, [&] { return launch_tail(tp, c->stream); });
-    if (adaptive) {
+    int unfused = 0;
+    for (int l = 0; l < L; ++l) unfused += adaptive && !adapt_fused(c, l);
+    if (unfused > 0) {
         r.run(slot++, [&] {
             OptParams op{};
-            op.count = L;
-            op.rule = c->opt == MLP_OPT_ADAM ? kOptAdam : kOptLaProp;
-            op.lr = lr;
-            op.b1 = c->opt_b1;
-            op.b2 = c->opt_b2;
-            op.om1 = (float)(1.0 - (double)c->opt_b1);
-            op.om2 = (float)(1.0 - (double)c->opt_b2);
-            op.eps = c->opt_eps;
-            op.inv_c1 = (float)(1.0 / (1.0 - std::pow((double)c->opt_b1, (double)c->opt_t)));
-            op.inv_c2 = (float)(1.0 / (1.0 - std::pow((double)c->opt_b2, (double)c->opt_t)));
+            op.o = osc;
             for (int l = 0; l < L; ++l) {
-                OptTensor& t = op.t[l];
+                if (adapt_fused(c, l)) continue;
+                OptTensor& t = op.t[op.count++];
                 t.W = c->W[l];
                 t.Wb = c->bf16 ? c->Wb[l] : nullptr;
                 t.g = c->opt_g[l];

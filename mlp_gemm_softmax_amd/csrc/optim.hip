@@ -16,24 +16,13 @@
 // rewritten from the new master.  The update is bound by HBM traffic: per
 // weight it reads g, m, v, W and writes m, v, W (+ the bf16 copy).
 #include "kernels.hpp"
+#include "optim_rule.hpp"
 
 namespace mlp {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxBlocksPerTensor = 2048;
-
-__device__ __forceinline__ void update1(const OptParams& p, float& w, float g, float& m, float& v) {
-    if (p.rule == kOptAdam) {
-        m = p.b1 * m + p.om1 * g;
-        v = p.b2 * v + p.om2 * (g * g);
-        w = w - p.lr * (m * p.inv_c1) / (sqrtf(v * p.inv_c2) + p.eps);
-    } else {
-        v = p.b2 * v + p.om2 * (g * g);
-        m = p.b1 * m + p.om1 * (g / (sqrtf(v * p.inv_c2) + p.eps));
-        w = w - p.lr * (m * p.inv_c1);
-    }
-}
 
 __global__ __launch_bounds__(kThreads) void opt_update_kernel(OptParams p) {
     // tensor of this block (uniform scan over at most kMaxOptTensors entries)
@@ -48,14 +37,7 @@ __global__ __launch_bounds__(kThreads) void opt_update_kernel(OptParams p) {
         const float4v g = *reinterpret_cast<const float4v*>(t.g + 4 * i);
         float4v m = *reinterpret_cast<const float4v*>(t.m + 4 * i);
         float4v v = *reinterpret_cast<const float4v*>(t.v + 4 * i);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float we = w[e], me = m[e], ve = v[e];
-            update1(p, we, g[e], me, ve);
-            w[e] = we;
-            m[e] = me;
-            v[e] = ve;
-        }
+        opt_apply4(p.o, w, g, m, v);
         *reinterpret_cast<float4v*>(t.W + 4 * i) = w;
         *reinterpret_cast<float4v*>(t.m + 4 * i) = m;
         *reinterpret_cast<float4v*>(t.v + 4 * i) = v;
@@ -70,7 +52,7 @@ __global__ __launch_bounds__(kThreads) void opt_update_kernel(OptParams p) {
     if (blockIdx.x == p.first_block[ti] && threadIdx.x < (t.n & 3)) {
         const int64_t j = 4 * n4 + threadIdx.x;
         float w = t.W[j], m = t.m[j], v = t.v[j];
-        update1(p, w, t.g[j], m, v);
+        opt_apply(p.o, w, t.g[j], m, v);
         t.W[j] = w;
         t.m[j] = m;
         t.v[j] = v;
@@ -87,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void zero_kernel(float4v* __restrict__ p,
 }  // namespace
 
 hipError_t launch_opt_update(OptParams p, hipStream_t s) {
-    if (p.count < 1 || p.count > kMaxOptTensors || (p.rule != kOptAdam && p.rule != kOptLaProp))
+    if (p.count < 1 || p.count > kMaxOptTensors || (p.o.rule != kOptAdam && p.o.rule != kOptLaProp))
         return hipErrorInvalidValue;
     int blocks = 0;
     for (int i = 0; i < p.count; ++i) {

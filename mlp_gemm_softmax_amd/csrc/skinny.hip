@@ -17,6 +17,7 @@
 // the last workgroup (integer ticket) adds in split order.
 // Every width and K must be a multiple of 4 (float4 rows).
 #include "kernels.hpp"
+#include "optim_rule.hpp"
 
 namespace mlp {
 namespace {
@@ -206,9 +207,12 @@ __global__ __launch_bounds__(NW * kWave) void skinny_ntu(SkinnyParams p) {
     const int nbeg = wave * nq;
     const int nend = min(p.N, nbeg + nq);
 
+    constexpr bool AD = EPI == Epi::Adapt;
     float4v acc[RG];
     const float* __restrict__ Wr[RG];
     float* __restrict__ Or[RG];
+    float* __restrict__ Mr[RG];   // Adapt: moments of the same rows
+    float* __restrict__ Vr[RG];
     bool rok[RG];
     float av[RG][S];   // a[4s + g][k0 + 16r + i]
 #pragma unroll
@@ -218,6 +222,8 @@ __global__ __launch_bounds__(NW * kWave) void skinny_ntu(SkinnyParams p) {
         rok[r] = krow < p.K;
         Wr[r] = p.A + (int64_t)krow * p.N;
         Or[r] = p.wout + (int64_t)krow * p.N;
+        Mr[r] = AD ? p.m + (int64_t)krow * p.N : nullptr;
+        Vr[r] = AD ? p.v + (int64_t)krow * p.N : nullptr;
 #pragma unroll
         for (int t = 0; t < S; ++t) {
             const int b = 4 * t + g;
@@ -228,8 +234,9 @@ __global__ __launch_bounds__(NW * kWave) void skinny_ntu(SkinnyParams p) {
     const float4v zero = {0.f, 0.f, 0.f, 0.f};
     // gv: G[i][cols] for the dX MFMA; gu: G[4s + g][n + 16h + i] for the update
     float4v gv[2], w[RG][2], gvn[2], wn[RG][2];
+    float4v mo[RG][2], vo[RG][2], mon[RG][2], von[RG][2];   // Adapt: moments
     float gu[2][S], gun[2][S];
-    auto fetch = [&](int n, float4v* gd, float4v (*wd)[2], float (*ud)[S]) {
+    auto fetch = [&](int n, float4v* gd, float4v (*wd)[2], float (*ud)[S], float4v (*md)[2], float4v (*vd)[2]) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int c = n + 16 * h + 4 * g;
@@ -241,6 +248,10 @@ __global__ __launch_bounds__(NW * kWave) void skinny_ntu(SkinnyParams p) {
                 const bool ok = cok && rok[r];
                 const float4v x = ld4(ok ? Wr[r] + c : p.A);
                 wd[r][h] = ok ? x : zero;
+                if constexpr (AD) {
+                    md[r][h] = ld4(ok ? Mr[r] + c : p.m);
+                    vd[r][h] = ld4(ok ? Vr[r] + c : p.v);
+                }
             }
             const int cu = n + 16 * h + i;
 #pragma unroll
@@ -252,17 +263,23 @@ __global__ __launch_bounds__(NW * kWave) void skinny_ntu(SkinnyParams p) {
             }
         }
     };
-    if (nbeg < nend) fetch(nbeg, gvn, wn, gun);
+    if (nbeg < nend) fetch(nbeg, gvn, wn, gun, mon, von);
     for (int n = nbeg; n < nend; n += 32) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             gv[h] = gvn[h];
 #pragma unroll
-            for (int r = 0; r < RG; ++r) w[r][h] = wn[r][h];
+            for (int r = 0; r < RG; ++r) {
+                w[r][h] = wn[r][h];
+                if constexpr (AD) {
+                    mo[r][h] = mon[r][h];
+                    vo[r][h] = von[r][h];
+                }
+            }
 #pragma unroll
             for (int t = 0; t < S; ++t) gu[h][t] = gun[h][t];
         }
-        if (n + 32 < nend) fetch(n + 32, gvn, wn, gun);
+        if (n + 32 < nend) fetch(n + 32, gvn, wn, gun, mon, von);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int c = n + 16 * h + 4 * g;
@@ -276,8 +293,17 @@ __global__ __launch_bounds__(NW * kWave) void skinny_ntu(SkinnyParams p) {
                 for (int t = 0; t < S; ++t) d = __builtin_amdgcn_mfma_f32_16x16x4f32(gu[h][t], av[r][t], d, 0, 0, 0);
                 if (c < nend && rok[r]) {
                     float4v* dst = reinterpret_cast<float4v*>(Or[r] + c);
-                    if constexpr (EPI == Epi::Sgd) *dst = w[r][h] - p.lr * d;
-                    else *dst = d;
+                    if constexpr (EPI == Epi::Sgd) {
+                        *dst = w[r][h] - p.lr * d;
+                    } else if constexpr (AD) {
+                        float4v wv = w[r][h], mv = mo[r][h], vv = vo[r][h];
+                        opt_apply4(p.opt, wv, d, mv, vv);
+                        *dst = wv;
+                        *reinterpret_cast<float4v*>(Mr[r] + c) = mv;
+                        *reinterpret_cast<float4v*>(Vr[r] + c) = vv;
+                    } else {
+                        *dst = d;
+                    }
                 }
             }
         }
@@ -316,7 +342,8 @@ __global__ __launch_bounds__(NW * kWave) void skinny_ntu(SkinnyParams p) {
 // updated); the per-row a[b][k] come from LDS.
 template <int MB, int ROWS, Epi EPI>
 __global__ __launch_bounds__(256) void skinny_tn(SkinnyParams p) {
-    constexpr int CH = 8;
+    constexpr bool AD = EPI == Epi::Adapt;
+    constexpr int CH = AD ? 4 : 8;   // Adapt streams W, m and v: fewer rows in flight
     __shared__ float sa[ROWS][MB];
     const int ncb = (p.N + 4 * 256 - 1) / (4 * 256);
     const int cb = blockIdx.x % ncb, rb = blockIdx.x / ncb;
@@ -335,19 +362,28 @@ __global__ __launch_bounds__(256) void skinny_tn(SkinnyParams p) {
         if (b < p.MB) gv[b] = ld4(p.B + (int64_t)b * p.N + n);
     }
     const int rows = min(ROWS, p.K - k0);
-    float* base = p.C + (int64_t)k0 * p.N + n;
-    float4v w[2][CH];
+    const int64_t off0 = (int64_t)k0 * p.N + n;
+    float* base = p.C + off0;
+    float* mbase = AD ? p.m + off0 : nullptr;
+    float* vbase = AD ? p.v + off0 : nullptr;
+    float4v w[2][CH], mo[2][CH], vo[2][CH];
     auto load_chunk = [&](int buf, int c0) {
 #pragma unroll
         for (int r = 0; r < CH; ++r)
-            if (c0 + r < rows) w[buf][r] = __builtin_nontemporal_load(
-                reinterpret_cast<const float4v*>(base + (int64_t)(c0 + r) * p.N));
+            if (c0 + r < rows) {
+                const int64_t o = (int64_t)(c0 + r) * p.N;
+                w[buf][r] = __builtin_nontemporal_load(reinterpret_cast<const float4v*>(base + o));
+                if constexpr (AD) {
+                    mo[buf][r] = __builtin_nontemporal_load(reinterpret_cast<const float4v*>(mbase + o));
+                    vo[buf][r] = __builtin_nontemporal_load(reinterpret_cast<const float4v*>(vbase + o));
+                }
+            }
     };
-    if constexpr (EPI == Epi::Sgd) load_chunk(0, 0);
+    if constexpr (EPI == Epi::Sgd || AD) load_chunk(0, 0);
 #pragma unroll
     for (int c0 = 0, buf = 0; c0 < ROWS; c0 += CH, buf ^= 1) {
         if (c0 >= rows) break;
-        if constexpr (EPI == Epi::Sgd) {
+        if constexpr (EPI == Epi::Sgd || AD) {
             if (c0 + CH < rows) load_chunk(buf ^ 1, c0 + CH);
         }
 #pragma unroll
@@ -361,6 +397,13 @@ __global__ __launch_bounds__(256) void skinny_tn(SkinnyParams p) {
             if constexpr (EPI == Epi::Sgd) {
                 const float4v v = w[buf][r] - p.lr * d;
                 __builtin_nontemporal_store(v, reinterpret_cast<float4v*>(dst));
+            } else if constexpr (AD) {
+                float4v wv = w[buf][r], mv = mo[buf][r], vv = vo[buf][r];
+                opt_apply4(p.opt, wv, d, mv, vv);
+                const int64_t o = (int64_t)rr * p.N;
+                __builtin_nontemporal_store(wv, reinterpret_cast<float4v*>(dst));
+                __builtin_nontemporal_store(mv, reinterpret_cast<float4v*>(mbase + o));
+                __builtin_nontemporal_store(vv, reinterpret_cast<float4v*>(vbase + o));
             } else {
                 *reinterpret_cast<float4v*>(dst) = d;
             }
@@ -375,6 +418,8 @@ template <int MB>
 hipError_t go_tn(const SkinnyLaunch& L, const SkinnyParams& p, hipStream_t s) {
     if (L.epi == Epi::Sgd)
         hipLaunchKernelGGL((skinny_tn<MB, kTnRows, Epi::Sgd>), dim3(L.grid), dim3(256), 0, s, p);
+    else if (L.epi == Epi::Adapt)
+        hipLaunchKernelGGL((skinny_tn<MB, kTnRows, Epi::Adapt>), dim3(L.grid), dim3(256), 0, s, p);
     else
         hipLaunchKernelGGL((skinny_tn<MB, kTnRows, Epi::Grad>), dim3(L.grid), dim3(256), 0, s, p);
     return hipGetLastError();
@@ -408,6 +453,12 @@ hipError_t launch_skinny(const SkinnyLaunch& L, const SkinnyParams& p, hipStream
                 if (p.MB <= 4) hipLaunchKernelGGL((skinny_ntu<8, 2, 1, Epi::Sgd>), dim3(L.grid), dim3(8 * 64), 0, s, p);
                 else if (p.MB <= 8) hipLaunchKernelGGL((skinny_ntu<8, 2, 2, Epi::Sgd>), dim3(L.grid), dim3(8 * 64), 0, s, p);
                 else hipLaunchKernelGGL((skinny_ntu<8, 2, 4, Epi::Sgd>), dim3(L.grid), dim3(8 * 64), 0, s, p);
+            } else if (L.epi == Epi::Adapt) {
+                // 16 rows per workgroup: W, m and v in flight need the registers
+                if (L.grid != (p.K + 15) / 16) return hipErrorInvalidValue;
+                if (p.MB <= 4) hipLaunchKernelGGL((skinny_ntu<8, 1, 1, Epi::Adapt>), dim3(L.grid), dim3(8 * 64), 0, s, p);
+                else if (p.MB <= 8) hipLaunchKernelGGL((skinny_ntu<8, 1, 2, Epi::Adapt>), dim3(L.grid), dim3(8 * 64), 0, s, p);
+                else hipLaunchKernelGGL((skinny_ntu<8, 1, 4, Epi::Adapt>), dim3(L.grid), dim3(8 * 64), 0, s, p);
             } else {
                 if (p.MB <= 4) hipLaunchKernelGGL((skinny_ntu<8, 2, 1, Epi::Grad>), dim3(L.grid), dim3(8 * 64), 0, s, p);
                 else if (p.MB <= 8) hipLaunchKernelGGL((skinny_ntu<8, 2, 2, Epi::Grad>), dim3(L.grid), dim3(8 * 64), 0, s, p);
