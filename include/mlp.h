@@ -7,7 +7,8 @@
  *     logits = matmul(h, wL)
  *     loss   = cross_entropy_loss(logits, labels)
  * with the backward pass the framework's autodiff derives for it and a plain
- * SGD update (README "Contents": SGD sessions).  A step is a fixed sequence
+ * SGD update (README "Contents": SGD sessions), or Adam / LaProp with moments
+ * kept only when requested (mlp_set_optimizer).  A step is a fixed sequence
  * of hand-written HIP kernels: MFMA GEMMs with fused ReLU/mask, mask-multiply
  * and SGD epilogues, and one row-wise softmax cross-entropy kernel.  For
  * narrow outputs (float32, at most 32 classes) the last layer's products,

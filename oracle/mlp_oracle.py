@@ -35,7 +35,8 @@ notes): no bias; dense labels with any non-negative rows (s_b = 1 for the
 one-hot rows the workloads use, which gives (softmax - onehot)/B); mean over
 the batch; the row max is subtracted before exponentiating; ReLU'(0) = 0;
 SGD without momentum or decay; the loss returned is the one at the
-pre-update weights.
+pre-update weights.  Adam and LaProp, which the README names without
+defining, follow their published algorithms (see ``adam`` and ``laprop``).
 
 Every input is upcast to float64 first; nothing here rounds to float32 or
 bfloat16, so the same oracle serves both contracts.
