@@ -184,6 +184,51 @@ size_t mlp_optimizer_bytes(const mlp_config* cfg, int32_t opt);
 mlp_status mlp_set_optimizer(mlp_ctx* ctx, int32_t opt, float beta1, float beta2, float eps,
                              void* state, size_t bytes);
 
+/* Checkpoints (README "Contents": checkpoints hold logical tensors without
+ * device padding, and a restore is preflighted before it mutates anything;
+ * the train-to-deploy example reloads one into a fresh inference session).
+ * A checkpoint is host memory: a 136-byte header (magic "MLPCKPT1", version
+ * 1, layer count, precision of the writer, update rule, widths, beta1, beta2,
+ * eps, step count, payload size, FNV-1a-64 checksum of the payload) and the
+ * payload: every W_l as float32 [dims[l], dims[l+1]] row-major, then, when
+ * the rule's state is included, every m_l and every v_l in the same shapes.
+ * Little-endian; the header's fields are, in order and without padding:
+ * char magic[8], uint32 version, n_layers, precision, optimizer, int32
+ * dims[17] (n_layers+1 used, the rest 0), float beta1, beta2, eps, uint32
+ * reserved[2] (0), int64 step, uint64 payload_bytes, uint64 checksum. */
+
+/* Size of the checkpoint mlp_save_checkpoint writes; with_optimizer != 0
+ * includes the Adam/LaProp moments when the session uses such a rule.
+ * 0 for ctx == NULL. */
+size_t mlp_checkpoint_bytes(const mlp_ctx* ctx, int32_t with_optimizer);
+
+/* Write the checkpoint of the current weights (and moments) into host
+ * memory `dst` of at least mlp_checkpoint_bytes bytes.  Synchronises the
+ * context's stream first, so the state after every enqueued step is saved.
+ * MLP_ERR_STATE if the weights were never set or the context is poisoned. */
+mlp_status mlp_save_checkpoint(mlp_ctx* ctx, void* dst, size_t bytes, int32_t with_optimizer);
+
+/* Check a checkpoint in host memory without a context (no device work):
+ * magic, version, ranges, payload size and checksum.  On success writes the
+ * layer count, the n_layers+1 widths (dims: room for 17), the update rule
+ * whose state it carries (MLP_OPT_SGD: none) and its step count, each when
+ * the pointer is non-NULL.  Errors: MLP_ERR_ARG, message in
+ * mlp_last_error(NULL). */
+mlp_status mlp_checkpoint_info(const void* src, size_t bytes, int32_t* n_layers, int32_t* dims,
+                               int32_t* optimizer, int64_t* step);
+
+/* Restore weights (and moments) from a checkpoint in host memory.  Preflight
+ * before anything is written: the checks of mlp_checkpoint_info, the same
+ * layer count and widths as the session (MLP_ERR_SHAPE otherwise), and, for
+ * a session using Adam/LaProp, the same rule, betas and eps with its state
+ * in the checkpoint (MLP_ERR_ARG otherwise); on any of these errors nothing
+ * changes.  A session on SGD restores the weights only (a forward-only or
+ * SGD session may load a checkpoint written with moments).  The bf16
+ * operand copies are rebuilt; the step count of the moments is restored.
+ * The precision of the writer does not matter (masters are float32).
+ * Synchronises the context's stream before returning. */
+mlp_status mlp_load_checkpoint(mlp_ctx* ctx, const void* src, size_t bytes);
+
 /* Copy an intermediate of the last step or forward to device memory `dst`
  * (see mlp_state_kind for shapes; `layer` is 1..n_layers-1 for ACT/MASK). */
 mlp_status mlp_read_state(mlp_ctx* ctx, int32_t which, int32_t layer, void* dst);

@@ -40,6 +40,12 @@ SIGNATURES = {
                              _c.c_void_p, _c.POINTER(_c.c_float)]),
     "mlp_read_state": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_int32, _c.c_void_p]),
     "mlp_optimizer_bytes": (_c.c_size_t, [_c.c_void_p, _c.c_int32]),
+    "mlp_checkpoint_bytes": (_c.c_size_t, [_c.c_void_p, _c.c_int32]),
+    "mlp_save_checkpoint": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_int32]),
+    "mlp_checkpoint_info": (_c.c_int, [_c.c_void_p, _c.c_size_t, _c.POINTER(_c.c_int32),
+                                       _c.POINTER(_c.c_int32), _c.POINTER(_c.c_int32),
+                                       _c.POINTER(_c.c_int64)]),
+    "mlp_load_checkpoint": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t]),
     "mlp_set_optimizer": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_float, _c.c_float, _c.c_float,
                                      _c.c_void_p, _c.c_size_t]),
     "mlp_profile_enable": (_c.c_int, [_c.c_void_p, _c.c_int32]),
@@ -51,6 +57,19 @@ SIGNATURES = {
     "mlp_status_string": (_c.c_char_p, [_c.c_int]),
     "mlp_last_error": (_c.c_char_p, [_c.c_void_p]),
 }
+
+
+def checkpoint_info(buf: bytes) -> dict:
+    """Header of a checkpoint held in host memory (no GPU work)."""
+    n = ctypes.c_int32()
+    dims = (ctypes.c_int32 * 17)()
+    opt = ctypes.c_int32()
+    step = ctypes.c_int64()
+    cbuf = ctypes.create_string_buffer(bytes(buf), len(buf))
+    st = lib().mlp_checkpoint_info(cbuf, len(buf), ctypes.byref(n), dims, ctypes.byref(opt), ctypes.byref(step))
+    if st != MLP_OK:
+        raise MlpError(st, lib().mlp_last_error(None).decode())
+    return {"n_layers": n.value, "dims": list(dims[:n.value + 1]), "optimizer": opt.value, "step": step.value}
 
 
 class MlpConfig(ctypes.Structure):
@@ -180,6 +199,17 @@ class Mlp:
         ptr = ctypes.c_void_p(state.data_ptr()) if state is not None else None
         self._check(lib().mlp_set_optimizer(self._h, opt, float(beta1), float(beta2), float(eps), ptr, nbytes))
         self.opt_state = state
+
+    def save_checkpoint(self, with_optimizer: bool = True) -> bytes:
+        """Weights (and Adam/LaProp moments) as checkpoint bytes in host memory."""
+        n = int(lib().mlp_checkpoint_bytes(self._h, 1 if with_optimizer else 0))
+        buf = ctypes.create_string_buffer(n)
+        self._check(lib().mlp_save_checkpoint(self._h, buf, n, 1 if with_optimizer else 0))
+        return buf.raw
+
+    def load_checkpoint(self, data: bytes):
+        buf = ctypes.create_string_buffer(bytes(data), len(data))
+        self._check(lib().mlp_load_checkpoint(self._h, buf, len(data)))
 
     def read_params(self) -> List:
         out = []

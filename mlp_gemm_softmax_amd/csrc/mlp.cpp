@@ -1159,6 +1159,196 @@ mlp_status mlp_set_optimizer(mlp_ctx* c, int32_t opt, float beta1, float beta2, 
     return MLP_OK;
 }
 
+// ------------------------------------------------------------ checkpoints --
+// Layout (little-endian, host memory): a 136-byte header, then the payload:
+// every W_l as float32 [dims[l]][dims[l+1]] row-major without padding, then,
+// when the checkpoint carries an adaptive rule's state, every m_l and then
+// every v_l in the same shapes.  The header's checksum is FNV-1a (64-bit)
+// over the payload bytes.
+namespace {
+
+constexpr char kCkptMagic[8] = {'M', 'L', 'P', 'C', 'K', 'P', 'T', '1'};
+constexpr uint32_t kCkptVersion = 1;
+
+struct CkptHeader {
+    char magic[8];
+    uint32_t version;
+    uint32_t n_layers;
+    uint32_t precision;      // of the session that wrote it (informational)
+    uint32_t optimizer;      // MLP_OPT_*; 0 = no moments in the payload
+    int32_t dims[kMaxLayers + 1];
+    float beta1, beta2, eps;
+    uint32_t reserved[2];    // zero
+    int64_t step;            // steps taken with the moments
+    uint64_t payload_bytes;
+    uint64_t checksum;
+};
+static_assert(sizeof(CkptHeader) == 136, "checkpoint header layout: no implicit padding");
+
+uint64_t fnv1a(const unsigned char* p, size_t n) {
+    uint64_t h = 1469598103934665603ull;
+    for (size_t i = 0; i < n; ++i) {
+        h ^= p[i];
+        h *= 1099511628211ull;
+    }
+    return h;
+}
+
+size_t ckpt_payload(int L, const int32_t* dims, bool moments) {
+    size_t n = 0;
+    for (int l = 0; l < L; ++l) n += (size_t)dims[l] * dims[l + 1];
+    return n * 4 * (moments ? 3 : 1);
+}
+
+// Header and payload checks shared by mlp_checkpoint_info and the load
+// preflight; no device memory is touched.
+mlp_status ckpt_check(const void* src, size_t bytes, CkptHeader* h, std::string* why) {
+    char buf[160];
+    if (!src) {
+        *why = "checkpoint pointer is NULL";
+        return MLP_ERR_ARG;
+    }
+    if (bytes < sizeof(CkptHeader)) {
+        std::snprintf(buf, sizeof buf, "checkpoint of %zu bytes is shorter than its %zu-byte header", bytes,
+                      sizeof(CkptHeader));
+        *why = buf;
+        return MLP_ERR_ARG;
+    }
+    std::memcpy(h, src, sizeof(CkptHeader));
+    if (std::memcmp(h->magic, kCkptMagic, 8) != 0) {
+        *why = "not a checkpoint (magic)";
+        return MLP_ERR_ARG;
+    }
+    if (h->version != kCkptVersion) {
+        std::snprintf(buf, sizeof buf, "checkpoint version %u, this library reads %u", h->version, kCkptVersion);
+        *why = buf;
+        return MLP_ERR_ARG;
+    }
+    if (h->n_layers < 1 || h->n_layers > (uint32_t)kMaxLayers || h->optimizer > MLP_OPT_LAPROP) {
+        *why = "checkpoint header out of range (layers or update rule)";
+        return MLP_ERR_ARG;
+    }
+    for (uint32_t i = 0; i <= h->n_layers; ++i)
+        if (h->dims[i] < 1 || h->dims[i] > kMaxDim) {
+            *why = "checkpoint header out of range (dims)";
+            return MLP_ERR_ARG;
+        }
+    const size_t want = ckpt_payload((int)h->n_layers, h->dims, h->optimizer != MLP_OPT_SGD);
+    if (h->payload_bytes != want || bytes < sizeof(CkptHeader) + want) {
+        std::snprintf(buf, sizeof buf, "checkpoint payload: header says %llu bytes, shapes need %zu, buffer holds %zu",
+                      (unsigned long long)h->payload_bytes, want, bytes - sizeof(CkptHeader));
+        *why = buf;
+        return MLP_ERR_ARG;
+    }
+    if (fnv1a((const unsigned char*)src + sizeof(CkptHeader), want) != h->checksum) {
+        *why = "checkpoint checksum mismatch (payload damaged)";
+        return MLP_ERR_ARG;
+    }
+    return MLP_OK;
+}
+
+}  // namespace
+
+size_t mlp_checkpoint_bytes(const mlp_ctx* c, int32_t with_optimizer) {
+    if (!c) return 0;
+    const bool mom = with_optimizer && c->opt != MLP_OPT_SGD;
+    return sizeof(CkptHeader) + ckpt_payload(c->L, c->dims, mom);
+}
+
+mlp_status mlp_save_checkpoint(mlp_ctx* c, void* dst, size_t bytes, int32_t with_optimizer) {
+    if (!c) return MLP_ERR_ARG;
+    c->err.clear();
+    if (c->poisoned) return set_err(c, MLP_ERR_STATE, "context poisoned by an earlier HIP failure");
+    const unsigned all = (1u << c->L) - 1u;
+    if (c->params_set != all) return set_err(c, MLP_ERR_STATE, "weights not initialised: nothing to save");
+    const bool mom = with_optimizer && c->opt != MLP_OPT_SGD;
+    const size_t need = mlp_checkpoint_bytes(c, with_optimizer);
+    if (!dst || bytes < need) return set_err(c, MLP_ERR_ARG, "checkpoint buffer %p of %zu bytes: need %zu", dst, bytes, need);
+    CkptHeader h{};
+    std::memcpy(h.magic, kCkptMagic, 8);
+    h.version = kCkptVersion;
+    h.n_layers = (uint32_t)c->L;
+    h.precision = c->bf16 ? MLP_BF16 : MLP_F32;
+    h.optimizer = mom ? (uint32_t)c->opt : 0u;
+    for (int i = 0; i <= c->L; ++i) h.dims[i] = c->dims[i];
+    h.beta1 = mom ? c->opt_b1 : 0.f;
+    h.beta2 = mom ? c->opt_b2 : 0.f;
+    h.eps = mom ? c->opt_eps : 0.f;
+    h.step = mom ? c->opt_t : 0;
+    h.payload_bytes = ckpt_payload(c->L, c->dims, mom);
+    unsigned char* out = (unsigned char*)dst + sizeof(CkptHeader);
+    // pending work on the stream (the last step) must finish first
+    hipError_t e = hipStreamSynchronize(c->stream);
+    size_t off = 0;
+    for (int part = 0; part < (mom ? 3 : 1) && e == hipSuccess; ++part)
+        for (int l = 0; l < c->L && e == hipSuccess; ++l) {
+            const size_t n = (size_t)c->dims[l] * c->dims[l + 1] * 4;
+            const float* srcp = part == 0 ? c->W[l] : (part == 1 ? c->opt_m[l] : c->opt_v[l]);
+            e = hipMemcpy(out + off, srcp, n, hipMemcpyDeviceToHost);
+            off += n;
+        }
+    if (e != hipSuccess) return hip_fail(c, e, "mlp_save_checkpoint");
+    h.checksum = fnv1a(out, h.payload_bytes);
+    std::memcpy(dst, &h, sizeof h);
+    return MLP_OK;
+}
+
+mlp_status mlp_checkpoint_info(const void* src, size_t bytes, int32_t* n_layers, int32_t* dims,
+                               int32_t* optimizer, int64_t* step) {
+    CkptHeader h;
+    std::string why;
+    g_create_error.clear();
+    const mlp_status st = ckpt_check(src, bytes, &h, &why);
+    if (st != MLP_OK) return set_err(nullptr, st, "%s", why.c_str());
+    if (n_layers) *n_layers = (int32_t)h.n_layers;
+    if (dims)
+        for (uint32_t i = 0; i <= h.n_layers; ++i) dims[i] = h.dims[i];
+    if (optimizer) *optimizer = (int32_t)h.optimizer;
+    if (step) *step = h.step;
+    return MLP_OK;
+}
+
+mlp_status mlp_load_checkpoint(mlp_ctx* c, const void* src, size_t bytes) {
+    if (!c) return MLP_ERR_ARG;
+    c->err.clear();
+    // preflight: everything is checked before any device memory changes
+    CkptHeader h;
+    std::string why;
+    mlp_status st = ckpt_check(src, bytes, &h, &why);
+    if (st != MLP_OK) return set_err(c, st, "%s", why.c_str());
+    if ((int)h.n_layers != c->L) return set_err(c, MLP_ERR_SHAPE, "checkpoint has %u layers, the session %d", h.n_layers, c->L);
+    for (int i = 0; i <= c->L; ++i)
+        if (h.dims[i] != c->dims[i])
+            return set_err(c, MLP_ERR_SHAPE, "checkpoint width d%d = %d, the session has %d", i, h.dims[i], c->dims[i]);
+    if (c->opt != MLP_OPT_SGD) {
+        if (h.optimizer != (uint32_t)c->opt)
+            return set_err(c, MLP_ERR_ARG, "the session uses update rule %d but the checkpoint carries %s", c->opt,
+                           h.optimizer ? "another rule's state" : "no optimizer state");
+        if (h.beta1 != c->opt_b1 || h.beta2 != c->opt_b2 || h.eps != c->opt_eps)
+            return set_err(c, MLP_ERR_ARG, "checkpoint betas/eps differ from the session's");
+    }
+    const unsigned char* in = (const unsigned char*)src + sizeof(CkptHeader);
+    const bool mom = c->opt != MLP_OPT_SGD;   // moments restored only into a session using them
+    hipError_t e = hipSuccess;
+    size_t off = 0;
+    for (int part = 0; part < (h.optimizer != MLP_OPT_SGD ? 3 : 1) && e == hipSuccess; ++part)
+        for (int l = 0; l < c->L && e == hipSuccess; ++l) {
+            const size_t n = (size_t)c->dims[l] * c->dims[l + 1] * 4;
+            float* dstp = part == 0 ? c->W[l] : (part == 1 ? c->opt_m[l] : c->opt_v[l]);
+            if (part == 0 || mom) e = hipMemcpyAsync(dstp, in + off, n, hipMemcpyHostToDevice, c->stream);
+            off += n;
+        }
+    for (int l = 0; l < c->L && e == hipSuccess && c->bf16; ++l)
+        e = launch_cast_bf16(c->W[l], c->Wb[l], (size_t)c->dims[l] * c->dims[l + 1], c->stream);
+    // the source is caller memory that may be reused at once
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "mlp_load_checkpoint");
+    if (mom) c->opt_t = h.step;
+    c->params_set = (1u << c->L) - 1u;
+    c->poisoned = false;
+    return MLP_OK;
+}
+
 mlp_status mlp_read_state(mlp_ctx* c, int32_t which, int32_t layer, void* dst) {
     if (!c) return MLP_ERR_ARG;
     c->err.clear();

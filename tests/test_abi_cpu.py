@@ -117,3 +117,64 @@ def test_null_context_calls():
     assert lib.mlp_profile_enable(None, 1) == binding.MLP_ERR_ARG
     assert lib.mlp_profile_slots(None) == 0
     lib.mlp_destroy(None)
+
+
+# ------------------------------------------------------------- checkpoints --
+# A checkpoint written here by hand from the format include/mlp.h documents
+# (no GPU): the host-side check accepts it and rejects every damaged copy.
+
+import struct
+
+import numpy as np
+
+
+def _fnv1a(data: bytes) -> int:
+    h = 1469598103934665603
+    for b in data:
+        h ^= b
+        h = (h * 1099511628211) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def _checkpoint(dims, opt=0, step=0, betas=(0.0, 0.0, 0.0), seed=0):
+    rng = np.random.default_rng(seed)
+    parts = [rng.standard_normal((dims[l], dims[l + 1])).astype("<f4") for l in range(len(dims) - 1)]
+    if opt:
+        parts = parts + [np.abs(p) for p in parts] + [p * p for p in parts]
+    payload = b"".join(p.tobytes() for p in parts)
+    d = list(dims) + [0] * (17 - len(dims))
+    head = struct.pack("<8s4I17i3f2Iq2Q", b"MLPCKPT1", 1, len(dims) - 1, 0, opt, *d, *betas, 0, 0, step,
+                       len(payload), _fnv1a(payload))
+    assert len(head) == 136
+    return head + payload
+
+
+def test_checkpoint_info_reads_the_documented_format():
+    _lib()
+    buf = _checkpoint((5, 3, 2), opt=binding.OPT_ADAM, step=7, betas=(0.9, 0.999, 1e-8))
+    info = binding.checkpoint_info(buf)
+    assert info == {"n_layers": 2, "dims": [5, 3, 2], "optimizer": binding.OPT_ADAM, "step": 7}
+    assert binding.checkpoint_info(_checkpoint((4, 4)))["optimizer"] == binding.OPT_SGD
+
+
+def _damaged():
+    good = _checkpoint((6, 4, 3))
+    yield "truncated header", good[:100]
+    yield "truncated payload", good[:-4]
+    yield "magic", b"X" + good[1:]
+    yield "version", good[:8] + struct.pack("<I", 2) + good[12:]
+    yield "layers", good[:12] + struct.pack("<I", 0) + good[16:]
+    yield "rule", good[:20] + struct.pack("<I", 9) + good[24:]
+    yield "width", good[:24] + struct.pack("<i", -1) + good[28:]
+    yield "payload size", good[:120] + struct.pack("<Q", 8) + good[128:]
+    flipped = bytearray(good)
+    flipped[200] ^= 1
+    yield "payload bit", bytes(flipped)
+
+
+@pytest.mark.parametrize("what,buf", list(_damaged()))
+def test_checkpoint_info_rejects_damage(what, buf):
+    _lib()
+    with pytest.raises(binding.MlpError) as ei:
+        binding.checkpoint_info(buf)
+    assert ei.value.status == binding.MLP_ERR_ARG, what

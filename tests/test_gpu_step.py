@@ -585,3 +585,104 @@ def test_adaptive_profile_slots_and_errors(torch_dev):
         assert ei.value.status == binding.MLP_ERR_ARG
     snet.close()
     net.close()
+
+
+# ------------------------------------------------------------- checkpoints --
+
+@pytest.mark.parametrize("dims,B,precision,rule", [((96, 160, 130, 40), 128, "f32", "adam"),
+                                                   ((256, 520, 64), 8, "f32", "laprop"),
+                                                   ((120, 136, 24), 256, "bf16", "adam")])
+def test_checkpoint_resumes_training_bit_for_bit(torch_dev, dims, B, precision, rule):
+    """Save after two steps (weights, moments, step count), restore into a
+    fresh session and continue: the next steps equal those of the session
+    that kept going."""
+    torch, dev = torch_dev
+    _announce(f"checkpoint resume dims={dims} B={B} {precision} {rule}")
+    Ws = synth.make_weights(dims, "glorot", seed=31)
+    xd, td = P.to_dev(synth.make_batch(B, dims[0], dims[-1], "normal", seed=32)[:2], dev)
+    a = make_net(dims, B, precision, Ws, dev)
+    a.set_optimizer(rule, 0.9, 0.99, 1e-7)
+    for _ in range(2):
+        a.train_step(xd, td, 1e-3)
+    ck = a.save_checkpoint()
+    for _ in range(2):
+        a.train_step(xd, td, 1e-3)
+    b = binding_net(dims, B, precision, dev)
+    b.set_optimizer(rule, 0.9, 0.99, 1e-7)
+    b.load_checkpoint(ck)
+    for _ in range(2):
+        b.train_step(xd, td, 1e-3)
+    for u, w in zip(a.read_params(), b.read_params()):
+        assert torch.equal(u, w)
+    a.close()
+    b.close()
+
+
+def binding_net(dims, B, precision, dev):
+    from mlp_gemm_softmax_amd import binding
+    return binding.Mlp(dims, B, precision, device=str(dev))
+
+
+def test_checkpoint_reloads_into_a_forward_session(torch_dev):
+    """A bf16 training session's checkpoint (with Adam moments) loads into a
+    fresh float32 session without an optimizer: the same masters, and the
+    same logits as a session given those masters directly."""
+    torch, dev = torch_dev
+    dims, B = (120, 136, 24), 256
+    Ws = synth.make_weights(dims, "glorot", seed=41)
+    xd, td = P.to_dev(synth.make_batch(B, dims[0], dims[-1], "normal", seed=42)[:2], dev)
+    a = make_net(dims, B, "bf16", Ws, dev)
+    a.set_optimizer("adam")
+    a.train_step(xd, td, 1e-3)
+    ck = a.save_checkpoint()
+    from mlp_gemm_softmax_amd import binding
+    assert binding.checkpoint_info(ck)["step"] == 1
+    masters = a.read_params()
+    inf = binding_net(dims, B, "f32", dev)
+    inf.load_checkpoint(ck)
+    for u, w in zip(inf.read_params(), masters):
+        assert torch.equal(u, w)
+    ref = binding_net(dims, B, "f32", dev)
+    ref.set_params([w.clone() for w in masters])
+    l1, _ = inf.forward(xd)
+    l2, _ = ref.forward(xd)
+    assert torch.equal(l1, l2)
+    for n in (a, inf, ref):
+        n.close()
+
+
+def test_checkpoint_preflight_changes_nothing(torch_dev):
+    """Restores that fail their checks leave the session's weights as they
+    were: another shape, a rule the checkpoint does not carry, a damaged
+    payload."""
+    from mlp_gemm_softmax_amd import binding
+    torch, dev = torch_dev
+    dims, B = (48, 40, 12), 32
+    src = make_net(dims, B, "f32", synth.make_weights(dims, "glorot", seed=51), dev)
+    ck = src.save_checkpoint()
+    other = make_net((48, 44, 12), B, "f32", synth.make_weights((48, 44, 12), "glorot", seed=52), dev)
+    before = [w.clone() for w in other.read_params()]
+    with pytest.raises(binding.MlpError) as ei:
+        other.load_checkpoint(ck)
+    assert ei.value.status == binding.MLP_ERR_SHAPE
+    same = make_net(dims, B, "f32", synth.make_weights(dims, "glorot", seed=53), dev)
+    same.set_optimizer("adam")
+    before_same = [w.clone() for w in same.read_params()]
+    with pytest.raises(binding.MlpError) as ei:
+        same.load_checkpoint(ck)            # no Adam state in an SGD checkpoint
+    assert ei.value.status == binding.MLP_ERR_ARG
+    bad = bytearray(ck)
+    bad[-1] ^= 0x40
+    same.set_optimizer("sgd")
+    with pytest.raises(binding.MlpError) as ei:
+        same.load_checkpoint(bytes(bad))
+    assert ei.value.status == binding.MLP_ERR_ARG
+    for u, w in zip(other.read_params(), before):
+        assert torch.equal(u, w)
+    for u, w in zip(same.read_params(), before_same):
+        assert torch.equal(u, w)
+    same.load_checkpoint(ck)                # the intact one restores
+    for u, w in zip(same.read_params(), src.read_params()):
+        assert torch.equal(u, w)
+    for n in (src, other, same):
+        n.close()
