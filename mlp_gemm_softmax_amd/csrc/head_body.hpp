@@ -26,6 +26,34 @@ constexpr int kHeadThreads = 1024;
 constexpr int kHeadWaves = kHeadThreads / kWave;
 constexpr int kHeadU = 8;   // staging loads in flight per thread
 
+// Sum / max over the 16 lanes of a DPP row, the result in every lane: pairs
+// (quad_perm 1,0,3,2), quads (2,3,0,1), half rows (row_half_mirror), rows
+// (row_mirror); a fixed order, plain VALU moves instead of LDS permutes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0x141>(v);
+    v += dpp_mov<0x140>(v);
+    return v;
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    v = fmaxf(v, dpp_mov<0x141>(v));
+    v = fmaxf(v, dpp_mov<0x140>(v));
+    return v;
+}
+
+// q = e / d and e - q d for 0 <= e < 2^22, 1 <= d <= 2^16, from a float
+// reciprocal (rinv = 1/d rounded): (e + 1/2)/d sits at least 1/(2d) away
+// from an integer and the product errs by far less, so the floor is exact.
+// Cheaper than the integer division sequence, which every lane would run.
+__device__ __forceinline__ int div_small(int e, float rinv) { return (int)(((float)e + 0.5f) * rinv); }
+
 template <bool COH>
 __device__ __forceinline__ void head_block(const HeadParams& p, int row0, float* lds, float4v (*s_red)[kWave]) {
     const int H = p.H, C = p.C, CP = p.CP, RB = p.RB;
@@ -37,6 +65,7 @@ __device__ __forceinline__ void head_block(const HeadParams& p, int row0, float*
     uint8_t* sM = (uint8_t*)(sT + RB * C);   // [RB][H] mask
     const int tid = threadIdx.x;
     const int rows = min(RB, p.B - row0);
+    const float rH = 1.0f / (float)H, rC = 1.0f / (float)C;
 
     // Stage everything the block reads once.  Loads go out kHeadU at a time per
     // thread from clamped (in-range) addresses before any is stored, so the
@@ -64,7 +93,8 @@ __device__ __forceinline__ void head_block(const HeadParams& p, int row0, float*
             for (int u = 0; u < kHeadU; ++u) {
                 const int e = e0 + u * kHeadThreads;
                 if (e < nA) {
-                    sA[(e / H) * HS + e % H] = a[u];
+                    const int r = div_small(e, rH);
+                    sA[r * HS + (e - r * H)] = a[u];
                     sM[e] = m[u];
                 }
             }
@@ -76,7 +106,10 @@ __device__ __forceinline__ void head_block(const HeadParams& p, int row0, float*
 #pragma unroll
             for (int u = 0; u < kHeadU; ++u) {
                 const int e = e0 + u * kHeadThreads;
-                if (e < nW) sW[(e / C) * CP + e % C] = w[u];
+                if (e < nW) {
+                    const int r = div_small(e, rC);
+                    sW[r * CP + (e - r * C)] = w[u];
+                }
             }
         }
         for (int e0 = tid; e0 < nT; e0 += kHeadU * kHeadThreads) {
@@ -97,7 +130,8 @@ __device__ __forceinline__ void head_block(const HeadParams& p, int row0, float*
     // A[m = l%16][k = l/16], B[k = l/16][n = l%16]; the result lane l holds
     // rows 4(l/16)..+3 of column l%16.  The waves split each block's K range
     // into KS parts, whose sums meet in LDS and are added in part order.
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar block/part arithmetic
     const int li = lane & 15, lk = lane >> 4;
     const int RBb = (rows + 15) / 16, CB = (C + 15) / 16, HB = (H + 15) / 16;
     {
@@ -110,11 +144,25 @@ __device__ __forceinline__ void head_block(const HeadParams& p, int row0, float*
             const int ba = b0 + li, cb = c0 + li;
             float4v acc = {0.f, 0.f, 0.f, 0.f};
             const int kb = part * kpart, ke = min(H, kb + kpart);
-            for (int k0 = kb; k0 < ke; k0 += 4) {
-                const int k = k0 + lk;
-                const float av = (ba < rows && k < ke) ? sA[ba * HS + k] : 0.f;
-                const float wv = (cb < C && k < ke) ? sW[k * CP + cb] : 0.f;
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wv, acc, 0, 0, 0);
+            // four k-steps per batch: all of a batch's LDS reads go out before
+            // its first MFMA.  Addresses are clamped in range and values past
+            // the edges are multiplied by 0 rather than selected, so no read
+            // is predicated (a predicated read waits before the next one is
+            // issued); the zero steps past ke add exact zeros.
+            const int bc = min(ba, rows - 1), cc = min(cb, C - 1);
+            const float am = ba < rows ? 1.f : 0.f, wm = cb < C ? 1.f : 0.f;
+            for (int k0 = kb; k0 < ke; k0 += 16) {
+                float av[4], wv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int k = k0 + 4 * u + lk;
+                    const int kc = min(k, ke - 1);
+                    const float km = k < ke ? 1.f : 0.f;
+                    av[u] = sA[bc * HS + kc] * (am * km);
+                    wv[u] = sW[kc * CP + cc] * wm;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], wv[u], acc, 0, 0, 0);
             }
             s_red[wave][lane] = acc;
         }
@@ -123,8 +171,15 @@ __device__ __forceinline__ void head_block(const HeadParams& p, int row0, float*
             const int blk = wave;
             const int b0 = (blk / CB) * 16, c0 = (blk % CB) * 16;
             const int cb = c0 + li;
-            float4v z = s_red[blk][lane];
-            for (int part = 1; part < KS; ++part) z += s_red[part * nb + blk][lane];
+            // every part's sum is read before the adds (uniform predicate on
+            // the count, clamped rows), then added in part order
+            float4v zp[kHeadWaves];
+#pragma unroll
+            for (int part = 0; part < kHeadWaves; ++part) zp[part] = s_red[min(part * nb + blk, kHeadWaves - 1)][lane];
+            float4v z = zp[0];
+#pragma unroll
+            for (int part = 1; part < kHeadWaves; ++part)
+                if (part < KS) z += zp[part];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int bb = b0 + 4 * lk + e;
@@ -135,8 +190,8 @@ __device__ __forceinline__ void head_block(const HeadParams& p, int row0, float*
     __syncthreads();
 
     // softmax cross-entropy, 16 lanes per row (classes j and j + 16 of the
-    // row on lane j); max and sums by a fixed xor butterfly inside the
-    // 16-lane group.  Only LDS is written before the next barrier (a barrier
+    // row on lane j); max and sums across the 16-lane row by DPP moves in a
+    // fixed order (row16_sum / row16_max).  Only LDS is written before the next barrier (a barrier
     // also waits for the thread's outstanding global stores): the logits,
     // dlogits and row loss stay in this thread's registers and are stored
     // after the last phase.
@@ -151,17 +206,11 @@ __device__ __forceinline__ void head_block(const HeadParams& p, int row0, float*
             const bool v0 = cv0, v1 = cv1;
             const float z0 = v0 ? z[j] : -INFINITY, z1 = v1 ? z[j + 16] : -INFINITY;
             const float t0 = v0 ? t[j] : 0.f, t1 = v1 ? t[j + 16] : 0.f;
-            float mx = fmaxf(z0, z1);
-#pragma unroll
-            for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+            const float mx = row16_max(fmaxf(z0, z1));
             const float e0 = v0 ? expf(z0 - mx) : 0.f, e1 = v1 ? expf(z1 - mx) : 0.f;
-            float se = e0 + e1, st = t0 + t1, stz = (v0 ? t0 * z0 : 0.f) + (v1 ? t1 * z1 : 0.f);
-#pragma unroll
-            for (int o = 8; o >= 1; o >>= 1) {
-                se += __shfl_xor(se, o, 16);
-                st += __shfl_xor(st, o, 16);
-                stz += __shfl_xor(stz, o, 16);
-            }
+            const float se = row16_sum(e0 + e1);
+            const float st = row16_sum(t0 + t1);
+            const float stz = row16_sum((v0 ? t0 * z0 : 0.f) + (v1 ? t1 * z1 : 0.f));
             const float lse = mx + logf(se);
             cz0 = z0;
             cz1 = z1;
@@ -184,12 +233,22 @@ __device__ __forceinline__ void head_block(const HeadParams& p, int row0, float*
         const int b0 = (blk / HB) * 16, h0 = (blk % HB) * 16;
         const int ba = b0 + li, hb = h0 + li;
         float4v acc = {0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < C; k0 += 4) {
-            const int k = k0 + lk;
-            const float zv = (ba < rows && k < C) ? sZ[ba * C + k] : 0.f;
-            const float wv = (hb < H && k < C) ? sW[hb * CP + k] : 0.f;
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(zv, wv, acc, 0, 0, 0);
+        // K = C <= 32: every read of the block goes out before the MFMAs
+        // (clamped addresses, edges multiplied by 0 as in the logits)
+        const int bc = min(ba, rows - 1), hc = min(hb, H - 1);
+        const float zm = ba < rows ? 1.f : 0.f, hm = hb < H ? 1.f : 0.f;
+        float zv[8], wv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int k = 4 * u + lk;
+            const int kc = min(k, C - 1);
+            const float km = k < C ? 1.f : 0.f;
+            zv[u] = sZ[bc * C + kc] * (zm * km);
+            wv[u] = sW[hc * CP + kc] * hm;
         }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (4 * u < C) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(zv[u], wv[u], acc, 0, 0, 0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int bb = b0 + 4 * lk + e;
