@@ -163,9 +163,9 @@ mlp_status mlp_grads(mlp_ctx* ctx, const float* x, const float* labels,
                      float* const* dw, float* dlogits, float* loss);
 
 /* Device memory (bytes, a multiple of 256) that update rule `opt` keeps for
- * this configuration: float32 first and second moments and a float32
- * gradient buffer per weight.  0 for MLP_OPT_SGD, for an unknown rule and
- * for an invalid configuration.  Host only. */
+ * this configuration: float32 first and second moments per weight.  0 for
+ * MLP_OPT_SGD, for an unknown rule and for an invalid configuration.  Host
+ * only. */
 size_t mlp_optimizer_bytes(const mlp_config* cfg, int32_t opt);
 
 /* Select the update rule of mlp_train_step / mlp_train_step_async (the
@@ -174,10 +174,10 @@ size_t mlp_optimizer_bytes(const mlp_config* cfg, int32_t opt);
  * aligned, that must stay alive while the rule is in use; both moments are
  * zeroed (enqueued on the context's stream) and the step count t restarts,
  * so the next step has t = 1.  beta1, beta2 in [0, 1); eps finite and > 0.
- * For SGD, state, bytes, beta1, beta2 and eps are ignored.  With an adaptive
- * rule a step stores every dW_l into the state, then one more launch updates
- * all layers; the step count is a launch argument, so such steps refuse
- * (MLP_ERR_ARG) to be enqueued while the stream is being captured.  Errors:
+ * For SGD, state, bytes, beta1, beta2 and eps are ignored.  Every dW launch
+ * applies the rule while it holds W (reading and writing W, m and v once);
+ * the step count is a launch argument, so such steps refuse (MLP_ERR_ARG)
+ * to be enqueued while the stream is being captured.  Errors:
  * MLP_ERR_ARG (rule, betas, eps), MLP_ERR_WORKSPACE (state), MLP_ERR_STATE
  * (poisoned context); nothing changes on an error.  Resets the per-launch
  * timing (the launch sequence changes). */

@@ -4,6 +4,7 @@
 #pragma once
 
 #include "kernels.hpp"
+#include "optim_rule.hpp"
 
 namespace mlp {
 
@@ -11,15 +12,20 @@ namespace mlp {
 // column count is a multiple of 8, so all four are inside or all outside).
 // `pre` is what epilogue_load fetched for the same place.
 struct Pre {
-    float4v w;        // Sgd: the f32 master weights
+    float4v w;        // Sgd, Adapt: the f32 master weights
     uint32_t m;       // MaskMul: four mask bytes
+    float4v m1, m2;   // Adapt: first and second moments
 };
 
 template <Epi EPI>
 __device__ __forceinline__ Pre epilogue_load(const GemmParams& p, int row, int col) {
     Pre pre{};
     const int64_t o = (int64_t)row * p.ldc + col;
-    if constexpr (EPI == Epi::Sgd) pre.w = *reinterpret_cast<const float4v*>(p.C + o);
+    if constexpr (EPI == Epi::Sgd || EPI == Epi::Adapt) pre.w = *reinterpret_cast<const float4v*>(p.C + o);
+    if constexpr (EPI == Epi::Adapt) {
+        pre.m1 = *reinterpret_cast<const float4v*>(p.m + o);
+        pre.m2 = *reinterpret_cast<const float4v*>(p.v + o);
+    }
     if constexpr (EPI == Epi::MaskMul) pre.m = *reinterpret_cast<const uint32_t*>(p.mask + o);
     return pre;
 }
@@ -65,6 +71,13 @@ __device__ __forceinline__ void epilogue4(const GemmParams& p, int row, int col,
 #pragma unroll
         for (int c = 0; c < 4; ++c) w[c] = pre.w[c] - p.lr * v[c];
         *reinterpret_cast<float4v*>(p.C + o) = w;
+        if (p.Cb) *reinterpret_cast<u32x2v*>(p.Cb + o) = pack_bf16x4(w);
+    } else if constexpr (EPI == Epi::Adapt) {
+        float4v w = pre.w, m1 = pre.m1, m2 = pre.m2;
+        opt_apply4(p.opt, w, v, m1, m2);
+        *reinterpret_cast<float4v*>(p.C + o) = w;
+        *reinterpret_cast<float4v*>(p.m + o) = m1;
+        *reinterpret_cast<float4v*>(p.v + o) = m2;
         if (p.Cb) *reinterpret_cast<u32x2v*>(p.Cb + o) = pack_bf16x4(w);
     }
 }

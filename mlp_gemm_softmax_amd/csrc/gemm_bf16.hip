@@ -15,6 +15,7 @@
 //     at row kb + s/4, columns m0 + 4(s%4) therefore gives lane i the four
 //     values k = kb..kb+3 of row m0 + i.
 #include "kernels.hpp"
+#include "epilogue1.hpp"
 
 namespace mlp {
 namespace {
@@ -104,25 +105,6 @@ struct Tile {
     }
 };
 
-template <Epi EPI>
-__device__ __forceinline__ void epilogue(const GemmParams& p, int row, int col, float v) {
-    const int64_t o = (int64_t)row * p.ldc + col;
-    if constexpr (EPI == Epi::Store || EPI == Epi::Grad) {
-        p.C[o] = v;
-    } else if constexpr (EPI == Epi::ReluMask) {
-        const bool pos = v > 0.f;
-        const float a = pos ? v : 0.f;
-        if (p.Cb) p.Cb[o] = f32_to_bf16(a); else p.C[o] = a;
-        p.mask[o] = pos ? 1 : 0;
-    } else if constexpr (EPI == Epi::MaskMul) {
-        const float g = p.mask[o] ? v : 0.f;
-        if (p.Cb) p.Cb[o] = f32_to_bf16(g); else p.C[o] = g;
-    } else if constexpr (EPI == Epi::Sgd) {
-        const float w = p.C[o] - p.lr * v;
-        p.C[o] = w;
-        if (p.Cb) p.Cb[o] = f32_to_bf16(w);
-    }
-}
 
 template <class S, Layout LAY, int VEC, Epi EPI>
 __global__ __launch_bounds__(kThreads, 2) void gemm_bf16_kernel(GemmParams p) {
@@ -277,6 +259,7 @@ hipError_t dispatch_shape(const GemmLaunch& L, const GemmParams& p, hipStream_t 
         break;
     case Layout::TN:
         if (L.epi == Epi::Sgd) return go_vec<S, Layout::TN, Epi::Sgd>(L, p, st);
+        if (L.epi == Epi::Adapt) return go_vec<S, Layout::TN, Epi::Adapt>(L, p, st);
         if (L.epi == Epi::Grad) return go_vec<S, Layout::TN, Epi::Grad>(L, p, st);
         break;
     }

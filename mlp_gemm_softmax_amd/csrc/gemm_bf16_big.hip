@@ -27,6 +27,8 @@
 //         ds_read_b64_tr_b16 per lane (transpose reads, as in the 128-wide
 //         kernel), the four k-rows one read touches landing in distinct banks.
 #include "epilogue4.hpp"
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace mlp {
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
     const int rbase = m0 + wm * 128 + (lane >> 5);
     const int col = n0 + wn * 128 + 4 * (lane & 31);
     constexpr bool kAllPre = EPI == Epi::MaskMul;
-    Pre pre[kAllPre ? 4 : 1][16];
+    Pre pre[kAllPre ? 4 : 1][EPI == Epi::Adapt ? 1 : 16];   // Adapt reads its inputs per quarter chunk
     if (kAllPre && p.splits == 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -271,8 +273,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
     __syncthreads();   // every wave is done with the stage buffers
     float* st = reinterpret_cast<float*>(wave == 0 ? sa0 : wave == 1 ? sb0 : wave == 2 ? sa1 : sb1);
     constexpr int SP = 132;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    // one 32-row chunk; the chunk index is a template constant so that the
+    // accumulators are indexed statically (a loop the compiler declines to
+    // unroll would put them in scratch memory)
+    auto chunk = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -291,18 +296,38 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
             for (int q = 0; q < 16; ++q)
                 if (row0 + 2 * q < p.M && col < p.N)
                     *reinterpret_cast<float4v*>(part + (int64_t)(row0 + 2 * q) * p.N + col) = v[q];
-            continue;
+            return;
         }
-        Pre* pr = pre[kAllPre ? i : 0];
-        if constexpr (!kAllPre) {
+        if constexpr (EPI == Epi::Adapt) {
+            // W, m and v of 16 rows would not fit the registers: 4 at a time
+#pragma unroll
+            for (int hq = 0; hq < 16; hq += 4) {
+                Pre ph[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (row0 + 2 * (hq + q) < p.M && col < p.N) ph[q] = epilogue_load<EPI>(p, row0 + 2 * (hq + q), col);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (row0 + 2 * (hq + q) < p.M && col < p.N)
+                        epilogue4<EPI>(p, row0 + 2 * (hq + q), col, v[hq + q], ph[q]);
+            }
+        } else {
+            Pre* pr = pre[kAllPre ? i : 0];
+            if constexpr (!kAllPre) {
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    if (row0 + 2 * q < p.M && col < p.N) pr[q] = epilogue_load<EPI>(p, row0 + 2 * q, col);
+            }
 #pragma unroll
             for (int q = 0; q < 16; ++q)
-                if (row0 + 2 * q < p.M && col < p.N) pr[q] = epilogue_load<EPI>(p, row0 + 2 * q, col);
+                if (row0 + 2 * q < p.M && col < p.N) epilogue4<EPI>(p, row0 + 2 * q, col, v[q], pr[q]);
         }
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-            if (row0 + 2 * q < p.M && col < p.N) epilogue4<EPI>(p, row0 + 2 * q, col, v[q], pr[q]);
-    }
+        };
+    chunk(std::integral_constant<int, 0>{});
+    chunk(std::integral_constant<int, 1>{});
+    chunk(std::integral_constant<int, 2>{});
+    chunk(std::integral_constant<int, 3>{});
+
 }
 
 template <Layout LAY, Epi EPI>
@@ -344,6 +369,7 @@ hipError_t launch_gemm_bf16_big(const GemmLaunch& L, const GemmParams& p, hipStr
         break;
     case Layout::TN:
         if (L.epi == Epi::Sgd) return go<Layout::TN, Epi::Sgd>(p, L.grid, reduce, st);
+        if (L.epi == Epi::Adapt) return go<Layout::TN, Epi::Adapt>(p, L.grid, reduce, st);
         if (L.epi == Epi::Grad) return go<Layout::TN, Epi::Grad>(p, L.grid, reduce, st);
         break;
     }

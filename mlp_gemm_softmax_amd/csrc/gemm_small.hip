@@ -15,6 +15,7 @@
 // chunk c, lanes 0-31 hold k = 8c..8c+3 and lanes 32-63 hold k = 8c+4..8c+7,
 // and MFMA q (0..3) takes the q-th of those four values.
 #include "kernels.hpp"
+#include "epilogue1.hpp"
 #include "head_body.hpp"
 #include "tail.hpp"
 
@@ -48,21 +49,6 @@ __device__ __forceinline__ float4v load_op(const float* __restrict__ g, int64_t 
     }
 }
 
-template <Epi EPI>
-__device__ __forceinline__ void epilogue(const GemmParams& p, int row, int col, float v) {
-    const int64_t o = (int64_t)row * p.ldc + col;
-    if constexpr (EPI == Epi::Store || EPI == Epi::Grad) {
-        p.C[o] = v;
-    } else if constexpr (EPI == Epi::ReluMask) {
-        const bool pos = v > 0.f;
-        p.C[o] = pos ? v : 0.f;
-        p.mask[o] = pos ? 1 : 0;
-    } else if constexpr (EPI == Epi::MaskMul) {
-        p.C[o] = p.mask[o] ? v : 0.f;
-    } else if constexpr (EPI == Epi::Sgd) {
-        p.C[o] = p.C[o] - p.lr * v;
-    }
-}
 
 template <int NW, Layout LAY, int VEC, Epi EPI>
 __global__ __launch_bounds__(NW * 64) void gemm_small_kernel(GemmParams p) {
@@ -295,6 +281,8 @@ template <int NW>
 hipError_t dispatch_tail(const GemmLaunch& L, const GemmParams& p, const TailParams& t, hipStream_t st) {
     if (L.epi == Epi::Sgd)
         return L.vec == 4 ? go_tail<NW, 4, Epi::Sgd>(p, L.grid, t, st) : go_tail<NW, 1, Epi::Sgd>(p, L.grid, t, st);
+    if (L.epi == Epi::Adapt)
+        return L.vec == 4 ? go_tail<NW, 4, Epi::Adapt>(p, L.grid, t, st) : go_tail<NW, 1, Epi::Adapt>(p, L.grid, t, st);
     if (L.epi == Epi::Grad)
         return L.vec == 4 ? go_tail<NW, 4, Epi::Grad>(p, L.grid, t, st) : go_tail<NW, 1, Epi::Grad>(p, L.grid, t, st);
     return hipErrorInvalidValue;
@@ -318,6 +306,7 @@ hipError_t dispatch(const GemmLaunch& L, const GemmParams& p, hipStream_t st) {
         break;
     case Layout::TN:
         if (L.epi == Epi::Sgd) return go_vec<NW, Layout::TN, Epi::Sgd>(L, p, st);
+        if (L.epi == Epi::Adapt) return go_vec<NW, Layout::TN, Epi::Adapt>(L, p, st);
         if (L.epi == Epi::Grad) return go_vec<NW, Layout::TN, Epi::Grad>(L, p, st);
         break;
     }

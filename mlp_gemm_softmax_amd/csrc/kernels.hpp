@@ -21,7 +21,7 @@ enum class Layout : int { NN = 0, NT = 1, TN = 2 };
 //   MaskMul  C = mask ? v : 0 (f32 or bf16)        (dX through the ReLU)
 //   Sgd      W = W - lr * v, optional bf16 copy    (dW + in-place update)
 //   Grad     C = v                                  (dW, no update)
-//   Adapt    W, m, v <- Adam or LaProp step with g = v (skinny-batch kernels)
+//   Adapt    W, m, v <- Adam or LaProp step with g = v (optional bf16 copy)
 enum class Epi : int { Store = 0, ReluMask = 1, MaskMul = 2, Sgd = 3, Grad = 4, Adapt = 5 };
 
 // Scalars of an adaptive update step (Adam or LaProp, see optim_rule.hpp).
@@ -48,6 +48,9 @@ struct GemmParams {
     float* partials;     // [splits][M][N] float32 when splits > 1
     unsigned* tickets;   // one zeroed counter per output tile when splits > 1
     int tiles_m, tiles_n;
+    float* m;            // Adapt: first and second moments, laid out as C
+    float* v;
+    OptScalars opt;      // Adapt: the step's scalars
 };
 
 // Tile configurations of the MFMA GEMM (workgroup tile BM x BN, 4 waves).
@@ -166,6 +169,9 @@ struct TailParams {
     float* loss;           // scalar mean loss
     int B, H, C;
     float lr, inv_b;
+    float* m;              // non-null (and dW null): Adam / LaProp moments of W_L
+    float* v;
+    OptScalars opt;
 };
 __host__ __device__ inline int tail_jobs(int H) { return (H + 15) / 16 + 1; }
 hipError_t launch_tail(const TailParams& t, hipStream_t s);
@@ -180,24 +186,7 @@ hipError_t launch_gemm_small_tail(const GemmLaunch& L, const GemmParams& p, int 
 // ---- f32 -> bf16 cast -----------------------------------------------------
 hipError_t launch_cast_bf16(const float* src, bf16_t* dst, size_t n, hipStream_t s);
 
-// ---- adaptive update rules (optim.hip) -------------------------------------
-constexpr int kMaxOptTensors = 16;
-struct OptTensor {
-    float* W;          // f32 master [n]
-    bf16_t* Wb;        // bf16 operand copy [n] or null
-    const float* g;    // gradient [n]
-    float* m;          // first moment [n]
-    float* v;          // second moment [n]
-    int64_t n;
-};
-struct OptParams {
-    OptTensor t[kMaxOptTensors];
-    int first_block[kMaxOptTensors + 1];   // filled by launch_opt_update
-    int count;
-    OptScalars o;
-};
-// Every tensor's arrays are 16-byte aligned.
-hipError_t launch_opt_update(OptParams p, hipStream_t s);
+// ---- optimizer state (optim.hip) --------------------------------------------
 // Zero n floats (n % 4 == 0, 16-byte aligned) with a kernel.
 hipError_t launch_zero(float* p, size_t n, hipStream_t s);
 // ---- bf16 -> f32 widen (state read-back) -----------------------------------

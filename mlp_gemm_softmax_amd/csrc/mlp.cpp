@@ -59,7 +59,6 @@ using namespace mlp;
 namespace {
 
 constexpr int kMaxLayers = 16;
-static_assert(kMaxLayers <= kMaxOptTensors, "one update tensor per layer");
 constexpr int kMaxDim = 1 << 20;
 constexpr int kSkinnyMaxBatch = 16;
 constexpr size_t kAlign = 256;
@@ -125,13 +124,13 @@ struct mlp_ctx {
     std::string err;
 
     // update rule of a training step: SGD (no state), or Adam / LaProp with
-    // moments and a gradient buffer in caller memory given to mlp_set_optimizer
+    // moments in caller memory given to mlp_set_optimizer, applied by the dW
+    // launches while they hold W
     int opt = MLP_OPT_SGD;
     float opt_b1 = 0.f, opt_b2 = 0.f, opt_eps = 0.f;
     int64_t opt_t = 0;                  // steps taken with the current moments
     float* opt_m[kMaxLayers] = {};
     float* opt_v[kMaxLayers] = {};
-    float* opt_g[kMaxLayers] = {};
 
     bool profiling = false;
     std::vector<Slot> slots;
@@ -263,13 +262,6 @@ bool head_fused(const mlp_ctx* c) {
            head_lds_bytes(c->dims[c->L - 1], c->dims[c->L], 32) <= 64 * 1024;
 }
 
-// The skinny-batch kernels apply an adaptive rule while W streams through
-// them; other layers store their gradients for the update launch.
-bool adapt_fused(const mlp_ctx* c, int l) {
-    if (c->opt == MLP_OPT_SGD || !c->skinny) return false;
-    return !(c->head && l == c->L - 1);   // the output layer's dW is the tail's
-}
-
 OptScalars opt_scalars(const mlp_ctx* c, float lr) {
     OptScalars o{};
     o.rule = c->opt == MLP_OPT_ADAM ? kOptAdam : kOptLaProp;
@@ -308,8 +300,9 @@ void build_slots(mlp_ctx* c) {
     const char* kind = c->skinny ? "skinny" : (c->bf16 ? "mfma_bf16" : "mfma_f32");
     // with an adaptive rule the dW launches store gradients and one more
     // launch applies the update
-    const std::string upd = c->opt == MLP_OPT_SGD ? "sgd" : "grad";
-    const std::string rule = c->opt == MLP_OPT_ADAM ? "adam" : "laprop";
+    // the update every dW launch applies while it holds W
+    const std::string upd = c->opt == MLP_OPT_SGD ? "sgd" : (c->opt == MLP_OPT_ADAM ? "adam" : "laprop");
+    const double mv = c->opt == MLP_OPT_SGD ? 0.0 : 16.0;   // m and v in and out, per weight
     if (c->bf16) add("cast_x_bf16", 0, (double)B * c->dims[0] * 6);
     const int C = c->dims[L];
     const int Lf = c->head ? L - 1 : L;   // layers whose forward is a plain GEMM
@@ -340,7 +333,7 @@ void build_slots(mlp_ctx* c) {
         }
         top = L - 2;
         tail_flops = 2.0 * B * H * C;
-        tail_bytes = B * H * 4 + B * C * 4 + H * C * 8 + B * 4.0;
+        tail_bytes = B * H * 4 + B * C * 4 + H * C * (8 + mv) + B * 4.0;
         tail_name = "tail_dw_" + upd + "_loss_l" + std::to_string(L - 1);
     } else {
         if (xf)   // labels in; logits, dlogits (+ bf16 copy) and row losses out
@@ -351,34 +344,24 @@ void build_slots(mlp_ctx* c) {
     for (int l = top; l >= 0; --l) {
         const double din = c->dims[l], dout = c->dims[l + 1];
         if (l > 0 && c->skinny) {
-            // dX and dW + SGD in one pass over W: W read and written once
-            // W read and written once; an adaptive rule also streams m and v
-            const double wb = adapt_fused(c, l) ? 24.0 : 8.0;
-            add(std::string(kind) + "_nt_mask_" + (adapt_fused(c, l) ? rule : upd) + "_l" + std::to_string(l),
-                4.0 * B * din * dout, wb * din * dout + 4.0 * B * dout + 4.0 * B * din + B * din * 5.0);
+            // dX and dW + update in one pass over W: W read and written once
+            // (with an adaptive rule m and v too)
+            add(std::string(kind) + "_nt_mask_" + upd + "_l" + std::to_string(l), 4.0 * B * din * dout,
+                (8.0 + mv) * din * dout + 4.0 * B * dout + 4.0 * B * din + B * din * 5.0);
             continue;
         }
         if (l > 0)
             add(std::string(kind) + "_nt_mask_l" + std::to_string(l), 2.0 * B * din * dout,
                 B * dout * e + din * dout * e + B * din * (1 + e));
-        // W in+out (+copy); dW out; or W, m, v in+out (rule applied here)
-        const double wb = c->opt == MLP_OPT_SGD ? 8 + (c->bf16 ? 2 : 0) : (adapt_fused(c, l) ? 24 : 4);
-        const std::string what = adapt_fused(c, l) ? rule : upd;
+        // W in+out (+ bf16 copy), and m, v in+out with an adaptive rule
+        const double wb = 8 + (c->bf16 ? 2 : 0) + mv;
         const double f = 2.0 * B * din * dout, b = B * din * e + B * dout * e + din * dout * wb;
         if (l == 0 && c->head && tail_fused(c))
-            add(std::string(kind) + "_tn_" + what + "_l0+" + tail_name, f + tail_flops, b + tail_bytes);
+            add(std::string(kind) + "_tn_" + upd + "_l0+" + tail_name, f + tail_flops, b + tail_bytes);
         else
-            add(std::string(kind) + "_tn_" + what + "_l" + std::to_string(l), f, b);
+            add(std::string(kind) + "_tn_" + upd + "_l" + std::to_string(l), f, b);
     }
     if (c->head && !tail_fused(c)) add(tail_name, tail_flops, tail_bytes);
-    if (c->opt != MLP_OPT_SGD) {
-        // per weight of the layers not updated in their dW launch: g, m, v, W
-        // in; m, v, W (+ bf16 copy) out
-        double n = 0;
-        for (int l = 0; l < L; ++l)
-            if (!adapt_fused(c, l)) n += (double)c->dims[l] * c->dims[l + 1];
-        if (n > 0) add("opt_update_" + rule, 0, n * (28 + (c->bf16 ? 2 : 0)));
-    }
 }
 
 // ---------------------------------------------------------------- launches --
@@ -418,7 +401,8 @@ struct Runner {
 
 hipError_t run_gemm(mlp_ctx* c, const GemmPlan& g, Layout lay, Epi epi, const void* A, int64_t lda,
                     const void* Bm, int64_t ldb, int M, int N, int K, float* C, bf16_t* Cb,
-                    uint8_t* mask, float lr, const TailParams* tail = nullptr, bool reduce = true) {
+                    uint8_t* mask, float lr, const TailParams* tail = nullptr, bool reduce = true,
+                    float* m = nullptr, float* v = nullptr, const OptScalars* opt = nullptr) {
     GemmLaunch L;
     L.layout = lay;
     L.epi = epi;
@@ -445,6 +429,9 @@ hipError_t run_gemm(mlp_ctx* c, const GemmPlan& g, Layout lay, Epi epi, const vo
     p.tickets = c->tickets;
     p.tiles_m = g.tiles_m;
     p.tiles_n = g.tiles_n;
+    p.m = m;
+    p.v = v;
+    p.opt = opt ? *opt : OptScalars{};
     if (tail) return launch_gemm_small_tail(L, p, g.small_waves, *tail, c->stream);
     if (g.small_waves > 0) return launch_gemm_small(L, p, g.small_waves, c->stream);
     if (g.cfg == TileCfg::T256x256) return launch_gemm_bf16_big(L, p, c->stream, reduce);
@@ -594,17 +581,20 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
     }
     if (mode == Mode::Forward) return r.err;
 
-    // ---- backward (an adaptive rule stores the gradients and updates after)
+    // ---- backward (every dW launch applies the update while it holds W)
     const bool adaptive = mode == Mode::Train && c->opt != MLP_OPT_SGD;
-    const bool grads = mode == Mode::Grads || adaptive;
-    float* const* dwo = adaptive ? c->opt_g : dw_out;
+    const bool grads = mode == Mode::Grads;
+    const Epi upd_epi = grads ? Epi::Grad : (adaptive ? Epi::Adapt : Epi::Sgd);
     const OptScalars osc = adaptive ? opt_scalars(c, lr) : OptScalars{};
     TailParams tp{};
     if (use_head) {
         tp.A = (const float*)c->act[L - 1];
         tp.dZ = c->dlogits;
         tp.W = c->W[L - 1];
-        tp.dW = grads ? dwo[L - 1] : nullptr;
+        tp.dW = grads ? dw_out[L - 1] : nullptr;
+        tp.m = adaptive ? c->opt_m[L - 1] : nullptr;
+        tp.v = adaptive ? c->opt_v[L - 1] : nullptr;
+        tp.opt = osc;
         tp.rowloss = c->rowloss;
         tp.loss = loss_dev ? loss_dev : c->loss_slot;
         tp.B = B;
@@ -631,11 +621,10 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
             void* out = c->dz[pp];
             pp ^= 1;
             r.run(slot++, [&] {
-                const bool fu = adaptive && adapt_fused(c, l);
                 SkinnyLaunch sl;
                 sl.layout = Layout::NT;
-                sl.epi = fu ? Epi::Adapt : (grads ? Epi::Grad : Epi::Sgd);
-                sl.grid = fu ? (din + 15) / 16 : c->sdx[l].grid;
+                sl.epi = upd_epi;
+                sl.grid = adaptive ? (din + 15) / 16 : c->sdx[l].grid;
                 sl.waves = 8;
                 sl.fused_update = true;
                 SkinnyParams sp{};
@@ -648,9 +637,9 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
                 sp.mask = c->mask[l];
                 sp.lr = lr;
                 sp.act = (const float*)c->act[l];
-                sp.wout = (grads && !fu) ? dwo[l] : c->W[l];
-                sp.m = fu ? c->opt_m[l] : nullptr;
-                sp.v = fu ? c->opt_v[l] : nullptr;
+                sp.wout = grads ? dw_out[l] : c->W[l];
+                sp.m = adaptive ? c->opt_m[l] : nullptr;
+                sp.v = adaptive ? c->opt_v[l] : nullptr;
                 sp.opt = osc;
                 return launch_skinny(sl, sp, c->stream);
             });
@@ -668,45 +657,24 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
             Gnext = out;
         }
         const void* a_in = l == 0 ? (c->bf16 ? (const void*)c->xb : (const void*)x) : c->act[l];
-        float* Wdst = grads ? dwo[l] : c->W[l];
+        float* Wdst = grads ? dw_out[l] : c->W[l];
         bf16_t* Wbdst = (!grads && c->bf16) ? c->Wb[l] : nullptr;
+        float* om = adaptive ? c->opt_m[l] : nullptr;
+        float* ov = adaptive ? c->opt_v[l] : nullptr;
         if (c->skinny) {
-            const bool fu = adaptive && adapt_fused(c, l);
             r.run(slot++, [&] {
-                if (fu)
-                    return run_skinny(c, c->sdw[l], Layout::TN, Epi::Adapt, (const float*)a_in, (const float*)G,
-                                      din, dout, c->W[l], nullptr, lr, c->opt_m[l], c->opt_v[l], &osc);
-                return run_skinny(c, c->sdw[l], Layout::TN, grads ? Epi::Grad : Epi::Sgd,
-                                  (const float*)a_in, (const float*)G, din, dout, Wdst, nullptr, lr);
+                return run_skinny(c, c->sdw[l], Layout::TN, upd_epi, (const float*)a_in, (const float*)G, din, dout,
+                                  Wdst, nullptr, lr, om, ov, &osc);
             });
         } else {
             r.run(slot++, [&] {
-                return run_gemm(c, c->dw[l], Layout::TN, grads ? Epi::Grad : Epi::Sgd, a_in, din, G, dout,
-                                din, dout, B, Wdst, Wbdst, nullptr, lr, (l == 0 && fuse_tail) ? &tp : nullptr);
+                return run_gemm(c, c->dw[l], Layout::TN, upd_epi, a_in, din, G, dout, din, dout, B, Wdst, Wbdst,
+                                nullptr, lr, (l == 0 && fuse_tail) ? &tp : nullptr, true, om, ov, &osc);
             });
         }
         G = Gnext;
     }
     if (use_head && !fuse_tail) r.run(slot++, [&] { return launch_tail(tp, c->stream); });
-    int unfused = 0;
-    for (int l = 0; l < L; ++l) unfused += adaptive && !adapt_fused(c, l);
-    if (unfused > 0) {
-        r.run(slot++, [&] {
-            OptParams op{};
-            op.o = osc;
-            for (int l = 0; l < L; ++l) {
-                if (adapt_fused(c, l)) continue;
-                OptTensor& t = op.t[op.count++];
-                t.W = c->W[l];
-                t.Wb = c->bf16 ? c->Wb[l] : nullptr;
-                t.g = c->opt_g[l];
-                t.m = c->opt_m[l];
-                t.v = c->opt_v[l];
-                t.n = (int64_t)c->dims[l] * c->dims[l + 1];
-            }
-            return launch_opt_update(op, c->stream);
-        });
-    }
     return r.err;
 }
 
@@ -1087,11 +1055,11 @@ mlp_status mlp_grads(mlp_ctx* c, const float* x, const float* labels, float* con
     return MLP_OK;
 }
 
-// Device bytes of an adaptive rule's state: first and second moments and a
-// gradient buffer, float32 per weight, each array 256-byte aligned.
+// Device bytes of an adaptive rule's state: first and second moments,
+// float32 per weight, each array 256-byte aligned.
 static size_t optimizer_bytes(const mlp_ctx* c) {
     size_t b = 0;
-    for (int l = 0; l < c->L; ++l) b += 3 * align_up((size_t)c->dims[l] * c->dims[l + 1] * 4, kAlign);
+    for (int l = 0; l < c->L; ++l) b += 2 * align_up((size_t)c->dims[l] * c->dims[l + 1] * 4, kAlign);
     return b;
 }
 
@@ -1121,15 +1089,13 @@ mlp_status mlp_set_optimizer(mlp_ctx* c, int32_t opt, float beta1, float beta2, 
     }
     float* m[kMaxLayers] = {};
     float* v[kMaxLayers] = {};
-    float* g[kMaxLayers] = {};
     if (opt != MLP_OPT_SGD) {
         char* p = (char*)state;
         for (int l = 0; l < c->L; ++l) {
             const size_t a = align_up((size_t)c->dims[l] * c->dims[l + 1] * 4, kAlign);
             m[l] = (float*)p;
             v[l] = (float*)(p + a);
-            g[l] = (float*)(p + 2 * a);
-            p += 3 * a;
+            p += 2 * a;
         }
         // zero both moments (one contiguous range per layer)
         for (int l = 0; l < c->L; ++l) {
@@ -1146,7 +1112,6 @@ mlp_status mlp_set_optimizer(mlp_ctx* c, int32_t opt, float beta1, float beta2, 
     for (int l = 0; l < kMaxLayers; ++l) {
         c->opt_m[l] = m[l];
         c->opt_v[l] = v[l];
-        c->opt_g[l] = g[l];
     }
     // the launch sequence of a step changed: new slot names, fresh counts
     collect_profile(c);

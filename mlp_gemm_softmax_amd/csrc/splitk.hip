@@ -52,6 +52,7 @@ hipError_t launch_splitk_epilogue(const GemmParams& p, Epi epi, hipStream_t st) 
     case Epi::MaskMul: return go<Epi::MaskMul>(p, st);
     case Epi::Sgd: return go<Epi::Sgd>(p, st);
     case Epi::Grad: return go<Epi::Grad>(p, st);
+    case Epi::Adapt: return go<Epi::Adapt>(p, st);
     }
     return hipErrorInvalidValue;
 }

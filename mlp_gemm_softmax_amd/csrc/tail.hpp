@@ -3,13 +3,14 @@
 // NW waves can run: job j < ceil(H/16) computes rows 16j..16j+15 of
 //   dW_L[h][c] = sum_b a[b][h] dlogits[b][c]
 // on v_mfma_f32_16x16x4f32 (the waves split the batch rows; their sums meet
-// in LDS and are added in wave order), then W_L -= lr * dW_L (or stores
-// dW_L); job ceil(H/16) averages the row losses.  Every output belongs to
+// in LDS and are added in wave order), then W_L -= lr * dW_L, an Adam /
+// LaProp step, or a store of dW_L; job ceil(H/16) averages the row losses.  Every output belongs to
 // one job, so no cross-workgroup reduction is needed; the head's writes are
 // visible because the tail runs in a later launch.
 #pragma once
 
 #include "kernels.hpp"
+#include "optim_rule.hpp"
 
 namespace mlp {
 
@@ -65,8 +66,17 @@ __device__ __forceinline__ void tail_job(const TailParams& t, int job, float4v* 
                 const int h = h0 + 4 * lk + e;
                 if (h < t.H && c < t.C) {
                     const int64_t o = (int64_t)h * t.C + c;
-                    if (t.dW) t.dW[o] = d[e];
-                    else t.W[o] = t.W[o] - t.lr * d[e];
+                    if (t.dW) {
+                        t.dW[o] = d[e];
+                    } else if (t.m) {
+                        float w = t.W[o], m = t.m[o], s = t.v[o];
+                        opt_apply(t.opt, w, d[e], m, s);
+                        t.W[o] = w;
+                        t.m[o] = m;
+                        t.v[o] = s;
+                    } else {
+                        t.W[o] = t.W[o] - t.lr * d[e];
+                    }
                 }
             }
         }

@@ -544,9 +544,9 @@ def test_adaptive_then_sgd_matches_fresh_sgd(torch_dev):
 
 
 def test_adaptive_profile_slots_and_errors(torch_dev):
-    """With Adam the dW launches store gradients and one update launch
-    follows; bad arguments are refused before anything is enqueued, and an
-    Adam step refuses stream capture."""
+    """With Adam every dW launch applies the rule (no extra launch); bad
+    arguments are refused before anything is enqueued, and an Adam step
+    refuses stream capture."""
     from mlp_gemm_softmax_amd import binding
     torch, dev = torch_dev
     dims, B = (16, 8, 40), 64
@@ -568,8 +568,7 @@ def test_adaptive_profile_slots_and_errors(torch_dev):
     net.train_step(xd, td, 0.01)
     names = [r["name"] for r in net.profile_read()]
     assert names == ["mfma_f32_nn_relu_mask_l0", "mfma_f32_nn_store_l1", "softmax_xent",
-                     "mfma_f32_nt_mask_l1", "mfma_f32_tn_grad_l1", "mfma_f32_tn_grad_l0",
-                     "opt_update_adam"], names
+                     "mfma_f32_nt_mask_l1", "mfma_f32_tn_adam_l1", "mfma_f32_tn_adam_l0"], names
     net.profile(False)
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
