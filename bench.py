@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--mode", choices=["train", "forward"], default="train",
+                    help="train: the training step (the headline metric); forward: logits only "
+                         "(inference of the same network)")
     ap.add_argument("--optimizer", choices=["sgd", "adam", "laprop"], default="sgd",
                     help="update rule of the step (Adam/LaProp: beta1 0.9, beta2 0.999, eps 1e-8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -301,10 +304,15 @@ def main():
         del src, dst
     torch.cuda.synchronize()
 
+    logits = torch.empty((w.batch, w.dims[-1]), dtype=torch.float32, device=dev)
+
     def run(k, offset=0):
         for i in range(k):
             xb, tb = batches[(offset + i) % n_batches]
-            net.train_step_async(xb, tb, w.lr, loss_dev)
+            if args.mode == "forward":
+                net.forward_async(xb, logits)
+            else:
+                net.train_step_async(xb, tb, w.lr, loss_dev)
 
     run(args.warmup)
     torch.cuda.synchronize()
@@ -329,11 +337,13 @@ def main():
         file=sys.stderr, flush=True)
 
     steps_per_s = args.steps / el
-    flops = w.gemm_flops()
+    fwd = args.mode == "forward"
+    flops = w.forward_flops() if fwd else w.gemm_flops()
     out = {
-        "metric": "MLP train steps/sec + achieved TFLOP/s (fraction of MFMA/HBM roofline), 1 GPU",
+        "metric": ("MLP forward passes/sec (logits, inference) + achieved TFLOP/s, 1 GPU" if fwd else
+                   "MLP train steps/sec + achieved TFLOP/s (fraction of MFMA/HBM roofline), 1 GPU"),
         "value": round(steps_per_s, 3),
-        "unit": "steps/s",
+        "unit": "forward passes/s" if fwd else "steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -345,13 +355,13 @@ def main():
         "data": "synthetic (seeded; MNIST-shaped uniform [0,1) pixels or N(0,1) features, uniform class ids)",
         "config": {"workload": w.name, "dims": list(w.dims), "batch": w.batch, "lr": w.lr,
                    "precision": w.precision, "fresh_batch_per_step": w.fresh_batch,
-                   "optimizer": args.optimizer},
+                   "optimizer": args.optimizer, "mode": args.mode},
         "achieved_tflops": round(flops * steps_per_s / 1e12, 4),
         "step_flops": flops,
         "final_loss": final_loss,
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not fwd:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s, args.optimizer)
     net.close()
     print(json.dumps(out), flush=True)

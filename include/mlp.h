@@ -236,10 +236,13 @@ mlp_status mlp_read_state(mlp_ctx* ctx, int32_t which, int32_t layer, void* dst)
 /* Per-launch timing.  When enabled, every kernel launch of a step is
  * bracketed by a pair of HIP events on the context's stream (the README's
  * per-dispatch GPU timing).  mlp_profile_read sums the recorded durations
- * per launch slot after the caller has synchronised the stream. */
+ * per launch slot after the caller has synchronised the stream.  Training
+ * steps (and mlp_grads), forward passes and forward passes with a loss are
+ * three launch sequences with slots of their own; the slot calls below
+ * report the sequence of the last call enqueued while timing was enabled. */
 mlp_status mlp_profile_enable(mlp_ctx* ctx, int32_t enable);
 mlp_status mlp_profile_reset(mlp_ctx* ctx);
-/* Number of launch slots in one training step. */
+/* Number of launch slots in that sequence. */
 int32_t mlp_profile_slots(const mlp_ctx* ctx);
 /* Slot `idx`: slot name (the launch's products, copied into `name`,
  * NUL-terminated), total

@@ -232,6 +232,11 @@ class Mlp:
                                       ctypes.c_void_p(_ptr(labels)), loss_p))
         return logits, (self._loss.value if loss_p is not None else None)
 
+    def forward_async(self, x, logits):
+        """Logits of batch x into the given device buffer; enqueue only."""
+        self._check(lib().mlp_forward(self._h, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(logits.data_ptr()),
+                                      None, None))
+
     def train_step(self, x, labels, lr: float) -> float:
         self._dev_f32(x, (self.batch, self.dims[0]))
         self._dev_f32(labels, (self.batch, self.dims[-1]))

@@ -84,9 +84,13 @@ struct Slot {
 };
 
 struct Pending {
-    int slot;
+    int kind, slot;
     hipEvent_t beg, end;
 };
+
+// Launch sequences that are timed separately: a training step (or
+// gradients), a forward pass, a forward pass with the loss.
+enum SlotKind { kStep = 0, kForward = 1, kForwardLoss = 2, kKinds = 3 };
 
 }  // namespace
 
@@ -133,7 +137,8 @@ struct mlp_ctx {
     float* opt_v[kMaxLayers] = {};
 
     bool profiling = false;
-    std::vector<Slot> slots;
+    std::vector<Slot> slots[kKinds];   // per launch sequence
+    int prof_kind = kStep;             // sequence of the last call enqueued while profiling
     std::vector<Pending> pending;
     std::vector<hipEvent_t> event_pool;
 };
@@ -285,9 +290,10 @@ bool xent_fused(const mlp_ctx* c) {
     return g.cfg == TileCfg::T256x256 && g.splits > 1 && splitk_xent_fits(c->dims[c->L], g.splits);
 }
 
-// Slot names and algorithmic work, in launch order.
-void build_slots(mlp_ctx* c) {
-    c->slots.clear();
+// Slot names and algorithmic work of one launch sequence, in launch order.
+void build_slot_list(mlp_ctx* c, int sk) {
+    std::vector<Slot>& slots = c->slots[sk];
+    slots.clear();
     const int L = c->L, B = c->B;
     const double e = es(c->bf16);
     auto add = [&](const std::string& n, double f, double b) {
@@ -295,8 +301,10 @@ void build_slots(mlp_ctx* c) {
         s.name = n;
         s.flops = f;
         s.bytes = b;
-        c->slots.push_back(s);
+        slots.push_back(s);
     };
+    // a forward call runs the output layer as plain products, never the head
+    const bool head = c->head && sk == kStep;
     const char* kind = c->skinny ? "skinny" : (c->bf16 ? "mfma_bf16" : "mfma_f32");
     // with an adaptive rule the dW launches store gradients and one more
     // launch applies the update
@@ -305,8 +313,8 @@ void build_slots(mlp_ctx* c) {
     const double mv = c->opt == MLP_OPT_SGD ? 0.0 : 16.0;   // m and v in and out, per weight
     if (c->bf16) add("cast_x_bf16", 0, (double)B * c->dims[0] * 6);
     const int C = c->dims[L];
-    const int Lf = c->head ? L - 1 : L;   // layers whose forward is a plain GEMM
-    const bool xf = xent_fused(c);
+    const int Lf = head ? L - 1 : L;   // layers whose forward is a plain GEMM
+    const bool xf = xent_fused(c) && sk != kForward;   // the loss launch adds the logits' partials
     for (int l = 0; l < Lf; ++l) {
         const double M = B, N = c->dims[l + 1], K = c->dims[l];
         const bool last = l == L - 1;
@@ -316,15 +324,16 @@ void build_slots(mlp_ctx* c) {
         const char* what = last ? (xf ? "partials" : "store") : "relu_mask";
         add(std::string(kind) + "_nn_" + what + "_l" + std::to_string(l), 2 * M * N * K, M * K * e + K * N * e + out);
     }
+    if (sk == kForward) return;
     int top = L - 1;
     double tail_flops = 0, tail_bytes = 0;
     std::string tail_name;
-    if (c->head) {
+    if (head) {
         const double H = c->dims[L - 1];
         const std::string hn = "head_logits_xent_dx_l" + std::to_string(L - 1);
         const double hf = 4.0 * B * H * C, hb = B * H * 4 + H * C * 4 + B * C * 12 + B * H * 5 + B * 4.0;
         if (head_fused(c)) {   // merge into the last hidden layer's forward slot
-            Slot& f = c->slots.back();
+            Slot& f = slots.back();
             f.name += "+" + hn;
             f.flops += hf;
             f.bytes += hb;
@@ -341,6 +350,7 @@ void build_slots(mlp_ctx* c) {
         else      // logits and labels in; dlogits (+ bf16 copy) and row losses out
             add("softmax_xent", 0, (double)B * C * (12 + (c->bf16 ? 2 : 0)) + B * 4.0);
     }
+    if (sk == kForwardLoss) return;
     for (int l = top; l >= 0; --l) {
         const double din = c->dims[l], dout = c->dims[l + 1];
         if (l > 0 && c->skinny) {
@@ -356,19 +366,23 @@ void build_slots(mlp_ctx* c) {
         // W in+out (+ bf16 copy), and m, v in+out with an adaptive rule
         const double wb = 8 + (c->bf16 ? 2 : 0) + mv;
         const double f = 2.0 * B * din * dout, b = B * din * e + B * dout * e + din * dout * wb;
-        if (l == 0 && c->head && tail_fused(c))
+        if (l == 0 && head && tail_fused(c))
             add(std::string(kind) + "_tn_" + upd + "_l0+" + tail_name, f + tail_flops, b + tail_bytes);
         else
             add(std::string(kind) + "_tn_" + upd + "_l" + std::to_string(l), f, b);
     }
-    if (c->head && !tail_fused(c)) add(tail_name, tail_flops, tail_bytes);
+    if (head && !tail_fused(c)) add(tail_name, tail_flops, tail_bytes);
+}
+
+void build_slots(mlp_ctx* c) {
+    for (int k = 0; k < kKinds; ++k) build_slot_list(c, k);
 }
 
 // ---------------------------------------------------------------- launches --
 
 struct Runner {
     mlp_ctx* c;
-    int slot = 0;
+    int kind = kStep;
     hipError_t err = hipSuccess;
 
     hipEvent_t ev() {
@@ -394,7 +408,7 @@ struct Runner {
         err = f();
         if (b && e) {
             hipEventRecord(e, c->stream);
-            c->pending.push_back({slot_id, b, e});
+            c->pending.push_back({kind, slot_id, b, e});
         }
     }
 };
@@ -475,7 +489,8 @@ enum class Mode { Forward, Train, Grads };
 // Enqueue the step.  Returns the first HIP error (launches stop there).
 hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, float lr,
                    float* const* dw_out, float* loss_dev) {
-    Runner r{c};
+    Runner r{c, mode != Mode::Forward ? kStep : (labels ? kForwardLoss : kForward)};
+    if (c->profiling) c->prof_kind = r.kind;
     const int L = c->L, B = c->B;
     int slot = 0;
     const void* a_prev;
@@ -705,9 +720,9 @@ mlp_status collect_profile(mlp_ctx* c) {
             keep.push_back(p);
             continue;
         }
-        if (e == hipSuccess && p.slot < (int)c->slots.size()) {
-            c->slots[p.slot].total_ms += ms;
-            c->slots[p.slot].launches += 1;
+        if (e == hipSuccess && p.slot < (int)c->slots[p.kind].size()) {
+            c->slots[p.kind][p.slot].total_ms += ms;
+            c->slots[p.kind][p.slot].launches += 1;
         }
         c->event_pool.push_back(p.beg);
         c->event_pool.push_back(p.end);
@@ -839,7 +854,7 @@ size_t plan_and_carve(mlp_ctx* c, char* base) {
     const size_t oTick = lay.take((max_tickets + 1) * sizeof(unsigned));
     const size_t oRow = lay.take((size_t)B * 4);
     const size_t oLoss = lay.take(16);
-    c->slots.clear();
+    for (auto& v : c->slots) v.clear();
     if (base) {
         for (int l = 0; l < L; ++l) {
             c->W[l] = (float*)(base + oW[l]);
@@ -1357,22 +1372,24 @@ mlp_status mlp_profile_enable(mlp_ctx* c, int32_t enable) {
 mlp_status mlp_profile_reset(mlp_ctx* c) {
     if (!c) return MLP_ERR_ARG;
     collect_profile(c);
-    for (Slot& s : c->slots) {
-        s.total_ms = 0;
-        s.launches = 0;
-    }
+    for (auto& v : c->slots)
+        for (Slot& s : v) {
+            s.total_ms = 0;
+            s.launches = 0;
+        }
     return MLP_OK;
 }
 
-int32_t mlp_profile_slots(const mlp_ctx* c) { return c ? (int32_t)c->slots.size() : 0; }
+int32_t mlp_profile_slots(const mlp_ctx* c) { return c ? (int32_t)c->slots[c->prof_kind].size() : 0; }
 
 mlp_status mlp_profile_read(mlp_ctx* c, int32_t idx, char* name, size_t name_len, double* total_ms,
                             int64_t* launches, double* flops, double* bytes) {
     if (!c) return MLP_ERR_ARG;
     c->err.clear();
-    if (idx < 0 || idx >= (int32_t)c->slots.size()) return set_err(c, MLP_ERR_ARG, "slot %d out of range", idx);
+    const std::vector<Slot>& slots = c->slots[c->prof_kind];
+    if (idx < 0 || idx >= (int32_t)slots.size()) return set_err(c, MLP_ERR_ARG, "slot %d out of range", idx);
     collect_profile(c);
-    const Slot& s = c->slots[idx];
+    const Slot& s = slots[idx];
     if (name && name_len) {
         std::strncpy(name, s.name.c_str(), name_len - 1);
         name[name_len - 1] = 0;

@@ -48,6 +48,11 @@ class Workload:
     def classes(self) -> int:
         return self.dims[-1]
 
+    def forward_flops(self) -> int:
+        """2*M*N*K summed over the forward products of one pass."""
+        B, d, L = self.batch, self.dims, self.n_layers
+        return sum(2 * B * d[l] * d[l + 1] for l in range(L))
+
     def gemm_flops(self) -> int:
         """2*M*N*K summed over the forward, dX and dW products of one step."""
         B, d, L = self.batch, self.dims, self.n_layers

@@ -416,6 +416,16 @@ def test_profile_slots(torch_dev):
     names = [r["name"] for r in net.profile_read()]
     assert names == ["mfma_f32_nn_relu_mask_l0", "mfma_f32_nn_store_l1", "softmax_xent",
                      "mfma_f32_nt_mask_l1", "mfma_f32_tn_sgd_l1", "mfma_f32_tn_sgd_l0"], names
+    # forward passes (without and with a loss) are sequences of their own
+    net.profile_reset()
+    net.forward(xd)
+    torch.cuda.synchronize()    # a forward without a loss returns once enqueued
+    rows = net.profile_read()
+    assert [r["name"] for r in rows] == ["mfma_f32_nn_relu_mask_l0", "mfma_f32_nn_store_l1"]
+    assert all(r["launches"] == 1 for r in rows)
+    net.forward(xd, td)
+    assert [r["name"] for r in net.profile_read()] == ["mfma_f32_nn_relu_mask_l0", "mfma_f32_nn_store_l1",
+                                                       "softmax_xent"]
     net.close()
 
 
@@ -685,3 +695,30 @@ def test_checkpoint_preflight_changes_nothing(torch_dev):
         assert torch.equal(u, w)
     for n in (src, other, same):
         n.close()
+
+
+# ---------------------------------------------------------------- inference --
+
+@pytest.mark.parametrize("name", ["mnist_b1024", "wide_f32", "wide_bf16", "skinny_b8"])
+def test_forward_logits_parity(torch_dev, name):
+    """Forward only (the inference path): logits of the workload's batch
+    against the oracle's forward, per-tensor gate as for the gradients, with
+    the GPU's ReLU choices adopted inside the rounding band only."""
+    from mlp_gemm_softmax_amd import binding
+    torch, dev = torch_dev
+    w = synth.WORKLOADS[name]
+    _announce(f"forward parity {name}")
+    Ws = synth.workload_weights(w)
+    x, t, _ = synth.workload_batch(w, 0)
+    net = make_net(w.dims, w.batch, w.precision, Ws, dev)
+    xd, = P.to_dev([x], dev)
+    logits = torch.empty((w.batch, w.dims[-1]), dtype=torch.float32, device=dev)
+    net.forward_async(xd, logits)
+    torch.cuda.synchronize()
+    masks = [net.read_state(binding.STATE_MASK, l).cpu().numpy() for l in range(1, net.n_layers)]
+    ref = mlp_oracle.forward(x, Ws, kink_choice=masks, kink_beta=mlp_oracle.kink_betas(w.dims, w.precision))
+    P.check_masks({"fwd": ref}, w.batch, w.dims, w.precision, name)
+    err, scale = P.rel_max(logits.cpu().numpy(), ref["logits"])
+    gtol = P.GRAD_TOL[w.precision]
+    assert err <= gtol * scale, f"{name} logits: {err:.3e} > {gtol} * {scale:.3e}"
+    net.close()
