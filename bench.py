@@ -42,6 +42,9 @@ def parse():
                          "(inference of the same network)")
     ap.add_argument("--optimizer", choices=["sgd", "adam", "laprop"], default="sgd",
                     help="update rule of the step (Adam/LaProp: beta1 0.9, beta2 0.999, eps 1e-8)")
+    ap.add_argument("--tune", type=int, default=0, metavar="R",
+                    help="before timing, let the library choose tile shapes and K splits by timing "
+                         "candidates over R steps each (mlp_tune); 0 = the planner's defaults")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--profile-steps", type=int, default=None,
@@ -303,6 +306,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     torch.cuda.synchronize()
+    if args.tune > 0:
+        t0 = time.perf_counter()
+        net.tune(*batches[0], args.tune)
+        print(f"[bench] mlp_tune over {args.tune} steps per candidate: {time.perf_counter() - t0:.1f} s",
+              file=sys.stderr, flush=True)
 
     logits = torch.empty((w.batch, w.dims[-1]), dtype=torch.float32, device=dev)
 
@@ -355,7 +363,7 @@ def main():
         "data": "synthetic (seeded; MNIST-shaped uniform [0,1) pixels or N(0,1) features, uniform class ids)",
         "config": {"workload": w.name, "dims": list(w.dims), "batch": w.batch, "lr": w.lr,
                    "precision": w.precision, "fresh_batch_per_step": w.fresh_batch,
-                   "optimizer": args.optimizer, "mode": args.mode},
+                   "optimizer": args.optimizer, "mode": args.mode, "tuned": args.tune > 0},
         "achieved_tflops": round(flops * steps_per_s / 1e12, 4),
         "step_flops": flops,
         "final_loss": final_loss,

@@ -229,6 +229,20 @@ mlp_status mlp_checkpoint_info(const void* src, size_t bytes, int32_t* n_layers,
  * Synchronises the context's stream before returning. */
 mlp_status mlp_load_checkpoint(mlp_ctx* ctx, const void* src, size_t bytes);
 
+/* Choose launch plans by measurement (README "Contents": MEGANEURA_TUNE and
+ * tune_with, a bounded per-shape search): for every product of the step, the
+ * tile shape and K split among a small fixed set, each timed over `repeats`
+ * steps (1..100) on this batch (device x [B, d0], labels [B, C]) with
+ * per-launch events; a candidate replaces the current plan only when the
+ * step gets at least 2% faster.  The timed steps use SGD with lr = 0, so
+ * finite weights and any optimizer state are unchanged.  Candidates stay
+ * within the workspace planned at creation; the plans the fused output
+ * layer depends on are kept, and skinny-batch sessions have nothing to
+ * choose.  Synchronises the stream.  A tuned context stays deterministic
+ * from step to step, but its sums may be ordered differently from an
+ * untuned one (other tile shapes or K splits).  Refuses stream capture. */
+mlp_status mlp_tune(mlp_ctx* ctx, const float* x, const float* labels, int32_t repeats);
+
 /* Copy an intermediate of the last step or forward to device memory `dst`
  * (see mlp_state_kind for shapes; `layer` is 1..n_layers-1 for ACT/MASK). */
 mlp_status mlp_read_state(mlp_ctx* ctx, int32_t which, int32_t layer, void* dst);

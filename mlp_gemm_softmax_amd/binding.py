@@ -46,6 +46,7 @@ SIGNATURES = {
                                        _c.POINTER(_c.c_int32), _c.POINTER(_c.c_int32),
                                        _c.POINTER(_c.c_int64)]),
     "mlp_load_checkpoint": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_size_t]),
+    "mlp_tune": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int32]),
     "mlp_set_optimizer": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_float, _c.c_float, _c.c_float,
                                      _c.c_void_p, _c.c_size_t]),
     "mlp_profile_enable": (_c.c_int, [_c.c_void_p, _c.c_int32]),
@@ -231,6 +232,13 @@ class Mlp:
                                       ctypes.c_void_p(logits.data_ptr()),
                                       ctypes.c_void_p(_ptr(labels)), loss_p))
         return logits, (self._loss.value if loss_p is not None else None)
+
+    def tune(self, x, labels, repeats: int = 3):
+        """Choose tile shapes and K splits by timing them on this batch."""
+        self._dev_f32(x, (self.batch, self.dims[0]))
+        self._dev_f32(labels, (self.batch, self.dims[-1]))
+        self._check(lib().mlp_tune(self._h, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(labels.data_ptr()),
+                                   int(repeats)))
 
     def forward_async(self, x, logits):
         """Logits of batch x into the given device buffer; enqueue only."""

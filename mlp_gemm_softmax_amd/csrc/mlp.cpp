@@ -116,6 +116,7 @@ struct mlp_ctx {
     void* dz[2] = {};
     float* partials = nullptr;
     unsigned* tickets = nullptr;
+    size_t partial_cap = 0, ticket_cap = 0;   // elements / counters the plans may use
     unsigned* xent_ticket = nullptr;
     float* rowloss = nullptr;
     float* loss_slot = nullptr;
@@ -850,6 +851,8 @@ size_t plan_and_carve(mlp_ctx* c, char* base) {
     const size_t oDlb = c->bf16 ? lay.take((size_t)B * C * 2) : 0;
     const size_t oDz0 = lay.take((size_t)B * max_hidden * e);
     const size_t oDz1 = lay.take((size_t)B * max_hidden * e);
+    c->partial_cap = max_partial;
+    c->ticket_cap = max_tickets;
     const size_t oPart = lay.take(max_partial * 4);
     const size_t oTick = lay.take((max_tickets + 1) * sizeof(unsigned));
     const size_t oRow = lay.take((size_t)B * 4);
@@ -1326,6 +1329,169 @@ mlp_status mlp_load_checkpoint(mlp_ctx* c, const void* src, size_t bytes) {
     if (mom) c->opt_t = h.step;
     c->params_set = (1u << c->L) - 1u;
     c->poisoned = false;
+    return MLP_OK;
+}
+
+// ---------------------------------------------------------------- tuning --
+// A bounded search over launch plans (the README's MEGANEURA_TUNE /
+// tune_with): for each product, the large-tile bf16 kernel with K split 1, 2
+// or 4, the tiled kernels' 128x128 / 128x64 / 64x64 tiles with K split 1..8,
+// and for the under-filled f32 products the small-product kernel's 4, 8 or
+// 16 waves on 32x16 or 32x32 tiles -- every candidate within the buffers the
+// context planned at creation.  Plans that the fused output layer relies on
+// are kept.
+namespace {
+
+std::vector<GemmPlan> gemm_candidates(const mlp_ctx* c, int M, int N, int K, bool kvec_ok, bool big_ok,
+                                      const GemmPlan& cur) {
+    std::vector<GemmPlan> out;
+    auto fits = [&](const GemmPlan& g) {
+        if (partial_elems(g, M, N) > c->partial_cap) return false;
+        if (g.splits > 1 && g.cfg != TileCfg::T256x256 && g.small_waves == 0 &&
+            (size_t)g.tiles_m * g.tiles_n > c->ticket_cap)
+            return false;
+        return true;
+    };
+    auto same = [](const GemmPlan& a, const GemmPlan& b) {
+        return a.cfg == b.cfg && a.splits == b.splits && a.small_waves == b.small_waves && a.kchunk == b.kchunk;
+    };
+    auto push = [&](const GemmPlan& g) {
+        if (!fits(g)) return;
+        for (const GemmPlan& o : out)
+            if (same(o, g)) return;
+        out.push_back(g);
+    };
+    push(cur);
+    auto split = [&](GemmPlan g, int s, int bk) {
+        int kchunk = (K + s - 1) / s;
+        kchunk = (kchunk + bk - 1) / bk * bk;
+        s = (K + kchunk - 1) / kchunk;
+        g.splits = s;
+        g.kchunk = s > 1 ? kchunk : std::max(K, 1);
+        g.grid = g.tiles_m * g.tiles_n * s;
+        return g;
+    };
+    if (c->bf16 && big_ok) {
+        for (int s : {1, 2, 4}) {
+            GemmPlan g;
+            g.cfg = TileCfg::T256x256;
+            g.tiles_m = (M + 255) / 256;
+            g.tiles_n = (N + 255) / 256;
+            g.vec = 8;
+            if (s > 1 && K / s < 512) continue;
+            push(split(g, s, 64));
+        }
+    }
+    const int bk = c->bf16 ? 64 : 32, kmin = c->bf16 ? 256 : 128;
+    for (TileCfg cfg : {TileCfg::T128x128, TileCfg::T128x64, TileCfg::T64x64}) {
+        int bm, bn;
+        tile_shape(cfg, &bm, &bn);
+        for (int s : {1, 2, 4, 8}) {
+            if (s > 1 && K / s < kmin) continue;
+            GemmPlan g;
+            g.cfg = cfg;
+            g.tiles_m = (M + bm - 1) / bm;
+            g.tiles_n = (N + bn - 1) / bn;
+            g.vec = kvec_ok ? (c->bf16 ? 8 : 4) : 1;
+            push(split(g, s, bk));
+        }
+    }
+    if (!c->bf16 && cur.small_waves > 0) {
+        for (int nw : {4, 8, 16})
+            for (TileCfg cfg : {TileCfg::T32x16, TileCfg::T32x32}) {
+                GemmPlan g;
+                g.cfg = cfg;
+                g.small_waves = nw;
+                g.splits = 1;
+                g.kchunk = std::max(K, 1);
+                g.tiles_m = (M + 31) / 32;
+                g.tiles_n = cfg == TileCfg::T32x16 ? (N + 15) / 16 : (N + 31) / 32;
+                g.grid = g.tiles_m * g.tiles_n;
+                g.vec = kvec_ok ? 4 : 1;
+                push(g);
+            }
+    }
+    return out;
+}
+
+}  // namespace
+
+mlp_status mlp_tune(mlp_ctx* c, const float* x, const float* labels, int32_t repeats) {
+    mlp_status st = check_ready(c);
+    if (st != MLP_OK) return st;
+    if (!x || !aligned16(x)) return set_err(c, MLP_ERR_ARG, "x must be a 16-byte aligned device pointer");
+    if (!labels || !aligned16(labels))
+        return set_err(c, MLP_ERR_ARG, "labels must be a 16-byte aligned device pointer");
+    if (repeats < 1 || repeats > 100) return set_err(c, MLP_ERR_ARG, "repeats must lie in 1..100");
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(c->stream, &cs);
+    if (e != hipSuccess) return hip_fail(c, e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone) return set_err(c, MLP_ERR_ARG, "tuning cannot run under stream capture");
+    if (c->skinny) return MLP_OK;   // one streaming pass per product: nothing to choose
+    // Timed steps are SGD steps with lr = 0: W - 0 * dW leaves every finite
+    // weight as it is and no optimizer state is touched.
+    const int opt = c->opt;
+    const bool prof = c->profiling;
+    c->opt = MLP_OPT_SGD;
+    e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, "mlp_tune");
+    collect_profile(c);
+    auto step_ms = [&](double* ms) -> hipError_t {
+        c->profiling = false;
+        hipError_t he = enqueue(c, Mode::Train, x, labels, 0.f, nullptr, nullptr);   // warm-up
+        c->profiling = true;
+        for (auto& v : c->slots)
+            for (Slot& sl : v) sl.total_ms = 0, sl.launches = 0;
+        for (int i = 0; i < repeats && he == hipSuccess; ++i)
+            he = enqueue(c, Mode::Train, x, labels, 0.f, nullptr, nullptr);
+        if (he == hipSuccess) he = hipStreamSynchronize(c->stream);
+        collect_profile(c);
+        double t = 0;
+        for (const Slot& sl : c->slots[kStep]) t += sl.total_ms;
+        *ms = t / repeats;
+        return he;
+    };
+    const int L = c->L, B = c->B;
+    for (int l = 0; l < L && e == hipSuccess; ++l) {
+        const int din = c->dims[l], dout = c->dims[l + 1];
+        const int vq = c->bf16 ? 8 : 4;
+        const bool wide = din % vq == 0 && dout % vq == 0;
+        struct Item {
+            GemmPlan* g;
+            int M, N, K;
+            bool big;
+            bool used;
+        } items[3] = {
+            {&c->fwd[l], B, dout, din, gemm_bf16_big_fits(Layout::NN, B, dout, din, din, dout),
+             !(c->head && l == L - 1) && !(head_fused(c) && l == L - 2)},
+            {&c->dx[l], B, din, dout, gemm_bf16_big_fits(Layout::NT, B, din, dout, dout, dout),
+             l > 0 && !(c->head && l == L - 1)},
+            {&c->dw[l], din, dout, B, gemm_bf16_big_fits(Layout::TN, din, dout, B, din, dout),
+             !(c->head && l == L - 1) && !(tail_fused(c) && l == 0)},
+        };
+        for (Item& it : items) {
+            if (!it.used || e != hipSuccess) continue;
+            const std::vector<GemmPlan> cands = gemm_candidates(c, it.M, it.N, it.K, wide, it.big, *it.g);
+            if (cands.size() < 2) continue;
+            GemmPlan best = *it.g;
+            double best_ms = 0;
+            e = step_ms(&best_ms);
+            for (size_t i = 1; i < cands.size() && e == hipSuccess; ++i) {
+                *it.g = cands[i];
+                double ms = 0;
+                e = step_ms(&ms);
+                if (e == hipSuccess && ms < 0.98 * best_ms) {   // a clear win only
+                    best = cands[i];
+                    best_ms = ms;
+                }
+            }
+            *it.g = best;
+        }
+    }
+    c->opt = opt;
+    c->profiling = prof;
+    if (e != hipSuccess) return hip_fail(c, e, "mlp_tune");
+    build_slots(c);   // plan changes can change which launches are fused
     return MLP_OK;
 }
 

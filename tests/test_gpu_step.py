@@ -722,3 +722,34 @@ def test_forward_logits_parity(torch_dev, name):
     gtol = P.GRAD_TOL[w.precision]
     assert err <= gtol * scale, f"{name} logits: {err:.3e} > {gtol} * {scale:.3e}"
     net.close()
+
+
+# ------------------------------------------------------------------- tuning --
+
+@pytest.mark.parametrize("dims,B,precision", [((200, 300, 36), 64, "f32"),
+                                              ((320, 2080, 40), 512, "f32"),
+                                              ((1024, 2048, 1000), 2048, "bf16"),
+                                              ((784, 128, 10), 1024, "f32")])
+def test_tuned_plans_keep_parity(torch_dev, dims, B, precision):
+    """After mlp_tune the weights are unchanged, and the step with the chosen
+    plans still passes the oracle's gates and is repeatable bit for bit."""
+    torch, dev = torch_dev
+    _announce(f"tune dims={dims} B={B} {precision}")
+    Ws = synth.make_weights(dims, "glorot", seed=61)
+    x, t, _ = synth.make_batch(B, dims[0], dims[-1], "normal", seed=62)
+    net = make_net(dims, B, precision, Ws, dev)
+    xd, td = P.to_dev([x, t], dev)
+    before = [w.clone() for w in net.read_params()]
+    net.tune(xd, td, 2)
+    for u, w in zip(net.read_params(), before):
+        assert torch.equal(u, w)
+    loss, dws, dl, masks = P.gpu_grads(net, xd, td)
+    loss_b, dws_b, dl_b, _ = P.gpu_grads(net, xd, td)
+    assert loss == loss_b and all(np.array_equal(a, b) for a, b in zip(dws, dws_b))
+    ref = P.oracle_step(x, t, Ws, 0.05, dims, precision, masks)
+    P.check_masks(ref, B, dims, precision, "tuned")
+    P.check_grads(loss, dws, dl, ref, precision, "tuned")
+    loss2, W_new, masks2 = P.gpu_train(net, xd, td, 0.05)
+    ref2 = P.oracle_step(x, t, Ws, 0.05, dims, precision, masks2)
+    P.check_update(loss2, W_new, Ws, ref2, precision, "tuned")
+    net.close()
