@@ -60,11 +60,15 @@ def parse():
 
 
 def source_digest():
-    """sha256 over the HIP/C++ sources of the library (kernel identity)."""
+    """sha256 over the HIP/C++ sources of the library (kernel identity):
+    source files only, so that build artefacts or editor files beside them
+    do not change it."""
     import glob
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "mlp_gemm_softmax_amd", "csrc", "*"))):
+    csrc = os.path.join(ROOT, "mlp_gemm_softmax_amd", "csrc")
+    files = [f for ext in ("hip", "hpp", "cpp", "h") for f in glob.glob(os.path.join(csrc, f"*.{ext}"))]
+    for f in sorted(files):
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode())
             h.update(fh.read())
@@ -228,7 +232,7 @@ def summarize(outdir, w, steps, warmup):
     roof = line["roofline"]
     dom = [i for i, (nm, _) in enumerate(slots) if nm == roof["kernel"]][0]
     lines = [f"# rocprofv3 summary: workload `{w}`", "",
-             f"Kernel source digest (sha256 of mlp_gemm_softmax_amd/csrc/*): `{source_digest()}`", "",
+             f"Kernel source digest (sha256 of the .hip/.hpp/.cpp/.h files in mlp_gemm_softmax_amd/csrc): `{source_digest()}`", "",
              "Commands (repository root on one MI355X; OUT is the output folder):", "",
              "```", TRACE_CMD.format(w=w, s=steps, wu=warmup),
              PMC_CMD.format(c="FETCH_SIZE", d="fetch", w=w),

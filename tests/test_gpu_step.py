@@ -204,6 +204,8 @@ EDGE_CASES = [
     ((128, 10), 300, "f32"),
     ((784, 128, 10), 7, "f32"),
     ((4100, 64, 8), 16, "f32"),      # skinny, many K splits
+    ((2052, 36, 20), 3, "f32"),      # skinny, batch <= 4, ragged last K chunk, one column group
+    ((8, 1028, 12), 16, "f32"),      # skinny, K shorter than one wave's rows, 4-column last group
     ((33, 70, 17, 10), 37, "bf16"),
     ((100, 31, 7), 5, "bf16"),
     ((72, 200, 1000), 48, "bf16"),
