@@ -234,11 +234,11 @@ size_t partial_elems(const GemmPlan& g, int M, int N) {
 SkinnyPlan plan_skinny_nn(int N, int K, int B) {
     (void)B;
     SkinnyPlan s;
-    // 64 output columns per workgroup of 16 waves (one such workgroup per
-    // CU); K splits only while the grid still fits one round of workgroups
-    // (measured: 8-wave workgroups with deeper splits stream no faster).
+    // 64 output columns per workgroup of 8 waves; K splits only while the
+    // grid still fits one round of workgroups (measured at batch 8: 16-wave
+    // workgroups and deeper splits stream slower).
     const int ncg = (N + 63) / 64;
-    s.waves = 16;
+    s.waves = 8;
     int sp = std::max(1, std::min(256 / ncg, K / 256));
     int kchunk = (K + sp - 1) / sp;
     kchunk = (kchunk + 15) / 16 * 16;
@@ -640,7 +640,7 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
                 SkinnyLaunch sl;
                 sl.layout = Layout::NT;
                 sl.epi = upd_epi;
-                sl.grid = adaptive ? (din + 15) / 16 : c->sdx[l].grid;
+                sl.grid = c->sdx[l].grid;
                 sl.waves = 8;
                 sl.fused_update = true;
                 SkinnyParams sp{};
@@ -798,7 +798,7 @@ size_t plan_and_carve(mlp_ctx* c, char* base) {
                 max_partial = std::max(max_partial, (size_t)c->sfwd[l].splits * B * dout);
                 max_tickets = std::max(max_tickets, (size_t)c->sfwd[l].tickets);
             }
-            c->sdx[l].grid = (din + 31) / 32;
+            c->sdx[l].grid = (din + 15) / 16;   // 16 rows of W per workgroup
             c->sdw[l].grid = ((dout + 1023) / 1024) * ((din + skinny_tn_rows() - 1) / skinny_tn_rows());
             continue;
         }
