@@ -161,6 +161,25 @@ def softmax_xent(logits, labels) -> Dict:
             "dlogits": dlogits, "lse": lse[:, 0], "p": p}
 
 
+def probabilities(logits) -> np.ndarray:
+    """Class probabilities of each row for inference (the deployed forward of
+    the README's train-to-deploy flow): the softmax that the loss above
+    normalises with, p[b,c] = exp(z[b,c] - lse_b), lse_b = mu_b +
+    log sum_c exp(z[b,c] - mu_b), mu_b = max_c z[b,c] (row max subtracted
+    before exponentiating, as for the loss)."""
+    z = _f64(logits)
+    mu = z.max(axis=1, keepdims=True)
+    lse = mu + np.log(np.exp(z - mu).sum(axis=1, keepdims=True))
+    return np.exp(z - lse)
+
+
+def forward_probabilities(x, weights: Sequence, kink_choice: Optional[Sequence] = None,
+                          kink_beta: Optional[Sequence[float]] = None) -> Dict:
+    """The forward pass followed by ``probabilities`` of its logits."""
+    fwd = forward(x, weights, kink_choice=kink_choice, kink_beta=kink_beta)
+    return {"fwd": fwd, "probs": probabilities(fwd["logits"])}
+
+
 # --------------------------------------------------------------------------
 # Backward (the derivative the README's autodiff produces for this graph).
 # --------------------------------------------------------------------------

@@ -175,6 +175,60 @@ def test_ce_shift_invariance_and_overflow():
         np.testing.assert_allclose(shifted["dlogits"], base["dlogits"], atol=1e-14)
 
 
+def _probs_pins_pass(fn, golden):
+    """Pins of the inference probabilities: the closed-form row, a batch whose
+    rows differ (catches a softmax over the wrong axis), rows summing to 1,
+    shift invariance without overflow, and agreement with the p that the
+    loss routine normalises with."""
+    g = golden("closed_forms.txt")
+    ok = True
+    with np.errstate(all="ignore"):
+        # z = (0, ln2, ln3): e^z = (1, 2, 3), p = (1/6, 1/3, 1/2)
+        p = fn(np.array([g["row_z"]]))
+        ok &= p.shape == (1, 3) and np.allclose(p[0], [1 / 6, 1 / 3, 1 / 2], rtol=0, atol=1e-15)
+        # two rows: (0, ln2, ln3) and (ln3, 0, 0) -> (3/5, 1/5, 1/5)
+        z2 = np.array([g["row_z"], [g["row_z"][2], 0.0, 0.0]])
+        p2 = fn(z2)
+        ok &= np.allclose(p2, [[1 / 6, 1 / 3, 1 / 2], [3 / 5, 1 / 5, 1 / 5]], rtol=0, atol=1e-15)
+        r = _rng(31)
+        z = r.standard_normal((8, 1000)) * 4
+        p = fn(z)
+        ok &= bool(np.all(p >= 0)) and np.max(np.abs(p.sum(1) - 1)) < 1e-13
+        # z + 1000 is rounded to ulp(1000)/2 ~ 6e-14, which moves p by at most twice that
+        shifted = fn(z + 1000.0)
+        ok &= bool(np.all(np.isfinite(shifted))) and np.allclose(shifted, p, rtol=0, atol=1e-12)
+        t = np.eye(1000)[r.integers(0, 1000, 8)]
+        ok &= np.allclose(p, O.softmax_xent(z, t)["p"], rtol=0, atol=1e-15)
+    return bool(ok)
+
+
+def test_probabilities_pins(golden):
+    assert _probs_pins_pass(O.probabilities, golden)
+
+
+@pytest.mark.parametrize("kind", ["no_shift", "batch_axis", "no_exp", "unnormalised"])
+def test_probabilities_pins_reject_planted_mistakes(golden, kind):
+    def mutant(z):
+        z = np.asarray(z, dtype=np.float64)
+        if kind == "no_shift":
+            return np.exp(z) / np.exp(z).sum(1, keepdims=True)
+        if kind == "batch_axis":
+            mu = z.max(0, keepdims=True)
+            return np.exp(z - mu) / np.exp(z - mu).sum(0, keepdims=True)
+        if kind == "no_exp":
+            return z / z.sum(1, keepdims=True)
+        return np.exp(z - z.max(1, keepdims=True))
+    assert not _probs_pins_pass(mutant, golden)
+
+
+def test_forward_probabilities_composes_forward_and_softmax():
+    r = _rng(12)
+    x = r.random((5, 6))
+    Ws = [r.standard_normal((6, 4)), r.standard_normal((4, 3))]
+    out = O.forward_probabilities(x, Ws)
+    np.testing.assert_array_equal(out["probs"], O.probabilities(O.forward(x, Ws)["logits"]))
+
+
 @pytest.mark.parametrize("soft", [False, True])
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_finite_differences_tiny_mlp(seed, soft):
