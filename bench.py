@@ -37,9 +37,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--mode", choices=["train", "forward"], default="train",
+    ap.add_argument("--mode", choices=["train", "forward", "probs"], default="train",
                     help="train: the training step (the headline metric); forward: logits only "
-                         "(inference of the same network)")
+                         "(inference of the same network); probs: class probabilities (inference)")
     ap.add_argument("--optimizer", choices=["sgd", "adam", "laprop"], default="sgd",
                     help="update rule of the step (Adam/LaProp: beta1 0.9, beta2 0.999, eps 1e-8)")
     ap.add_argument("--tune", type=int, default=0, metavar="R",
@@ -323,6 +323,8 @@ def main():
             xb, tb = batches[(offset + i) % n_batches]
             if args.mode == "forward":
                 net.forward_async(xb, logits)
+            elif args.mode == "probs":
+                net.forward_probs(xb, logits)
             else:
                 net.train_step_async(xb, tb, w.lr, loss_dev)
 
@@ -349,10 +351,11 @@ def main():
         file=sys.stderr, flush=True)
 
     steps_per_s = args.steps / el
-    fwd = args.mode == "forward"
+    fwd = args.mode in ("forward", "probs")
     flops = w.forward_flops() if fwd else w.gemm_flops()
     out = {
-        "metric": ("MLP forward passes/sec (logits, inference) + achieved TFLOP/s, 1 GPU" if fwd else
+        "metric": (f"MLP forward passes/sec ({'probabilities' if args.mode == 'probs' else 'logits'}, "
+                   "inference) + achieved TFLOP/s, 1 GPU" if fwd else
                    "MLP train steps/sec + achieved TFLOP/s (fraction of MFMA/HBM roofline), 1 GPU"),
         "value": round(steps_per_s, 3),
         "unit": "forward passes/s" if fwd else "steps/s",

@@ -142,6 +142,18 @@ mlp_status mlp_read_params(mlp_ctx* ctx, int32_t layer, float* dst);
 mlp_status mlp_forward(mlp_ctx* ctx, const float* x, float* logits,
                        const float* labels, float* loss);
 
+/* Forward pass to class probabilities, for inference (the deployed model of
+ * the README's train-to-deploy flow): probs[b][c] = exp(z[b][c] - mu_b) /
+ * sum_c exp(z[b][c] - mu_b) of the logits z, mu_b = max_c z[b][c] -- the
+ * normalisation the loss uses.  x: device float32 [B, d0]; probs: device
+ * float32 [B, C], written in stream order (nothing waits).  In strict-f32
+ * sessions whose logits product runs on 32 x 16 small-product tiles and
+ * C <= 16, the product's epilogue normalises each row itself; otherwise one
+ * row-softmax launch follows the forward.  Both pointers must be 16-byte
+ * aligned (MLP_ERR_ARG).  The logits kept for mlp_forward are not updated
+ * on the fused path. */
+mlp_status mlp_forward_probs(mlp_ctx* ctx, const float* x, float* probs);
+
 /* One training step: forward, mean softmax-CE, backward and the update of
  * every layer (W_l <- W_l - lr * dW_l, or the rule mlp_set_optimizer chose),
  * all gradients taken at the pre-update weights.  x: device float32 [B, d0]; labels: device float32

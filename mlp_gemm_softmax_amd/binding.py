@@ -30,6 +30,7 @@ SIGNATURES = {
     "mlp_destroy": (None, [_c.c_void_p]),
     "mlp_set_params": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_void_p]),
     "mlp_read_params": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_void_p]),
+    "mlp_forward_probs": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "mlp_forward": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p,
                                _c.POINTER(_c.c_float)]),
     "mlp_train_step": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_float,
@@ -239,6 +240,17 @@ class Mlp:
         self._dev_f32(labels, (self.batch, self.dims[-1]))
         self._check(lib().mlp_tune(self._h, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(labels.data_ptr()),
                                    int(repeats)))
+
+    def forward_probs(self, x, probs=None):
+        """Class probabilities of batch x (softmax of the logits); enqueue only."""
+        B, C = self.batch, self.dims[-1]
+        self._dev_f32(x, (B, self.dims[0]))
+        if probs is None:
+            probs = self.torch.empty((B, C), dtype=self.torch.float32, device=self.device)
+        self._dev_f32(probs, (B, C))
+        self._check(lib().mlp_forward_probs(self._h, ctypes.c_void_p(x.data_ptr()),
+                                            ctypes.c_void_p(probs.data_ptr())))
+        return probs
 
     def forward_async(self, x, logits):
         """Logits of batch x into the given device buffer; enqueue only."""

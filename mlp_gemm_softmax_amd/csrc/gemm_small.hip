@@ -236,6 +236,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_small16_kernel(GemmParams p, Tai
 #pragma unroll
         for (int w = 1; w < NW; ++w) v += red[w][rbk][l];
         const int col = n0 + (l & 15);
+        if constexpr (EPI == Epi::Softmax) {
+            // One column tile holds every class (N <= 16): the 16 lanes of a
+            // DPP row hold the same four rows, columns 0..15, so each row's
+            // max and sum are 16-lane reductions (columns past N masked).
+            const bool cok = col < p.N;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = m0 + 16 * rbk + 4 * (l >> 4) + e;
+                const float z = cok ? v[e] : -INFINITY;
+                const float mx = row16_max(z);
+                const float ex = cok ? expf(z - mx) : 0.f;
+                const float se = row16_sum(ex);
+                if (row < p.M && cok) p.C[(int64_t)row * p.ldc + col] = ex / se;
+            }
+        } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int row = m0 + 16 * rbk + 4 * (l >> 4) + e;
@@ -249,6 +264,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_small16_kernel(GemmParams p, Tai
                     epilogue<EPI>(p, row, col, v[e]);
                 }
             }
+        }
         }
     }
     if constexpr (HEAD) {
@@ -292,6 +308,19 @@ template <int NW, Layout LAY, Epi EPI>
 hipError_t go_vec(const GemmLaunch& L, const GemmParams& p, hipStream_t st) {
     const bool t16 = L.cfg == TileCfg::T32x16;
     return L.vec == 4 ? go<NW, LAY, 4, EPI>(p, L.grid, t16, st) : go<NW, LAY, 1, EPI>(p, L.grid, t16, st);
+}
+
+template <int NW>
+hipError_t go_softmax(const GemmLaunch& L, const GemmParams& p, hipStream_t st) {
+    const TailParams none{};
+    const HeadParams nohead{};
+    if (L.vec == 4)
+        hipLaunchKernelGGL((gemm_small16_kernel<NW, Layout::NN, 4, Epi::Softmax, false, false>), dim3(L.grid),
+                           dim3(NW * 64), 0, st, p, none, nohead);
+    else
+        hipLaunchKernelGGL((gemm_small16_kernel<NW, Layout::NN, 1, Epi::Softmax, false, false>), dim3(L.grid),
+                           dim3(NW * 64), 0, st, p, none, nohead);
+    return hipGetLastError();
 }
 
 template <int NW>
@@ -356,6 +385,18 @@ hipError_t launch_gemm_small_tail(const GemmLaunch& L, const GemmParams& p, int 
 
 hipError_t launch_gemm_small(const GemmLaunch& L, const GemmParams& p, int waves, hipStream_t st) {
     if (L.bf16 || p.Cb) return hipErrorInvalidValue;
+    if (L.epi == Epi::Softmax) {
+        // probabilities straight from the logits product: one 16-column tile
+        if (L.cfg != TileCfg::T32x16 || L.layout != Layout::NN || p.N > 16 || p.N < 1 ||
+            L.grid != (p.M + 31) / 32)
+            return hipErrorInvalidValue;
+        switch (waves) {
+        case 4: return go_softmax<4>(L, p, st);
+        case 8: return go_softmax<8>(L, p, st);
+        case 16: return go_softmax<16>(L, p, st);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (waves) {
     case 4: return dispatch<4>(L, p, st);
     case 8: return dispatch<8>(L, p, st);

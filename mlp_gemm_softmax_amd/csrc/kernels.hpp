@@ -22,7 +22,7 @@ enum class Layout : int { NN = 0, NT = 1, TN = 2 };
 //   Sgd      W = W - lr * v, optional bf16 copy    (dW + in-place update)
 //   Grad     C = v                                  (dW, no update)
 //   Adapt    W, m, v <- Adam or LaProp step with g = v (optional bf16 copy)
-enum class Epi : int { Store = 0, ReluMask = 1, MaskMul = 2, Sgd = 3, Grad = 4, Adapt = 5 };
+enum class Epi : int { Store = 0, ReluMask = 1, MaskMul = 2, Sgd = 3, Grad = 4, Adapt = 5, Softmax = 6 };
 
 // Scalars of an adaptive update step (Adam or LaProp, see optim_rule.hpp).
 constexpr int kOptAdam = 1;
@@ -117,6 +117,11 @@ struct SkinnyLaunch {
 };
 hipError_t launch_skinny(const SkinnyLaunch& L, const SkinnyParams& p, hipStream_t s);
 int skinny_tn_rows();   // rows of W per dW+SGD workgroup
+
+// ---- class probabilities (inference) -----------------------------------
+// probs[b][c] = exp(z[b][c] - max_c z[b]) / sum_c exp(z[b][c] - max_c z[b]),
+// one wavefront per row, fixed-order wavefront reductions.
+hipError_t launch_softmax_rows(const float* logits, float* probs, int B, int C, hipStream_t st);
 
 // ---- softmax cross-entropy -------------------------------------------------
 struct XentParams {

@@ -89,8 +89,9 @@ struct Pending {
 };
 
 // Launch sequences that are timed separately: a training step (or
-// gradients), a forward pass, a forward pass with the loss.
-enum SlotKind { kStep = 0, kForward = 1, kForwardLoss = 2, kKinds = 3 };
+// gradients), a forward pass, a forward pass with the loss, a forward pass
+// to class probabilities.
+enum SlotKind { kStep = 0, kForward = 1, kForwardLoss = 2, kForwardProbs = 3, kKinds = 4 };
 
 }  // namespace
 
@@ -291,6 +292,14 @@ bool xent_fused(const mlp_ctx* c) {
     return g.cfg == TileCfg::T256x256 && g.splits > 1 && splitk_xent_fits(c->dims[c->L], g.splits);
 }
 
+// Whether a forward pass to probabilities normalises inside the logits
+// product (f32 small-product kernel, every class in one 16-column tile),
+// else a row-softmax launch follows the product.
+bool probs_fused(const mlp_ctx* c) {
+    const GemmPlan& g = c->fwd[c->L - 1];
+    return !c->bf16 && !c->skinny && g.small_waves > 0 && g.cfg == TileCfg::T32x16 && c->dims[c->L] <= 16;
+}
+
 // Slot names and algorithmic work of one launch sequence, in launch order.
 void build_slot_list(mlp_ctx* c, int sk) {
     std::vector<Slot>& slots = c->slots[sk];
@@ -315,17 +324,22 @@ void build_slot_list(mlp_ctx* c, int sk) {
     if (c->bf16) add("cast_x_bf16", 0, (double)B * c->dims[0] * 6);
     const int C = c->dims[L];
     const int Lf = head ? L - 1 : L;   // layers whose forward is a plain GEMM
-    const bool xf = xent_fused(c) && sk != kForward;   // the loss launch adds the logits' partials
+    const bool xf = xent_fused(c) && (sk == kStep || sk == kForwardLoss);   // the loss launch adds the logits' partials
+    const bool pf = sk == kForwardProbs && probs_fused(c);
     for (int l = 0; l < Lf; ++l) {
         const double M = B, N = c->dims[l + 1], K = c->dims[l];
         const bool last = l == L - 1;
         // a product that leaves its split-K sums to the loss kernel has no
         // compulsory output of its own
         const double out = last ? (xf ? 0.0 : M * N * 4) : M * N * (e + 1);
-        const char* what = last ? (xf ? "partials" : "store") : "relu_mask";
+        const char* what = last ? (xf ? "partials" : (pf ? "softmax" : "store")) : "relu_mask";
         add(std::string(kind) + "_nn_" + what + "_l" + std::to_string(l), 2 * M * N * K, M * K * e + K * N * e + out);
     }
     if (sk == kForward) return;
+    if (sk == kForwardProbs) {
+        if (!pf) add("softmax_probs", 0, (double)B * C * 8);   // logits in, probabilities out
+        return;
+    }
     int top = L - 1;
     double tail_flops = 0, tail_bytes = 0;
     std::string tail_name;
@@ -489,8 +503,8 @@ enum class Mode { Forward, Train, Grads };
 
 // Enqueue the step.  Returns the first HIP error (launches stop there).
 hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, float lr,
-                   float* const* dw_out, float* loss_dev) {
-    Runner r{c, mode != Mode::Forward ? kStep : (labels ? kForwardLoss : kForward)};
+                   float* const* dw_out, float* loss_dev, float* probs = nullptr) {
+    Runner r{c, mode != Mode::Forward ? kStep : (probs ? kForwardProbs : (labels ? kForwardLoss : kForward))};
     if (c->profiling) c->prof_kind = r.kind;
     const int L = c->L, B = c->B;
     int slot = 0;
@@ -563,7 +577,11 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
         } else {
             // with labels the loss kernel adds a split logits product's partials
             const bool partials_only = last && labels && xent_fused(c);
+            const bool to_probs = last && probs && probs_fused(c);
             r.run(slot++, [&] {
+                if (to_probs)
+                    return run_gemm(c, c->fwd[l], Layout::NN, Epi::Softmax, a_prev, K, Wop, N, B, N, K, probs,
+                                    nullptr, nullptr, 0.f);
                 float* Cf = last ? c->logits : (c->bf16 ? nullptr : (float*)c->act[l + 1]);
                 bf16_t* Cb = (!last && c->bf16) ? (bf16_t*)c->act[l + 1] : nullptr;
                 return run_gemm(c, c->fwd[l], Layout::NN, last ? Epi::Store : Epi::ReluMask, a_prev, K,
@@ -572,6 +590,10 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
             });
         }
         if (!last) a_prev = c->act[l + 1];
+    }
+    if (mode == Mode::Forward && probs) {
+        if (!probs_fused(c)) r.run(slot++, [&] { return launch_softmax_rows(c->logits, probs, B, C, c->stream); });
+        return r.err;
     }
     if (mode == Mode::Forward && !labels) return r.err;
 
@@ -1019,6 +1041,16 @@ mlp_status mlp_forward(mlp_ctx* c, const float* x, float* logits, const float* l
                            c->stream);
     if (e != hipSuccess) return hip_fail(c, e, "mlp_forward");
     if (labels && loss) return read_loss(c, loss);
+    return MLP_OK;
+}
+
+mlp_status mlp_forward_probs(mlp_ctx* c, const float* x, float* probs) {
+    mlp_status st = check_ready(c);
+    if (st != MLP_OK) return st;
+    if (!x || !aligned16(x)) return set_err(c, MLP_ERR_ARG, "x must be a 16-byte aligned device pointer");
+    if (!probs || !aligned16(probs)) return set_err(c, MLP_ERR_ARG, "probs must be a 16-byte aligned device pointer");
+    const hipError_t e = enqueue(c, Mode::Forward, x, nullptr, 0.f, nullptr, nullptr, probs);
+    if (e != hipSuccess) return hip_fail(c, e, "mlp_forward_probs");
     return MLP_OK;
 }
 

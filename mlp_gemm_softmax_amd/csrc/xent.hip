@@ -367,7 +367,106 @@ __global__ __launch_bounds__(kThreads) void xent_stream(XentParams p) {
     if (last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
 }
 
+// Class probabilities of each row (inference): the same normalisation as the
+// loss, p = exp(z - mu) / S.  Each thread keeps its VPT values of the row in
+// registers (every load in flight at once), so the row is read once:
+// rows of up to 64 * VPT classes take one wavefront each, wider rows (up to
+// kThreads * VPT) one workgroup each, with the four wavefronts' partial max
+// and sum combined through LDS in wave order.  Still wider rows stream the
+// row three times (max, sum, write).
+template <int VPT, bool GROUP>
+__global__ __launch_bounds__(kThreads) void softmax_rows(const float* __restrict__ logits,
+                                                         float* __restrict__ probs, int B, int C) {
+    __shared__ float s_red[2][kThreads / kWave];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int kWaves = kThreads / kWave;
+    const int width = GROUP ? kThreads : kWave;           // threads per row
+    const int t = GROUP ? (int)threadIdx.x : lane;
+    const int rows_per_group = GROUP ? 1 : kWaves;
+    for (int row = blockIdx.x * rows_per_group + (GROUP ? 0 : wave); row < B; row += gridDim.x * rows_per_group) {
+        const float* z = logits + (int64_t)row * C;
+        float v[VPT];
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int c = t + i * width;
+            v[i] = c < C ? z[c] : -INFINITY;
+        }
+        float mx = v[0];
+#pragma unroll
+        for (int i = 1; i < VPT; ++i) mx = fmaxf(mx, v[i]);
+        mx = wave_max(mx);
+        if constexpr (GROUP) {
+            if (lane == 0) s_red[0][wave] = mx;
+            __syncthreads();
+            mx = s_red[0][0];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, s_red[0][w]);
+        }
+        float se = 0.f;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            v[i] = t + i * width < C ? expf(v[i] - mx) : 0.f;
+            se += v[i];
+        }
+        se = wave_sum(se);
+        if constexpr (GROUP) {
+            if (lane == 0) s_red[1][wave] = se;
+            __syncthreads();
+            se = s_red[1][0];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) se += s_red[1][w];
+            __syncthreads();   // s_red is reused by the next row
+        }
+        float* p = probs + (int64_t)row * C;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int c = t + i * width;
+            if (c < C) p[c] = v[i] / se;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void softmax_rows_stream(const float* __restrict__ logits,
+                                                                float* __restrict__ probs, int B, int C) {
+    const int lane = threadIdx.x & 63;
+    const int rows_per_group = kThreads / kWave;
+    for (int row = blockIdx.x * rows_per_group + (threadIdx.x >> 6); row < B; row += gridDim.x * rows_per_group) {
+        const float* z = logits + (int64_t)row * C;
+        float mx = -INFINITY;
+        for (int c = lane; c < C; c += kWave) mx = fmaxf(mx, z[c]);
+        mx = wave_max(mx);
+        float se = 0.f;
+        for (int c = lane; c < C; c += kWave) se += expf(z[c] - mx);
+        se = wave_sum(se);
+        float* p = probs + (int64_t)row * C;
+        for (int c = lane; c < C; c += kWave) p[c] = expf(z[c] - mx) / se;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_softmax_rows(const float* logits, float* probs, int B, int C, hipStream_t st) {
+    if (B < 1 || C < 1 || !logits || !probs) return hipErrorInvalidValue;
+    const int rows_per_group = kThreads / kWave;
+    const int wave_grid = std::min((B + rows_per_group - 1) / rows_per_group, 4 * kMaxGroups);
+    const int group_grid = std::min(B, 4 * kMaxGroups);
+#define MLP_SOFTMAX(V, G, GRID) hipLaunchKernelGGL((softmax_rows<V, G>), dim3(GRID), dim3(kThreads), 0, st, logits, probs, B, C)
+    // wide rows with few of them: a workgroup per row keeps the CUs busy
+    const bool group = C > 16 * kWave || (B < 512 && C > 4 * kWave);
+    if (!group) {
+        if (C <= kWave) MLP_SOFTMAX(1, false, wave_grid);
+        else if (C <= 4 * kWave) MLP_SOFTMAX(4, false, wave_grid);
+        else MLP_SOFTMAX(16, false, wave_grid);
+    } else if (C <= 8 * kThreads) {
+        MLP_SOFTMAX(8, true, group_grid);
+    } else if (C <= 32 * kThreads) {
+        MLP_SOFTMAX(32, true, group_grid);
+    } else {
+        hipLaunchKernelGGL(softmax_rows_stream, dim3(wave_grid), dim3(kThreads), 0, st, logits, probs, B, C);
+    }
+#undef MLP_SOFTMAX
+    return hipGetLastError();
+}
 
 hipError_t launch_xent(const XentParams& p, int* grid_out, hipStream_t s) {
     int grid;

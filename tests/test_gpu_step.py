@@ -726,6 +726,94 @@ def test_forward_logits_parity(torch_dev, name):
     net.close()
 
 
+# ------------------------------------------------------ class probabilities --
+
+PROBS_CASES = [
+    # (dims, B, precision): the workloads' shapes and edges of both paths
+    ((784, 128, 10), 1024, "f32"),      # logits tile normalises in its epilogue
+    ((784, 128, 10), 32, "f32"),
+    ((33, 70, 17, 10), 37, "f32"),      # three layers, widths not multiples of 4
+    ((128, 10), 300, "f32"),            # no hidden layer
+    ((1, 1, 1), 1, "f32"),              # one class: p = 1
+    ((784, 128, 20), 64, "f32"),        # C > 16: row-softmax launch
+    ((64, 260, 36), 12, "f32"),         # skinny kernels
+    ((1024, 512, 1000), 512, "f32"),    # wide rows
+    ((72, 200, 1000), 48, "bf16"),      # bf16 operands
+    ((1024, 2048, 1000), 2048, "bf16"),  # large bf16 tiles with split-K logits
+    ((64, 4096), 8, "f32"),             # few wide rows: a workgroup per row
+    ((16, 9000), 3, "f32"),             # rows wider than the registers hold: streamed
+    ((40, 600), 700, "f32"),            # many rows of 600 classes: a wavefront per row
+]
+
+
+@pytest.mark.parametrize("dims,B,precision", PROBS_CASES)
+def test_forward_probs_parity(torch_dev, dims, B, precision):
+    """Inference probabilities against the oracle's softmax of its forward
+    logits.  With every logit within delta = tol * max|z_ref| of the oracle
+    (the forward gate), each probability is within a factor e^(+-2 delta) of
+    the oracle's, so |dp| <= (e^(2 delta) - 1) max p_ref, plus the float32
+    rounding of the normalisation ((C + 4) units of 2^-24).  Rows sum to 1
+    within that rounding; two calls agree bitwise."""
+    from mlp_gemm_softmax_amd import binding
+    torch, dev = torch_dev
+    _announce(f"forward probs {dims} B={B} {precision}")
+    rng = np.random.default_rng([7, len(dims), B])
+    Ws = [rng.uniform(-1, 1, (a, b)).astype(np.float32) * np.float32(math.sqrt(6.0 / (a + b)))
+          for a, b in zip(dims[:-1], dims[1:])]
+    x = rng.standard_normal((B, dims[0])).astype(np.float32)
+    net = make_net(dims, B, precision, Ws, dev)
+    xd, = P.to_dev([x], dev)
+    net.profile(True)
+    net.profile_reset()
+    probs = net.forward_probs(xd)
+    again = net.forward_probs(xd)
+    torch.cuda.synchronize()
+    names = [r["name"] for r in net.profile_read()]
+    net.profile(False)
+    masks = [net.read_state(binding.STATE_MASK, l).cpu().numpy() for l in range(1, net.n_layers)]
+    ref = mlp_oracle.forward_probabilities(x, Ws, kink_choice=masks,
+                                           kink_beta=mlp_oracle.kink_betas(dims, precision))
+    P.check_masks({"fwd": ref["fwd"]}, B, dims, precision, "probs")
+    p = probs.cpu().numpy()
+    assert np.array_equal(p, again.cpu().numpy()), "two calls differ"
+    C = dims[-1]
+    delta = P.GRAD_TOL[precision] * float(np.max(np.abs(ref["fwd"]["logits"])))
+    rnd = (C + 4) * 2.0 ** -24
+    bound = math.expm1(2 * delta) * float(np.max(ref["probs"])) + rnd
+    err = float(np.max(np.abs(p - ref["probs"])))
+    assert err <= bound, f"probs: {err:.3e} > {bound:.3e}"
+    assert np.all(p >= 0)
+    assert float(np.max(np.abs(p.astype(np.float64).sum(1) - 1.0))) <= 2 * rnd
+    # the last launch of the sequence is the normalising one; the README
+    # MLP's 10 classes normalise inside the logits product
+    assert names[-1].endswith("softmax_l" + str(len(dims) - 2)) or names[-1] == "softmax_probs", names
+    if dims == (784, 128, 10):
+        assert names[-1] == "mfma_f32_nn_softmax_l1", names
+    net.close()
+
+
+def test_forward_probs_argument_errors(torch_dev):
+    from mlp_gemm_softmax_amd import binding
+    torch, dev = torch_dev
+    dims, B = (784, 128, 10), 32
+    Ws = synth.workload_weights(synth.WORKLOADS["mnist_b32"])
+    net = make_net(dims, B, "f32", Ws, dev)
+    x = torch.zeros((B, dims[0]), dtype=torch.float32, device=dev)
+    buf = torch.zeros(B * dims[-1] + 4, dtype=torch.float32, device=dev)
+    L = binding.lib()
+    st = L.mlp_forward_probs(net._h, ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(buf.data_ptr() + 4))
+    assert st == binding.MLP_ERR_ARG
+    st = L.mlp_forward_probs(net._h, ctypes.c_void_p(x.data_ptr()), None)
+    assert st == binding.MLP_ERR_ARG
+    st = L.mlp_forward_probs(net._h, None, ctypes.c_void_p(buf.data_ptr()))
+    assert st == binding.MLP_ERR_ARG
+    # the context still works
+    p = net.forward_probs(x)
+    torch.cuda.synchronize()
+    assert abs(float(p.sum().item()) - B) < 1e-4
+    net.close()
+
+
 # ------------------------------------------------------------------- tuning --
 
 @pytest.mark.parametrize("dims,B,precision", [((200, 300, 36), 64, "f32"),
