@@ -75,10 +75,10 @@ def source_digest():
     return h.hexdigest()
 
 
-def recorded_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` from the committed counter runs
-    (profiles/traffic.json), or None when absent or when the kernel sources
-    changed since the counters were taken."""
+def recorded_counters(workload, kernel):
+    """The committed counter record of `kernel` (profiles/traffic.json), or
+    None when absent or when the kernel sources changed since the counters
+    were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -87,7 +87,14 @@ def recorded_traffic(workload, kernel):
         return None
     if not rec or rec.get("source_sha") != source_digest() or rec.get("kernel") != kernel:
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter runs, or
+    None (see recorded_counters)."""
+    rec = recorded_counters(workload, kernel)
+    return rec.get("bytes_per_launch") if rec else None
 
 
 def roofline(rows, precision, steps):
@@ -151,6 +158,9 @@ TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace_
              "python3 bench.py --workload {w} --steps {s} --warmup {wu} --no-cpu-baseline")
 PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d OUT/{d}_{w} -o {w} -- python3 bench.py "
            "--workload {w} --steps 2 --warmup 1 --profile-steps 1 --no-cpu-baseline --calib-copy-mb 256")
+MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_{p} SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE"
+N_SIMDS = 256 * 4     # MI355X: 256 CUs of 4 SIMDs
+N_XCDS = 8            # GRBM_GUI_ACTIVE is summed over the 8 XCDs
 
 
 def _csv(path):
@@ -229,6 +239,28 @@ def summarize(outdir, w, steps, warmup):
         _, per = _per_slot(vals, n, 2)
         counters[cname] = [v * scale[cname] * 1024 for v in per]   # bytes per launch
 
+    # optional third pass: matrix-core busy cycles, MFMA ops and active cycles
+    mfma = None
+    mpath = os.path.join(outdir, f"mfma_{w}", f"{w}_counter_collection.csv")
+    if os.path.exists(mpath):
+        rows = _csv(mpath)
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        prec = "BF16" if line["config"]["precision"] == "bf16" else "F32"
+        per = {}
+        for cname in ("SQ_VALU_MFMA_BUSY_CYCLES", f"SQ_INSTS_VALU_MFMA_MOPS_{prec}", "GRBM_GUI_ACTIVE"):
+            vals = [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows if r["Counter_Name"] == cname]
+            per[cname] = _per_slot(vals, n, 2)[1]
+        spans = {}
+        for r in rows:   # duration of each dispatch, from the same run
+            spans[r["Dispatch_Id"]] = (r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        dur = _per_slot([spans[k] for k in sorted(spans, key=int)], n, 2)[1]
+        mfma = []
+        for i in range(n):
+            cyc = per["GRBM_GUI_ACTIVE"][i] / N_XCDS
+            mfma.append({"busy": per["SQ_VALU_MFMA_BUSY_CYCLES"][i] / (cyc * N_SIMDS) if cyc else 0.0,
+                         "flops": per[f"SQ_INSTS_VALU_MFMA_MOPS_{prec}"][i] * 512,
+                         "clock_ghz": cyc / (dur[i] * 1e3) if dur[i] else 0.0, "dur_us": dur[i]})
+
     roof = line["roofline"]
     dom = [i for i, (nm, _) in enumerate(slots) if nm == roof["kernel"]][0]
     lines = [f"# rocprofv3 summary: workload `{w}`", "",
@@ -236,7 +268,11 @@ def summarize(outdir, w, steps, warmup):
              "Commands (repository root on one MI355X; OUT is the output folder):", "",
              "```", TRACE_CMD.format(w=w, s=steps, wu=warmup),
              PMC_CMD.format(c="FETCH_SIZE", d="fetch", w=w),
-             PMC_CMD.format(c="WRITE_SIZE", d="write", w=w), "```", "",
+             PMC_CMD.format(c="WRITE_SIZE", d="write", w=w)]
+    if mfma is not None:
+        p = "BF16" if line["config"]["precision"] == "bf16" else "F32"
+        lines.append(PMC_CMD.format(c=MFMA_COUNTERS.format(p=p), d="mfma", w=w).replace(" --calib-copy-mb 256", ""))
+    lines += ["```", "",
              f"bench: {line['value']} steps/s, {line['ms_per_step']} ms/step, "
              f"{line['achieved_tflops']} TFLOP/s; dominant kernel `{roof['kernel']}` "
              f"{roof['achieved']} {roof['unit']} = {roof['frac']:.4f} of {roof['peak']} ({roof['bound']})", "",
@@ -250,6 +286,19 @@ def summarize(outdir, w, steps, warmup):
         kn = names[i]
         lines.append(f"| {nm} | `{kn}` | {ev:.2f} | {trace_us[i]:.2f} | "
                      f"{counters['FETCH_SIZE'][i] / 1e6:.2f} | {counters['WRITE_SIZE'][i] / 1e6:.2f} |")
+    if mfma is not None:
+        lines += ["", "## Matrix cores per launch slot", "",
+                  "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); MFMA "
+                  "GFLOP = SQ_INSTS_VALU_MFMA_MOPS x 512; clock = GRBM_GUI_ACTIVE / 8 over the dispatch's "
+                  "duration in the same run, shown for launches of at least 100 us (the counter window "
+                  "adds cycles outside the dispatch, which only long launches amortise).", "",
+                  "| slot | MFMA busy | MFMA GFLOP (counter) | clock GHz |",
+                  "|---|---|---|---|"]
+        for i, (nm, _) in enumerate(slots):
+            clk = f"{mfma[i]['clock_ghz']:.2f}" if mfma[i]["dur_us"] >= 100 else "-"
+            lines.append(f"| {nm} | {mfma[i]['busy']:.3f} | {mfma[i]['flops'] / 1e9:.2f} | {clk} |")
+        lines += ["", f"Dominant slot `{roof['kernel']}`: {mfma[dom]['flops'] / 1e9:.2f} GFLOP counted on the "
+                      f"matrix cores against {roof['algorithmic_flops'] / 1e9:.2f} GFLOP of GEMM work (2MNK)."]
     lines += ["", "## kernel_stats (whole run)", "", "| kernel | calls | avg us | % |", "|---|---|---|---|"]
     for r in stats[:12]:
         kn = _short(r["Name"])[:90]
@@ -264,6 +313,8 @@ def summarize(outdir, w, steps, warmup):
     except (OSError, ValueError):
         allrec = {}
     allrec[w] = {"kernel": roof["kernel"], "source_sha": source_digest(),
+                 "mfma_busy": round(mfma[dom]["busy"], 4) if mfma else None,
+                 "clock_ghz": round(mfma[dom]["clock_ghz"], 3) if mfma and mfma[dom]["dur_us"] >= 100 else None,
                  "bytes_per_launch": round(counters["FETCH_SIZE"][dom] + counters["WRITE_SIZE"][dom]),
                  "fetch_bytes": round(counters["FETCH_SIZE"][dom]),
                  "write_bytes": round(counters["WRITE_SIZE"][dom]),
@@ -346,6 +397,10 @@ def main():
     net.profile(False)
     roof = roofline(rows, w.precision, pk)
     roof["traffic"] = recorded_traffic(w.name, roof["kernel"])
+    rec = recorded_counters(w.name, roof["kernel"]) or {}
+    for key in ("mfma_busy", "clock_ghz"):   # matrix-core busy share and clock from the counter runs
+        if rec.get(key) is not None:
+            roof[key] = rec[key]
     print("[bench] per-launch (ms avg): " + ", ".join(
         f"{r['name']}={r['total_ms'] / max(r['launches'], 1):.4f}" for r in rows),
         file=sys.stderr, flush=True)
