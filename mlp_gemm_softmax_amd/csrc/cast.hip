@@ -12,10 +12,10 @@ __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict_
     for (size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < n; i += stride) {
         if (i + 4 <= n) {
             const float4 v = *reinterpret_cast<const float4*>(src + i);
-            ushort4 o;
-            o.x = f32_to_bf16(v.x); o.y = f32_to_bf16(v.y);
-            o.z = f32_to_bf16(v.z); o.w = f32_to_bf16(v.w);
-            *reinterpret_cast<ushort4*>(dst + i) = o;
+            uint2 o;
+            o.x = pack2_bf16(v.x, v.y);
+            o.y = pack2_bf16(v.z, v.w);
+            *reinterpret_cast<uint2*>(dst + i) = o;
         } else {
             for (size_t j = i; j < n; ++j) dst[j] = f32_to_bf16(src[j]);
         }

@@ -34,8 +34,8 @@ typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ u32x2v pack_bf16x4(float4v v) {
     u32x2v r;
-    r[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    r[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    r[0] = pack2_bf16(v[0], v[1]);
+    r[1] = pack2_bf16(v[2], v[3]);
     return r;
 }
 

@@ -245,8 +245,8 @@ __global__ __launch_bounds__(kThreads) void splitk_xent_kernel(XentParams p, con
                 *reinterpret_cast<float4v*>(p.dlogits + base + c) = g;
                 if (p.dlogits_b) {
                     uint2 h;
-                    h.x = (uint32_t)f32_to_bf16(g[0]) | ((uint32_t)f32_to_bf16(g[1]) << 16);
-                    h.y = (uint32_t)f32_to_bf16(g[2]) | ((uint32_t)f32_to_bf16(g[3]) << 16);
+                    h.x = pack2_bf16(g[0], g[1]);
+                    h.y = pack2_bf16(g[2], g[3]);
                     *reinterpret_cast<uint2*>(p.dlogits_b + base + c) = h;
                 }
             }
