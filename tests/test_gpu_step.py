@@ -726,6 +726,82 @@ def test_forward_logits_parity(torch_dev, name):
     net.close()
 
 
+# ------------------------------------------------- bf16 rounding (exactly) --
+
+def _rne_bf16(v):
+    """float32 -> bfloat16 -> float32, round to nearest, ties to even
+    (integer form: add 0x7fff plus the lowest kept bit, drop 16 bits)."""
+    u = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def _rounding_values(n, seed):
+    """Positive normal float32 values whose dropped 16 bits sit below, at and
+    above the halfway point, with even and odd kept mantissas."""
+    rng = np.random.default_rng(seed)
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    hi = (rng.integers(0x3E00, 0x4200, n).astype(np.uint32) & 0xFFFE) | (np.arange(n, dtype=np.uint32) & 1)
+    return ((hi << 16) | lows[np.arange(n) % len(lows)]).view(np.float32)
+
+
+def test_bf16_rounding_is_nearest_even(torch_dev):
+    """A7 precision conversions, bit for bit: the cast of x, the bf16 copy of
+    W and the activation written by the ReLU epilogue all round to nearest
+    even.  Each net is built so that the stored activation is exactly one
+    rounded value: a1 = rne(x0) * 1, a1 = 1 * rne(w), and a1 = rne(1 + d) with
+    1 + d exact in float32 (d a bfloat16 value); the products and their
+    float32 sums are exact, so any other rounding shows."""
+    from mlp_gemm_softmax_amd import binding
+    torch, dev = torch_dev
+    B, H = 64, 64
+    dims = (8, H, 8)
+    W2 = np.zeros((H, 8), dtype=np.float32)
+
+    def act(x, W1):
+        net = make_net(dims, B, "bf16", [W1, W2], dev)
+        xd, = P.to_dev([x], dev)
+        logits = torch.empty((B, 8), dtype=torch.float32, device=dev)
+        net.forward_async(xd, logits)
+        a = net.read_state(binding.STATE_ACT, 1).cpu().numpy()
+        net.close()
+        return a
+
+    # the cast of x: x[b][0] = v_b, W1[0][:] = 1
+    v = _rounding_values(B, 1)
+    x = np.zeros((B, 8), dtype=np.float32)
+    x[:, 0] = v
+    W1 = np.zeros((8, H), dtype=np.float32)
+    W1[0, :] = 1.0
+    a = act(x, W1)
+    assert np.array_equal(a, np.repeat(_rne_bf16(v)[:, None], H, axis=1)), "cast of x"
+    # the bf16 copy of W: x[b][0] = 1, W1[0][c] = w_c
+    w = _rounding_values(H, 2)
+    x = np.zeros((B, 8), dtype=np.float32)
+    x[:, 0] = 1.0
+    W1 = np.zeros((8, H), dtype=np.float32)
+    W1[0, :] = w
+    a = act(x, W1)
+    assert np.array_equal(a, np.repeat(_rne_bf16(w)[None, :], B, axis=0)), "bf16 copy of W"
+    # the epilogue: x[b][0] = x[b][1] = 1, W1[0][c] = 1, W1[1][c] = d_c with
+    # d_c = m * 2^-9 .. m * 2^-12 (bf16-exact), so 1 + d_c falls below, on
+    # and above the halfway points between bfloat16 neighbours of 1
+    m = np.arange(H, dtype=np.float32)
+    d = (m % 16) * np.float32(2.0) ** -(9 + (m // 16))
+    x = np.zeros((B, 8), dtype=np.float32)
+    x[:, 0] = 1.0
+    x[:, 1] = 1.0
+    W1 = np.zeros((8, H), dtype=np.float32)
+    W1[0, :] = 1.0
+    W1[1, :] = d
+    assert np.array_equal(_rne_bf16(d), d)
+    a = act(x, W1)
+    want = _rne_bf16(np.float32(1.0) + d)
+    assert np.array_equal(a, np.repeat(want[None, :], B, axis=0)), "ReLU epilogue rounding"
+    # the cases include ties that truncation would get wrong
+    assert np.any(want != (np.float32(1.0) + d).view(np.uint32).__and__(0xFFFF0000).view(np.float32))
+
+
 # ------------------------------------------------------ class probabilities --
 
 PROBS_CASES = [
