@@ -8,8 +8,10 @@ softmax cross-entropy, dX and dW+SGD GEMMs) over one batch of synthetic
 input, through the C ABI.  Inputs are generated from fixed seeds, copied to
 HBM before the timed region, and reused cyclically (the batch-1024 workload
 draws a fresh batch for each of its 100 steps).  W untimed warm-up steps,
-then K steps bracketed by device synchronisations.  After the timed region
-the same K steps run again with per-launch HIP events on the library's
+then K steps bracketed by device synchronisations (asynchronous launches:
+the headline).  Then up to 50 synchronous steps (the loss read back after
+each one) give `sync_ms_per_step`.  After that the same K steps run again
+with per-launch HIP events on the library's
 stream, to price the dominant kernel against its roofline; then the float64
 oracle is timed on the host cores over a bounded sample.  Prints ONE JSON
 line.
@@ -387,6 +389,18 @@ def main():
     el = time.perf_counter() - t0
     final_loss = float(loss_dev.item())
 
+    # Synchronous steps (mlp_train_step: the loss read back to the host after
+    # every step), a bounded number of them, reported beside the headline.
+    sync_ms = None
+    if args.mode == "train":
+        ks = min(args.steps, 50)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(ks):
+            xb, tb = batches[i % n_batches]
+            net.train_step(xb, tb, w.lr)
+        sync_ms = (time.perf_counter() - t0) / ks * 1e3
+
     # Per-launch HIP events on the library's stream, same step sequence.
     pk = args.profile_steps or args.steps
     net.profile(True)
@@ -427,6 +441,7 @@ def main():
                    "precision": w.precision, "fresh_batch_per_step": w.fresh_batch,
                    "optimizer": args.optimizer, "mode": args.mode, "tuned": args.tune > 0},
         "achieved_tflops": round(flops * steps_per_s / 1e12, 4),
+        "sync_ms_per_step": round(sync_ms, 5) if sync_ms is not None else None,
         "step_flops": flops,
         "final_loss": final_loss,
         "roofline": roof,
