@@ -448,6 +448,11 @@ def main():
     }
     if not args.no_cpu_baseline and not fwd:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s, args.optimizer)
+        if w.name in ("mnist_b32", "mnist_b1024", "skinny_b8"):
+            # the same oracle restricted to one BLAS thread, over a shorter sample
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                out["cpu_baseline_1thread"] = cpu_baseline(w, min(args.cpu_budget_s, 8.0), args.optimizer)
     net.close()
     print(json.dumps(out), flush=True)
 
