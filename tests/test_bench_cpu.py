@@ -102,3 +102,79 @@ def test_recorded_traffic_needs_the_same_sources_and_kernel(tmp_path, monkeypatc
     assert bench.recorded_traffic("missing", "slot") is None
     (csrc / "k.hip").write_text("kernel changed")
     assert bench.recorded_traffic("w", "slot") is None
+
+
+def _write_csv(path, header, rows):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(header)
+        wr.writerows(rows)
+
+
+def test_summarize_prices_counters_per_slot(tmp_path, monkeypatch):
+    """The profile summary from synthetic rocprofv3 output: per-slot grouping
+    (a split-K epilogue joins its product), copy-calibrated HBM bytes, and
+    the matrix-core busy share and clock of the dominant slot."""
+    root = tmp_path / "root"
+    (root / "mlp_gemm_softmax_amd" / "csrc").mkdir(parents=True)
+    (root / "mlp_gemm_softmax_amd" / "csrc" / "k.hip").write_text("kernel")
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    out = tmp_path / "out"
+    out.mkdir()
+    w = "toy"
+    ka = "void mlp::(anonymous namespace)::ka(mlp::GemmParams)"
+    kb = "void mlp::(anonymous namespace)::kb(mlp::GemmParams)"
+    fol = "void mlp::(anonymous namespace)::splitk_epilogue_kernel<(mlp::Epi)3>(mlp::GemmParams)"
+    copy = "__amd_rocclr_copyBuffer"
+    line = {"value": 1.0, "ms_per_step": 1.0, "achieved_tflops": 1.0, "config": {"precision": "f32"},
+            "roofline": {"kernel": "slot_b", "achieved": 1.0, "unit": "TFLOP/s", "frac": 0.5, "peak": 157.3,
+                         "bound": "mfma", "algorithmic_flops": 2e9, "algorithmic_bytes": 1e6}}
+    (out / f"bench_{w}.log").write_text("[bench] per-launch (ms avg): slot_a=0.0100, slot_b=0.2000\n"
+                                        + json.dumps(line) + "\n")
+    # three steps in the trace: ka 10 us, kb 150 us + its split-K epilogue 50 us
+    trace, t, d = [], 0, 0
+    for _ in range(3):
+        for name, us in ((ka, 10), (kb, 150), (fol, 50)):
+            d += 1
+            trace.append([d, name, t, t + us * 1000])
+            t += us * 1000 + 500
+    _write_csv(str(out / f"trace_{w}" / f"{w}_kernel_trace.csv"),
+               ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"], trace)
+    _write_csv(str(out / f"trace_{w}" / f"{w}_kernel_stats.csv"), ["Name", "Calls", "AverageNs", "Percentage"],
+               [[kb, 3, 150000, 70.0], [fol, 3, 50000, 20.0], [ka, 3, 10000, 10.0]])
+    # counters: a 256 MiB copy counted as 131072 KiB fetched (scale 2) and 262144 KiB written (scale 1)
+    for cname, d_, copy_kib in (("FETCH_SIZE", "fetch", 131072.0), ("WRITE_SIZE", "write", 262144.0)):
+        rows, i = [[1, copy, cname, copy_kib]], 1
+        for _ in range(2):
+            for name, kib in ((ka, 10.0), (kb, 100.0), (fol, 20.0)):
+                i += 1
+                rows.append([i, name, cname, kib])
+        _write_csv(str(out / f"{d_}_{w}" / f"{w}_counter_collection.csv"),
+                   ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"], rows)
+    # matrix cores: kb busy for 0.6 of 1024 SIMDs x 240000 cycles over 100 us (2.4 GHz)
+    rows, i, t = [], 0, 0
+    for _ in range(2):
+        for name, busy, mops, grbm, us in ((ka, 0.0, 0.0, 8 * 24000.0, 10), (kb, 0.6 * 1024 * 240000, 2e9 / 512,
+                                                                             8 * 200000.0, 100), (fol, 0.0, 0.0, 8 * 40000.0, 20)):
+            i += 1
+            for cname, v in (("SQ_VALU_MFMA_BUSY_CYCLES", busy), ("SQ_INSTS_VALU_MFMA_MOPS_F32", mops),
+                             ("GRBM_GUI_ACTIVE", grbm), ("SQ_BUSY_CU_CYCLES", 1.0)):
+                rows.append([i, name, cname, v, t, t + us * 1000])
+            t += us * 1000 + 1000
+    _write_csv(str(out / f"mfma_{w}" / f"{w}_counter_collection.csv"),
+               ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"], rows)
+
+    bench.summarize(str(out), w, 3, 1)
+    rec = json.loads((root / "profiles" / "traffic.json").read_text())[w]
+    assert rec["kernel"] == "slot_b" and rec["source_sha"] == bench.source_digest()
+    assert rec["fetch_bytes"] == round((100 + 20) * 2.0 * 1024)
+    assert rec["write_bytes"] == round((100 + 20) * 1.0 * 1024)
+    assert rec["bytes_per_launch"] == rec["fetch_bytes"] + rec["write_bytes"]
+    # busy over the slot's cycles (product + epilogue: 240000 per XCD)
+    assert rec["mfma_busy"] == pytest.approx(0.6, abs=1e-4)
+    assert rec["clock_ghz"] == pytest.approx(240000 / 120e3, abs=1e-3)   # 120 us for the slot
+    md = (root / "profiles" / f"{w}.md").read_text()
+    assert "`kb + splitk_epilogue_kernel<(mlp::Epi)3>`" in md
+    assert "| slot_b |" in md and "Matrix cores per launch slot" in md
