@@ -77,6 +77,12 @@ WORKLOADS = {
                           precision="bf16"),
     "skinny_b8": Workload("skinny_b8", (4096, 11008, 4096), 8, "normal",
                           "glorot", 1e-3, 1, False),
+    # One GPU's share of skinny_b8 under 8-way tensor parallelism: W1 split by
+    # columns and W2 by rows (11008 / 8 = 1376 hidden units per GPU).  Run on
+    # one GPU it measures the per-GPU kernels at their real shapes; the
+    # exchange of partial logits between GPUs is not part of it.
+    "skinny_b8_tp8_shard": Workload("skinny_b8_tp8_shard", (4096, 1376, 4096), 8, "normal",
+                                    "glorot", 1e-3, 1, False),
 }
 
 

@@ -138,6 +138,12 @@ def test_parity_skinny_b8(torch_dev):
     _workload_parity(torch_dev, "skinny_b8")
 
 
+def test_parity_skinny_b8_tp8_shard(torch_dev):
+    """One GPU's share of the skinny workload under 8-way tensor parallelism
+    (the per-GPU kernels at their real shapes)."""
+    _workload_parity(torch_dev, "skinny_b8_tp8_shard")
+
+
 # ------------------------------------------------- multi-step trajectories --
 
 def _oracle_trajectory(w, Ws, steps):
