@@ -128,9 +128,12 @@ def cpu_baseline(w, budget_s, rule="sgd"):
     import numpy as np
     from mlp_gemm_softmax_amd import synth
     from oracle import mlp_oracle
+    blas = "BLAS"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = " + ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info})) or blas
     except Exception:
         cores = len(os.sched_getaffinity(0))
     Ws = synth.workload_weights(w)
@@ -150,8 +153,8 @@ def cpu_baseline(w, budget_s, rule="sgd"):
             break
     # batch generation is inside the loop; it is small next to the f64 step
     return {"value": round(n / el, 4), "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n} consecutive training steps ({rule}) of {w.name} (float64 numpy, BLAS threads "
-                      f"{cores}), {el:.1f} s"}
+            "sample": f"{n} consecutive training steps ({rule}) of {w.name} (float64 numpy on {blas}, "
+                      f"BLAS threads {cores}), {el:.1f} s"}
 
 
 # ---------------------------------------------------------------- profiles --
