@@ -679,6 +679,10 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
                 sp.m = adaptive ? c->opt_m[l] : nullptr;
                 sp.v = adaptive ? c->opt_v[l] : nullptr;
                 sp.opt = osc;
+                sp.splits = c->sdx[l].splits;
+                sp.kchunk = c->sdx[l].kchunk;
+                sp.partials = c->partials;
+                sp.tickets = c->tickets;
                 return launch_skinny(sl, sp, c->stream);
             });
             G = out;
@@ -820,7 +824,23 @@ size_t plan_and_carve(mlp_ctx* c, char* base) {
                 max_partial = std::max(max_partial, (size_t)c->sfwd[l].splits * B * dout);
                 max_tickets = std::max(max_tickets, (size_t)c->sfwd[l].tickets);
             }
-            c->sdx[l].grid = (din + 15) / 16;   // 16 rows of W per workgroup
+            {
+                // 16 rows of W per workgroup; the columns split too while the
+                // row groups alone would leave CUs idle (at least 256 columns
+                // per split, a multiple of 32)
+                const int rgroups = (din + 15) / 16;
+                int cs = std::max(1, std::min((512 + rgroups - 1) / rgroups, dout / 256));
+                int kc = (dout + cs - 1) / cs;
+                kc = (kc + 31) / 32 * 32;
+                cs = (dout + kc - 1) / kc;
+                c->sdx[l].splits = cs;
+                c->sdx[l].kchunk = kc;
+                c->sdx[l].grid = rgroups * cs;
+                if (cs > 1 && l > 0) {
+                    max_partial = std::max(max_partial, (size_t)cs * B * din);
+                    max_tickets = std::max(max_tickets, (size_t)rgroups);
+                }
+            }
             c->sdw[l].grid = ((dout + 1023) / 1024) * ((din + skinny_tn_rows() - 1) / skinny_tn_rows());
             continue;
         }

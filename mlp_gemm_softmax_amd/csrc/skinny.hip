@@ -196,17 +196,27 @@ __global__ __launch_bounds__(NW * kWave) void skinny_nn(SkinnyParams p) {
 // are ordinary (cached): one instruction covers 64 bytes of each of 16 rows,
 // and the L2 merges the two halves of every 128-byte line before it goes to
 // HBM (non-temporal stores of half lines measured at half the bandwidth).
+//
+// When W has few rows (K / 16 row groups leave CUs idle), the columns are
+// split too: workgroup (row group, column split cs) covers columns
+// [cs * kchunk, (cs + 1) * kchunk); its dX sums are partial, go to
+// partials [splits][B][K], and the last workgroup of the row group (integer
+// ticket) adds them in split order before the mask.
 template <int NW, int RG, int S, Epi EPI>
 __global__ __launch_bounds__(NW * kWave) void skinny_ntu(SkinnyParams p) {
     __shared__ float4v red[NW - 1][RG][kWave];
+    __shared__ int s_last;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int k0 = blockIdx.x * 16 * RG;
+    const int rgroups = (p.K + 16 * RG - 1) / (16 * RG);
+    const int rg = blockIdx.x % rgroups, cs = blockIdx.x / rgroups;
+    const int k0 = rg * 16 * RG;
     const int i = lane & 15, g = lane >> 4;
     const bool bok = i < p.MB;
-    const int nq = ((p.N + 32 * NW - 1) / (32 * NW)) * 32;   // slice, multiple of 32
-    const int nbeg = wave * nq;
-    const int nend = min(p.N, nbeg + nq);
+    const int cbeg = cs * p.kchunk, cend = min(p.N, cbeg + p.kchunk);
+    const int nq = ((cend - cbeg + 32 * NW - 1) / (32 * NW)) * 32;   // slice, multiple of 32
+    const int nbeg = cbeg + wave * nq;
+    const int nend = min(cend, nbeg + nq);
 
     constexpr bool AD = EPI == Epi::Adapt;
     float4v acc[RG];
@@ -314,12 +324,51 @@ __global__ __launch_bounds__(NW * kWave) void skinny_ntu(SkinnyParams p) {
         for (int r = 0; r < RG; ++r) red[wave - 1][r][lane] = acc[r];
     }
     __syncthreads();
-    if (wave != 0) return;
-    for (int v = 0; v < NW - 1; ++v)
+    if (wave == 0) {
+        for (int v = 0; v < NW - 1; ++v)
 #pragma unroll
-        for (int r = 0; r < RG; ++r) acc[r] += red[v][r][lane];
+            for (int r = 0; r < RG; ++r) acc[r] += red[v][r][lane];
+    }
     // acc[r][e] = out[b = lane%16][k = k0 + 16r + 4*(lane/16) + e]
     const int b = lane & 15;
+    if (p.splits > 1) {
+        if (wave == 0 && b < p.MB) {
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                const int k = k0 + 16 * r + 4 * g;
+                if (k >= p.K) continue;
+                float* dst = p.partials + ((int64_t)cs * p.MB + b) * p.K + k;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) store_coherent(dst + e, acc[r][e]);
+            }
+        }
+        if (!last_arrival(&p.tickets[rg], (unsigned)p.splits, &s_last)) return;
+        if (wave != 0 || b >= p.MB) return;
+        // every split's partial, this workgroup's own included, in split
+        // order; four splits' loads in flight at a time (clamped addresses,
+        // the extra ones dropped)
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            const int k = min(k0 + 16 * r + 4 * g, p.K - 4);
+            float4v sum = {0.f, 0.f, 0.f, 0.f};
+            for (int t0 = 0; t0 < p.splits; t0 += 4) {
+                float x[4][4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float* src = p.partials + ((int64_t)min(t0 + u, p.splits - 1) * p.MB + b) * p.K + k;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[u][e] = load_coherent(src + e);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sum[e] += t0 + u < p.splits ? x[u][e] : 0.f;
+            }
+            acc[r] = sum;
+        }
+    } else if (wave != 0) {
+        return;
+    }
     if (b >= p.MB) return;
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
@@ -456,7 +505,10 @@ hipError_t launch_skinny(const SkinnyLaunch& L, const SkinnyParams& p, hipStream
             // 16 rows of W per workgroup (measured at batch 8 over an
             // 11008 x 4096 W: 64.6 us against 76.8 with 32 rows and 67.5
             // with 64; 16-wave workgroups were slower)
-            if (L.grid != (p.K + 15) / 16) return hipErrorInvalidValue;
+            if (p.splits < 1 || p.kchunk < 1 || (int64_t)p.splits * p.kchunk < p.N ||
+                (int64_t)(p.splits - 1) * p.kchunk >= p.N || L.grid != ((p.K + 15) / 16) * p.splits ||
+                (p.splits > 1 && (!p.partials || !p.tickets)))
+                return hipErrorInvalidValue;
             if (L.epi == Epi::Sgd) return go_ntu<Epi::Sgd>(L, p, s);
             if (L.epi == Epi::Adapt) return go_ntu<Epi::Adapt>(L, p, s);
             if (L.epi == Epi::Grad) return go_ntu<Epi::Grad>(L, p, s);

@@ -42,6 +42,7 @@ EXACT_CASES = [
     ((784, 128, 16), 32, "f32", 2),          # the README MLP's widths, 32x128 tiles
     ((256, 520, 64), 8, "f32", 2),           # skinny-batch kernels, ragged columns
     ((1024, 1100, 260), 16, "f32", 1),       # skinny-batch with K splits
+    ((64, 100, 1040), 8, "f32", 1),          # skinny dX + dW with its columns split, ragged rows and split
     ((320, 2080, 40), 512, "f32", 1),        # tiled NN with split-K, ragged N
     ((2080, 1040, 40), 512, "f32", 1),       # tiled TN and NT with split-K, ragged tiles
     ((64, 32, 8), 8, "f32", 2),              # fused output layer with skinny kernels, tail on its own
@@ -482,6 +483,7 @@ ADAPTIVE_CASES = [
     ((784, 128, 10), 1024, "f32", False),     # fused output layer: head in the forward, tail in dW
     ((64, 32, 8), 8, "f32", True),            # skinny kernels with the fused output layer
     ((256, 520, 64), 8, "f32", False),        # skinny kernels, ragged columns
+    ((64, 100, 1040), 8, "f32", True),        # skinny dX + dW pass with its columns split
     ((33, 70, 17, 10), 37, "f32", False),     # three layers, widths not multiples of 4
     ((120, 136, 24), 256, "bf16", True),      # bf16 operands: the update refreshes the bf16 copy
     ((1024, 2048, 1000), 2048, "bf16", False),  # large bf16 tiles, split-K logits into the loss
