@@ -249,8 +249,9 @@ mlp_status mlp_load_checkpoint(mlp_ctx* ctx, const void* src, size_t bytes);
  * step gets at least 2% faster.  The timed steps use SGD with lr = 0, so
  * finite weights and any optimizer state are unchanged.  Candidates stay
  * within the workspace planned at creation; the plans the fused output
- * layer depends on are kept, and skinny-batch sessions have nothing to
- * choose.  Synchronises the stream.  A tuned context stays deterministic
+ * layer depends on are kept.  Skinny-batch sessions (batch <= 16) choose the
+ * K split of each forward pass and the column split of each fused dX + dW
+ * pass instead.  Synchronises the stream.  A tuned context stays deterministic
  * from step to step, but its sums may be ordered differently from an
  * untuned one (other tile shapes or K splits).  Refuses stream capture. */
 mlp_status mlp_tune(mlp_ctx* ctx, const float* x, const float* labels, int32_t repeats);

@@ -1479,7 +1479,6 @@ mlp_status mlp_tune(mlp_ctx* c, const float* x, const float* labels, int32_t rep
     hipError_t e = hipStreamIsCapturing(c->stream, &cs);
     if (e != hipSuccess) return hip_fail(c, e, "hipStreamIsCapturing");
     if (cs != hipStreamCaptureStatusNone) return set_err(c, MLP_ERR_ARG, "tuning cannot run under stream capture");
-    if (c->skinny) return MLP_OK;   // one streaming pass per product: nothing to choose
     // Timed steps are SGD steps with lr = 0: W - 0 * dW leaves every finite
     // weight as it is and no optimizer state is touched.
     const int opt = c->opt;
@@ -1504,7 +1503,62 @@ mlp_status mlp_tune(mlp_ctx* c, const float* x, const float* labels, int32_t rep
         return he;
     };
     const int L = c->L, B = c->B;
-    for (int l = 0; l < L && e == hipSuccess; ++l) {
+    // Keep a candidate only on a clear win (2%) over the best so far.
+    auto choose = [&](auto* plan, const auto& cands) {
+        auto best = *plan;
+        double best_ms = 0;
+        e = step_ms(&best_ms);
+        for (size_t i = 0; i < cands.size() && e == hipSuccess; ++i) {
+            *plan = cands[i];
+            double ms = 0;
+            e = step_ms(&ms);
+            if (e == hipSuccess && ms < 0.98 * best_ms) {
+                best = cands[i];
+                best_ms = ms;
+            }
+        }
+        *plan = best;
+    };
+    if (c->skinny) {
+        // Skinny sessions: the K splits of each forward pass and the column
+        // splits of each fused dX + dW pass, within the planned workspace.
+        for (int l = 0; l < L && e == hipSuccess; ++l) {
+            const int din = c->dims[l], dout = c->dims[l + 1];
+            std::vector<SkinnyPlan> fc;
+            const int ncg = (dout + 63) / 64;
+            for (int want : {1, 2, 4, 8, 16, 32}) {
+                SkinnyPlan s = c->sfwd[l];
+                int kchunk = (din + want - 1) / want;
+                kchunk = (kchunk + 15) / 16 * 16;
+                const int sp = (din + kchunk - 1) / kchunk;
+                if (sp == c->sfwd[l].splits) continue;
+                if (sp > 1 && ((size_t)sp * B * dout > c->partial_cap || (size_t)ncg > c->ticket_cap)) continue;
+                s.splits = sp;
+                s.kchunk = sp > 1 ? kchunk : din;
+                s.grid = ncg * sp;
+                s.tickets = ncg;
+                fc.push_back(s);
+            }
+            choose(&c->sfwd[l], fc);
+            if (l == 0 || e != hipSuccess) continue;
+            std::vector<SkinnyPlan> xc;
+            const int rgroups = (din + 15) / 16;
+            for (int want : {1, 2, 4, 8, 16}) {
+                SkinnyPlan s = c->sdx[l];
+                int kc = (dout + want - 1) / want;
+                kc = (kc + 31) / 32 * 32;
+                const int cs = (dout + kc - 1) / kc;
+                if (cs == c->sdx[l].splits) continue;
+                if (cs > 1 && ((size_t)cs * B * din > c->partial_cap || (size_t)rgroups > c->ticket_cap)) continue;
+                s.splits = cs;
+                s.kchunk = kc;
+                s.grid = rgroups * cs;
+                xc.push_back(s);
+            }
+            choose(&c->sdx[l], xc);
+        }
+    }
+    for (int l = 0; l < L && e == hipSuccess && !c->skinny; ++l) {
         const int din = c->dims[l], dout = c->dims[l + 1];
         const int vq = c->bf16 ? 8 : 4;
         const bool wide = din % vq == 0 && dout % vq == 0;

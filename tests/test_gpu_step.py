@@ -903,7 +903,8 @@ def test_forward_probs_argument_errors(torch_dev):
 @pytest.mark.parametrize("dims,B,precision", [((200, 300, 36), 64, "f32"),
                                               ((320, 2080, 40), 512, "f32"),
                                               ((1024, 2048, 1000), 2048, "bf16"),
-                                              ((784, 128, 10), 1024, "f32")])
+                                              ((784, 128, 10), 1024, "f32"),
+                                              ((512, 2048, 1040), 8, "f32")])   # skinny: K and column splits
 def test_tuned_plans_keep_parity(torch_dev, dims, B, precision):
     """After mlp_tune the weights are unchanged, and the step with the chosen
     plans still passes the oracle's gates and is repeatable bit for bit."""
