@@ -497,11 +497,24 @@ def test_adaptive_update_parity(torch_dev, rule, dims, B, precision, exact):
     oracle's own gradients.  Before each step the GPU gradients (same
     kernels, no update) pass the gradient gate; the weights after each step
     must lie within the bound derived from that gate and the update rule."""
+    _adaptive_parity(torch_dev, rule, dims, B, precision, exact)
+
+
+def test_adaptive_update_parity_skinny_full_size(torch_dev):
+    """The same three Adam steps on the skinny workload's full shapes
+    (4096 -> 11008 -> 4096, batch 8): the fused dX + dW pass and the first
+    layer's streaming update carrying W, m and v."""
+    # each Adam step moves every weight by about lr, and 11008 hidden units
+    # add those moves up: lr 1e-5 keeps three steps' loss well away from 0
+    _adaptive_parity(torch_dev, "adam", (4096, 11008, 4096), 8, "f32", False, lr=1e-5)
+
+
+def _adaptive_parity(torch_dev, rule, dims, B, precision, exact, lr=1e-3):
     torch, dev = torch_dev
     _announce(f"{rule} dims={dims} B={B} {precision}")
     # small enough that three steps keep the loss away from 0 (the loss gate
     # is relative, and a near-zero loss is a difference of near-equal terms)
-    lr, b1, b2, eps = 1e-3, 0.9, 0.999, 1e-8
+    b1, b2, eps = 0.9, 0.999, 1e-8
     if exact:
         x, t, Ws = P.integer_problem(dims, B, seed=sum(dims), bf16=precision == "bf16")
     else:
