@@ -216,6 +216,9 @@ EDGE_CASES = [
     ((33, 70, 17, 10), 37, "bf16"),
     ((100, 31, 7), 5, "bf16"),
     ((72, 200, 1000), 48, "bf16"),
+    ((1 << 20, 8), 2, "f32"),        # a 2^20-wide input: long K splits in the skinny forward
+    ((16, 16), 1 << 17, "f32"),      # 2^17 rows: long dW reduction, wide grids
+    ((64, 64), 1 << 17, "bf16"),
 ]
 
 
