@@ -1,8 +1,11 @@
-// bf16-operand MFMA GEMM with 256 x 256 workgroup tiles for the large
-// products of the bf16 fast path (float32 accumulate, same layouts and
-// epilogues as the 128-wide bf16 kernel; with the K split in up to 4 parts
+// MFMA GEMM with 256 x 256 workgroup tiles for the large products of both
+// contracts: bfloat16 operands (v_mfma_f32_32x32x16_bf16, 64-deep k stages)
+// or float32 operands (v_mfma_f32_32x32x2f32, 32-deep stages), float32
+// accumulate, the step's fused epilogues; with the K split in up to 4 parts
 // the partial sums go to memory and a separate all-CU kernel adds them and
-// applies the epilogue).
+// applies the epilogue.  A stage is 128 bytes of k per tile row in both
+// precisions, so the LDS geometry below is shared; where the text says
+// "element" it is 2 bytes (bf16) or 4 (f32).
 //
 // Why a second kernel: at 128 x 128 tiles the LDS traffic per MFMA flop
 // (fragment reads plus tile writes) exceeds what one CU's LDS delivers while
@@ -14,18 +17,26 @@
 //     buffer_load_dwordx4 ... lds (no staging registers, no ds_write); lanes
 //     whose element lies outside the matrix get an offset past the buffer's
 //     size, which the hardware turns into zeros;
-//   - two 64-deep k stages (2 x 64 KB of LDS, four static arrays): the loads
+//   - two k stages (2 x 64 KB of LDS, four static arrays): the loads
 //     of stage k+1 are in flight while stage k is multiplied; one barrier per
 //     stage;
 //   - bank-conflict-free layouts by XOR swizzles (the direct loads write 1 KB
 //     contiguous per wave instruction, so rows cannot be padded):
-//       k-contiguous operand: LDS row r (128 B = 64 k) holds 16-byte chunk j
+//       k-contiguous operand: LDS row r (128 B of k) holds 16-byte chunk j
 //         of the global row at chunk slot j ^ ((r >> 1) & 7); an MFMA operand
-//         is one ds_read_b128 per lane;
-//       r-contiguous operand: LDS k-row (512 B = 256 r) holds the 64-byte
-//         segment s (32 r) at slot s ^ (k & 3); an MFMA operand is two
-//         ds_read_b64_tr_b16 per lane (transpose reads, as in the 128-wide
-//         kernel), the four k-rows one read touches landing in distinct banks.
+//         is one ds_read_b128 per lane (8 bf16 or 4 f32 k-values);
+//       r-contiguous operand, bf16: LDS k-row (512 B = 256 r) holds the
+//         64-byte segment s (32 r) at slot s ^ (k & 3); an MFMA operand is
+//         two ds_read_b64_tr_b16 per lane (transpose reads, as in the
+//         128-wide kernel), the four k-rows one read touches landing in
+//         distinct banks;
+//       r-contiguous operand, f32: LDS k-row (1 KB = 256 r) in global order;
+//         an operand is four ds_read_b32 per lane (k, k+1, k+2, k+3), each
+//         half-wave reading 32 consecutive floats.
+//   - float32: one ds_read_b128 of the k-contiguous operand holds 4 k-values,
+//     and MFMA q (0..3) of a chunk takes value q: lanes 0-31 supply
+//     k = 8c + q and lanes 32-63 k = 8c + 4 + q, the same map for both
+//     operands, so the four MFMAs of a chunk add up all 8 k-values.
 #include "epilogue4.hpp"
 #include <type_traits>
 
@@ -35,9 +46,16 @@ namespace mlp {
 namespace {
 
 constexpr int kT = 256;                  // tile rows and columns
-constexpr int kBK = 64;                  // k per stage
 constexpr int kThreads = 256;            // 4 waves, 2 x 2, 128 x 128 each
-constexpr int kOpBytes = kT * kBK * 2;   // one operand tile: 32 KB
+constexpr int kOpBytes = 32 * 1024;      // one operand tile per stage: 256 rows x 128 bytes of k
+
+// Per-precision constants: k per stage, bytes per element, the MFMA operand.
+template <bool F32>
+struct Elem {
+    static constexpr int kBK = F32 ? 32 : 64;
+    static constexpr int ES = F32 ? 4 : 2;
+    using Frag = typename std::conditional<F32, float4v, bf16x8v>::type;
+};
 constexpr unsigned kOob = 0x80000000u;   // buffer offset that reads as zero
 constexpr int kMaxSplits = 4;            // K splits the reduction handles
 
@@ -47,20 +65,25 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Per-lane source offsets of one operand tile's 8 direct-load instructions
 // (this wave's share of 32 KB), relative to the tile's first k.
-template <bool KC>
+template <bool KC, bool F32>
 struct Loader {
     unsigned off[8];   // element offset of the row (KC) or column (MN) part, or kOob outside the matrix
     int kk[8];         // k of this lane's chunk within the stage
 
     __device__ __forceinline__ void init(int64_t ld, int r0, int rmax, int wave, int lane) {
+        constexpr int VE = 16 / Elem<F32>::ES;   // elements per 16-byte chunk
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int q = wave * 8 + i;
             if constexpr (KC) {
                 const int r = 8 * q + (lane >> 3);
                 const int j = (lane & 7) ^ ((r >> 1) & 7);
-                kk[i] = 8 * j;
+                kk[i] = VE * j;
                 off[i] = r0 + r < rmax ? (unsigned)((int64_t)(r0 + r) * ld) : kOob;
+            } else if constexpr (F32) {
+                // one k-row of 256 floats per instruction, in global order
+                kk[i] = q;
+                off[i] = r0 + 4 * lane < rmax ? (unsigned)(r0 + 4 * lane) : kOob;
             } else {
                 const int k = 2 * q + (lane >> 5);
                 const int p = lane & 31;
@@ -79,19 +102,30 @@ struct Loader {
             unsigned o = kOob;
             const int k = k0 + kk[i];
             if (off[i] != kOob && k < kmax)
-                o = 2u * (KC ? off[i] + (unsigned)k : (unsigned)((int64_t)k * ld) + off[i]);
+                o = (unsigned)Elem<F32>::ES * (KC ? off[i] + (unsigned)k : (unsigned)((int64_t)k * ld) + off[i]);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (wave * 8 + i) * 1024), 16, o, 0, 0, 0);
         }
     }
 };
 
-// Eight k-values (16c + 8*(lane/32) + 0..7) of tile row `base` + lane%32.
-template <bool KC>
-__device__ __forceinline__ bf16x8v frag(const char* s, int base, int c, int lane) {
+// The k-values of chunk c for tile row `base` + lane%32: bf16, eight
+// (16c + 8*(lane/32) + 0..7); f32, four (8c + 4*(lane/32) + 0..3).
+template <bool KC, bool F32>
+__device__ __forceinline__ typename Elem<F32>::Frag frag(const char* s, int base, int c, int lane) {
+    using Frag = typename Elem<F32>::Frag;
     if constexpr (KC) {
         const int r = base + (lane & 31);
         const int j = (2 * c + (lane >> 5)) ^ ((r >> 1) & 7);
-        return *reinterpret_cast<const bf16x8v*>(s + r * 128 + j * 16);
+        return *reinterpret_cast<const Frag*>(s + r * 128 + j * 16);
+    } else if constexpr (F32) {
+        const int k = 8 * c + 4 * (lane >> 5);
+        const float* p = reinterpret_cast<const float*>(s) + k * kT + base + (lane & 31);
+        float4v v;
+        v[0] = p[0];
+        v[1] = p[kT];
+        v[2] = p[2 * kT];
+        v[3] = p[3 * kT];
+        return v;
     } else {
         const int sl = lane & 15;
         const int k = 16 * c + 8 * (lane >> 5) + (sl >> 2);
@@ -106,8 +140,22 @@ __device__ __forceinline__ bf16x8v frag(const char* s, int base, int c, int lane
 
 // Bytes from the first element to one past the last of a row-major matrix
 // with `rows` rows of `cols` used elements and leading dimension ld.
+template <bool F32>
 __device__ __forceinline__ unsigned extent_bytes(int rows, int cols, int64_t ld) {
-    return (unsigned)(2 * ((int64_t)(rows - 1) * ld + cols));
+    return (unsigned)(Elem<F32>::ES * ((int64_t)(rows - 1) * ld + cols));
+}
+
+// The MFMAs of one chunk for accumulator block (i, j).
+template <bool F32>
+__device__ __forceinline__ float16v mfma_chunk(const typename Elem<F32>::Frag& a, const typename Elem<F32>::Frag& b,
+                                               float16v acc) {
+    if constexpr (F32) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[q], b[q], acc, 0, 0, 0);
+        return acc;
+    } else {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    }
 }
 
 // One k stage on LDS buffer (ca, cb); (na, nb) holds the next stage.
@@ -118,67 +166,88 @@ __device__ __forceinline__ unsigned extent_bytes(int rows, int cols, int64_t ld)
 // stage is read.  The buffers are distinct LDS arrays known at compile time,
 // so the compiler's wait counting sees that reads of one buffer do not depend
 // on the direct loads in flight into the other.
-template <bool AKC, bool BKC>
-__device__ __forceinline__ void stage(float16v (&acc)[4][4], bf16x8v (&a)[2][4], bf16x8v (&b)[2][4],
-                                      char* ca, char* cb, const char* na, const char* nb,
-                                      const Loader<AKC>& la, const Loader<BKC>& lb,
+template <bool AKC, bool BKC, bool F32>
+__device__ __forceinline__ void stage(float16v (&acc)[4][4], typename Elem<F32>::Frag (&a)[2][4],
+                                      typename Elem<F32>::Frag (&b)[2][4], char* ca, char* cb, const char* na,
+                                      const char* nb, const Loader<AKC, F32>& la, const Loader<BKC, F32>& lb,
                                       __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                       const GemmParams& p, int kload, int kend, int wm, int wn,
                                       int wave, int lane) {
+    // f32: 64 MFMAs per chunk and up to 32 LDS reads (four per r-contiguous
+    // operand); one read after every second MFMA, one direct load after
+    // every fourth in the last chunk
+    constexpr int ND = 4 * (AKC ? 1 : 4) + 4 * (BKC ? 1 : 4);
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
         const int f = c & 1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[f ^ 1][i] = frag<AKC>(ca, wm * 128 + 32 * i, c + 1, lane);
+        for (int i = 0; i < 4; ++i) a[f ^ 1][i] = frag<AKC, F32>(ca, wm * 128 + 32 * i, c + 1, lane);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[f ^ 1][j] = frag<BKC>(cb, wn * 128 + 32 * j, c + 1, lane);
+        for (int j = 0; j < 4; ++j) b[f ^ 1][j] = frag<BKC, F32>(cb, wn * 128 + 32 * j, c + 1, lane);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[f][i], b[f][j], acc[i][j], 0, 0, 0);
-        // one fragment read after each MFMA
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma_chunk<F32>(a[f][i], b[f][j], acc[i][j]);
+        if constexpr (F32) {
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int u = 0; u < 64; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (u % 2 == 0 && u / 2 < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        } else {
+            // one fragment read after each MFMA
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
     wait_loads();
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[0][i] = frag<AKC>(na, wm * 128 + 32 * i, 0, lane);
+    for (int i = 0; i < 4; ++i) a[0][i] = frag<AKC, F32>(na, wm * 128 + 32 * i, 0, lane);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[0][j] = frag<BKC>(nb, wn * 128 + 32 * j, 0, lane);
+    for (int j = 0; j < 4; ++j) b[0][j] = frag<BKC, F32>(nb, wn * 128 + 32 * j, 0, lane);
     la.issue(ra, p.lda, kload, kend, ca, wave);
     lb.issue(rb, p.ldb, kload, kend, cb, wave);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][i], b[1][j], acc[i][j], 0, 0, 0);
-    // one fragment read and one direct load after each of the first 12
-    // MFMAs, the remaining loads after the last 4 (the reads target the
-    // other buffer, which the compiler's wait counting tells apart)
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_chunk<F32>(a[1][i], b[1][j], acc[i][j]);
+    if constexpr (F32) {
 #pragma unroll
-    for (int u = 0; u < 12; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
+        for (int u = 0; u < 64; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (u % 2 == 0 && u / 2 < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (u % 4 == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+    } else {
+        // one fragment read and one direct load after each of the first 12
+        // MFMAs, the remaining loads after the last 4 (the reads target the
+        // other buffer, which the compiler's wait counting tells apart)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        for (int u = 0; u < 12; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <Layout LAY, Epi EPI>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p) {
+template <bool F32, Layout LAY, Epi EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmParams p) {
     constexpr bool AKC = LAY != Layout::TN;   // A stored [M][K]
     constexpr bool BKC = LAY == Layout::NT;   // B stored [N][K]
+    constexpr int kBK = Elem<F32>::kBK;
+    using Frag = typename Elem<F32>::Frag;
     __shared__ __attribute__((aligned(16))) char sa0[kOpBytes], sb0[kOpBytes], sa1[kOpBytes], sb1[kOpBytes];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -207,13 +276,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
     const int nk = kend > kbeg ? (kend - kbeg + kBK - 1) / kBK : 0;
 
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(p.A), (short)0, AKC ? extent_bytes(p.M, p.K, p.lda) : extent_bytes(p.K, p.M, p.lda),
+        const_cast<void*>(p.A), (short)0,
+        AKC ? extent_bytes<F32>(p.M, p.K, p.lda) : extent_bytes<F32>(p.K, p.M, p.lda),
         0x00020000);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(p.B), (short)0, BKC ? extent_bytes(p.N, p.K, p.ldb) : extent_bytes(p.K, p.N, p.ldb),
+        const_cast<void*>(p.B), (short)0,
+        BKC ? extent_bytes<F32>(p.N, p.K, p.ldb) : extent_bytes<F32>(p.K, p.N, p.ldb),
         0x00020000);
-    Loader<AKC> la;
-    Loader<BKC> lb;
+    Loader<AKC, F32> la;
+    Loader<BKC, F32> lb;
     la.init(p.lda, m0, p.M, wave, lane);
     lb.init(p.ldb, n0, p.N, wave, lane);
 
@@ -234,18 +305,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
         __syncthreads();
         la.issue(ra, p.lda, kbeg + kBK, kend, sa1, wave);
         lb.issue(rb, p.ldb, kbeg + kBK, kend, sb1, wave);
-        bf16x8v a[2][4], b[2][4];
+        Frag a[2][4], b[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[0][i] = frag<AKC>(sa0, wm * 128 + 32 * i, 0, lane);
+        for (int i = 0; i < 4; ++i) a[0][i] = frag<AKC, F32>(sa0, wm * 128 + 32 * i, 0, lane);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[0][j] = frag<BKC>(sb0, wn * 128 + 32 * j, 0, lane);
+        for (int j = 0; j < 4; ++j) b[0][j] = frag<BKC, F32>(sb0, wn * 128 + 32 * j, 0, lane);
         // Stages in pairs (buffer 0, buffer 1); an odd count multiplies one
         // all-zero stage at the end, which adds exact zeros.
         for (int kt = 0; kt < nk; kt += 2) {
-            stage<AKC, BKC>(acc, a, b, sa0, sb0, sa1, sb1, la, lb, ra, rb, p, kbeg + (kt + 2) * kBK, kend, wm,
-                            wn, wave, lane);
-            stage<AKC, BKC>(acc, a, b, sa1, sb1, sa0, sb0, la, lb, ra, rb, p, kbeg + (kt + 3) * kBK, kend, wm,
-                            wn, wave, lane);
+            stage<AKC, BKC, F32>(acc, a, b, sa0, sb0, sa1, sb1, la, lb, ra, rb, p, kbeg + (kt + 2) * kBK, kend,
+                                 wm, wn, wave, lane);
+            stage<AKC, BKC, F32>(acc, a, b, sa1, sb1, sa0, sb0, la, lb, ra, rb, p, kbeg + (kt + 3) * kBK, kend,
+                                 wm, wn, wave, lane);
         }
         // the zero-filling loads of the stages past the end
         wait_loads();
@@ -330,50 +401,58 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_big_kernel(GemmParams p
 
 }
 
-template <Layout LAY, Epi EPI>
+template <bool F32, Layout LAY, Epi EPI>
 hipError_t go(const GemmParams& p, int grid, bool reduce, hipStream_t st) {
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<LAY, EPI>), dim3(grid), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((gemm_big_kernel<F32, LAY, EPI>), dim3(grid), dim3(kThreads), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && p.splits > 1 && reduce) e = launch_splitk_epilogue(p, EPI, st);
     return e;
 }
 
+template <bool F32>
+hipError_t dispatch(const GemmLaunch& L, const GemmParams& p, hipStream_t st, bool reduce) {
+    switch (L.layout) {
+    case Layout::NN:
+        if (L.epi == Epi::ReluMask) return go<F32, Layout::NN, Epi::ReluMask>(p, L.grid, reduce, st);
+        if (L.epi == Epi::Store) return go<F32, Layout::NN, Epi::Store>(p, L.grid, reduce, st);
+        break;
+    case Layout::NT:
+        if (L.epi == Epi::MaskMul) return go<F32, Layout::NT, Epi::MaskMul>(p, L.grid, reduce, st);
+        break;
+    case Layout::TN:
+        if (L.epi == Epi::Sgd) return go<F32, Layout::TN, Epi::Sgd>(p, L.grid, reduce, st);
+        if (L.epi == Epi::Adapt) return go<F32, Layout::TN, Epi::Adapt>(p, L.grid, reduce, st);
+        if (L.epi == Epi::Grad) return go<F32, Layout::TN, Epi::Grad>(p, L.grid, reduce, st);
+        break;
+    }
+    return hipErrorInvalidValue;
+}
+
 
 }  // namespace
 
-bool gemm_bf16_big_fits(Layout lay, int M, int N, int K, int64_t lda, int64_t ldb) {
+bool gemm_big_fits(bool bf16, Layout lay, int M, int N, int K, int64_t lda, int64_t ldb) {
     // 16-byte direct loads: contiguous extents and leading dimensions in
-    // multiples of 8 elements; buffer offsets below 2^31 bytes.
+    // whole 16-byte chunks; buffer offsets below 2^31 bytes.
+    const int ve = bf16 ? 8 : 4, es = bf16 ? 2 : 4;
     const bool akc = lay != Layout::TN, bkc = lay == Layout::NT;
     const int acont = akc ? K : M, bcont = bkc ? K : N;
-    if (acont % 8 || bcont % 8 || lda % 8 || ldb % 8) return false;
+    if (acont % ve || bcont % ve || lda % ve || ldb % ve) return false;
     const int64_t arows = akc ? M : K, brows = bkc ? N : K;
-    return 2 * arows * lda < (int64_t)kOob && 2 * brows * ldb < (int64_t)kOob;
+    return es * arows * lda < (int64_t)kOob && es * brows * ldb < (int64_t)kOob;
 }
 
-hipError_t gemm_bf16_big_prepare() { return hipSuccess; }
+hipError_t gemm_big_prepare() { return hipSuccess; }
 
-hipError_t launch_gemm_bf16_big(const GemmLaunch& L, const GemmParams& p, hipStream_t st, bool reduce) {
+hipError_t launch_gemm_big(const GemmLaunch& L, const GemmParams& p, hipStream_t st, bool reduce) {
     if (p.splits < 1 || p.splits > kMaxSplits || L.grid != p.tiles_m * p.tiles_n * p.splits)
         return hipErrorInvalidValue;
     // without the reduction only the raw partials of a split product are
     // written; its epilogue must then be Store (the caller reduces them)
     if (!reduce && p.splits > 1 && L.epi != Epi::Store) return hipErrorInvalidValue;
-    switch (L.layout) {
-    case Layout::NN:
-        if (L.epi == Epi::ReluMask) return go<Layout::NN, Epi::ReluMask>(p, L.grid, reduce, st);
-        if (L.epi == Epi::Store) return go<Layout::NN, Epi::Store>(p, L.grid, reduce, st);
-        break;
-    case Layout::NT:
-        if (L.epi == Epi::MaskMul) return go<Layout::NT, Epi::MaskMul>(p, L.grid, reduce, st);
-        break;
-    case Layout::TN:
-        if (L.epi == Epi::Sgd) return go<Layout::TN, Epi::Sgd>(p, L.grid, reduce, st);
-        if (L.epi == Epi::Adapt) return go<Layout::TN, Epi::Adapt>(p, L.grid, reduce, st);
-        if (L.epi == Epi::Grad) return go<Layout::TN, Epi::Grad>(p, L.grid, reduce, st);
-        break;
-    }
-    return hipErrorInvalidValue;
+    // float32 sessions keep no bfloat16 copies
+    if (!L.bf16 && p.Cb) return hipErrorInvalidValue;
+    return L.bf16 ? dispatch<false>(L, p, st, reduce) : dispatch<true>(L, p, st, reduce);
 }
 
 }  // namespace mlp

@@ -54,7 +54,7 @@ struct GemmParams {
 };
 
 // Tile configurations of the MFMA GEMM (workgroup tile BM x BN, 4 waves).
-// T256x256 is the bf16-only large-tile kernel (direct-to-LDS loads).
+// T256x256 is the large-tile kernel (direct-to-LDS loads, bf16 or f32 operands).
 // T32x32 / T32x16 are the small-product kernel's tiles (one per workgroup).
 enum class TileCfg : int { T128x128 = 0, T64x64 = 1, T32x128 = 2, T128x32 = 3, T128x64 = 4,
                            T256x256 = 5, T32x32 = 6, T32x16 = 7 };
@@ -71,13 +71,13 @@ struct GemmLaunch {
 
 hipError_t launch_gemm(const GemmLaunch& L, const GemmParams& p, hipStream_t s);
 
-// Large-tile bf16 kernel: whether its 16-byte direct loads suit the operands,
-// the one-time raise of its dynamic-LDS limit, and the launch.
-bool gemm_bf16_big_fits(Layout lay, int M, int N, int K, int64_t lda, int64_t ldb);
-hipError_t gemm_bf16_big_prepare();
+// Large-tile kernel (bf16 or f32 operands, L.bf16): whether its 16-byte
+// direct loads suit the operands, its one-time set-up, and the launch.
+bool gemm_big_fits(bool bf16, Layout lay, int M, int N, int K, int64_t lda, int64_t ldb);
+hipError_t gemm_big_prepare();
 // With reduce = false a split product (Store epilogue only) leaves its sums
 // in p.partials for a later launch (launch_splitk_xent) to add.
-hipError_t launch_gemm_bf16_big(const GemmLaunch& L, const GemmParams& p, hipStream_t s, bool reduce = true);
+hipError_t launch_gemm_big(const GemmLaunch& L, const GemmParams& p, hipStream_t s, bool reduce = true);
 // Adds the K splits' partials [splits][M][N] in split order and applies the
 // epilogue (used by the large-tile kernel when it splits K).
 hipError_t launch_splitk_epilogue(const GemmParams& p, Epi epi, hipStream_t s);

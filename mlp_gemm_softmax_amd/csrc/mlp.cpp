@@ -35,7 +35,7 @@ hipError_t launch_gemm_f32(const GemmLaunch& L, const GemmParams& p, hipStream_t
 hipError_t launch_gemm_bf16(const GemmLaunch& L, const GemmParams& p, hipStream_t st);
 
 hipError_t launch_gemm(const GemmLaunch& L, const GemmParams& p, hipStream_t st) {
-    if (L.cfg == TileCfg::T256x256) return launch_gemm_bf16_big(L, p, st);
+    if (L.cfg == TileCfg::T256x256) return launch_gemm_big(L, p, st);
     return L.bf16 ? launch_gemm_bf16(L, p, st) : launch_gemm_f32(L, p, st);
 }
 
@@ -166,16 +166,17 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 GemmPlan plan_gemm(int M, int N, int K, bool bf16, bool kvec_ok, bool big_ok) {
     GemmPlan g;
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    if (bf16 && big_ok) {
-        // Large bf16 products: 256 x 256 tiles, one workgroup per CU; K is
-        // split (up to 4 ways, at least 512 deep) while the tiles fill fewer
-        // than half the CUs.
+    if (big_ok) {
+        // Large products: 256 x 256 tiles, one workgroup per CU; K is split
+        // (up to 4 ways, at least 512 deep) while the tiles fill fewer than
+        // half the CUs.
         const int nt = tiles(256, 256);
+        const int sk = bf16 ? 64 : 32;   // k per stage
         int s = 1;
         if (nt < 128) s = std::max(1, std::min({4, (256 + nt - 1) / nt, K / 512}));
         if (nt * s >= 128) {
             int kchunk = (K + s - 1) / s;
-            kchunk = (kchunk + 63) / 64 * 64;
+            kchunk = (kchunk + sk - 1) / sk * sk;
             s = (K + kchunk - 1) / kchunk;
             g.cfg = TileCfg::T256x256;
             g.tiles_m = (M + 255) / 256;
@@ -183,7 +184,7 @@ GemmPlan plan_gemm(int M, int N, int K, bool bf16, bool kvec_ok, bool big_ok) {
             g.splits = s;
             g.kchunk = s > 1 ? kchunk : std::max(K, 1);
             g.grid = nt * s;
-            g.vec = 8;
+            g.vec = bf16 ? 8 : 4;
             return g;
         }
     }
@@ -463,7 +464,7 @@ hipError_t run_gemm(mlp_ctx* c, const GemmPlan& g, Layout lay, Epi epi, const vo
     p.opt = opt ? *opt : OptScalars{};
     if (tail) return launch_gemm_small_tail(L, p, g.small_waves, *tail, c->stream);
     if (g.small_waves > 0) return launch_gemm_small(L, p, g.small_waves, c->stream);
-    if (g.cfg == TileCfg::T256x256) return launch_gemm_bf16_big(L, p, c->stream, reduce);
+    if (g.cfg == TileCfg::T256x256) return launch_gemm_big(L, p, c->stream, reduce);
     return launch_gemm(L, p, c->stream);
 }
 
@@ -849,11 +850,11 @@ size_t plan_and_carve(mlp_ctx* c, char* base) {
         // contiguous run of the three products) to be multiples of the vector.
         const bool wide = din % vq == 0 && dout % vq == 0;
         // forward NN: A = a_l [B][din] (k-contiguous, K = din), B = W [din][dout]
-        c->fwd[l] = plan_gemm(B, dout, din, c->bf16, wide, gemm_bf16_big_fits(Layout::NN, B, dout, din, din, dout));
+        c->fwd[l] = plan_gemm(B, dout, din, c->bf16, wide, gemm_big_fits(c->bf16, Layout::NN, B, dout, din, din, dout));
         // dX NT: A = G [B][dout], B = W [din][dout] (both k-contiguous, K = dout)
-        c->dx[l] = plan_gemm(B, din, dout, c->bf16, wide, gemm_bf16_big_fits(Layout::NT, B, din, dout, dout, dout));
+        c->dx[l] = plan_gemm(B, din, dout, c->bf16, wide, gemm_big_fits(c->bf16, Layout::NT, B, din, dout, dout, dout));
         // dW TN: A = a_l [B][din], B = G [B][dout]: M = din, N = dout, K = B
-        c->dw[l] = plan_gemm(din, dout, B, c->bf16, wide, gemm_bf16_big_fits(Layout::TN, din, dout, B, din, dout));
+        c->dw[l] = plan_gemm(din, dout, B, c->bf16, wide, gemm_big_fits(c->bf16, Layout::TN, din, dout, B, din, dout));
         for (const GemmPlan* g : {&c->fwd[l], &c->dx[l], &c->dw[l]}) {
             if (g->splits > 1) {
                 int bm, bn;
@@ -979,7 +980,7 @@ mlp_status mlp_create(const mlp_config* cfg, void* workspace, size_t bytes, mlp_
     for (int l = 0; l < c->L; ++l)
         for (const GemmPlan* g : {&c->fwd[l], &c->dx[l], &c->dw[l]}) big = big || g->cfg == TileCfg::T256x256;
     if (big) {
-        const hipError_t he = gemm_bf16_big_prepare();
+        const hipError_t he = gemm_big_prepare();
         if (he != hipSuccess) {
             set_err(nullptr, MLP_ERR_HIP, "large-tile GEMM set-up: %s", hipGetErrorString(he));
             delete c;
@@ -1423,15 +1424,15 @@ std::vector<GemmPlan> gemm_candidates(const mlp_ctx* c, int M, int N, int K, boo
         g.grid = g.tiles_m * g.tiles_n * s;
         return g;
     };
-    if (c->bf16 && big_ok) {
+    if (big_ok) {
         for (int s : {1, 2, 4}) {
             GemmPlan g;
             g.cfg = TileCfg::T256x256;
             g.tiles_m = (M + 255) / 256;
             g.tiles_n = (N + 255) / 256;
-            g.vec = 8;
+            g.vec = c->bf16 ? 8 : 4;
             if (s > 1 && K / s < 512) continue;
-            push(split(g, s, 64));
+            push(split(g, s, c->bf16 ? 64 : 32));
         }
     }
     const int bk = c->bf16 ? 64 : 32, kmin = c->bf16 ? 256 : 128;
@@ -1568,11 +1569,11 @@ mlp_status mlp_tune(mlp_ctx* c, const float* x, const float* labels, int32_t rep
             bool big;
             bool used;
         } items[3] = {
-            {&c->fwd[l], B, dout, din, gemm_bf16_big_fits(Layout::NN, B, dout, din, din, dout),
+            {&c->fwd[l], B, dout, din, gemm_big_fits(c->bf16, Layout::NN, B, dout, din, din, dout),
              !(c->head && l == L - 1) && !(head_fused(c) && l == L - 2)},
-            {&c->dx[l], B, din, dout, gemm_bf16_big_fits(Layout::NT, B, din, dout, dout, dout),
+            {&c->dx[l], B, din, dout, gemm_big_fits(c->bf16, Layout::NT, B, din, dout, dout, dout),
              l > 0 && !(c->head && l == L - 1)},
-            {&c->dw[l], din, dout, B, gemm_bf16_big_fits(Layout::TN, din, dout, B, din, dout),
+            {&c->dw[l], din, dout, B, gemm_big_fits(c->bf16, Layout::TN, din, dout, B, din, dout),
              !(c->head && l == L - 1) && !(tail_fused(c) && l == 0)},
         };
         for (Item& it : items) {

@@ -52,16 +52,16 @@ def test_roofline_below_the_ridge_is_hbm_bound():
 
 
 def test_per_slot_groups_split_k_epilogues_with_their_product():
-    prod = "void mlp::(anonymous namespace)::gemm_bf16_big_kernel<(mlp::Layout)2, (mlp::Epi)3>(mlp::GemmParams)"
+    prod = "void mlp::(anonymous namespace)::gemm_big_kernel<true, (mlp::Layout)2, (mlp::Epi)3>(mlp::GemmParams)"
     epi = "void mlp::(anonymous namespace)::splitk_epilogue_kernel<(mlp::Epi)3>(mlp::GemmParams)"
-    fwd = "void mlp::(anonymous namespace)::gemm_bf16_big_kernel<(mlp::Layout)0, (mlp::Epi)1>(mlp::GemmParams)"
+    fwd = "void mlp::(anonymous namespace)::gemm_big_kernel<true, (mlp::Layout)0, (mlp::Epi)1>(mlp::GemmParams)"
     other = "void at::native::vectorized_elementwise_kernel<4>"
     disp = [(other, 99.0)]
     for step in range(3):
         disp += [(fwd, 10.0 + step), (prod, 5.0), (epi, 2.0)]
     names, avg = bench._per_slot(disp, 2, 2)
     assert len(names) == 2
-    assert "splitk_epilogue_kernel" in names[1] and "gemm_bf16_big_kernel" in names[1]
+    assert "splitk_epilogue_kernel" in names[1] and "gemm_big_kernel" in names[1]
     assert avg[0] == pytest.approx(11.5)      # the last two steps
     assert avg[1] == pytest.approx(7.0)       # product + its epilogue
 

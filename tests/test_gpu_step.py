@@ -47,6 +47,7 @@ EXACT_CASES = [
     ((2080, 1040, 40), 512, "f32", 1),       # tiled TN and NT with split-K, ragged tiles
     ((64, 32, 8), 8, "f32", 2),              # fused output layer with skinny kernels, tail on its own
     ((512, 2048, 16), 1024, "f32", 1),       # fused output layer with tiled GEMMs, tail on its own
+    ((1024, 2048, 1040), 2048, "f32", 1),    # f32 256x256 tiles: K splits, split logits into the loss, ragged N
     ((200, 300, 36), 64, "bf16", 1),
     ((120, 136, 24), 256, "bf16", 1),
     ((256, 4096, 40), 2048, "bf16", 1),      # 256-wide bf16 tiles, no split (forward)
@@ -490,6 +491,7 @@ ADAPTIVE_CASES = [
     ((33, 70, 17, 10), 37, "f32", False),     # three layers, widths not multiples of 4
     ((120, 136, 24), 256, "bf16", True),      # bf16 operands: the update refreshes the bf16 copy
     ((1024, 2048, 1000), 2048, "bf16", False),  # large bf16 tiles, split-K logits into the loss
+    ((1024, 2048, 1000), 2048, "f32", False),   # large f32 tiles
 ]
 
 
