@@ -855,16 +855,8 @@ size_t plan_and_carve(mlp_ctx* c, char* base) {
         c->dx[l] = plan_gemm(B, din, dout, c->bf16, wide, gemm_big_fits(c->bf16, Layout::NT, B, din, dout, dout, dout));
         // dW TN: A = a_l [B][din], B = G [B][dout]: M = din, N = dout, K = B
         c->dw[l] = plan_gemm(din, dout, B, c->bf16, wide, gemm_big_fits(c->bf16, Layout::TN, din, dout, B, din, dout));
-        for (const GemmPlan* g : {&c->fwd[l], &c->dx[l], &c->dw[l]}) {
-            if (g->splits > 1) {
-                int bm, bn;
-                tile_shape(g->cfg, &bm, &bn);
-                const size_t M = (size_t)g->tiles_m * bm, N = (size_t)g->tiles_n * bn;
-                (void)M;
-                (void)N;
-                max_tickets = std::max(max_tickets, (size_t)g->tiles_m * g->tiles_n);
-            }
-        }
+        for (const GemmPlan* g : {&c->fwd[l], &c->dx[l], &c->dw[l]})
+            if (g->splits > 1) max_tickets = std::max(max_tickets, (size_t)g->tiles_m * g->tiles_n);
         max_partial = std::max(max_partial, partial_elems(c->fwd[l], B, dout));
         max_partial = std::max(max_partial, partial_elems(c->dx[l], B, din));
         max_partial = std::max(max_partial, partial_elems(c->dw[l], din, dout));
