@@ -13,10 +13,15 @@
 // flop is twice that of a 256 x 256 tile.  Here
 //   - 4 waves, each owning a 128 x 128 sub-tile (16 accumulators of 32 x 32,
 //     v_mfma_f32_32x32x16_bf16), so every LDS fragment feeds 4 MFMAs;
-//   - operands go from global memory straight into LDS with
-//     buffer_load_dwordx4 ... lds (no staging registers, no ds_write); lanes
-//     whose element lies outside the matrix get an offset past the buffer's
-//     size, which the hardware turns into zeros;
+//   - operands go from global memory into LDS 16 bytes per lane, either
+//     straight (buffer_load_dwordx4 ... lds) or through registers
+//     (buffer_load_dwordx4, then ds_write_b128 into the same place before the
+//     next barrier); the results are the same bit for bit.  Direct loads are
+//     faster for bf16 NT (both operands read with ds_read_b128), staging
+//     through registers for the layouts with transpose reads and for f32
+//     (measured 3-11% and about 1%).  Lanes whose element lies outside the
+//     matrix get an offset past the buffer's size, which the hardware turns
+//     into zeros;
 //   - two k stages (2 x 64 KB of LDS, four static arrays): the loads
 //     of stage k+1 are in flight while stage k is multiplied; one barrier per
 //     stage;
@@ -60,6 +65,7 @@ constexpr unsigned kOob = 0x80000000u;   // buffer offset that reads as zero
 constexpr int kMaxSplits = 4;            // K splits the reduction handles
 
 typedef short short4v __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -94,17 +100,32 @@ struct Loader {
         }
     }
 
+    // Byte offset of load i of stage k0, or kOob.
+    __device__ __forceinline__ unsigned src(int i, int64_t ld, int k0, int kmax) const {
+        const int k = k0 + kk[i];
+        if (off[i] == kOob || k >= kmax) return kOob;
+        return (unsigned)Elem<F32>::ES * (KC ? off[i] + (unsigned)k : (unsigned)((int64_t)k * ld) + off[i]);
+    }
+
+    // Register staging: load stage k0 into r, later write r where the direct
+    // loads would have put it.
+    __device__ __forceinline__ void fetch(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0, int kmax,
+                                          u32x4v (&r)[8]) const {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)src(i, ld, k0, kmax), 0, 0);
+    }
+    __device__ __forceinline__ static void commit(char* dst, int wave, int lane, const u32x4v (&r)[8]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4v*>(dst + (wave * 8 + i) * 1024 + lane * 16) = r[i];
+    }
+
     // Issue the 8 loads of stage k0 into `dst` (this operand's 32 KB tile).
     __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int64_t ld, int k0, int kmax,
                                           char* dst, int wave) const {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            unsigned o = kOob;
-            const int k = k0 + kk[i];
-            if (off[i] != kOob && k < kmax)
-                o = (unsigned)Elem<F32>::ES * (KC ? off[i] + (unsigned)k : (unsigned)((int64_t)k * ld) + off[i]);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (wave * 8 + i) * 1024), 16, o, 0, 0, 0);
-        }
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + (wave * 8 + i) * 1024), 16,
+                                                     src(i, ld, k0, kmax), 0, 0, 0);
     }
 };
 
@@ -165,11 +186,15 @@ __device__ __forceinline__ float16v mfma_chunk(const typename Elem<F32>::Frag& a
 // buffer just finished, and chunk 3 multiplies while chunk 0 of the next
 // stage is read.  The buffers are distinct LDS arrays known at compile time,
 // so the compiler's wait counting sees that reads of one buffer do not depend
-// on the direct loads in flight into the other.
-template <bool AKC, bool BKC, bool F32>
+// on the direct loads in flight into the other.  With register staging (REG)
+// the stage after next is loaded into (pa, pb) instead, and those registers,
+// loaded during the previous stage, are written into (na, nb) during chunk 2,
+// before the barrier that makes them visible.
+template <bool AKC, bool BKC, bool F32, bool REG>
 __device__ __forceinline__ void stage(float16v (&acc)[4][4], typename Elem<F32>::Frag (&a)[2][4],
-                                      typename Elem<F32>::Frag (&b)[2][4], char* ca, char* cb, const char* na,
-                                      const char* nb, const Loader<AKC, F32>& la, const Loader<BKC, F32>& lb,
+                                      typename Elem<F32>::Frag (&b)[2][4], char* ca, char* cb, char* na,
+                                      char* nb, const Loader<AKC, F32>& la, const Loader<BKC, F32>& lb,
+                                      u32x4v (&pa)[8], u32x4v (&pb)[8],
                                       __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                       const GemmParams& p, int kload, int kend, int wm, int wn,
                                       int wave, int lane) {
@@ -188,30 +213,42 @@ __device__ __forceinline__ void stage(float16v (&acc)[4][4], typename Elem<F32>:
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = mfma_chunk<F32>(a[f][i], b[f][j], acc[i][j]);
+        const bool kCommit = REG && c == 2;   // constant once the loop is unrolled
+        if (kCommit) {
+            Loader<AKC, F32>::commit(na, wave, lane, pa);
+            Loader<BKC, F32>::commit(nb, wave, lane, pb);
+        }
         if constexpr (F32) {
 #pragma unroll
             for (int u = 0; u < 64; ++u) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 if (u % 2 == 0 && u / 2 < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (kCommit && u % 4 == 0) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
             }
         } else {
-            // one fragment read after each MFMA
+            // one fragment read (and in chunk 2 one staged write) after each MFMA
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (kCommit) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
-    wait_loads();
+    if constexpr (!REG) wait_loads();
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[0][i] = frag<AKC, F32>(na, wm * 128 + 32 * i, 0, lane);
 #pragma unroll
     for (int j = 0; j < 4; ++j) b[0][j] = frag<BKC, F32>(nb, wn * 128 + 32 * j, 0, lane);
-    la.issue(ra, p.lda, kload, kend, ca, wave);
-    lb.issue(rb, p.ldb, kload, kend, cb, wave);
+    if constexpr (REG) {
+        la.fetch(ra, p.lda, kload, kend, pa);
+        lb.fetch(rb, p.ldb, kload, kend, pb);
+    } else {
+        la.issue(ra, p.lda, kload, kend, ca, wave);
+        lb.issue(rb, p.ldb, kload, kend, cb, wave);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -246,6 +283,7 @@ template <bool F32, Layout LAY, Epi EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmParams p) {
     constexpr bool AKC = LAY != Layout::TN;   // A stored [M][K]
     constexpr bool BKC = LAY == Layout::NT;   // B stored [N][K]
+    constexpr bool kReg = F32 || LAY != Layout::NT;   // register staging (see the header)
     constexpr int kBK = Elem<F32>::kBK;
     using Frag = typename Elem<F32>::Frag;
     __shared__ __attribute__((aligned(16))) char sa0[kOpBytes], sb0[kOpBytes], sa1[kOpBytes], sb1[kOpBytes];
@@ -299,12 +337,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmParams p) {
     if (nk > 0) {
         // Stage t lives in buffer t & 1; stages past the end load as zeros
         // and are never multiplied.
-        la.issue(ra, p.lda, kbeg, kend, sa0, wave);
-        lb.issue(rb, p.ldb, kbeg, kend, sb0, wave);
-        wait_loads();
-        __syncthreads();
-        la.issue(ra, p.lda, kbeg + kBK, kend, sa1, wave);
-        lb.issue(rb, p.ldb, kbeg + kBK, kend, sb1, wave);
+        u32x4v pa[8], pb[8];
+        if constexpr (kReg) {
+            // stage 0 written now, stage 1 held in registers until the
+            // first stage writes it
+            la.fetch(ra, p.lda, kbeg, kend, pa);
+            lb.fetch(rb, p.ldb, kbeg, kend, pb);
+            Loader<AKC, F32>::commit(sa0, wave, lane, pa);
+            Loader<BKC, F32>::commit(sb0, wave, lane, pb);
+            la.fetch(ra, p.lda, kbeg + kBK, kend, pa);
+            lb.fetch(rb, p.ldb, kbeg + kBK, kend, pb);
+            __syncthreads();
+        } else {
+            la.issue(ra, p.lda, kbeg, kend, sa0, wave);
+            lb.issue(rb, p.ldb, kbeg, kend, sb0, wave);
+            wait_loads();
+            __syncthreads();
+            la.issue(ra, p.lda, kbeg + kBK, kend, sa1, wave);
+            lb.issue(rb, p.ldb, kbeg + kBK, kend, sb1, wave);
+        }
         Frag a[2][4], b[2][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) a[0][i] = frag<AKC, F32>(sa0, wm * 128 + 32 * i, 0, lane);
@@ -313,13 +364,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmParams p) {
         // Stages in pairs (buffer 0, buffer 1); an odd count multiplies one
         // all-zero stage at the end, which adds exact zeros.
         for (int kt = 0; kt < nk; kt += 2) {
-            stage<AKC, BKC, F32>(acc, a, b, sa0, sb0, sa1, sb1, la, lb, ra, rb, p, kbeg + (kt + 2) * kBK, kend,
-                                 wm, wn, wave, lane);
-            stage<AKC, BKC, F32>(acc, a, b, sa1, sb1, sa0, sb0, la, lb, ra, rb, p, kbeg + (kt + 3) * kBK, kend,
-                                 wm, wn, wave, lane);
+            stage<AKC, BKC, F32, kReg>(acc, a, b, sa0, sb0, sa1, sb1, la, lb, pa, pb, ra, rb, p,
+                                       kbeg + (kt + 2) * kBK, kend, wm, wn, wave, lane);
+            stage<AKC, BKC, F32, kReg>(acc, a, b, sa1, sb1, sa0, sb0, la, lb, pa, pb, ra, rb, p,
+                                       kbeg + (kt + 3) * kBK, kend, wm, wn, wave, lane);
         }
-        // the zero-filling loads of the stages past the end
-        wait_loads();
+        // the zero-filling direct loads of the stages past the end (staged
+        // loads of those stages land in registers that are never read)
+        if constexpr (!kReg) wait_loads();
     }
 
     // Epilogue.  Each wave stages its 128 x 128 accumulators through LDS, 32
