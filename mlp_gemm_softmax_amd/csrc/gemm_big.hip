@@ -188,8 +188,8 @@ __device__ __forceinline__ float16v mfma_chunk(const typename Elem<F32>::Frag& a
 // so the compiler's wait counting sees that reads of one buffer do not depend
 // on the direct loads in flight into the other.  With register staging (REG)
 // the stage after next is loaded into (pa, pb) instead, and those registers,
-// loaded during the previous stage, are written into (na, nb) during chunk 2,
-// before the barrier that makes them visible.
+// loaded during the previous stage, are written into (na, nb) during chunks
+// 1 (A) and 2 (B), before the barrier that makes them visible.
 template <bool AKC, bool BKC, bool F32, bool REG>
 __device__ __forceinline__ void stage(float16v (&acc)[4][4], typename Elem<F32>::Frag (&a)[2][4],
                                       typename Elem<F32>::Frag (&b)[2][4], char* ca, char* cb, char* na,
@@ -213,11 +213,11 @@ __device__ __forceinline__ void stage(float16v (&acc)[4][4], typename Elem<F32>:
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = mfma_chunk<F32>(a[f][i], b[f][j], acc[i][j]);
-        const bool kCommit = REG && c == 2;   // constant once the loop is unrolled
-        if (kCommit) {
-            Loader<AKC, F32>::commit(na, wave, lane, pa);
-            Loader<BKC, F32>::commit(nb, wave, lane, pb);
-        }
+        // constant once the loop is unrolled: A's staged writes in chunk 1,
+        // B's in chunk 2
+        const bool kCommit = REG && (c == 1 || c == 2);
+        if (REG && c == 1) Loader<AKC, F32>::commit(na, wave, lane, pa);
+        if (REG && c == 2) Loader<BKC, F32>::commit(nb, wave, lane, pb);
         if constexpr (F32) {
 #pragma unroll
             for (int u = 0; u < 64; ++u) {
@@ -226,7 +226,7 @@ __device__ __forceinline__ void stage(float16v (&acc)[4][4], typename Elem<F32>:
                 if (kCommit && u % 4 == 0) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
             }
         } else {
-            // one fragment read (and in chunk 2 one staged write) after each MFMA
+            // one fragment read (and in chunks 1-2 one staged write) after each MFMA
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
