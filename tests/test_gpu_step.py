@@ -48,6 +48,7 @@ EXACT_CASES = [
     ((64, 32, 8), 8, "f32", 2),              # fused output layer with skinny kernels, tail on its own
     ((512, 2048, 16), 1024, "f32", 1),       # fused output layer with tiled GEMMs, tail on its own
     ((1024, 2048, 1040), 2048, "f32", 1),    # f32 256x256 tiles: K splits, split logits into the loss, ragged N
+    ((2056, 4096, 1024), 2048, "f32", 1),    # f32 256x256 tiles in all three layouts, ragged K and M
     ((200, 300, 36), 64, "bf16", 1),
     ((120, 136, 24), 256, "bf16", 1),
     ((256, 4096, 40), 2048, "bf16", 1),      # 256-wide bf16 tiles, no split (forward)
