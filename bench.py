@@ -2,6 +2,13 @@
 """Throughput of the MLP training step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--extra-workloads A,B]
+
+The figure is the wide MLP in strict float32 (1024 -> 4096 -> 4096 -> 1000,
+batch 4096, the largest workload that is judged against the f32 matrix-core
+peak); the bf16 fast path of the same MLP and the skinny batch-8 MLP (judged
+against HBM bandwidth) are measured the same way in the same run and reported
+under "also".
 
 A step is one pass of the whole hot path (forward GEMMs with fused ReLU/mask,
 softmax cross-entropy, dX and dW+SGD GEMMs) over one batch of synthetic
@@ -13,8 +20,9 @@ the headline).  Then up to 50 synchronous steps (the loss read back after
 each one) give `sync_ms_per_step`.  After that the same K steps run again
 with per-launch HIP events on the library's
 stream, to price the dominant kernel against its roofline; then the float64
-oracle is timed on the host cores over a bounded sample.  Prints ONE JSON
-line.
+oracle is timed on the host cores over a bounded sample, and the GPU's ReLU
+masks of the first step are counted against the oracle's rounding band.
+Prints ONE JSON line.
 """
 from __future__ import annotations
 
@@ -30,7 +38,9 @@ if ROOT not in sys.path:
 
 # MI355X published peaks (dense).
 PEAK = {"f32_mfma_tflops": 157.3, "bf16_mfma_tflops": 2516.6, "hbm_gbps": 8000.0}
-DEFAULT_WORKLOAD = "mnist_b1024"
+DEFAULT_WORKLOAD = "wide_f32"
+# measured in the same run and reported under "also"
+DEFAULT_EXTRA = "wide_bf16,skinny_b8"
 
 
 def parse():
@@ -39,6 +49,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--extra-workloads", default=DEFAULT_EXTRA, metavar="A,B",
+                    help="further workloads measured the same way and reported under \"also\" "
+                         "(empty: none)")
     ap.add_argument("--mode", choices=["train", "forward", "probs"], default="train",
                     help="train: the training step (the headline metric); forward: logits only "
                          "(inference of the same network); probs: class probabilities (inference)")
@@ -160,9 +173,10 @@ def cpu_baseline(w, budget_s, rule="sgd"):
 # ---------------------------------------------------------------- profiles --
 
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d OUT/trace_{w} -o {w} -- "
-             "python3 bench.py --workload {w} --steps {s} --warmup {wu} --no-cpu-baseline")
+             "python3 bench.py --workload {w} --extra-workloads none --steps {s} --warmup {wu} --no-cpu-baseline")
 PMC_CMD = ("rocprofv3 --pmc {c} --output-format csv -d OUT/{d}_{w} -o {w} -- python3 bench.py "
-           "--workload {w} --steps 2 --warmup 1 --profile-steps 1 --no-cpu-baseline --calib-copy-mb 256")
+           "--workload {w} --extra-workloads none --steps 2 --warmup 1 --profile-steps 1 --no-cpu-baseline "
+           "--calib-copy-mb 256")
 MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_{p} SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE"
 N_SIMDS = 256 * 4     # MI355X: 256 CUs of 4 SIMDs
 N_XCDS = 8            # GRBM_GUI_ACTIVE is summed over the 8 XCDs
@@ -178,7 +192,7 @@ def _bench_log(path):
     slots, line = [], None
     with open(path) as f:
         for ln in f:
-            if ln.startswith("[bench] per-launch"):
+            if ln.startswith("[bench] per-launch") and not slots:   # the headline workload
                 body = ln.split(":", 1)[1]
                 for item in body.split(","):
                     name, val = item.strip().rsplit("=", 1)
@@ -330,26 +344,31 @@ def summarize(outdir, w, steps, warmup):
     print(f"wrote profiles/{w}.md and profiles/traffic.json[{w}]")
 
 
-def main():
-    args = parse()
-    if args.summarize:
-        summarize(args.summarize, args.workload, args.steps, args.warmup)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the path has no multi-GPU mode)", file=sys.stderr)
-        sys.exit(2)
+def mask_counts(w, x, Ws, masks):
+    """Per hidden layer of the first step (batch 0, initial weights): units,
+    units inside the oracle's rounding band, GPU mask bits the oracle adopts
+    there and bits that differ outside it (which the parity gate requires to
+    be 0).  Runs the oracle's forward, untimed, after the CPU baseline."""
+    from oracle import mlp_oracle
+    ref = mlp_oracle.forward(x, Ws, kink_choice=masks, precision=w.precision)
+    return [{"layer": l + 1, "units": int(w.batch * w.dims[l + 1]), "in_band": ib, "adopted": ad,
+             "outside": out}
+            for l, (ib, ad, out) in enumerate(zip(ref["in_band"], ref["adopted"], ref["outside"]))]
+
+
+def measure(w, args, dev, want_cpu, want_masks):
+    """Time one workload through the C ABI: warm-up, K asynchronous steps
+    (the figure), up to 50 synchronous steps, then the same K steps with
+    per-launch events for the roofline; then the oracle on the host."""
     import numpy as np
     import torch
     from mlp_gemm_softmax_amd import binding, synth
 
-    w = synth.WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
     print(f"[bench] workload {w.name} dims={w.dims} B={w.batch} {w.precision} "
           f"steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
-
+    Ws = synth.workload_weights(w)
     net = binding.Mlp(w.dims, w.batch, w.precision, device="cuda:0")
-    net.set_params([torch.from_numpy(a).to(dev) for a in synth.workload_weights(w)])
+    net.set_params([torch.from_numpy(a).to(dev) for a in Ws])
     if args.optimizer != "sgd":
         net.set_optimizer(args.optimizer, 0.9, 0.999, 1e-8)
     n_batches = w.steps if w.fresh_batch else 1
@@ -357,6 +376,11 @@ def main():
     for s in range(n_batches):
         x, t, _ = synth.workload_batch(w, s)
         batches.append((torch.from_numpy(x).to(dev), torch.from_numpy(t).to(dev)))
+    masks = None
+    if want_masks and w.n_layers > 1 and args.mode == "train":
+        # the GPU's ReLU masks of the first step, before any update
+        net.grads(*batches[0])
+        masks = [net.read_state(binding.STATE_MASK, l).cpu().numpy() for l in range(1, w.n_layers)]
     loss_dev = torch.zeros(1, dtype=torch.float32, device=dev)
     if args.calib_copy_mb > 0:
         src = torch.ones(args.calib_copy_mb << 18, dtype=torch.float32, device=dev)
@@ -412,51 +436,100 @@ def main():
     torch.cuda.synchronize()
     rows = net.profile_read()
     net.profile(False)
+    net.close()
+    del net, batches
+    torch.cuda.empty_cache()
     roof = roofline(rows, w.precision, pk)
     roof["traffic"] = recorded_traffic(w.name, roof["kernel"])
     rec = recorded_counters(w.name, roof["kernel"]) or {}
     for key in ("mfma_busy", "clock_ghz"):   # matrix-core busy share and clock from the counter runs
         if rec.get(key) is not None:
             roof[key] = rec[key]
-    print("[bench] per-launch (ms avg): " + ", ".join(
+    print(f"[bench] per-launch (ms avg) [{w.name}]: " + ", ".join(
         f"{r['name']}={r['total_ms'] / max(r['launches'], 1):.4f}" for r in rows),
         file=sys.stderr, flush=True)
 
     steps_per_s = args.steps / el
     fwd = args.mode in ("forward", "probs")
     flops = w.forward_flops() if fwd else w.gemm_flops()
-    out = {
-        "metric": (f"MLP forward passes/sec ({'probabilities' if args.mode == 'probs' else 'logits'}, "
-                   "inference) + achieved TFLOP/s, 1 GPU" if fwd else
-                   "MLP train steps/sec + achieved TFLOP/s (fraction of MFMA/HBM roofline), 1 GPU"),
+    step_bytes = sum(r["bytes"] for r in rows if r["launches"] > 0)
+    peak = PEAK["bf16_mfma_tflops"] if w.precision == "bf16" else PEAK["f32_mfma_tflops"]
+    res = {
         "value": round(steps_per_s, 3),
-        "unit": "forward passes/s" if fwd else "steps/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(el / args.steps * 1e3, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": "bf16" if w.precision == "bf16" else "f32",
-        "data": "synthetic (seeded; MNIST-shaped uniform [0,1) pixels or N(0,1) features, uniform class ids)",
         "config": {"workload": w.name, "dims": list(w.dims), "batch": w.batch, "lr": w.lr,
                    "precision": w.precision, "fresh_batch_per_step": w.fresh_batch,
                    "optimizer": args.optimizer, "mode": args.mode, "tuned": args.tune > 0},
         "achieved_tflops": round(flops * steps_per_s / 1e12, 4),
-        "sync_ms_per_step": round(sync_ms, 5) if sync_ms is not None else None,
         "step_flops": flops,
+        # algorithmic HBM bytes of the launches one step makes (each operand
+        # read once, each output written once), and their rate over the step
+        "step_bytes": int(step_bytes),
+        "step_gbps": round(step_bytes * steps_per_s / 1e9, 2),
+        "sync_ms_per_step": round(sync_ms, 5) if sync_ms is not None else None,
         "final_loss": final_loss,
         "roofline": roof,
     }
-    if not args.no_cpu_baseline and not fwd:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s, args.optimizer)
+    # the whole step against the bound of its dominant kernel
+    if roof["bound"] == "mfma":
+        res["step_frac"] = round(res["achieved_tflops"] / peak, 4)
+    else:
+        res["step_frac"] = round(res["step_gbps"] / PEAK["hbm_gbps"], 4)
+    if want_cpu and not fwd:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s, args.optimizer)
         if w.name in ("mnist_b32", "mnist_b1024", "skinny_b8"):
             # the same oracle restricted to one BLAS thread, over a shorter sample
             from threadpoolctl import threadpool_limits
             with threadpool_limits(limits=1):
-                out["cpu_baseline_1thread"] = cpu_baseline(w, min(args.cpu_budget_s, 8.0), args.optimizer)
-    net.close()
+                res["cpu_baseline_1thread"] = cpu_baseline(w, min(args.cpu_budget_s, 8.0), args.optimizer)
+    if masks is not None:
+        x0, _, _ = synth.workload_batch(w, 0)
+        res["mask_bits"] = mask_counts(w, x0, Ws, masks)
+    return res
+
+
+def main():
+    args = parse()
+    if args.summarize:
+        summarize(args.summarize, args.workload, args.steps, args.warmup)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mlp_gemm_softmax_amd import synth
+
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    fwd = args.mode in ("forward", "probs")
+    head = measure(w, args, dev, not args.no_cpu_baseline, not args.no_cpu_baseline)
+    out = {
+        "metric": (f"MLP forward passes/sec ({'probabilities' if args.mode == 'probs' else 'logits'}, "
+                   "inference) + achieved TFLOP/s, 1 GPU" if fwd else
+                   "MLP train steps/sec + achieved TFLOP/s (fraction of MFMA/HBM roofline), 1 GPU"),
+        "value": head.pop("value"),
+        "unit": "forward passes/s" if fwd else "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head.pop("dtype"),
+        "data": "synthetic (seeded; MNIST-shaped uniform [0,1) pixels or N(0,1) features, uniform class ids)",
+        "config": head.pop("config"),
+    }
+    out.update(head)
+    # the other targeted workloads, measured the same way in the same run
+    extra = [n for n in args.extra_workloads.split(",") if n and n not in ("none", w.name)]
+    if extra:
+        out["also"] = {}
+        for name in extra:
+            out["also"][name] = measure(synth.WORKLOADS[name], args, dev, not args.no_cpu_baseline,
+                                        not args.no_cpu_baseline)
     print(json.dumps(out), flush=True)
 
 

@@ -45,9 +45,9 @@ ReLU kinks.  Where |z| is within the rounding-error bound of a float32 (or
 bfloat16-operand) evaluation, the sign of z -- and so the mask bit -- is not
 determined by the inputs at working precision, and both mask values give a
 correct derivative.  ``forward`` accepts an optional ``kink_choice`` per
-hidden layer; the choice is honoured only inside that band (|z| <= band,
-band = beta * (|a_{l-1}| @ |W_l|)) and the function reports how many bits it
-took from the choice and how many bits outside the band disagree with it.
+hidden layer; the choice is honoured only inside that band (|z_l| <= e_l,
+``mask_band``) and the function reports how many bits it took from the choice
+and how many bits outside the band disagree with it.
 """
 from __future__ import annotations
 
@@ -63,7 +63,24 @@ def _f64(a) -> np.ndarray:
 
 # --------------------------------------------------------------------------
 # Rounding-error bands for the mask tie-break.
+#
+# Rounding model of an evaluation at working precision (not of the oracle,
+# which is float64):
+#   * every float32 addition or multiplication of a dot product returns the
+#     exact result times (1 + d), |d| <= U_ACC = 2^-23, one unit in the last
+#     place: this holds for round-to-nearest and for truncation alike, since
+#     the rounding inside a matrix-core accumulation is not specified;
+#   * a bfloat16 operand is the float32 value times (1 + d), |d| <= U_BF16 =
+#     2^-8, the unit roundoff of round-to-nearest-even to 8 significant bits;
+#   * no underflow.
+# Then (Higham, "Accuracy and Stability of Numerical Algorithms", 2nd ed.,
+# section 3.1) a K-term dot product evaluated in any order is off by at most
+# gamma_K * sum_k |a_k w_k|, gamma_K = K u / (1 - K u).
 # --------------------------------------------------------------------------
+
+U_ACC = 2.0 ** -23
+U_BF16 = 2.0 ** -8
+
 
 def gamma(k: int, u: float) -> float:
     """Higham's gamma_k = k u / (1 - k u): relative bound on a k-term
@@ -74,26 +91,45 @@ def gamma(k: int, u: float) -> float:
     return ku / (1.0 - ku)
 
 
-def kink_betas(dims: Sequence[int], precision: str, safety: float = 2.0) -> List[float]:
-    """Per-hidden-layer band factor beta_l (l = 1..L-1).
+def layer_error_factors(K: int, precision: str):
+    """(c_own, c_in) of one layer z = a @ W with K = rows of W (the layer's
+    input width):
 
-    f32: the product chain up to layer l accumulates at most
-    sum_{j<=l} gamma_{d_{j-1}}(2^-24) relative error in |a||w| units.
-    bf16 operands add two roundings to 8 significant bits per product
-    (2 * 2^-8) on top of the f32 accumulation.  A safety factor of 2 covers
-    the error already present in a_{l-1}."""
-    u32 = 2.0 ** -24
-    ub = 2.0 ** -8
-    out = []
-    acc = 0.0
-    for l in range(1, len(dims) - 1):
-        k = dims[l - 1]
-        step = gamma(k, u32)
-        if precision == "bf16":
-            step += 2.0 * ub + ub * ub
-        acc += step
-        out.append(safety * acc)
-    return out
+        |z~ - z| <= c_own * (|a| @ |W|) + c_in * (|a~ - a| @ |W|)
+
+    where a~ is the evaluation's own (already perturbed) input.  Float32:
+    the dot product of a~ and W is off by gamma_K (|a~| @ |W|) <= gamma_K
+    (|a| + |a~ - a|) @ |W|, and the input error adds (|a~ - a| @ |W|), so
+    c_own = gamma_K, c_in = 1 + gamma_K.  bfloat16 operands: a^ = a~(1+s),
+    W^ = W(1+t) with |s|, |t| <= U_BF16, so a^ W^ - a W = a W((1+s)(1+t) - 1)
+    + (a~ - a) W (1+s)(1+t), and the float32 sum of the exact bf16 products
+    adds gamma_K (1+U_BF16)^2 (|a| + |a~ - a|) @ |W|:
+    c_own = 2 U_BF16 + U_BF16^2 + gamma_K (1+U_BF16)^2,
+    c_in = (1+U_BF16)^2 (1+gamma_K)."""
+    g = gamma(K, U_ACC)
+    ub = U_BF16 if precision == "bf16" else 0.0
+    return 2.0 * ub + ub * ub + g * (1.0 + ub) ** 2, (1.0 + ub) ** 2 * (1.0 + g)
+
+
+def mask_band(a, W, err_in, precision: str):
+    """Band e_l of one hidden layer: the elementwise bound
+
+        e_l = c_own (|a| @ |W|) + c_in (err_in @ |W|)  >=  |z~_l - z_l|
+
+    (``layer_error_factors``), with err_in the elementwise bound on
+    |a~_{l-1} - a_{l-1}| (None for the input x, which both sides hold
+    exactly).  Outside |z_l| <= e_l the evaluation's sign of z_l equals the
+    exact one.  ``forward`` hands e_l on to the next layer where
+    z_l > -e_l and 0 elsewhere: ReLU is 1-Lipschitz, and where z_l <= -e_l
+    both sides give 0."""
+    a = _f64(a)
+    W = _f64(W)
+    c_own, c_in = layer_error_factors(W.shape[0], precision)
+    absW = np.abs(W)
+    e = c_own * (np.abs(a) @ absW)
+    if err_in is not None:
+        e = e + c_in * (_f64(err_in) @ absW)
+    return e
 
 
 # --------------------------------------------------------------------------
@@ -101,18 +137,21 @@ def kink_betas(dims: Sequence[int], precision: str, safety: float = 2.0) -> List
 # --------------------------------------------------------------------------
 
 def forward(x, weights: Sequence, kink_choice: Optional[Sequence] = None,
-            kink_beta: Optional[Sequence[float]] = None) -> Dict:
+            precision: str = "f32") -> Dict:
     """Forward pass in float64.
 
     Returns a dict with ``a`` (a_0..a_{L-1}), ``z`` (z_1..z_L), ``m``
     (m_1..m_{L-1}, bool), ``logits`` (= z_L), and, when ``kink_choice`` is
-    given, ``adopted`` (bits taken from the choice inside the band) and
-    ``outside`` (bits of the choice that disagree with sign(z) outside the
-    band) per hidden layer."""
+    given, per hidden layer ``band`` (e_l of ``mask_band`` for an evaluation
+    in ``precision``), ``in_band`` (units with |z_l| <= e_l), ``adopted``
+    (bits taken from the choice inside the band, where it differs from
+    [z_l > 0]) and ``outside`` (bits of the choice that differ from
+    [z_l > 0] outside the band)."""
     W = [_f64(w) for w in weights]
     L = len(W)
     a = [_f64(x)]
-    zs, ms, adopted, outside = [], [], [], []
+    zs, ms, adopted, outside, bands, in_bands = [], [], [], [], [], []
+    err = None
     for l in range(1, L + 1):
         z = a[-1] @ W[l - 1]
         zs.append(z)
@@ -120,19 +159,24 @@ def forward(x, weights: Sequence, kink_choice: Optional[Sequence] = None,
             break
         m = z > 0.0
         if kink_choice is not None:
-            band = kink_beta[l - 1] * (np.abs(a[-1]) @ np.abs(W[l - 1]))
+            band = mask_band(a[-1], W[l - 1], err, precision)
             choice = np.asarray(kink_choice[l - 1]).astype(bool)
             in_band = np.abs(z) <= band
             differ = choice != m
             adopted.append(int(np.count_nonzero(differ & in_band)))
             outside.append(int(np.count_nonzero(differ & ~in_band)))
+            in_bands.append(int(np.count_nonzero(in_band)))
+            bands.append(band)
             m = np.where(in_band, choice, m)
+            err = np.where(z > -band, band, 0.0)
         ms.append(m)
         a.append(z * m)
     out = {"a": a, "z": zs, "m": ms, "logits": zs[-1]}
     if kink_choice is not None:
         out["adopted"] = adopted
         out["outside"] = outside
+        out["in_band"] = in_bands
+        out["band"] = bands
     return out
 
 
@@ -174,9 +218,9 @@ def probabilities(logits) -> np.ndarray:
 
 
 def forward_probabilities(x, weights: Sequence, kink_choice: Optional[Sequence] = None,
-                          kink_beta: Optional[Sequence[float]] = None) -> Dict:
+                          precision: str = "f32") -> Dict:
     """The forward pass followed by ``probabilities`` of its logits."""
-    fwd = forward(x, weights, kink_choice=kink_choice, kink_beta=kink_beta)
+    fwd = forward(x, weights, kink_choice=kink_choice, precision=precision)
     return {"fwd": fwd, "probs": probabilities(fwd["logits"])}
 
 
@@ -266,13 +310,12 @@ OPTIMIZERS = {"adam": adam, "laprop": laprop}
 # --------------------------------------------------------------------------
 
 def train_step(x, labels, weights: Sequence, lr: float,
-               kink_choice: Optional[Sequence] = None,
-               kink_beta: Optional[Sequence[float]] = None) -> Dict:
+               kink_choice: Optional[Sequence] = None, precision: str = "f32") -> Dict:
     """Forward, mean softmax-CE, backward and SGD for one batch.
 
     Returns loss (at the pre-update weights), dlogits, dW (per layer),
     W_new (per layer), and the forward dict under "fwd"."""
-    fwd = forward(x, weights, kink_choice, kink_beta)
+    fwd = forward(x, weights, kink_choice, precision)
     ce = softmax_xent(fwd["logits"], labels)
     bwd = backward(fwd, ce["dlogits"], weights)
     W_new = sgd(weights, bwd["dW"], lr)
@@ -280,7 +323,3 @@ def train_step(x, labels, weights: Sequence, lr: float,
             "dlogits": ce["dlogits"], "dW": bwd["dW"], "G": bwd["G"],
             "W_new": W_new, "fwd": fwd}
 
-
-def loss_only(x, labels, weights: Sequence) -> float:
-    """Mean loss at the given weights (forward + CE only)."""
-    return softmax_xent(forward(x, weights)["logits"], labels)["loss"]

@@ -28,3 +28,27 @@ def load_golden(name):
 @pytest.fixture(scope="session")
 def golden():
     return load_golden
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Per-layer ReLU-mask counts of the GPU parity checks: every row of the
+    named workloads, and one aggregate line for the other cases."""
+    try:
+        from tests import parity
+        from mlp_gemm_softmax_amd import synth
+    except Exception:
+        return
+    rows = parity.MASK_REPORT
+    if not rows:
+        return
+    tr = terminalreporter
+    tr.section("ReLU mask bits (GPU against the float64 oracle and against its own operands)")
+    tr.write_line("case | layer | units | oracle band | adopted | outside | self band | self differ in | self differ out")
+    named = [r for r in rows if r[0].split()[-1] in synth.WORKLOADS]
+    for r in named:
+        tr.write_line(" | ".join("-" if v is None else str(v) for v in r))
+    other = [r for r in rows if r[0].split()[-1] not in synth.WORKLOADS]
+    if other:
+        worst = max(r[4] / r[2] for r in other)
+        tr.write_line(f"other cases: {len(other)} layer checks, adopted at most {worst:.2e} of a "
+                      f"layer's units, {sum(r[5] for r in other)} bits outside the oracle's band")

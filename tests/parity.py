@@ -7,7 +7,9 @@ Gates (strict f32 / bf16 fast path):
   update     max|dW'_gpu - dW'_ref| <= tol * max|dW'_ref| + ulp(max|W|),  dW' = W' - W_old
   weights    max|W'_gpu - W'_ref| <= tol * max|W'_ref|
   masks      identical outside the rounding band of the oracle (inside it either
-             value is a correct ReLU derivative and the oracle follows the GPU's)
+             value is a correct ReLU derivative and the oracle follows the GPU's);
+             and, layer by layer, identical to the sign of the exact product of
+             the GPU's own operands outside that product's float32 summation bound
 """
 from __future__ import annotations
 
@@ -19,6 +21,12 @@ TOL = {"f32": 1e-5, "bf16": 2e-2}
 GRAD_TOL = {"f32": 1e-4, "bf16": 2e-2}
 # fraction of hidden units allowed to sit in the rounding band and differ
 MAX_ADOPTED = {"f32": 1e-4, "bf16": 2e-2}
+
+# Per-layer mask counts of every check, printed at the end of the test run
+# (tests/conftest.py): label, layer, units, units in the oracle's band, bits
+# adopted from the GPU there, bits differing outside it, units in the
+# self-consistency band, bits differing there, bits differing outside it.
+MASK_REPORT = []
 
 
 def to_dev(arrs, dev):
@@ -42,21 +50,71 @@ def gpu_train(net, x, t, lr):
 
 
 def oracle_step(x, t, Ws, lr, dims, precision, masks):
-    betas = mlp_oracle.kink_betas(dims, precision)
-    return mlp_oracle.train_step(x, t, Ws, lr, kink_choice=masks, kink_beta=betas)
+    return mlp_oracle.train_step(x, t, Ws, lr, kink_choice=masks, precision=precision)
 
 
-def check_masks(ref, B, dims, precision, label="", limit_band=True):
+def gpu_acts(net):
+    """The GPU's hidden activations a_1..a_{L-1} (float32; bf16 ones widened)."""
+    from mlp_gemm_softmax_amd import binding
+    return [net.read_state(binding.STATE_ACT, l).cpu().numpy() for l in range(1, net.n_layers)]
+
+
+def rne_bf16(v):
+    """float32 -> bfloat16 -> float32, round to nearest, ties to even
+    (integer form: add 0x7fff plus the lowest kept bit, drop 16 bits)."""
+    u = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def check_masks(ref, B, dims, precision, label="", limit_band=True, self_counts=None):
     """limit_band=False drops the cap on band adoptions (weights that left an
-    integer lattice put many pre-activations next to 0 on purpose)."""
+    integer lattice put many pre-activations next to 0 on purpose).
+    self_counts: per-layer (in band, differing in band, differing outside)
+    of ``check_mask_self_consistency``, for the report."""
     fwd = ref["fwd"]
     if len(dims) <= 2:
         return
-    for l, (ad, out) in enumerate(zip(fwd["adopted"], fwd["outside"]), start=1):
+    for l, (ad, out, ib) in enumerate(zip(fwd["adopted"], fwd["outside"], fwd["in_band"]), start=1):
+        sc = self_counts[l - 1] if self_counts else (None, None, None)
+        MASK_REPORT.append((label, l, B * dims[l], ib, ad, out) + tuple(sc))
         assert out == 0, f"{label} layer {l}: {out} mask bits differ outside the rounding band"
         frac = ad / float(B * dims[l])
         if limit_band:
             assert frac <= MAX_ADOPTED[precision], f"{label} layer {l}: {ad} band bits differ ({frac:.2e})"
+
+
+def check_mask_self_consistency(x, Ws, masks, acts, precision, label=""):
+    """Each hidden layer's mask against its own operands: the GPU forms
+    z_l from x (layer 1) or its own a_{l-1}, and the operand copy of W_l
+    (bf16-rounded in bf16 mode, as are x and the activations it stores), so
+    its mask must equal [z > 0] of the exact product of those operands
+    wherever |z| exceeds the float32 summation bound gamma_K (|a| @ |W|),
+    gamma_K = K u / (1 - K u), u = 2^-23 (one ulp per operation, whatever the
+    matrix cores' rounding).  Returns per layer (units in that band, bits
+    differing inside it, bits differing outside it); asserts the last is 0."""
+    bf16 = precision == "bf16"
+    out = []
+    a = np.asarray(x, np.float32)
+    for l in range(1, len(Ws)):
+        W = np.asarray(Ws[l - 1], np.float32)
+        aop = (rne_bf16(a) if bf16 else a).astype(np.float64)
+        Wop = (rne_bf16(W) if bf16 else W).astype(np.float64)
+        K = W.shape[0]
+        u = 2.0 ** -23
+        g = K * u / (1.0 - K * u)
+        z = aop @ Wop
+        band = g * (np.abs(aop) @ np.abs(Wop))
+        m = np.asarray(masks[l - 1]).astype(bool)
+        in_band = np.abs(z) <= band
+        differ = m != (z > 0)
+        counts = (int(np.count_nonzero(in_band)), int(np.count_nonzero(differ & in_band)),
+                  int(np.count_nonzero(differ & ~in_band)))
+        assert counts[2] == 0, (f"{label} layer {l}: {counts[2]} mask bits disagree with the sign of the "
+                                f"GPU's own operands' product outside its summation bound")
+        out.append(counts)
+        a = np.asarray(acts[l - 1], np.float32)
+    return out
 
 
 def rel_max(a, ref):

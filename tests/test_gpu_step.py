@@ -110,11 +110,13 @@ def _workload_parity(torch_dev, name, steps_to_check=(0,)):
     xd, td = P.to_dev([x, t], dev)
     # gradients, no update
     loss, dws, dl, masks = P.gpu_grads(net, xd, td)
+    sc = P.check_mask_self_consistency(x, Ws, masks, P.gpu_acts(net), prec, name)
     ref = P.oracle_step(x, t, Ws, w.lr, w.dims, prec, masks)
-    P.check_masks(ref, w.batch, w.dims, prec, name)
+    P.check_masks(ref, w.batch, w.dims, prec, name, self_counts=sc)
     P.check_grads(loss, dws, dl, ref, prec, name)
     # fused update from the same weights
     loss2, W_new, masks2 = P.gpu_train(net, xd, td, w.lr)
+    P.check_mask_self_consistency(x, Ws, masks2, P.gpu_acts(net), prec, name)
     ref2 = P.oracle_step(x, t, Ws, w.lr, w.dims, prec, masks2)
     P.check_update(loss2, W_new, Ws, ref2, prec, name)
     P.check_fused_update_matches_grads(W_new, Ws, dws, w.lr)
@@ -234,8 +236,9 @@ def test_edge_shapes(torch_dev, dims, B, precision):
     net = make_net(dims, B, precision, Ws, dev)
     xd, td = P.to_dev([x, t], dev)
     loss, dws, dl, masks = P.gpu_grads(net, xd, td)
+    sc = P.check_mask_self_consistency(x, Ws, masks, P.gpu_acts(net), precision, str(dims))
     ref = P.oracle_step(x, t, Ws, lr, dims, precision, masks)
-    P.check_masks(ref, B, dims, precision, str(dims))
+    P.check_masks(ref, B, dims, precision, str(dims), self_counts=sc)
     if dims[-1] == 1:
         assert loss == 0.0 and np.all(dl == 0.0)
     P.check_grads(loss, dws, dl, ref, precision, str(dims))
@@ -537,14 +540,14 @@ def _adaptive_parity(torch_dev, rule, dims, B, precision, exact, lr=1e-3):
         W_now = [w.cpu().numpy() for w in net.read_params()]
         loss_g, dws, dl, masks = P.gpu_grads(net, xd, td)
         ref = mlp_oracle.train_step(x, t, W_now, 0.0, kink_choice=masks,
-                                    kink_beta=mlp_oracle.kink_betas(dims, precision))
+                                    precision=precision)
         # after one step from an integer problem many pre-activations sit
         # next to 0 (they were exactly 0): no cap on band adoptions there
         P.check_masks(ref, B, dims, precision, f"{rule} step {step}", limit_band=not exact)
         P.check_grads(loss_g, dws, dl, ref, precision, f"{rule} step {step}")
         # the trajectory's own oracle gradients (at the oracle's weights)
         rt = mlp_oracle.train_step(x, t, W_ref, 0.0, kink_choice=masks,
-                                   kink_beta=mlp_oracle.kink_betas(dims, precision))
+                                   precision=precision)
         dg = [P.GRAD_TOL[precision] * float(np.max(np.abs(g))) for g in rt["dW"]]
         if exact and step == 1:
             for a, r in zip(dws, rt["dW"]):
@@ -745,8 +748,9 @@ def test_forward_logits_parity(torch_dev, name):
     net.forward_async(xd, logits)
     torch.cuda.synchronize()
     masks = [net.read_state(binding.STATE_MASK, l).cpu().numpy() for l in range(1, net.n_layers)]
-    ref = mlp_oracle.forward(x, Ws, kink_choice=masks, kink_beta=mlp_oracle.kink_betas(w.dims, w.precision))
-    P.check_masks({"fwd": ref}, w.batch, w.dims, w.precision, name)
+    sc = P.check_mask_self_consistency(x, Ws, masks, P.gpu_acts(net), w.precision, name)
+    ref = mlp_oracle.forward(x, Ws, kink_choice=masks, precision=w.precision)
+    P.check_masks({"fwd": ref}, w.batch, w.dims, w.precision, "forward " + name, self_counts=sc)
     err, scale = P.rel_max(logits.cpu().numpy(), ref["logits"])
     gtol = P.GRAD_TOL[w.precision]
     assert err <= gtol * scale, f"{name} logits: {err:.3e} > {gtol} * {scale:.3e}"
@@ -875,7 +879,7 @@ def test_forward_probs_parity(torch_dev, dims, B, precision):
     net.profile(False)
     masks = [net.read_state(binding.STATE_MASK, l).cpu().numpy() for l in range(1, net.n_layers)]
     ref = mlp_oracle.forward_probabilities(x, Ws, kink_choice=masks,
-                                           kink_beta=mlp_oracle.kink_betas(dims, precision))
+                                           precision=precision)
     P.check_masks({"fwd": ref["fwd"]}, B, dims, precision, "probs")
     p = probs.cpu().numpy()
     assert np.array_equal(p, again.cpu().numpy()), "two calls differ"

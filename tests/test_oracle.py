@@ -333,16 +333,17 @@ def test_kink_tiebreak_only_inside_band():
     base = O.forward(x, Ws)
     z = base["z"][0]
     flipped = ~base["m"][0]
-    betas = O.kink_betas((16, 12, 3), "f32")
-    out = O.forward(x, Ws, kink_choice=[flipped], kink_beta=betas)
-    band = betas[0] * (np.abs(x) @ np.abs(Ws[0]))
+    out = O.forward(x, Ws, kink_choice=[flipped], precision="f32")
+    band = O.mask_band(x, Ws[0], None, "f32")
+    np.testing.assert_array_equal(out["band"][0], band)
     assert out["adopted"][0] == int(np.count_nonzero(np.abs(z) <= band))
     assert out["outside"][0] == int(np.count_nonzero(np.abs(z) > band))
+    assert out["in_band"][0] == out["adopted"][0]
     np.testing.assert_array_equal(out["m"][0], base["m"][0])  # nothing in band here
-    # Force one element into the band: the choice is then taken there.
+    # Force one column into the band: the choice is then taken there.
     Ws2 = [w.copy() for w in Ws]
     Ws2[0][:, 0] *= 0.0
-    out2 = O.forward(x, Ws2, kink_choice=[np.ones_like(flipped)], kink_beta=betas)
+    out2 = O.forward(x, Ws2, kink_choice=[np.ones_like(flipped)], precision="f32")
     assert np.all(out2["m"][0][:, 0])
     assert out2["adopted"][0] == 8
 
@@ -352,6 +353,241 @@ def test_gamma_bound():
     assert O.gamma(1, u) == pytest.approx(u, rel=1e-6)
     assert O.gamma(4096, u) == pytest.approx(4096 * u / (1 - 4096 * u))
     assert O.gamma(2 ** 25, u) == math.inf
+
+
+# ------------------------------------------------------------ mask band --
+# The band bounds |z~ - z| for any evaluation of a layer in float32 (or with
+# bfloat16 operands and float32 sums) under the rounding model the oracle
+# states: one unit in the last place per float32 operation, round-to-nearest-
+# even for bfloat16 operands.  The pins evaluate dot products and small
+# networks in emulated float32 -- several summation orders, round-to-nearest
+# and truncation -- and check (a) that the band always covers the error, and
+# (b) that constructed worst cases come close to the band, so that a band
+# with a wrong width index, a dropped cross-layer term, a round-to-nearest-
+# only unit or a single bfloat16 rounding fails.
+
+def _f32_round(v, mode):
+    """float64 values (each the exact result of one float32 operation) to
+    float32: "rne" round to nearest even, "rz" toward zero."""
+    v = np.asarray(v, np.float64)
+    f = v.astype(np.float32)
+    if mode == "rz":
+        over = np.abs(f.astype(np.float64)) > np.abs(v)
+        f = np.where(over, np.nextafter(f, np.float32(0)), f)
+    return f.astype(np.float64)
+
+
+def _bf16_rne(v):
+    """float32 -> bfloat16 -> float32, round to nearest, ties to even."""
+    u = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _emulate_dot(a, W, order="seq", mode="rne", bf16=False):
+    """z~ = a @ W evaluated in float32: products exact (as in a fused
+    multiply-add, and exact anyway for bfloat16 operands) and each addition
+    rounded; order "seq" (k = 0, 1, ...), "blk32" (sequential sums of 32-long
+    blocks, then of the block sums) or "pair" (pairwise tree)."""
+    a = np.asarray(a, np.float32).astype(np.float64)
+    W = np.asarray(W, np.float32).astype(np.float64)
+    if bf16:
+        a, W = _bf16_rne(a), _bf16_rne(W)
+    P = a[:, :, None] * W[None, :, :]          # [n, K, m], exact in float64
+    P = _f32_round(P, mode) if not bf16 else P  # float32 products (exact for bf16)
+
+    def seq(Q):
+        s = Q[:, 0, :]
+        for k in range(1, Q.shape[1]):
+            s = _f32_round(s + Q[:, k, :], mode)
+        return s
+
+    if order == "seq":
+        return seq(P)
+    if order == "blk32":
+        K = P.shape[1]
+        parts = [seq(P[:, i:i + 32, :])[:, None, :] for i in range(0, K, 32)]
+        return seq(np.concatenate(parts, axis=1))
+    while P.shape[1] > 1:   # pairwise
+        if P.shape[1] % 2:
+            P = np.concatenate([P, np.zeros_like(P[:, :1, :])], axis=1)
+        P = _f32_round(P[:, 0::2, :] + P[:, 1::2, :], mode)
+    return P[:, 0, :]
+
+
+def _exact_dot(a, W):
+    a = np.asarray(a, np.float32).astype(np.float64)
+    W = np.asarray(W, np.float32).astype(np.float64)
+    return np.array([[math.fsum(a[i] * W[:, j]) for j in range(W.shape[1])] for i in range(a.shape[0])])
+
+
+def _band_covers_random_dots(band_fn, K, precision, seed):
+    """Random dot products of width K in four evaluation orders: the band
+    covers every error."""
+    r = _rng(500 + seed)
+    a = r.standard_normal((6, K)).astype(np.float32)
+    W = r.uniform(-1, 1, (K, 2)).astype(np.float32) * np.float32(math.sqrt(6.0 / K))
+    a[3:] = np.abs(a[3:])                       # rows without cancellation
+    W[:, 1] = np.abs(W[:, 1])
+    z = _exact_dot(a, W)
+    band = band_fn(a, W, None, precision)
+    for order, mode in (("seq", "rne"), ("blk32", "rne"), ("pair", "rne"), ("seq", "rz")):
+        zt = _emulate_dot(a, W, order, mode, bf16=precision == "bf16")
+        if not np.all(np.abs(zt - z) <= band):
+            return False
+    return True
+
+
+def _worst_cases_reach_band(band_fn, K):
+    """Constructed float32 sums whose error comes close to the band."""
+    ok = True
+    # round-to-nearest, sequential: 2^24 + 1 + 1 + ... keeps rounding back to
+    # 2^24, an error of (K - 1) ulp/2 against sum |a w| = 2^24 + K - 1
+    a = np.ones((1, K), np.float32)
+    a[0, 0] = 2.0 ** 24
+    W = np.ones((K, 3), np.float32)
+    err = abs(_emulate_dot(a, W, "seq", "rne")[0, 0] - (2.0 ** 24 + K - 1))
+    band = band_fn(a, W, None, "f32")[0, 0]
+    ok &= err <= band and err >= 0.4 * band
+    # truncation: adding just under 2 to 2^24 truncates back, an error of
+    # nearly a whole ulp per addition
+    a = np.full((1, K), 2.0 - 2.0 ** -22, np.float32)
+    a[0, 0] = 2.0 ** 24
+    exact = 2.0 ** 24 + (K - 1) * (2.0 - 2.0 ** -22)
+    err = abs(_emulate_dot(a, W, "seq", "rz")[0, 0] - exact)
+    band = band_fn(a, W, None, "f32")[0, 0]
+    ok &= err <= band and err >= 0.85 * band
+    # bfloat16 operands that both round down by nearly 2^-8 relative
+    v = np.float32(1.0 + 2.0 ** -8 - 2.0 ** -20)
+    a = np.full((1, K), v, np.float32)
+    W = np.full((K, 3), v, np.float32)
+    exact = K * float(v) * float(v)
+    err = abs(_emulate_dot(a, W, "seq", "rne", bf16=True)[0, 0] - exact)
+    band = band_fn(a, W, None, "bf16")[0, 0]
+    ok &= err <= band and (K > 1024 or err >= 0.9 * band)
+    return bool(ok)
+
+
+def _emulate_forward(x, Ws, order, mode, bf16):
+    """Hidden pre-activations z~_l of an evaluation in emulated float32 (its
+    own ReLU outputs feed the next layer, rounded to bfloat16 as operands)."""
+    a, zs = np.asarray(x, np.float32), []
+    for W in Ws[:-1]:
+        z = _emulate_dot(a, W, order, mode, bf16)
+        zs.append(z)
+        a = np.maximum(z, 0.0).astype(np.float32)
+    return zs
+
+
+def _network_band_holds(x, Ws, precision, order, mode):
+    zt = _emulate_forward(x, Ws, order, mode, precision == "bf16")
+    masks = [z > 0 for z in zt]
+    ref = O.forward(x, Ws, kink_choice=masks, precision=precision)
+    ok = all(o == 0 for o in ref["outside"])
+    for l, (z_em, band) in enumerate(zip(zt, ref["band"])):
+        # exact z_l of the oracle's forward (float64 matmul on float32 data
+        # reaches float32-rounding-free values here: widths <= 300)
+        ok &= bool(np.all(np.abs(z_em - ref["z"][l]) <= band + 1e-9 * np.abs(ref["z"][l])))
+    return bool(ok)
+
+
+def _cross_layer_case():
+    """A first layer whose truncated sum loses 2(K - 1) units and a second
+    layer that passes the error on unchanged: dims K -> 1 -> 1 -> 2."""
+    K = 200
+    x = np.full((1, K), 2.0 - 2.0 ** -22, np.float32)
+    x[0, 0] = 2.0 ** 24
+    Ws = [np.ones((K, 1), np.float32), np.ones((1, 1), np.float32), np.ones((1, 2), np.float32)]
+    return x, Ws
+
+
+def _band_pins_pass():
+    """All band pins against the current ``O.mask_band`` (and ``O.forward``,
+    which calls it)."""
+    try:
+        ok = True
+        for i, K in enumerate((10, 784, 1024, 4096, 11008)):
+            for prec in ("f32", "bf16"):
+                ok &= _band_covers_random_dots(O.mask_band, K, prec, i)
+        for K in (10, 784, 4096):
+            ok &= _worst_cases_reach_band(O.mask_band, K)
+        x, Ws = _cross_layer_case()
+        ok &= _network_band_holds(x, Ws, "f32", "seq", "rz")
+        r = _rng(31)
+        x = r.standard_normal((4, 300)).astype(np.float32)
+        Ws = [(r.uniform(-1, 1, (300, 64)) * 0.14).astype(np.float32),
+              (r.uniform(-1, 1, (64, 48)) * 0.3).astype(np.float32),
+              (r.uniform(-1, 1, (48, 5)) * 0.35).astype(np.float32)]
+        for prec in ("f32", "bf16"):
+            for order, mode in (("seq", "rne"), ("pair", "rne"), ("blk32", "rz")):
+                ok &= _network_band_holds(x, Ws, prec, order, mode)
+        return bool(ok)
+    except Exception:
+        return False
+
+
+def test_mask_band_pins():
+    assert _band_pins_pass()
+
+
+def test_mask_band_factors_closed_form():
+    """The per-layer factors written out: float32 gamma_K at one ulp
+    (2^-23); bfloat16 adds two operand roundings of 2^-8."""
+    g = 1024 * 2.0 ** -23 / (1 - 1024 * 2.0 ** -23)
+    assert O.layer_error_factors(1024, "f32") == pytest.approx((g, 1 + g), rel=1e-15)
+    g = 4096 * 2.0 ** -23 / (1 - 4096 * 2.0 ** -23)
+    ub = 2.0 ** -8
+    c_own, c_in = O.layer_error_factors(4096, "bf16")
+    assert c_own == pytest.approx(2 * ub + ub * ub + g * (1 + ub) ** 2, rel=1e-15)
+    assert c_in == pytest.approx((1 + ub) ** 2 * (1 + g), rel=1e-15)
+
+
+def test_mask_band_two_dims_sets(golden):
+    """Bands of two small networks checked against values worked by hand
+    (tests/golden/mask_band.txt)."""
+    g = golden("mask_band.txt")
+    for tag in ("n1", "n2"):
+        dims = [int(d) for d in g[f"{tag}_dims"]]
+        x = np.array(g[f"{tag}_x"]).reshape(1, dims[0])
+        Ws, off = [], 0
+        flat = g[f"{tag}_W"]
+        for a, b in zip(dims[:-1], dims[1:]):
+            Ws.append(np.array(flat[off:off + a * b]).reshape(a, b))
+            off += a * b
+        prec = "bf16" if g[f"{tag}_bf16"][0] else "f32"
+        fwd = O.forward(x, Ws)
+        out = O.forward(x, Ws, kink_choice=fwd["m"], precision=prec)
+        for l in range(len(dims) - 2):
+            want = np.array(g[f"{tag}_e{l + 1}"])
+            np.testing.assert_allclose(out["band"][l].ravel(), want, rtol=1e-12, atol=0)
+
+
+def _band_mutant(kind):
+    def band(a, W, err_in, precision):
+        a = np.asarray(a, np.float64)
+        W = np.asarray(W, np.float64)
+        K = W.shape[1] if kind == "wrong_width" else W.shape[0]
+        u = 2.0 ** -24 if kind == "nearest_only" else 2.0 ** -23
+        g = O.gamma(K, u)
+        ub = 2.0 ** -8 if precision == "bf16" else 0.0
+        rb = ub if kind == "bf16_one_rounding" else 2 * ub + ub * ub
+        e = (rb + g * (1 + ub) ** 2) * (np.abs(a) @ np.abs(W))
+        if err_in is not None and kind != "no_cross_layer":
+            e = e + (1 + ub) ** 2 * (1 + g) * (np.asarray(err_in) @ np.abs(W))
+        return e
+    return band
+
+
+@pytest.mark.parametrize("kind", ["wrong_width", "nearest_only", "bf16_one_rounding", "no_cross_layer"])
+def test_mask_band_pins_reject_planted_mistakes(monkeypatch, kind):
+    monkeypatch.setattr(O, "mask_band", _band_mutant(kind))
+    assert not _band_pins_pass()
+
+
+def test_mask_band_mutant_harness_matches_the_oracle(monkeypatch):
+    """The unmutated form of the mutant harness is the oracle's band."""
+    monkeypatch.setattr(O, "mask_band", _band_mutant("none"))
+    assert _band_pins_pass()
 
 
 # ---------------------------------------------------------------- mutants --
