@@ -30,8 +30,8 @@
  *   - Layers are numbered 0 .. n_layers-1; weight l has shape
  *     [dims[l], dims[l+1]] ([in, out], out = in @ W, as in the README).
  *   - Every tensor is row-major and contiguous with its logical shape; no
- *     padding is visible (README "Contents": checkpoints hold logical tensors
- *     without device padding).
+ *     padding is visible (README "Contents" says checkpoints keep tensors at
+ *     their logical shapes, free of the device's padding).
  *   - Pointers named *dev* or documented as device pointers are HIP device
  *     memory, 16-byte aligned; they are owned by the caller.  Host pointers
  *     are documented as such.
@@ -41,8 +41,9 @@
  *     inputs must be ready in that stream's order.  One context may be used
  *     by one host thread at a time; calls on one context are not
  *     re-entrant.
- *   - Every argument is checked before anything is enqueued (the README's
- *     "preflight the restore before mutation"): on an error return the
+ *   - Every argument is checked before anything is enqueued (README
+ *     "Contents": a restore is validated in full before it changes any
+ *     state; the same rule applies to every call here): on an error return the
  *     context and device state are unchanged, and mlp_last_error() describes
  *     the problem.  A HIP failure after work was enqueued returns
  *     MLP_ERR_HIP and poisons the context: later calls return MLP_ERR_STATE
@@ -112,7 +113,11 @@ typedef struct mlp_config {
 int32_t mlp_abi_version(void);
 
 /* Device workspace the configuration needs, in bytes (a multiple of 256);
- * 0 if the configuration is invalid.  Host only. */
+ * 0 if the configuration is invalid.  Host only.  The session's buffer plan
+ * (README "Environment variables": buffers are planned at build with
+ * lifetime aliasing, MEGANEURA_NO_ALIAS / MEGANEURA_DUMP_PLAN) made static:
+ * weights, activations, masks, a ping-pong pair of gradient buffers, split-K
+ * partials and counters, laid out once for this shape. */
 size_t mlp_workspace_bytes(const mlp_config* cfg);
 
 /* Create a context that lives in `workspace` (device memory of at least
@@ -123,18 +128,29 @@ size_t mlp_workspace_bytes(const mlp_config* cfg);
  * ahead of time, so this only plans buffers and launch shapes. */
 mlp_status mlp_create(const mlp_config* cfg, void* workspace, size_t bytes, mlp_ctx** out);
 
-/* Free the host-side context.  Device memory is the caller's. */
+/* Free the host-side context (the end of the session that README "Example"
+ * builds with build_session).  Device memory is the caller's; NULL is
+ * ignored. */
 void mlp_destroy(mlp_ctx* ctx);
 
 /* Copy weight `layer` in: w is a device float32 [dims[layer], dims[layer+1]]
- * array.  In MLP_BF16 mode the bfloat16 operand copy is refreshed too. */
+ * array (the parameter g.parameter("w1", &[784, 128]) of README "Example";
+ * the upload the README's "Environment variables" table calls
+ * set_parameter).  In MLP_BF16 mode the bfloat16 operand copy is refreshed
+ * too.  Errors: MLP_ERR_ARG (layer out of range, w NULL or not 16-byte
+ * aligned), MLP_ERR_HIP. */
 mlp_status mlp_set_params(mlp_ctx* ctx, int32_t layer, const float* w);
 
 /* Copy the float32 master of weight `layer` out to device memory `dst`
- * ([dims[layer], dims[layer+1]]). */
+ * ([dims[layer], dims[layer+1]]), in stream order: the analogue of
+ * read_node_by_name on a parameter (README "Debugging": debug sessions read
+ * materialised values after a step).  Errors: MLP_ERR_ARG, MLP_ERR_STATE
+ * (context poisoned), MLP_ERR_HIP. */
 mlp_status mlp_read_params(mlp_ctx* ctx, int32_t layer, float* dst);
 
-/* Forward pass only.  x: device float32 [B, d0].  logits: device float32
+/* Forward pass only: the graph of README "Example" up to its logits (and
+ * the loss when labels are given), as run by the fresh inference session of
+ * the train-to-deploy example (README "Contents").  x: device float32 [B, d0].  logits: device float32
  * [B, C] or NULL.  labels: device float32 [B, C] (dense, non-negative rows)
  * or NULL.  loss: host float, written (after a stream synchronisation) with
  * the mean softmax cross-entropy when labels and loss are both non-NULL.
@@ -154,7 +170,8 @@ mlp_status mlp_forward(mlp_ctx* ctx, const float* x, float* logits,
  * on the fused path. */
 mlp_status mlp_forward_probs(mlp_ctx* ctx, const float* x, float* probs);
 
-/* One training step: forward, mean softmax-CE, backward and the update of
+/* One training step (README "Example": trainer.train, one batch; the
+ * autodiff of build_session gives the backward): forward, mean softmax-CE, backward and the update of
  * every layer (W_l <- W_l - lr * dW_l, or the rule mlp_set_optimizer chose),
  * all gradients taken at the pre-update weights.  x: device float32 [B, d0]; labels: device float32
  * [B, C]; lr: finite.  loss: host float or NULL; the call synchronises the
@@ -163,12 +180,18 @@ mlp_status mlp_train_step(mlp_ctx* ctx, const float* x, const float* labels,
                           float lr, float* loss);
 
 /* As mlp_train_step, but nothing waits: the mean loss is written to
- * `loss_dev` (device float32, or NULL to drop it) in stream order. */
+ * `loss_dev` (device float32, or NULL to drop it) in stream order (README
+ * "Debugging" separates a session's step() from its wait()).  Errors as
+ * mlp_train_step; a HIP failure after the first launch poisons the
+ * context. */
 mlp_status mlp_train_step_async(mlp_ctx* ctx, const float* x, const float* labels,
                                 float lr, float* loss_dev);
 
 /* Gradients without an update, from the same kernels and accumulation order
- * as a training step.  dw: host array of n_layers device pointers, each a
+ * as a training step: the backward of README "Example" read out as a debug
+ * session would (README "Debugging"), so that forward and backward can be
+ * gated separately (arXiv abstract of "Meganeura: Portable GPU Training and
+ * Inference through Vulkan and Metal").  dw: host array of n_layers device pointers, each a
  * float32 [dims[l], dims[l+1]] output.  dlogits: device float32 [B, C] or
  * NULL.  loss: host float or NULL (the call synchronises when non-NULL). */
 mlp_status mlp_grads(mlp_ctx* ctx, const float* x, const float* labels,
@@ -196,9 +219,10 @@ size_t mlp_optimizer_bytes(const mlp_config* cfg, int32_t opt);
 mlp_status mlp_set_optimizer(mlp_ctx* ctx, int32_t opt, float beta1, float beta2, float eps,
                              void* state, size_t bytes);
 
-/* Checkpoints (README "Contents": checkpoints hold logical tensors without
- * device padding, and a restore is preflighted before it mutates anything;
- * the train-to-deploy example reloads one into a fresh inference session).
+/* Checkpoints (README "Contents": tensors are stored at their logical
+ * shapes without the device's padding, and a restore is validated in full
+ * before it changes any state; the train-to-deploy example reloads one into
+ * a fresh inference session).
  * A checkpoint is host memory: a 136-byte header (magic "MLPCKPT1", version
  * 1, layer count, precision of the writer, update rule, widths, beta1, beta2,
  * eps, step count, payload size, FNV-1a-64 checksum of the payload) and the
@@ -279,9 +303,14 @@ mlp_status mlp_profile_read(mlp_ctx* ctx, int32_t idx, char* name, size_t name_l
                             double* total_ms, int64_t* launches,
                             double* flops, double* bytes);
 
+/* Name of a status code ("MLP_OK", ...; "MLP_ERR_UNKNOWN" otherwise), a
+ * static string.  With mlp_last_error, the structured errors of README
+ * "Debugging". */
 const char* mlp_status_string(mlp_status s);
 /* Message of the last error on this context ("" if none); valid until the
- * next call on the context.  With ctx == NULL: the last creation error. */
+ * next call on the context.  With ctx == NULL: the last creation error (or
+ * checkpoint_info error) of this thread.  README "Debugging": failures come
+ * back as structured errors that name what went wrong. */
 const char* mlp_last_error(const mlp_ctx* ctx);
 
 #ifdef __cplusplus

@@ -260,14 +260,20 @@ bool tail_fused(const mlp_ctx* c) {
     return c->head && !c->skinny && c->dw[0].small_waves > 0 && c->dw[0].cfg == TileCfg::T32x16;
 }
 
-// Whether the output layer's head runs inside the last hidden layer's
-// forward launch (32 x 16 small-product tiles with 16 waves; the workgroup
-// finishing a 32-row block runs the head for it), else in a launch of its own.
-bool head_fused(const mlp_ctx* c) {
+// Whether the last hidden layer's forward plan could carry the output
+// layer's head (32 x 16 small-product tiles with 16 waves; the workgroup
+// finishing a 32-row block runs the head for it).
+bool head_fusable(const mlp_ctx* c) {
     if (!c->head || c->skinny || c->L < 2) return false;
     const GemmPlan& g = c->fwd[c->L - 2];
     return g.small_waves == 16 && g.cfg == TileCfg::T32x16 &&
            head_lds_bytes(c->dims[c->L - 1], c->dims[c->L], 32) <= 64 * 1024;
+}
+
+// Whether the head runs inside that launch, which takes one ticket per
+// 32-row block; else the head runs in a launch of its own.
+bool head_fused(const mlp_ctx* c) {
+    return head_fusable(c) && (size_t)(c->B + 31) / 32 <= c->ticket_cap;
 }
 
 OptScalars opt_scalars(const mlp_ctx* c, float lr) {
@@ -863,12 +869,14 @@ size_t plan_and_carve(mlp_ctx* c, char* base) {
     }
     if (c->head && !c->skinny && L >= 2) {
         // the head rides along with the last hidden layer's forward: that
-        // launch needs 16 waves and one ticket per 32-row block
+        // launch needs 16 waves and one ticket per 32-row block.  The
+        // tickets are reserved whenever the session has the fused output
+        // layer, so that mlp_tune may switch that forward to such a plan.
         GemmPlan& g = c->fwd[L - 2];
         if (g.small_waves > 0 && g.cfg == TileCfg::T32x16 &&
             head_lds_bytes(c->dims[L - 1], c->dims[L], 32) <= 64 * 1024)
             g.small_waves = 16;
-        if (head_fused(c)) max_tickets = std::max(max_tickets, (size_t)(B + 31) / 32);
+        max_tickets = std::max(max_tickets, (size_t)(B + 31) / 32);
     }
     int max_hidden = 1;
     for (int l = 1; l < L; ++l) max_hidden = std::max(max_hidden, c->dims[l]);

@@ -49,6 +49,7 @@ def pytest_terminal_summary(terminalreporter):
         tr.write_line(" | ".join("-" if v is None else str(v) for v in r))
     other = [r for r in rows if r[0].split()[-1] not in synth.WORKLOADS]
     if other:
-        worst = max(r[4] / r[2] for r in other)
-        tr.write_line(f"other cases: {len(other)} layer checks, adopted at most {worst:.2e} of a "
-                      f"layer's units, {sum(r[5] for r in other)} bits outside the oracle's band")
+        worst = max(other, key=lambda r: r[4] / r[2])
+        tr.write_line(f"other cases: {len(other)} layer checks, adopted at most {worst[4] / worst[2]:.2e} "
+                      f"of a layer's units ({worst[0]} layer {worst[1]}), "
+                      f"{sum(r[5] for r in other)} bits outside the oracle's band")

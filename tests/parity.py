@@ -19,8 +19,15 @@ from oracle import mlp_oracle
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
 GRAD_TOL = {"f32": 1e-4, "bf16": 2e-2}
-# fraction of hidden units allowed to sit in the rounding band and differ
-MAX_ADOPTED = {"f32": 1e-4, "bf16": 2e-2}
+# Fraction of a layer's hidden units whose mask bit may differ from the
+# oracle's inside its rounding band.  Every such bit is a valid ReLU choice
+# (the band is a worst-case bound), so the cap is a regression guard, set
+# from measurement: on one MI355X the wide workload differs in 1 and 6 of
+# 16.8M units per layer in float32 (3.6e-7) and in 12858 and 17816 with
+# bf16 operands (7.7e-4, 1.06e-3); the small and ragged cases stay below
+# 1.4e-3.  The caps sit at about 4x the largest of these (bf16) and well
+# above them (f32, where a dozen units of a small layer are already 1e-4).
+MAX_ADOPTED = {"f32": 1e-4, "bf16": 5e-3}
 
 # Per-layer mask counts of every check, printed at the end of the test run
 # (tests/conftest.py): label, layer, units, units in the oracle's band, bits

@@ -127,26 +127,15 @@ import struct
 
 import numpy as np
 
-
-def _fnv1a(data: bytes) -> int:
-    h = 1469598103934665603
-    for b in data:
-        h ^= b
-        h = (h * 1099511628211) & 0xFFFFFFFFFFFFFFFF
-    return h
+from tests import ckpt_format
 
 
 def _checkpoint(dims, opt=0, step=0, betas=(0.0, 0.0, 0.0), seed=0):
     rng = np.random.default_rng(seed)
-    parts = [rng.standard_normal((dims[l], dims[l + 1])).astype("<f4") for l in range(len(dims) - 1)]
-    if opt:
-        parts = parts + [np.abs(p) for p in parts] + [p * p for p in parts]
-    payload = b"".join(p.tobytes() for p in parts)
-    d = list(dims) + [0] * (17 - len(dims))
-    head = struct.pack("<8s4I17i3f2Iq2Q", b"MLPCKPT1", 1, len(dims) - 1, 0, opt, *d, *betas, 0, 0, step,
-                       len(payload), _fnv1a(payload))
-    assert len(head) == 136
-    return head + payload
+    Ws = [rng.standard_normal((dims[l], dims[l + 1])).astype("<f4") for l in range(len(dims) - 1)]
+    m = [np.abs(w) for w in Ws] if opt else None
+    v = [w * w for w in Ws] if opt else None
+    return ckpt_format.build(dims, Ws, m, v, opt=opt, step=step, betas=betas)
 
 
 def test_checkpoint_info_reads_the_documented_format():

@@ -327,7 +327,16 @@ def test_fused_splitk_loss_matches_forward(torch_dev):
 
 
 def test_dlogits_rows_sum_to_zero(torch_dev):
-    """P2 on the GPU: row sums of dlogits vanish to float32 rounding."""
+    """P2 on the GPU: row sums of dlogits vanish to float32 rounding.
+
+    The kernel forms e_c = exp(z_c - max), S = sum_c e_c (float32, any
+    order: off by at most (C-1)u sum e, u = 2^-24, all terms positive),
+    p_c = e_c / S (correctly rounded: no fast-math), then (p_c s - t_c)/B
+    with s = 1 exactly for one-hot rows.  sum_c e_c/S = 1 within (C-1)u;
+    rounding the C quotients adds at most u (they sum to ~1); p - 1 on the
+    label's column rounds by at most u (exact when p >= 1/2, Sterbenz); the
+    other columns subtract 0; B = 512 makes 1/B exact.  So every row sums to
+    within (C+1)u/B of 0, under the 2Cu/B asserted here."""
     torch, dev = torch_dev
     w = synth.WORKLOADS["wide_f32"]
     dims, B = (256, 512, 1000), 512
@@ -336,7 +345,7 @@ def test_dlogits_rows_sum_to_zero(torch_dev):
     net = make_net(dims, B, "f32", Ws, dev)
     _, _, dl, _ = P.gpu_grads(net, *P.to_dev([x, t], dev))
     C = dims[-1]
-    assert np.max(np.abs(dl.astype(np.float64).sum(1))) <= 2 * C * 2.0 ** -24 / B * 4
+    assert np.max(np.abs(dl.astype(np.float64).sum(1))) <= 2 * C * 2.0 ** -24 / B
     del w
     net.close()
 
@@ -729,6 +738,110 @@ def test_checkpoint_preflight_changes_nothing(torch_dev):
         n.close()
 
 
+def _f32(v):
+    return float(np.float32(v))
+
+
+def test_checkpoint_payload_decodes_from_the_documented_layout(torch_dev):
+    """A checkpoint the library writes, decoded in Python from the layout
+    include/mlp.h documents (tests/ckpt_format.py): header fields, the
+    checksum, W_l at their logical [in, out] shapes bit for bit equal to
+    mlp_read_params, and the Adam moments of one step from exact gradients
+    equal to the oracle's m = (1-b1) g, v = (1-b2) g^2 within the float32
+    roundings of that arithmetic (4 units of 2^-24, relative)."""
+    from mlp_gemm_softmax_amd import binding
+    from tests import ckpt_format
+    torch, dev = torch_dev
+    dims, B = (48, 40, 12), 64
+    x, t, Ws = P.integer_problem(dims, B, seed=71)
+    b1, b2, eps = 0.9, 0.99, 1e-7
+    net = make_net(dims, B, "f32", Ws, dev)
+    net.set_optimizer("adam", b1, b2, eps)
+    xd, td = P.to_dev([x, t], dev)
+    _, dws, _, _ = P.gpu_grads(net, xd, td)
+    ref = mlp_oracle.train_step(x, t, Ws, 0.0)
+    for a, r in zip(dws, ref["dW"]):
+        assert np.array_equal(a, r.astype(np.float32))      # exact gradients
+    net.train_step(xd, td, 1e-3)
+    ck = net.save_checkpoint(with_optimizer=True)
+    h = ckpt_format.parse(ck)
+    n_w = sum(a * b for a, b in zip(dims[:-1], dims[1:]))
+    assert h["magic"] == b"MLPCKPT1" and h["version"] == 1 and h["n_layers"] == 2
+    assert h["dims"] == list(dims) and h["unused_dims"] == [0] * (17 - len(dims))
+    assert h["precision"] == binding.MLP_F32 and h["optimizer"] == binding.OPT_ADAM
+    assert h["betas"] == (_f32(b1), _f32(b2), _f32(eps)) and h["reserved"] == (0, 0)
+    assert h["step"] == 1
+    assert h["payload_bytes"] == h["payload_len"] == 3 * 4 * n_w and h["trailing"] == 0
+    assert h["checksum"] == h["payload_checksum"]
+    for w_ck, w_dev in zip(h["W"], net.read_params()):
+        assert w_ck.shape == tuple(w_dev.shape)
+        assert np.array_equal(w_ck, w_dev.cpu().numpy())
+    zeros = [np.zeros(w.shape) for w in Ws]
+    upd = mlp_oracle.adam(Ws, ref["dW"], zeros, zeros, 1, 1e-3, _f32(b1), _f32(b2), _f32(eps))
+    u = 2.0 ** -24
+    for l in range(2):
+        for got, want in ((h["m"][l], upd["m"][l]), (h["v"][l], upd["v"][l])):
+            err = np.abs(got.astype(np.float64) - want)
+            assert np.all(err <= 4 * u * np.abs(want)), f"layer {l}: moments off the documented layout"
+    # without the rule's state: the weights only
+    h2 = ckpt_format.parse(net.save_checkpoint(with_optimizer=False))
+    assert h2["optimizer"] == binding.OPT_SGD and h2["payload_len"] == 4 * n_w and h2["trailing"] == 0
+    for a, b in zip(h2["W"], h["W"]):
+        assert np.array_equal(a, b)
+    net.close()
+
+
+def test_hand_built_checkpoint_restores_weights_and_moments(torch_dev):
+    """A checkpoint written in Python from the documented layout loads into
+    a session: the weights come back bit for bit (SGD session: weights only;
+    Adam session: with its moments and step count), and the next Adam step
+    from them equals the oracle's rule at t = step + 1 from the same moments
+    within the float32 roundings of the update.  The moments share the sign
+    of the (exact) gradient, so no cancellation enlarges those roundings."""
+    from mlp_gemm_softmax_amd import binding
+    from tests import ckpt_format
+    torch, dev = torch_dev
+    dims, B = (48, 40, 12), 64
+    x, t, Ws = P.integer_problem(dims, B, seed=72)
+    g = mlp_oracle.train_step(x, t, Ws, 0.0)["dW"]
+    rng = np.random.default_rng([73, 1])
+    sign = [np.where(gl >= 0, 1.0, -1.0) for gl in g]
+    m0 = [(sg * rng.uniform(0.01, 0.5, sg.shape)).astype(np.float32) for sg in sign]
+    v0 = [rng.uniform(0.5, 2.0, w.shape).astype(np.float32) for w in Ws]
+    b1, b2, eps = _f32(0.9), _f32(0.99), _f32(1e-7)
+    ck = ckpt_format.build(dims, Ws, m0, v0, opt=binding.OPT_ADAM, step=7, betas=(b1, b2, eps))
+    assert binding.checkpoint_info(ck) == {"n_layers": 2, "dims": list(dims),
+                                           "optimizer": binding.OPT_ADAM, "step": 7}
+    sgd = binding_net(dims, B, "f32", dev)
+    sgd.load_checkpoint(ck)
+    for got, w in zip(sgd.read_params(), Ws):
+        assert np.array_equal(got.cpu().numpy(), w)
+    net = binding_net(dims, B, "f32", dev)
+    net.set_optimizer("adam", b1, b2, eps)
+    net.load_checkpoint(ck)
+    for got, w in zip(net.read_params(), Ws):
+        assert np.array_equal(got.cpu().numpy(), w)
+    xd, td = P.to_dev([x, t], dev)
+    _, dws, _, _ = P.gpu_grads(net, xd, td)
+    for a, r in zip(dws, g):
+        assert np.array_equal(a, r.astype(np.float32))
+    lr = 1e-3
+    net.train_step(xd, td, lr)
+    upd = mlp_oracle.adam(Ws, g, m0, v0, 8, lr, b1, b2, eps)
+    for l, (got, want, w0) in enumerate(zip(net.read_params(), upd["W_new"], Ws)):
+        step = want - np.asarray(w0, np.float64)
+        bound = P._f32_update_rounding(want, step)
+        err = np.abs(got.cpu().numpy().astype(np.float64) - want)
+        assert np.all(err <= bound), f"layer {l}: {int((err > bound).sum())} weights off the restored rule"
+        # and the restored moments matter: from zero moments the step differs
+        fresh = mlp_oracle.adam([w0], [g[l]], [np.zeros_like(w0)], [np.zeros_like(w0)], 1, lr, b1, b2, eps)
+        assert np.max(np.abs(fresh["W_new"][0] - want)) > 100 * np.max(bound)
+    ck2 = ckpt_format.parse(net.save_checkpoint(with_optimizer=True))
+    assert ck2["step"] == 8
+    sgd.close()
+    net.close()
+
+
 # ---------------------------------------------------------------- inference --
 
 @pytest.mark.parametrize("name", ["mnist_b1024", "wide_f32", "wide_bf16", "skinny_b8"])
@@ -927,6 +1040,9 @@ def test_forward_probs_argument_errors(torch_dev):
                                               ((320, 2080, 40), 512, "f32"),
                                               ((1024, 2048, 1000), 2048, "bf16"),
                                               ((784, 128, 10), 1024, "f32"),
+                                              # the head is not fused at creation (32 x 32 tiles) but a
+                                              # candidate (32 x 16, 16 waves) fuses it: 128 row blocks
+                                              ((784, 128, 10), 4096, "f32"),
                                               ((512, 2048, 1040), 8, "f32")])   # skinny: K and column splits
 def test_tuned_plans_keep_parity(torch_dev, dims, B, precision):
     """After mlp_tune the weights are unchanged, and the step with the chosen
