@@ -179,6 +179,36 @@ mlp_status mlp_forward_probs(mlp_ctx* ctx, const float* x, float* probs);
 mlp_status mlp_train_step(mlp_ctx* ctx, const float* x, const float* labels,
                           float lr, float* loss);
 
+/* Size of the static device buffer of mlp_train_step_static, per GPU. */
+#define MLP_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): one SGD
+ * training step of a float32 configuration, the computation of
+ * mlp_train_step_async, without a context or a workspace.  weights: host
+ * array of cfg->n_layers device pointers, each a float32
+ * [dims[l], dims[l+1]] weight that the step reads and updates in place.
+ * x: device float32 [B, d0]; labels: device float32 [B, C]; lr finite;
+ * loss_dev: device float32 or NULL (the mean loss at the pre-update
+ * weights, in stream order).  Everything else the step needs lives in a
+ * static device array of the library, MLP_STATIC_SCRATCH_BYTES per GPU,
+ * held from the library's load on that GPU until the process ends; its
+ * address is looked up once per GPU.  Nothing is allocated and nothing
+ * waits; the launches go to cfg->stream.  The plan of the last
+ * configuration is kept per GPU and rebuilt (host work) when the
+ * configuration or stream changes, and the buffer's counters are then
+ * cleared by a kernel; every step leaves them cleared again.  All calls on
+ * one GPU share that buffer: calls whose work may overlap on the GPU (other
+ * streams, other host threads) race and must be ordered by the caller.
+ * Errors (checked before anything is enqueued; message in
+ * mlp_last_error(NULL)): MLP_ERR_SHAPE / MLP_ERR_ARG as for mlp_create,
+ * MLP_ERR_ARG for a bf16 configuration, NULL or misaligned pointers or a
+ * non-finite lr, MLP_ERR_WORKSPACE when the configuration needs more than
+ * MLP_STATIC_SCRATCH_BYTES, MLP_ERR_HIP for a failed launch (the weights
+ * are then undefined). */
+mlp_status mlp_train_step_static(const mlp_config* cfg, float* const* weights, const float* x,
+                                 const float* labels, float lr, float* loss_dev);
+
 /* As mlp_train_step, but nothing waits: the mean loss is written to
  * `loss_dev` (device float32, or NULL to drop it) in stream order (README
  * "Debugging" separates a session's step() from its wait()).  Errors as

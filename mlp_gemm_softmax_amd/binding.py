@@ -37,6 +37,8 @@ SIGNATURES = {
                                   _c.POINTER(_c.c_float)]),
     "mlp_train_step_async": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_float,
                                         _c.c_void_p]),
+    "mlp_train_step_static": (_c.c_int, [_c.c_void_p, _c.POINTER(_c.c_void_p), _c.c_void_p, _c.c_void_p,
+                                         _c.c_float, _c.c_void_p]),
     "mlp_grads": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.POINTER(_c.c_void_p),
                              _c.c_void_p, _c.POINTER(_c.c_float)]),
     "mlp_read_state": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_int32, _c.c_void_p]),
@@ -59,6 +61,27 @@ SIGNATURES = {
     "mlp_status_string": (_c.c_char_p, [_c.c_int]),
     "mlp_last_error": (_c.c_char_p, [_c.c_void_p]),
 }
+
+
+STATIC_SCRATCH_BYTES = 64 << 20   # MLP_STATIC_SCRATCH_BYTES
+
+
+def train_step_static(dims: Sequence[int], batch: int, weights: Sequence, x, labels, lr: float,
+                      loss_dev=None, stream=None):
+    """mlp_train_step_static: one float32 SGD step on the caller's weights
+    (updated in place) with every intermediate in the library's static
+    device buffer; enqueue only.  Tensors are contiguous float32 CUDA
+    tensors; the stream defaults to torch's current one."""
+    import torch
+    dev = x.device
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    cfg = make_config(dims, batch, MLP_F32, st.cuda_stream)
+    arr = (ctypes.c_void_p * len(weights))(*[w.data_ptr() for w in weights])
+    rc = lib().mlp_train_step_static(ctypes.byref(cfg), arr, ctypes.c_void_p(x.data_ptr()),
+                                     ctypes.c_void_p(labels.data_ptr()), float(lr),
+                                     ctypes.c_void_p(_ptr(loss_dev)))
+    if rc != MLP_OK:
+        raise MlpError(rc, lib().mlp_last_error(None).decode())
 
 
 def checkpoint_info(buf: bytes) -> dict:

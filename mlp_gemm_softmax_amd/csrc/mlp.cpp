@@ -24,6 +24,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -102,6 +103,7 @@ struct mlp_ctx {
     bool bf16 = false;
     bool skinny = false;
     bool head = false;      // fused output layer (C <= 32, f32)
+    bool external_w = false;   // weights are the caller's (no workspace room for them)
     int head_rb = 0;        // batch rows per head workgroup
     hipStream_t stream = nullptr;
 
@@ -884,7 +886,7 @@ size_t plan_and_carve(mlp_ctx* c, char* base) {
 
     Layout_ lay;
     size_t oW[kMaxLayers], oWb[kMaxLayers], oA[kMaxLayers], oM[kMaxLayers];
-    for (int l = 0; l < L; ++l) oW[l] = lay.take((size_t)c->dims[l] * c->dims[l + 1] * 4);
+    for (int l = 0; l < L; ++l) oW[l] = c->external_w ? 0 : lay.take((size_t)c->dims[l] * c->dims[l + 1] * 4);
     for (int l = 0; l < L; ++l) oWb[l] = c->bf16 ? lay.take((size_t)c->dims[l] * c->dims[l + 1] * 2) : 0;
     for (int l = 1; l < L; ++l) oA[l] = lay.take((size_t)B * c->dims[l] * e);
     for (int l = 1; l < L; ++l) oM[l] = lay.take((size_t)B * c->dims[l]);
@@ -903,7 +905,7 @@ size_t plan_and_carve(mlp_ctx* c, char* base) {
     for (auto& v : c->slots) v.clear();
     if (base) {
         for (int l = 0; l < L; ++l) {
-            c->W[l] = (float*)(base + oW[l]);
+            c->W[l] = c->external_w ? nullptr : (float*)(base + oW[l]);
             c->Wb[l] = c->bf16 ? (bf16_t*)(base + oWb[l]) : nullptr;
         }
         for (int l = 1; l < L; ++l) {
@@ -1096,6 +1098,119 @@ mlp_status mlp_train_step_async(mlp_ctx* c, const float* x, const float* labels,
     }
     const hipError_t e = enqueue(c, Mode::Train, x, labels, lr, nullptr, loss_dev);
     if (e != hipSuccess) return hip_fail(c, e, "mlp_train_step");
+    return MLP_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------- allocation-free step --
+//
+// mlp_train_step_static serves callers that cannot allocate device memory:
+// every intermediate of the step (activations, masks, logits, dlogits, the
+// dZ pair, split-K partials, counters, row losses) lives in `scratch`, a
+// static device array of this library (one copy per GPU, held until the
+// process ends); the weights stay in the caller's buffers and are updated
+// there.  The plan of the last configuration is kept per device and rebuilt
+// (host work only) when the configuration changes; the counters are cleared
+// with a fill kernel then, and every step leaves them at zero again.
+namespace {
+
+constexpr size_t kStaticScratchBytes = MLP_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+struct StaticPlan {
+    char* base = nullptr;     // scratch's device address on this GPU (host code never uses the name)
+    mlp_ctx* ctx = nullptr;   // plan of the last configuration run here
+    bool zeroed = false;      // counters known to be zero
+};
+
+std::mutex g_static_mu;
+StaticPlan g_static[kMaxDevices];
+
+bool same_plan_inputs(const mlp_ctx& a, const mlp_ctx& b) {
+    if (a.L != b.L || a.B != b.B || a.bf16 != b.bf16 || a.stream != b.stream) return false;
+    for (int i = 0; i <= a.L; ++i)
+        if (a.dims[i] != b.dims[i]) return false;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+mlp_status mlp_train_step_static(const mlp_config* cfg, float* const* weights, const float* x,
+                                 const float* labels, float lr, float* loss_dev) {
+    g_create_error.clear();
+    mlp_ctx probe;
+    mlp_status st = validate(cfg, &probe);
+    if (st != MLP_OK) return st;
+    if (probe.bf16)
+        return set_err(nullptr, MLP_ERR_ARG, "the allocation-free step runs float32 sessions only "
+                                             "(bf16 sessions keep operand copies of the weights)");
+    if (!weights) return set_err(nullptr, MLP_ERR_ARG, "weights is NULL");
+    for (int l = 0; l < probe.L; ++l)
+        if (!weights[l] || !aligned16(weights[l]))
+            return set_err(nullptr, MLP_ERR_ARG, "weights[%d] must be a 16-byte aligned device pointer", l);
+    if (!x || !aligned16(x)) return set_err(nullptr, MLP_ERR_ARG, "x must be a 16-byte aligned device pointer");
+    if (!labels || !aligned16(labels))
+        return set_err(nullptr, MLP_ERR_ARG, "labels must be a 16-byte aligned device pointer");
+    if (!std::isfinite(lr)) return set_err(nullptr, MLP_ERR_ARG, "lr must be finite");
+    if (loss_dev && ((uintptr_t)loss_dev & 3u)) return set_err(nullptr, MLP_ERR_ARG, "loss_dev must be 4-byte aligned");
+    probe.external_w = true;
+    const size_t need = plan_and_carve(&probe, nullptr);
+    if (need > kStaticScratchBytes)
+        return set_err(nullptr, MLP_ERR_WORKSPACE,
+                       "this configuration needs %zu bytes of scratch; the static buffer holds %zu "
+                       "(use mlp_create with a workspace)", need, kStaticScratchBytes);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return set_err(nullptr, MLP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return set_err(nullptr, MLP_ERR_ARG, "device %d beyond %d", dev, kMaxDevices);
+
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    StaticPlan& sp = g_static[dev];
+    if (!sp.base) {   // once per device, with that device current
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return set_err(nullptr, MLP_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        sp.base = (char*)p;
+    }
+    if (!sp.ctx || !same_plan_inputs(*sp.ctx, probe)) {
+        if (!sp.ctx) sp.ctx = new mlp_ctx();
+        mlp_ctx* c = sp.ctx;
+        *c = mlp_ctx();
+        validate(cfg, c);
+        c->external_w = true;
+        plan_and_carve(c, sp.base);
+        build_slots(c);
+        sp.zeroed = false;
+        if (c->head) {
+            e = head_prepare();
+            if (e != hipSuccess) {
+                delete sp.ctx;
+                sp.ctx = nullptr;
+                return set_err(nullptr, MLP_ERR_HIP, "head kernel set-up: %s", hipGetErrorString(e));
+            }
+        }
+    }
+    mlp_ctx* c = sp.ctx;
+    if (!sp.zeroed) {
+        // a fill kernel, not a memset, so that the call may be captured
+        e = launch_zero((float*)c->tickets, tickets_bytes(c) / sizeof(float), c->stream);
+        if (e != hipSuccess) return set_err(nullptr, MLP_ERR_HIP, "clearing counters: %s", hipGetErrorString(e));
+        sp.zeroed = true;
+    }
+    for (int l = 0; l < c->L; ++l) c->W[l] = weights[l];
+    c->params_set = c->L >= 32 ? ~0u : ((1u << c->L) - 1u);
+    c->poisoned = false;
+    e = enqueue(c, Mode::Train, x, labels, lr, nullptr, loss_dev);
+    if (e != hipSuccess) {
+        sp.zeroed = false;   // a step cut short may leave counters raised
+        return set_err(nullptr, MLP_ERR_HIP, "mlp_train_step_static: %s", hipGetErrorString(e));
+    }
     return MLP_OK;
 }
 

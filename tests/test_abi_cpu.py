@@ -105,6 +105,33 @@ def test_workspace_preflight(ptr, delta):
     assert "workspace" in lib.mlp_last_error(None).decode()
 
 
+def _static_call(lib, dims, batch, prec=binding.MLP_F32, weights=True, x=4096, labels=4096, lr=0.1, loss=None):
+    cfg = _cfg(dims, batch, prec)
+    arr = (ctypes.c_void_p * (len(dims) - 1))(*([4096] * (len(dims) - 1))) if weights else None
+    return lib.mlp_train_step_static(ctypes.byref(cfg), arr, ctypes.c_void_p(x), ctypes.c_void_p(labels),
+                                     lr, ctypes.c_void_p(loss) if loss else None)
+
+
+def test_static_step_preflight():
+    """The allocation-free step rejects, before touching the GPU: bf16
+    configurations, missing or misaligned pointers, a non-finite lr, and
+    configurations whose scratch exceeds the static buffer."""
+    lib = _lib()
+    assert lib.mlp_train_step_static(None, None, None, None, 0.1, None) == binding.MLP_ERR_ARG
+    assert _static_call(lib, (784, 128, 10), 32, prec=binding.MLP_BF16) == binding.MLP_ERR_ARG
+    assert "float32" in lib.mlp_last_error(None).decode()
+    assert _static_call(lib, (784, 128, 10), 32, weights=False) == binding.MLP_ERR_ARG
+    assert _static_call(lib, (784, 128, 10), 32, x=4100) == binding.MLP_ERR_ARG
+    assert _static_call(lib, (784, 128, 10), 32, labels=0) == binding.MLP_ERR_ARG
+    assert _static_call(lib, (784, 128, 10), 32, lr=float("nan")) == binding.MLP_ERR_ARG
+    assert _static_call(lib, (784, 128, 10), 32, loss=4098) == binding.MLP_ERR_ARG
+    assert _static_call(lib, (784, 128, 10), 0) == binding.MLP_ERR_SHAPE
+    w = WORKLOADS["wide_f32"]
+    assert _static_call(lib, w.dims, w.batch) == binding.MLP_ERR_WORKSPACE
+    msg = lib.mlp_last_error(None).decode()
+    assert "static buffer" in msg and str(binding.STATIC_SCRATCH_BYTES) in msg
+
+
 def test_null_context_calls():
     lib = _lib()
     assert lib.mlp_set_params(None, 0, None) == binding.MLP_ERR_ARG
