@@ -188,6 +188,39 @@ def _damaged():
     yield "payload bit", bytes(flipped)
 
 
+def test_checkpoint_info_survives_random_damage():
+    """Seeded mutations of a valid checkpoint -- truncations, random bytes in
+    the header and payload, random lengths and whole random buffers -- come
+    back as MLP_OK (checksum and fields still consistent) or MLP_ERR_ARG,
+    never anything else; under the host sanitizers (test_sanitizers_cpu.py)
+    this also checks that the parser reads only the bytes it was given."""
+    _lib()
+    rng = np.random.default_rng([20, 26])
+    good = _checkpoint((6, 4, 3), opt=binding.OPT_ADAM, step=3, betas=(0.9, 0.99, 1e-7))
+    ok = 0
+    for it in range(600):
+        kind = it % 4
+        b = bytearray(good)
+        if kind == 0:
+            b = b[: int(rng.integers(0, len(b)))]
+        elif kind == 1:
+            for _ in range(int(rng.integers(1, 6))):
+                b[int(rng.integers(0, 136))] = int(rng.integers(0, 256))
+        elif kind == 2:
+            for _ in range(int(rng.integers(1, 6))):
+                b[int(rng.integers(0, len(b)))] = int(rng.integers(0, 256))
+        else:
+            b = bytearray(rng.integers(0, 256, int(rng.integers(0, 400))).astype(np.uint8).tobytes())
+            if len(b) >= 8 and rng.random() < 0.5:
+                b[:8] = b"MLPCKPT1"
+        try:
+            binding.checkpoint_info(bytes(b))
+            ok += 1
+        except binding.MlpError as e:
+            assert e.status == binding.MLP_ERR_ARG
+    assert ok < 600
+
+
 @pytest.mark.parametrize("what,buf", list(_damaged()))
 def test_checkpoint_info_rejects_damage(what, buf):
     _lib()
