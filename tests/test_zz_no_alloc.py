@@ -68,3 +68,42 @@ def test_static_step_after_a_larger_one_and_errors(torch_dev):
         binding.train_step_static(w.dims, w.batch, ws, xs, ts, 0.01)
     assert ei.value.status == binding.MLP_ERR_WORKSPACE
     _run_pair(torch, dev, (784, 128, 10), 32, seed=401, steps=2)
+
+
+@pytest.mark.parametrize("name", ["mnist_b1024", "skinny_b8"])
+def test_static_step_under_graph_capture(torch_dev, name):
+    """The use the call is for: a step captured into a HIP graph
+    (torch.cuda.graph) after one warm-up call has built the plan for this
+    configuration and stream, replayed three times with eager work and
+    synchronisations between the replays; every replay equals a workspace
+    step bit for bit."""
+    from mlp_gemm_softmax_amd import binding
+    torch, dev = torch_dev
+    w = synth.WORKLOADS[name]
+    print(f"\n[case] static step under capture {name}", flush=True)
+    Ws = synth.workload_weights(w)
+    x, t, _ = synth.workload_batch(w)
+    xd, td = P.to_dev([x, t], dev)
+    eager = binding.Mlp(w.dims, w.batch, "f32", device=str(dev))
+    eager.set_params(P.to_dev(Ws, dev))
+    s = torch.cuda.Stream(device=dev)
+    warm = P.to_dev(Ws, dev)          # a throw-away copy: the warm-up trains it
+    weights = P.to_dev(Ws, dev)
+    loss_e = torch.zeros(1, dtype=torch.float32, device=dev)
+    loss_g = torch.zeros(1, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    binding.train_step_static(w.dims, w.batch, warm, xd, td, w.lr, loss_g, stream=s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        binding.train_step_static(w.dims, w.batch, weights, xd, td, w.lr, loss_g, stream=s)
+    torch.cuda.synchronize()
+    for step in range(3):
+        eager.train_step_async(xd, td, w.lr, loss_e)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(loss_g, loss_e), f"step {step}: loss {loss_g.item()} vs {loss_e.item()}"
+        for l, (a, b) in enumerate(zip(eager.read_params(), weights)):
+            assert torch.equal(a, b), f"step {step}: W{l} differs"
+    eager.close()
