@@ -5,10 +5,10 @@
                     [--extra-workloads A,B]
 
 The figure is the wide MLP in strict float32 (1024 -> 4096 -> 4096 -> 1000,
-batch 4096, the largest workload that is judged against the f32 matrix-core
-peak); the bf16 fast path of the same MLP and the skinny batch-8 MLP (judged
-against HBM bandwidth) are measured the same way in the same run and reported
-under "also".
+batch 4096, the largest workload, priced against the f32 matrix-core peak);
+the bf16 fast path of the same MLP and the skinny batch-8 MLP (priced against
+HBM bandwidth) are measured the same way in the same run and reported under
+"also".
 
 A step is one pass of the whole hot path (forward GEMMs with fused ReLU/mask,
 softmax cross-entropy, dX and dW+SGD GEMMs) over one batch of synthetic
