@@ -204,8 +204,9 @@ mlp_status mlp_train_step(mlp_ctx* ctx, const float* x, const float* labels,
  * mlp_last_error(NULL)): MLP_ERR_SHAPE / MLP_ERR_ARG as for mlp_create,
  * MLP_ERR_ARG for a bf16 configuration, NULL or misaligned pointers or a
  * non-finite lr, MLP_ERR_WORKSPACE when the configuration needs more than
- * MLP_STATIC_SCRATCH_BYTES, MLP_ERR_HIP for a failed launch (the weights
- * are then undefined). */
+ * MLP_STATIC_SCRATCH_BYTES, MLP_ERR_ARG when cfg->stream belongs to another
+ * device than the current one (the buffer used is the current device's),
+ * MLP_ERR_HIP for a failed launch (the weights are then undefined). */
 mlp_status mlp_train_step_static(const mlp_config* cfg, float* const* weights, const float* x,
                                  const float* labels, float lr, float* loss_dev);
 

@@ -1168,6 +1168,14 @@ mlp_status mlp_train_step_static(const mlp_config* cfg, float* const* weights, c
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return set_err(nullptr, MLP_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
     if (dev < 0 || dev >= kMaxDevices) return set_err(nullptr, MLP_ERR_ARG, "device %d beyond %d", dev, kMaxDevices);
+    if (cfg->stream) {
+        // the buffer used is the current device's: the stream must run there
+        int sdev = -1;
+        e = hipStreamGetDevice((hipStream_t)cfg->stream, &sdev);
+        if (e != hipSuccess) return set_err(nullptr, MLP_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+        if (sdev != dev)
+            return set_err(nullptr, MLP_ERR_ARG, "the stream belongs to device %d but device %d is current", sdev, dev);
+    }
 
     std::lock_guard<std::mutex> lock(g_static_mu);
     StaticPlan& sp = g_static[dev];
