@@ -91,18 +91,21 @@ def source_digest():
 
 
 def recorded_counters(workload, kernel):
-    """The committed counter record of `kernel` (profiles/traffic.json), or
-    None when absent or when the kernel sources changed since the counters
-    were taken."""
+    """The committed counter record of launch slot `kernel` of `workload`
+    (profiles/traffic.json keeps one per slot, since which of several
+    near-equal slots dominates can change from run to run), or None when
+    absent or when the kernel sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha") != source_digest() or rec.get("kernel") != kernel:
+    if not rec or rec.get("source_sha") != source_digest():
         return None
-    return rec
+    if "slots" in rec:
+        return rec["slots"].get(kernel)
+    return rec if rec.get("kernel") == kernel else None
 
 
 def recorded_traffic(workload, kernel):
@@ -331,14 +334,17 @@ def summarize(outdir, w, steps, warmup):
             allrec = json.load(f)
     except (OSError, ValueError):
         allrec = {}
-    allrec[w] = {"kernel": roof["kernel"], "source_sha": source_digest(),
-                 "mfma_busy": round(mfma[dom]["busy"], 4) if mfma else None,
-                 "clock_ghz": round(mfma[dom]["clock_ghz"], 3) if mfma and mfma[dom]["dur_us"] >= 100 else None,
-                 "bytes_per_launch": round(counters["FETCH_SIZE"][dom] + counters["WRITE_SIZE"][dom]),
-                 "fetch_bytes": round(counters["FETCH_SIZE"][dom]),
-                 "write_bytes": round(counters["WRITE_SIZE"][dom]),
-                 "algorithmic_bytes": roof["algorithmic_bytes"],
-                 "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"]}
+    def slot_rec(i):
+        return {"mfma_busy": round(mfma[i]["busy"], 4) if mfma else None,
+                "clock_ghz": round(mfma[i]["clock_ghz"], 3) if mfma and mfma[i]["dur_us"] >= 100 else None,
+                "bytes_per_launch": round(counters["FETCH_SIZE"][i] + counters["WRITE_SIZE"][i]),
+                "fetch_bytes": round(counters["FETCH_SIZE"][i]),
+                "write_bytes": round(counters["WRITE_SIZE"][i])}
+    # every slot's counters, and the profiled run's dominant slot at the top
+    allrec[w] = dict(slot_rec(dom), kernel=roof["kernel"], source_sha=source_digest(),
+                     algorithmic_bytes=roof["algorithmic_bytes"],
+                     fetch_scale=scale["FETCH_SIZE"], write_scale=scale["WRITE_SIZE"],
+                     slots={nm: slot_rec(i) for i, (nm, _) in enumerate(slots)})
     with open(tpath, "w") as f:
         json.dump(allrec, f, indent=1, sort_keys=True)
     print(f"wrote profiles/{w}.md and profiles/traffic.json[{w}]")

@@ -102,6 +102,14 @@ def test_recorded_traffic_needs_the_same_sources_and_kernel(tmp_path, monkeypatc
     assert bench.recorded_traffic("missing", "slot") is None
     (csrc / "k.hip").write_text("kernel changed")
     assert bench.recorded_traffic("w", "slot") is None
+    # per-slot records: any slot of the profiled run, same sources only
+    rec = {"w": {"kernel": "a", "source_sha": bench.source_digest(), "bytes_per_launch": 1,
+                 "slots": {"a": {"bytes_per_launch": 1}, "b": {"bytes_per_launch": 2}}}}
+    (tmp_path / "profiles" / "traffic.json").write_text(json.dumps(rec))
+    assert bench.recorded_traffic("w", "b") == 2 and bench.recorded_traffic("w", "a") == 1
+    assert bench.recorded_traffic("w", "c") is None
+    (csrc / "k.hip").write_text("kernel changed again")
+    assert bench.recorded_traffic("w", "b") is None
 
 
 def _write_csv(path, header, rows):
@@ -175,6 +183,8 @@ def test_summarize_prices_counters_per_slot(tmp_path, monkeypatch):
     # busy over the slot's cycles (product + epilogue: 240000 per XCD)
     assert rec["mfma_busy"] == pytest.approx(0.6, abs=1e-4)
     assert rec["clock_ghz"] == pytest.approx(240000 / 120e3, abs=1e-3)   # 120 us for the slot
+    assert rec["slots"]["slot_b"]["bytes_per_launch"] == rec["bytes_per_launch"]
+    assert set(rec["slots"]) == {"slot_a", "slot_b"}
     md = (root / "profiles" / f"{w}.md").read_text()
     assert "`kb + splitk_epilogue_kernel<(mlp::Epi)3>`" in md
     assert "| slot_b |" in md and "Matrix cores per launch slot" in md
