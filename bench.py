@@ -17,7 +17,10 @@ HBM before the timed region, and reused cyclically (the batch-1024 workload
 draws a fresh batch for each of its 100 steps).  W untimed warm-up steps,
 then K steps bracketed by device synchronisations (asynchronous launches:
 the headline).  Then up to 50 synchronous steps (the loss read back after
-each one) give `sync_ms_per_step`.  After that the same K steps run again
+each one) give `sync_ms_per_step`.  For batches of at most 8 rows (float32,
+SGD) the same K steps also run as one `mlp_train_steps` call, whose
+first-layer update launch makes the next step's first forward too:
+`run_ms_per_step`.  After that the same K steps run again
 with per-launch HIP events on the library's
 stream, to price the dominant kernel against its roofline; then the float64
 oracle is timed on the host cores over a bounded sample, and the GPU's ReLU
@@ -434,6 +437,23 @@ def measure(w, args, dev, want_cpu, want_masks):
             net.train_step(xb, tb, w.lr)
         sync_ms = (time.perf_counter() - t0) / ks * 1e3
 
+    # The same K steps as one mlp_train_steps run (batches stacked), where
+    # the library hands the first layer's update to the next step's first
+    # forward launch (batch <= 8, float32, SGD); reported beside the figure.
+    run_ms = None
+    if args.mode == "train" and w.precision == "f32" and w.batch <= 8 and args.optimizer == "sgd":
+        order = [batches[(args.warmup + i) % n_batches] for i in range(args.steps)]
+        xs = torch.stack([b[0] for b in order]).contiguous()
+        ts = torch.stack([b[1] for b in order]).contiguous()
+        run_loss = torch.zeros(args.steps, dtype=torch.float32, device=dev)
+        net.train_steps(xs[:max(args.warmup, 1)], ts[:max(args.warmup, 1)], w.lr, run_loss[:max(args.warmup, 1)])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        net.train_steps(xs, ts, w.lr, run_loss)
+        torch.cuda.synchronize()
+        run_ms = (time.perf_counter() - t0) / args.steps * 1e3
+        del xs, ts, run_loss
+
     # Per-launch HIP events on the library's stream, same step sequence.
     pk = args.profile_steps or args.steps
     net.profile(True)
@@ -474,6 +494,8 @@ def measure(w, args, dev, want_cpu, want_masks):
         "step_bytes": int(step_bytes),
         "step_gbps": round(step_bytes * steps_per_s / 1e9, 2),
         "sync_ms_per_step": round(sync_ms, 5) if sync_ms is not None else None,
+        # K steps as one mlp_train_steps call (first-layer passes fused across steps)
+        "run_ms_per_step": round(run_ms, 5) if run_ms is not None else None,
         "final_loss": final_loss,
         "roofline": roof,
     }

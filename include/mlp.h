@@ -218,6 +218,24 @@ mlp_status mlp_train_step_static(const mlp_config* cfg, float* const* weights, c
 mlp_status mlp_train_step_async(mlp_ctx* ctx, const float* x, const float* labels,
                                 float lr, float* loss_dev);
 
+/* n training steps on n successive batches, enqueued without waiting: the
+ * loop the README "Example" trainer runs over its data loader's batches.
+ * The result is bitwise that of n calls of mlp_train_step_async on the same
+ * batches in order.  x: device float32 [n, B, dims[0]] and labels: device
+ * float32 [n, B, dims[n_layers]], batch after batch, 16-byte aligned; all of
+ * them must stay valid until the stream has run the steps.  loss_dev:
+ * device float32 [n] (step s's mean loss at loss_dev[s]) or NULL.  In
+ * sessions whose batch has at most 8 rows (the weight-streaming kernels),
+ * float32 with SGD, the launch that updates the first layer's weights also
+ * computes the next step's first-layer forward from the updated values, so
+ * each step after the first makes one pass fewer over that matrix.  Errors
+ * as mlp_train_step_async, and MLP_ERR_ARG for n < 1 or, when n > 1, a
+ * batch whose x or labels size is not a multiple of 16 bytes (later batches
+ * would lose the alignment); a HIP failure poisons the context and leaves
+ * the weights undefined. */
+mlp_status mlp_train_steps(mlp_ctx* ctx, int32_t n, const float* x, const float* labels,
+                           float lr, float* loss_dev);
+
 /* Gradients without an update, from the same kernels and accumulation order
  * as a training step: the backward of README "Example" read out as a debug
  * session would (README "Debugging"), so that forward and backward can be

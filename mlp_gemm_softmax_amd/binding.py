@@ -37,6 +37,8 @@ SIGNATURES = {
                                   _c.POINTER(_c.c_float)]),
     "mlp_train_step_async": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_float,
                                         _c.c_void_p]),
+    "mlp_train_steps": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_void_p, _c.c_void_p, _c.c_float,
+                                   _c.c_void_p]),
     "mlp_train_step_static": (_c.c_int, [_c.c_void_p, _c.POINTER(_c.c_void_p), _c.c_void_p, _c.c_void_p,
                                          _c.c_float, _c.c_void_p]),
     "mlp_grads": (_c.c_int, [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.POINTER(_c.c_void_p),
@@ -292,6 +294,18 @@ class Mlp:
         self._check(lib().mlp_train_step_async(self._h, ctypes.c_void_p(x.data_ptr()),
                                                ctypes.c_void_p(labels.data_ptr()), float(lr),
                                                ctypes.c_void_p(_ptr(loss_dev))))
+
+    def train_steps(self, x, labels, lr: float, loss_dev=None):
+        """len(x) training steps on the batches x[s], labels[s]; enqueue
+        only.  loss_dev: device float32 [n] or None."""
+        n = int(x.shape[0]) if x.dim() == 3 else 0
+        self._dev_f32(x, (n, self.batch, self.dims[0]))
+        self._dev_f32(labels, (n, self.batch, self.dims[-1]))
+        if loss_dev is not None:
+            self._dev_f32(loss_dev, (n,))
+        self._check(lib().mlp_train_steps(self._h, n, ctypes.c_void_p(x.data_ptr()),
+                                          ctypes.c_void_p(labels.data_ptr()), float(lr),
+                                          ctypes.c_void_p(_ptr(loss_dev))))
 
     def grads(self, x, labels):
         """(loss, [dW_l], dlogits) without an update."""

@@ -107,13 +107,15 @@ struct SkinnyParams {
     float* m;          // Adapt: first and second moments, laid out as W
     float* v;
     OptScalars opt;    // Adapt: the step's scalars
+    const float* grad; // NN with fused update: G [MB][N] of the previous step (act: its input a)
 };
 struct SkinnyLaunch {
     Layout layout;
     Epi epi;
     int grid;
     int waves;       // waves per workgroup
-    bool fused_update = false;   // NT: also apply the layer's dW (+ SGD) in the same pass
+    bool fused_update = false;   // NT: also apply the layer's dW (+ SGD) in the same pass;
+                                 // NN: first apply the previous step's dW + SGD to W (act, grad, wout = W)
 };
 hipError_t launch_skinny(const SkinnyLaunch& L, const SkinnyParams& p, hipStream_t s);
 int skinny_tn_rows();   // rows of W per dW+SGD workgroup

@@ -407,6 +407,7 @@ void build_slots(mlp_ctx* c) {
 struct Runner {
     mlp_ctx* c;
     int kind = kStep;
+    bool off = false;   // no per-launch timing for this sequence
     hipError_t err = hipSuccess;
 
     hipEvent_t ev() {
@@ -424,7 +425,7 @@ struct Runner {
     void run(int slot_id, F&& f) {
         if (err != hipSuccess) return;
         hipEvent_t b = nullptr, e = nullptr;
-        if (c->profiling && slot_id >= 0) {
+        if (c->profiling && !off && slot_id >= 0) {
             b = ev();
             e = ev();
             if (b && e) hipEventRecord(b, c->stream);
@@ -504,17 +505,31 @@ hipError_t run_skinny(mlp_ctx* c, const SkinnyPlan& s, Layout lay, Epi epi, cons
     p.m = m;
     p.v = v;
     p.opt = opt ? *opt : OptScalars{};
+    p.grad = nullptr;
     return launch_skinny(L, p, c->stream);
+}
+
+// Whether a run of training steps can hand the first layer's dW + SGD of one
+// step to the next step's first forward launch: skinny float32 sessions with
+// plain SGD and at most 8 batch rows.
+bool steps_fusable(const mlp_ctx* c) {
+    return c->skinny && !c->bf16 && c->opt == MLP_OPT_SGD && c->B <= 8;
 }
 
 
 enum class Mode { Forward, Train, Grads };
 
 // Enqueue the step.  Returns the first HIP error (launches stop there).
+// Within a run of steps (mlp_train_steps, skinny sessions): with x_next the
+// first layer's dW + SGD launch also computes the next step's first forward
+// on x_next, and first_done says this step's first forward was made that way.
 hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, float lr,
-                   float* const* dw_out, float* loss_dev, float* probs = nullptr) {
+                   float* const* dw_out, float* loss_dev, float* probs = nullptr,
+                   bool first_done = false, const float* x_next = nullptr) {
     Runner r{c, mode != Mode::Forward ? kStep : (probs ? kForwardProbs : (labels ? kForwardLoss : kForward))};
-    if (c->profiling) c->prof_kind = r.kind;
+    // the per-launch timing names the single-step launch sequence
+    r.off = first_done || x_next;
+    if (c->profiling && !r.off) c->prof_kind = r.kind;
     const int L = c->L, B = c->B;
     int slot = 0;
     const void* a_prev;
@@ -550,7 +565,9 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
         const int K = c->dims[l], N = c->dims[l + 1];
         const bool last = l == L - 1;
         const void* Wop = c->bf16 ? (const void*)c->Wb[l] : (const void*)c->W[l];
-        if (c->skinny) {
+        if (c->skinny && l == 0 && first_done) {
+            // made by the previous step's first-layer update launch
+        } else if (c->skinny) {
             r.run(slot++, [&] {
                 return run_skinny(c, c->sfwd[l], Layout::NN, last ? Epi::Store : Epi::ReluMask,
                                   (const float*)a_prev, (const float*)Wop, K, N,
@@ -651,6 +668,11 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
         tp.inv_b = 1.0f / (float)B;
     }
     const bool fuse_tail = use_head && tail_fused(c);
+    // The separate tail reads a_{L-1}, which a first-layer launch that also
+    // makes the next step's forward overwrites when L = 2: it needs only the
+    // head's outputs, so then it goes first.
+    const bool tail_early = use_head && !fuse_tail && x_next;
+    if (tail_early) r.run(slot++, [&] { return launch_tail(tp, c->stream); });
     const void* G = c->bf16 ? (const void*)c->dlogits_b : (const void*)c->dlogits;
     int pp = 0;
     int top = L - 1;
@@ -712,7 +734,37 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
         bf16_t* Wbdst = (!grads && c->bf16) ? c->Wb[l] : nullptr;
         float* om = adaptive ? c->opt_m[l] : nullptr;
         float* ov = adaptive ? c->opt_v[l] : nullptr;
-        if (c->skinny) {
+        if (c->skinny && l == 0 && x_next) {
+            // this step's dW + SGD of W_0, then the next step's forward of
+            // layer 0 on x_next with the updated W_0, in one pass over W_0
+            r.run(slot++, [&] {
+                const SkinnyPlan& sf = c->sfwd[0];
+                const bool only = L == 1;
+                SkinnyLaunch sl;
+                sl.layout = Layout::NN;
+                sl.epi = only ? Epi::Store : Epi::ReluMask;
+                sl.grid = sf.grid;
+                sl.waves = sf.waves;
+                sl.fused_update = true;
+                SkinnyParams sp{};
+                sp.A = x_next;
+                sp.B = c->W[0];
+                sp.MB = B;
+                sp.K = din;
+                sp.N = dout;
+                sp.C = only ? c->logits : (float*)c->act[1];
+                sp.mask = only ? nullptr : c->mask[1];
+                sp.lr = lr;
+                sp.splits = sf.splits;
+                sp.kchunk = sf.kchunk;
+                sp.partials = c->partials;
+                sp.tickets = c->tickets;
+                sp.act = x;
+                sp.grad = (const float*)G;
+                sp.wout = c->W[0];
+                return launch_skinny(sl, sp, c->stream);
+            });
+        } else if (c->skinny) {
             r.run(slot++, [&] {
                 return run_skinny(c, c->sdw[l], Layout::TN, upd_epi, (const float*)a_in, (const float*)G, din, dout,
                                   Wdst, nullptr, lr, om, ov, &osc);
@@ -725,7 +777,7 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
         }
         G = Gnext;
     }
-    if (use_head && !fuse_tail) r.run(slot++, [&] { return launch_tail(tp, c->stream); });
+    if (use_head && !fuse_tail && !tail_early) r.run(slot++, [&] { return launch_tail(tp, c->stream); });
     return r.err;
 }
 
@@ -1098,6 +1150,39 @@ mlp_status mlp_train_step_async(mlp_ctx* c, const float* x, const float* labels,
     }
     const hipError_t e = enqueue(c, Mode::Train, x, labels, lr, nullptr, loss_dev);
     if (e != hipSuccess) return hip_fail(c, e, "mlp_train_step");
+    return MLP_OK;
+}
+
+mlp_status mlp_train_steps(mlp_ctx* c, int32_t n, const float* x, const float* labels, float lr,
+                           float* loss_dev) {
+    mlp_status st = check_ready(c);
+    if (st != MLP_OK) return st;
+    if (n < 1) return set_err(c, MLP_ERR_ARG, "n must be at least 1");
+    if (!x || !aligned16(x)) return set_err(c, MLP_ERR_ARG, "x must be a 16-byte aligned device pointer");
+    if (!labels || !aligned16(labels))
+        return set_err(c, MLP_ERR_ARG, "labels must be a 16-byte aligned device pointer");
+    if (!std::isfinite(lr)) return set_err(c, MLP_ERR_ARG, "lr must be finite");
+    if (loss_dev && ((uintptr_t)loss_dev & 3u)) return set_err(c, MLP_ERR_ARG, "loss_dev must be 4-byte aligned");
+    const size_t xs = (size_t)c->B * c->dims[0], ls = (size_t)c->B * c->dims[c->L];
+    // every batch of the run must keep the 16-byte alignment of the first
+    if (n > 1 && ((xs * 4) % 16 != 0 || (ls * 4) % 16 != 0))
+        return set_err(c, MLP_ERR_ARG, "batch rows x width must be a multiple of 4 for a run of steps");
+    if (c->opt != MLP_OPT_SGD) {
+        // Adam / LaProp: one mlp_train_step_async per batch (its preflight
+        // refuses graph capture and advances the step count)
+        for (int32_t s = 0; s < n; ++s) {
+            st = mlp_train_step_async(c, x + s * xs, labels + s * ls, lr, loss_dev ? loss_dev + s : nullptr);
+            if (st != MLP_OK) return st;
+        }
+        return MLP_OK;
+    }
+    const bool fuse = steps_fusable(c);
+    for (int32_t s = 0; s < n; ++s) {
+        const float* xn = (fuse && s + 1 < n) ? x + (s + 1) * xs : nullptr;
+        const hipError_t e = enqueue(c, Mode::Train, x + s * xs, labels + s * ls, lr, nullptr,
+                                     loss_dev ? loss_dev + s : nullptr, nullptr, fuse && s > 0, xn);
+        if (e != hipSuccess) return hip_fail(c, e, "mlp_train_steps");
+    }
     return MLP_OK;
 }
 

@@ -7,6 +7,8 @@
 //              W[k][n] -= lr * sum_b a[b][k] G[b][n]           its dW + SGD,
 //              in one pass over W (hidden layers)
 //   skinny_tn  W[k][n]  -= lr * sum_b a[b][k] G[b][n]          dW + SGD (first layer)
+//   skinny_nn with MBT > 0: the first layer's dW + SGD of one step and the
+//              next step's forward of that layer, in one pass over W
 //
 // skinny_nn and skinny_ntu reduce inside v_mfma_f32_16x16x4f32 (the batch is
 // the MFMA's 16-wide M or N side, rows >= B are zero), so every 16-byte load
@@ -32,8 +34,18 @@ __device__ __forceinline__ float4v ld4(const float* p) { return *reinterpret_cas
 // W[k+4g+i][n0+4j .. n0+4j+3] for step i, and x[m = lane%16][k+4g .. k+4g+3]
 // once for the block.  MFMA q (0..3) of step i multiplies component q of the
 // W row: output column n0 + 4j + q.
-template <int NW, Epi EPI>
+//
+// With MBT > 0 (batch rows padded to MBT = 4 or 8) the launch also finishes
+// the previous step's first layer: every element of W it loads is updated,
+// W' = W - lr * sum_b a[b][k] G[b][n] with the previous step's input a
+// (p.act) and gradient G (p.grad), in exactly the arithmetic of skinny_tn
+// (b ascending, one fma per b, then one fma for the step), stored once by the
+// lane that loaded it (p.wout, in place), and W' is what this forward
+// multiplies.  Results are bitwise those of skinny_tn followed by the plain
+// forward on the next batch.
+template <int NW, Epi EPI, int MBT = 0>
 __global__ __launch_bounds__(NW * kWave) void skinny_nn(SkinnyParams p) {
+    constexpr bool UPD = MBT > 0;
     __shared__ float4v red[NW - 1][4][kWave];
     __shared__ int s_last;
     const int lane = threadIdx.x & 63;
@@ -60,24 +72,46 @@ __global__ __launch_bounds__(NW * kWave) void skinny_nn(SkinnyParams p) {
     // address (the matrix base) and zero the value.  The next block's loads
     // are issued before the current block's MFMAs, so memory latency overlaps
     // the matrix-core work.
-    const float* __restrict__ W = p.B;
+    // (not __restrict__: with MBT > 0 the same rows are written through p.wout)
+    const float* W = p.B;
     const float* __restrict__ X = p.A + (int64_t)(mok ? j : 0) * p.K;
     // One block is in flight ahead of the one being multiplied (deeper
     // look-ahead measured slower: 45-48 us against 43 for the 4096 x 11008
     // forward at batch 8).  Loads use clamped in-range addresses; values
     // past the slice or past N are zeroed where they are multiplied.
     const float4v zero = {0.f, 0.f, 0.f, 0.f};
-    constexpr int kAhead = 1;
-    float4v wq[kAhead][4], xq[kAhead];
-    auto fetch = [&](int k, float4v* wd, float4v& xd) {
+    constexpr int kAhead = UPD ? 2 : 1;
+    constexpr int NA = UPD ? MBT : 1;
+    float4v wq[kAhead][4], xq[kAhead], aq[kAhead][NA];
+    // MBT > 0: G[b][n..n+3] of this lane's columns, fixed for the whole launch
+    float4v gcol[NA];
+#pragma unroll
+    for (int b = 0; b < NA; ++b) gcol[b] = zero;
+    if constexpr (UPD) {
+#pragma unroll
+        for (int b = 0; b < MBT; ++b)
+            if (b < p.MB && nok) gcol[b] = ld4(p.grad + (int64_t)b * p.N + n);
+    }
+    auto fetch = [&](int k, float4v* wd, float4v& xd, float4v* ad) {
         const int kr = min(k + 4 * g, kw1 - 4);   // this lane group's 4 rows (K is a multiple of 4)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wd[i] = ld4(W + (int64_t)(kr + i) * p.N + (nok ? n : 0));
+        for (int i = 0; i < 4; ++i) {
+            const float* src = W + (int64_t)(kr + i) * p.N + (nok ? n : 0);
+            if constexpr (UPD)
+                wd[i] = __builtin_nontemporal_load(reinterpret_cast<const float4v*>(src));
+            else
+                wd[i] = ld4(src);
+        }
         xd = ld4(X + kr);
+        if constexpr (UPD) {
+            // a[b][kr .. kr+3] of the previous step (rows past the batch are zero where used)
+#pragma unroll
+            for (int b = 0; b < MBT; ++b) ad[b] = ld4(p.act + (int64_t)min(b, p.MB - 1) * p.K + kr);
+        }
     };
 #pragma unroll
     for (int a = 0; a < kAhead; ++a)
-        if (kw0 + 16 * a < kw1) fetch(kw0 + 16 * a, wq[a], xq[a]);
+        if (kw0 + 16 * a < kw1) fetch(kw0 + 16 * a, wq[a], xq[a], aq[a]);
     for (int k = kw0; k < kw1; k += 16 * kAhead) {
 #pragma unroll
         for (int a = 0; a < kAhead; ++a) {
@@ -85,10 +119,38 @@ __global__ __launch_bounds__(NW * kWave) void skinny_nn(SkinnyParams p) {
             if (kb < kw1) {
                 const bool ok = kb + 4 * g < kw1;
                 float4v w[4], xv;
+                if constexpr (UPD) {
+                    // W' of rows kb+4g+i, columns n..n+3: the order of skinny_tn
 #pragma unroll
-                for (int i = 0; i < 4; ++i) w[i] = (ok && nok) ? wq[a][i] : zero;
+                    for (int i = 0; i < 4; ++i) {
+                        float4v d = zero;
+#pragma unroll
+                        for (int b = 0; b < MBT; ++b) {
+                            const float av = b < p.MB ? aq[a][b][i] : 0.f;
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) d[q] = fmaf(av, gcol[b][q], d[q]);
+                        }
+                        float4v u;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) u[q] = fmaf(-p.lr, d[q], wq[a][i][q]);
+                        w[i] = (ok && nok) ? u : zero;
+                    }
+                    if (ok && nok) {
+                        // non-temporal, as skinny_tn's: 16 lanes write a whole 256-byte
+                        // segment of each row, and no later launch of the step re-reads W'
+                        // soon enough for the last-level cache to hold it, where dirty
+                        // lines would slow the next launches' reads
+                        const int kr = kb + 4 * g;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            __builtin_nontemporal_store(w[i], reinterpret_cast<float4v*>(p.wout + (int64_t)(kr + i) * p.N + n));
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) w[i] = (ok && nok) ? wq[a][i] : zero;
+                }
                 xv = (ok && mok) ? xq[a] : zero;
-                if (kb + 16 * kAhead < kw1) fetch(kb + 16 * kAhead, wq[a], xq[a]);
+                if (kb + 16 * kAhead < kw1) fetch(kb + 16 * kAhead, wq[a], xq[a], aq[a]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -440,12 +502,20 @@ __global__ __launch_bounds__(256) void skinny_tn(SkinnyParams p) {
         for (int r = 0; r < CH; ++r) {
             const int rr = c0 + r;
             if (rr >= rows) break;
+            // b ascending, one fma per b, then one fma for the step (the
+            // fused pass in skinny_nn repeats exactly this arithmetic)
             float4v d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int b = 0; b < MB; ++b) d += sa[rr][b] * gv[b];
+            for (int b = 0; b < MB; ++b) {
+                const float av = sa[rr][b];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) d[q] = fmaf(av, gv[b][q], d[q]);
+            }
             float* dst = base + (int64_t)rr * p.N;
             if constexpr (EPI == Epi::Sgd) {
-                const float4v v = w[buf][r] - p.lr * d;
+                float4v v;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = fmaf(-p.lr, d[q], w[buf][r][q]);
                 __builtin_nontemporal_store(v, reinterpret_cast<float4v*>(dst));
             } else if constexpr (AD) {
                 float4v wv = w[buf][r], mv = mo[buf][r], vv = vo[buf][r];
@@ -491,6 +561,24 @@ hipError_t launch_skinny(const SkinnyLaunch& L, const SkinnyParams& p, hipStream
     if (p.MB < 1 || p.MB > 16) return hipErrorInvalidValue;
     switch (L.layout) {
     case Layout::NN:
+        if (L.fused_update) {
+            // previous step's dW + SGD of this W, then this forward (batch <= 8)
+            if (L.waves != 8 || p.MB > 8 || !p.act || !p.grad || p.wout != p.B ||
+                (L.epi != Epi::ReluMask && L.epi != Epi::Store))
+                return hipErrorInvalidValue;
+            if (p.MB <= 4) {
+                if (L.epi == Epi::ReluMask)
+                    hipLaunchKernelGGL((skinny_nn<8, Epi::ReluMask, 4>), dim3(L.grid), dim3(8 * 64), 0, s, p);
+                else
+                    hipLaunchKernelGGL((skinny_nn<8, Epi::Store, 4>), dim3(L.grid), dim3(8 * 64), 0, s, p);
+            } else {
+                if (L.epi == Epi::ReluMask)
+                    hipLaunchKernelGGL((skinny_nn<8, Epi::ReluMask, 8>), dim3(L.grid), dim3(8 * 64), 0, s, p);
+                else
+                    hipLaunchKernelGGL((skinny_nn<8, Epi::Store, 8>), dim3(L.grid), dim3(8 * 64), 0, s, p);
+            }
+            return hipGetLastError();
+        }
         if (L.waves == 8) {
             if (L.epi == Epi::ReluMask)
                 hipLaunchKernelGGL((skinny_nn<8, Epi::ReluMask>), dim3(L.grid), dim3(8 * 64), 0, s, p);

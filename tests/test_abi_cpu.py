@@ -139,6 +139,7 @@ def test_null_context_calls():
     assert lib.mlp_forward(None, None, None, None, None) == binding.MLP_ERR_ARG
     assert lib.mlp_train_step(None, None, None, 0.1, None) == binding.MLP_ERR_ARG
     assert lib.mlp_train_step_async(None, None, None, 0.1, None) == binding.MLP_ERR_ARG
+    assert lib.mlp_train_steps(None, 1, None, None, 0.1, None) == binding.MLP_ERR_ARG
     assert lib.mlp_grads(None, None, None, None, None, None) == binding.MLP_ERR_ARG
     assert lib.mlp_read_state(None, 0, 1, None) == binding.MLP_ERR_ARG
     assert lib.mlp_profile_enable(None, 1) == binding.MLP_ERR_ARG

@@ -1068,3 +1068,108 @@ def test_tuned_plans_keep_parity(torch_dev, dims, B, precision):
     ref2 = P.oracle_step(x, t, Ws, 0.05, dims, precision, masks2)
     P.check_update(loss2, W_new, Ws, ref2, precision, "tuned")
     net.close()
+
+
+# ------------------------------------------------------------ runs of steps --
+
+STEPS_CASES = [
+    # dims, B, precision, optimizer, steps
+    ((4096, 11008, 4096), 8, "f32", "sgd", 3),   # the skinny batch-8 workload: fused first-layer passes
+    ((256, 520, 64), 8, "f32", "sgd", 4),        # ragged last column group
+    ((1024, 1100, 260), 6, "f32", "sgd", 3),     # forward K splits (partials and tickets), 6 of 8 rows
+    ((4100, 64, 8), 3, "f32", "sgd", 3),         # many K splits, batch <= 4
+    ((64, 32, 8), 8, "f32", "sgd", 3),           # fused output layer with L = 2: its tail goes first
+    ((96, 160, 132, 40), 8, "f32", "sgd", 3),    # three layers: dX + dW pass of the middle layer
+    ((64, 12), 5, "f32", "sgd", 3),              # one layer: the fused launch makes the next logits
+    ((1024, 1100, 260), 16, "f32", "sgd", 2),    # 16 rows: not fused, one step after another
+    ((200, 300, 36), 64, "f32", "sgd", 2),       # tiled kernels: not fused
+    ((200, 300, 36), 64, "bf16", "sgd", 2),
+    ((256, 520, 64), 8, "f32", "adam", 3),       # adaptive rule: not fused
+]
+
+
+@pytest.mark.parametrize("dims,B,precision,opt,steps", STEPS_CASES)
+def test_train_steps_match_single_steps(torch_dev, dims, B, precision, opt, steps):
+    """mlp_train_steps over n batches equals n mlp_train_step_async calls on
+    the same batches, bit for bit: weights, per-step losses, and the last
+    step's activations and masks (in the skinny sessions the first layer's
+    update and the next step's first forward share one launch)."""
+    from mlp_gemm_softmax_amd import binding
+    torch, dev = torch_dev
+    _announce(f"train_steps dims={dims} B={B} {precision} {opt} n={steps}")
+    Ws = synth.make_weights(dims, "glorot", seed=sum(dims) + B)
+    xs, ts = [], []
+    for s in range(steps):
+        x, t, _ = synth.make_batch(B, dims[0], dims[-1], "normal", seed=B + 7, step=s)
+        xs.append(x)
+        ts.append(t)
+    xd, td = P.to_dev([np.stack(xs), np.stack(ts)], dev)
+    lr = 0.05 if opt == "sgd" else 1e-3
+    out = []
+    for mode in ("run", "single"):
+        net = make_net(dims, B, precision, Ws, dev)
+        if opt != "sgd":
+            net.set_optimizer(opt, 0.9, 0.999, 1e-8)
+        losses = torch.full((steps,), float("nan"), dtype=torch.float32, device=dev)
+        if mode == "run":
+            net.train_steps(xd, td, lr, losses)
+        else:
+            for s in range(steps):
+                net.train_step_async(xd[s], td[s], lr, losses[s:s + 1])
+        torch.cuda.synchronize()
+        state = [net.read_state(binding.STATE_ACT, l).cpu().numpy() for l in range(1, len(dims) - 1)]
+        state += [net.read_state(binding.STATE_MASK, l).cpu().numpy() for l in range(1, len(dims) - 1)]
+        out.append((losses.cpu().numpy(), [w.cpu().numpy() for w in net.read_params()], state))
+        net.close()
+    (la, wa, sa), (lb, wb, sb) = out
+    assert np.all(np.isfinite(la))
+    assert np.array_equal(la.view(np.uint32), lb.view(np.uint32)), (la, lb)
+    for l, (u, v) in enumerate(zip(wa, wb)):
+        assert np.array_equal(u.view(np.uint32), v.view(np.uint32)), f"W_{l} differs"
+    for u, v in zip(sa, sb):
+        assert np.array_equal(u, v)
+
+
+def test_train_steps_follow_the_oracle(torch_dev):
+    """A fused run's per-step losses track the oracle's own trajectory over
+    the same batches (free-running: each implementation feeds its updated
+    weights to the next step), and its first loss is the oracle's at the
+    strict loss gate."""
+    torch, dev = torch_dev
+    dims, B, steps, lr = (256, 520, 64), 8, 4, 0.05
+    Ws = synth.make_weights(dims, "glorot", seed=11)
+    batches = [synth.make_batch(B, dims[0], dims[-1], "normal", seed=12, step=s)[:2] for s in range(steps)]
+    ref, cur = [], [np.asarray(a, np.float32) for a in Ws]
+    for x, t in batches:
+        r = mlp_oracle.train_step(x, t, cur, lr)
+        ref.append(r["loss"])
+        cur = [a.astype(np.float32) for a in r["W_new"]]
+    xd, td = P.to_dev([np.stack([b[0] for b in batches]), np.stack([b[1] for b in batches])], dev)
+    net = make_net(dims, B, "f32", Ws, dev)
+    losses = torch.zeros(steps, dtype=torch.float32, device=dev)
+    net.train_steps(xd, td, lr, losses)
+    got = losses.cpu().numpy()
+    net.close()
+    assert abs(got[0] - ref[0]) <= 1e-5 * abs(ref[0])
+    for s in range(steps):
+        assert abs(got[s] - ref[s]) <= 1e-4 * abs(ref[s]), (s, got[s], ref[s])
+
+
+def test_train_steps_argument_errors(torch_dev):
+    """Preflight of mlp_train_steps: nothing is enqueued and the weights stay."""
+    from mlp_gemm_softmax_amd import binding
+    torch, dev = torch_dev
+    dims, B = (64, 32, 8), 8
+    Ws = synth.make_weights(dims, "glorot", seed=3)
+    net = make_net(dims, B, "f32", Ws, dev)
+    x = torch.zeros((2, B, dims[0]), dtype=torch.float32, device=dev)
+    t = torch.zeros((2, B, dims[-1]), dtype=torch.float32, device=dev)
+    lib = binding.lib()
+    h = net._h
+    assert lib.mlp_train_steps(h, 0, ctypes_ptr(x), ctypes_ptr(t), 0.1, None) == binding.MLP_ERR_ARG
+    assert lib.mlp_train_steps(h, 2, None, ctypes_ptr(t), 0.1, None) == binding.MLP_ERR_ARG
+    assert lib.mlp_train_steps(h, 2, ctypes_ptr(x), ctypes_ptr(t), float("nan"), None) == binding.MLP_ERR_ARG
+    torch.cuda.synchronize()
+    for a, b in zip(net.read_params(), Ws):
+        assert np.array_equal(a.cpu().numpy(), b)
+    net.close()
