@@ -1173,3 +1173,39 @@ def test_train_steps_argument_errors(torch_dev):
     for a, b in zip(net.read_params(), Ws):
         assert np.array_equal(a.cpu().numpy(), b)
     net.close()
+
+
+def test_train_steps_graph_replay_matches_eager(torch_dev):
+    """A run of steps on the batch-8 4096-11008-4096 net (the merged
+    first-layer launches included) captured into a HIP graph replays bit for
+    bit like the same run enqueued eagerly, with eager work and
+    synchronisations between the replays."""
+    from mlp_gemm_softmax_amd import binding
+    torch, dev = torch_dev
+    w = synth.WORKLOADS["skinny_b8"]
+    _announce("graph replay of a run of skinny_b8 steps")
+    Ws = synth.workload_weights(w)
+    n = 3
+    bs = [synth.workload_batch(w, s)[:2] for s in range(n)]
+    xd, td = P.to_dev([np.stack([b[0] for b in bs]), np.stack([b[1] for b in bs])], dev)
+    eager = make_net(w.dims, w.batch, "f32", Ws, dev)
+    s = torch.cuda.Stream(device=dev)
+    graphed = binding.Mlp(w.dims, w.batch, "f32", device=str(dev), stream=s)
+    graphed.set_params(P.to_dev(Ws, dev))
+    loss_e = torch.zeros(n, dtype=torch.float32, device=dev)
+    loss_g = torch.zeros(n, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        graphed.train_steps(xd, td, w.lr, loss_g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        eager.train_steps(xd, td, w.lr, loss_e)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(loss_g, loss_e), f"replay {rep}: losses {loss_g.tolist()} vs {loss_e.tolist()}"
+        for l, (a, b) in enumerate(zip(graphed.read_params(), eager.read_params())):
+            assert torch.equal(a, b), f"replay {rep}: W{l} differs"
+    eager.close()
+    graphed.close()
