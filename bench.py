@@ -251,7 +251,9 @@ def summarize(outdir, w, steps, warmup):
     trace.sort(key=lambda r: int(r["Dispatch_Id"]))
     disp = [(r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in trace]
     full_steps = sum(1 for d in disp if "mlp::" in d[0] and _FOLLOWER not in d[0]) // n
-    names, trace_us = _per_slot(disp, n, max(1, full_steps - 1))
+    # the last `steps` steps: the bench's final pass of single steps (a run of
+    # merged steps, with another launch sequence, may come before it)
+    names, trace_us = _per_slot(disp, n, max(1, min(full_steps - 1, steps)))
     stats = _csv(os.path.join(outdir, f"trace_{w}", f"{w}_kernel_stats.csv"))
 
     counters, scale = {}, {}
@@ -440,8 +442,11 @@ def measure(w, args, dev, want_cpu, want_masks):
     # The same K steps as one mlp_train_steps run (batches stacked), where
     # the library hands the first layer's update to the next step's first
     # forward launch (batch <= 8, float32, SGD); reported beside the figure.
+    # Not in counter runs (--profile-steps), whose dispatches must repeat
+    # the single-step sequence.
     run_ms = None
-    if args.mode == "train" and w.precision == "f32" and w.batch <= 8 and args.optimizer == "sgd":
+    if (args.mode == "train" and w.precision == "f32" and w.batch <= 8 and args.optimizer == "sgd"
+            and not args.profile_steps):
         order = [batches[(args.warmup + i) % n_batches] for i in range(args.steps)]
         xs = torch.stack([b[0] for b in order]).contiguous()
         ts = torch.stack([b[1] for b in order]).contiguous()
