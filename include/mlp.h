@@ -228,7 +228,8 @@ mlp_status mlp_train_step_async(mlp_ctx* ctx, const float* x, const float* label
  * sessions whose batch has at most 8 rows (the weight-streaming kernels),
  * float32 with SGD, the launch that updates the first layer's weights also
  * computes the next step's first-layer forward from the updated values, so
- * each step after the first makes one pass fewer over that matrix.  Errors
+ * each step after the first makes one pass fewer over that matrix; per-launch
+ * timing (mlp_profile_enable) records none of such a run's steps.  Errors
  * as mlp_train_step_async, and MLP_ERR_ARG for n < 1 or, when n > 1, a
  * batch whose x or labels size is not a multiple of 16 bytes (later batches
  * would lose the alignment); a HIP failure poisons the context and leaves
