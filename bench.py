@@ -55,9 +55,10 @@ def parse():
     ap.add_argument("--extra-workloads", default=DEFAULT_EXTRA, metavar="A,B",
                     help="further workloads measured the same way and reported under \"also\" "
                          "(empty: none)")
-    ap.add_argument("--mode", choices=["train", "forward", "probs"], default="train",
+    ap.add_argument("--mode", choices=["train", "forward", "probs", "checkpoint"], default="train",
                     help="train: the training step (the headline metric); forward: logits only "
-                         "(inference of the same network); probs: class probabilities (inference)")
+                         "(inference of the same network); probs: class probabilities (inference); "
+                         "checkpoint: save and restore of the state through host memory")
     ap.add_argument("--optimizer", choices=["sgd", "adam", "laprop"], default="sgd",
                     help="update rule of the step (Adam/LaProp: beta1 0.9, beta2 0.999, eps 1e-8)")
     ap.add_argument("--tune", type=int, default=0, metavar="R",
@@ -522,6 +523,49 @@ def measure(w, args, dev, want_cpu, want_masks):
     return res
 
 
+def measure_checkpoint(w, args, dev):
+    """Save and restore the workload's state through the C ABI: the weights,
+    and with --optimizer adam|laprop the moments too, into a pinned and into
+    a pageable host buffer (min(K, 20) of each after the warm-up).  A save
+    synchronises, copies to the host and checksums; a restore checks the
+    whole checkpoint, then copies to the device."""
+    import torch
+    from mlp_gemm_softmax_amd import binding, synth
+
+    Ws = synth.workload_weights(w)
+    net = binding.Mlp(w.dims, w.batch, w.precision, device="cuda:0")
+    net.set_params([torch.from_numpy(a).to(dev) for a in Ws])
+    withopt = args.optimizer != "sgd"
+    if withopt:
+        net.set_optimizer(args.optimizer, 0.9, 0.999, 1e-8)
+    nbytes = net.checkpoint_bytes(withopt)
+    reps = max(1, min(args.steps, 20))
+    res = {}
+    for kind in ("pinned", "pageable"):
+        buf = torch.empty(nbytes, dtype=torch.uint8, pin_memory=kind == "pinned")
+        for _ in range(max(args.warmup, 1)):
+            net.save_checkpoint(withopt, out=buf)
+            net.load_checkpoint(buf)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            net.save_checkpoint(withopt, out=buf)
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            net.load_checkpoint(buf)
+        t2 = time.perf_counter()
+        save_s, load_s = (t1 - t0) / reps, (t2 - t1) / reps
+        res[kind] = {"save_ms": round(save_s * 1e3, 4), "load_ms": round(load_s * 1e3, 4),
+                     "save_gbps": round(nbytes / save_s / 1e9, 2), "load_gbps": round(nbytes / load_s / 1e9, 2)}
+        del buf
+    net.close()
+    rt = res["pinned"]["save_ms"] + res["pinned"]["load_ms"]
+    return {"value": round(1e3 / rt, 3), "ms_per_step": round(rt, 4), "dtype": "f32",
+            "config": {"workload": w.name, "dims": list(w.dims), "batch": w.batch, "precision": w.precision,
+                       "optimizer": args.optimizer, "mode": "checkpoint", "with_moments": withopt},
+            "checkpoint_bytes": nbytes, "reps": reps, "pinned": res["pinned"], "pageable": res["pageable"]}
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -536,6 +580,19 @@ def main():
 
     dev = torch.device("cuda:0")
     w = synth.WORKLOADS[args.workload]
+    if args.mode == "checkpoint":
+        head = measure_checkpoint(w, args, dev)
+        out = {"metric": "checkpoint save + restore round trips/sec (pinned host buffer), 1 GPU",
+               "value": head.pop("value"), "unit": "round trips/s", "n_gpus": 1, "steps": head.pop("reps"),
+               "warmup": args.warmup, "ms_per_step": head.pop("ms_per_step"), "higher_is_better": True,
+               "scaling": "weak", "vs_baseline": None, "dtype": head.pop("dtype"),
+               "data": "synthetic (seeded initial weights)", "config": head.pop("config")}
+        out.update(head)
+        extra = [n for n in args.extra_workloads.split(",") if n and n not in ("none", w.name)]
+        if extra:
+            out["also"] = {n: measure_checkpoint(synth.WORKLOADS[n], args, dev) for n in extra}
+        print(json.dumps(out), flush=True)
+        return
     fwd = args.mode in ("forward", "probs")
     head = measure(w, args, dev, not args.no_cpu_baseline, not args.no_cpu_baseline)
     out = {

@@ -274,14 +274,21 @@ mlp_status mlp_set_optimizer(mlp_ctx* ctx, int32_t opt, float beta1, float beta2
  * before it changes any state; the train-to-deploy example reloads one into
  * a fresh inference session).
  * A checkpoint is host memory: a 136-byte header (magic "MLPCKPT1", version
- * 1, layer count, precision of the writer, update rule, widths, beta1, beta2,
- * eps, step count, payload size, FNV-1a-64 checksum of the payload) and the
+ * 2, layer count, precision of the writer, update rule, widths, beta1, beta2,
+ * eps, step count, payload size, checksum of the payload) and the
  * payload: every W_l as float32 [dims[l], dims[l+1]] row-major, then, when
  * the rule's state is included, every m_l and every v_l in the same shapes.
  * Little-endian; the header's fields are, in order and without padding:
  * char magic[8], uint32 version, n_layers, precision, optimizer, int32
  * dims[17] (n_layers+1 used, the rest 0), float beta1, beta2, eps, uint32
- * reserved[2] (0), int64 step, uint64 payload_bytes, uint64 checksum. */
+ * reserved[2] (0), int64 step, uint64 payload_bytes, uint64 checksum.
+ * Checksum: with FNV-1a-64's offset basis B = 0xcbf29ce484222325 and prime
+ * P = 0x100000001b3, the payload is read as little-endian uint64 words (a
+ * final 4-byte remainder zero-extended to a word); word i is folded into lane
+ * i mod 4, h = (h XOR word) * P mod 2^64, every lane starting at B; the
+ * checksum is byte-wise FNV-1a-64 (r = B; per byte r = (r XOR byte) * P) over
+ * the 32 little-endian bytes of lanes 0, 1, 2, 3.  Version 1 checkpoints
+ * (another checksum) are refused. */
 
 /* Size of the checkpoint mlp_save_checkpoint writes; with_optimizer != 0
  * includes the Adam/LaProp moments when the session uses such a rule.

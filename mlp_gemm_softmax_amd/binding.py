@@ -227,14 +227,32 @@ class Mlp:
         self._check(lib().mlp_set_optimizer(self._h, opt, float(beta1), float(beta2), float(eps), ptr, nbytes))
         self.opt_state = state
 
-    def save_checkpoint(self, with_optimizer: bool = True) -> bytes:
-        """Weights (and Adam/LaProp moments) as checkpoint bytes in host memory."""
-        n = int(lib().mlp_checkpoint_bytes(self._h, 1 if with_optimizer else 0))
+    def checkpoint_bytes(self, with_optimizer: bool = True) -> int:
+        return int(lib().mlp_checkpoint_bytes(self._h, 1 if with_optimizer else 0))
+
+    def save_checkpoint(self, with_optimizer: bool = True, out=None):
+        """Weights (and Adam/LaProp moments) as checkpoint bytes in host
+        memory; with `out` (a contiguous uint8 CPU tensor, e.g. pinned, of at
+        least checkpoint_bytes()) they are written there and `out` returned."""
+        n = self.checkpoint_bytes(with_optimizer)
+        if out is not None:
+            if out.device.type != "cpu" or out.dtype != self.torch.uint8 or not out.is_contiguous() \
+                    or out.numel() < n:
+                raise ValueError(f"out must be a contiguous uint8 CPU tensor of at least {n} bytes")
+            self._check(lib().mlp_save_checkpoint(self._h, ctypes.c_void_p(out.data_ptr()), n,
+                                                  1 if with_optimizer else 0))
+            return out
         buf = ctypes.create_string_buffer(n)
         self._check(lib().mlp_save_checkpoint(self._h, buf, n, 1 if with_optimizer else 0))
         return buf.raw
 
-    def load_checkpoint(self, data: bytes):
+    def load_checkpoint(self, data):
+        """Restore from checkpoint bytes, or from a contiguous uint8 CPU tensor."""
+        if hasattr(data, "data_ptr"):
+            if data.device.type != "cpu" or data.dtype != self.torch.uint8 or not data.is_contiguous():
+                raise ValueError("expected checkpoint bytes or a contiguous uint8 CPU tensor")
+            self._check(lib().mlp_load_checkpoint(self._h, ctypes.c_void_p(data.data_ptr()), data.numel()))
+            return
         buf = ctypes.create_string_buffer(bytes(data), len(data))
         self._check(lib().mlp_load_checkpoint(self._h, buf, len(data)))
 

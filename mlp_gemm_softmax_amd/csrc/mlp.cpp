@@ -1407,12 +1407,12 @@ mlp_status mlp_set_optimizer(mlp_ctx* c, int32_t opt, float beta1, float beta2, 
 // Layout (little-endian, host memory): a 136-byte header, then the payload:
 // every W_l as float32 [dims[l]][dims[l+1]] row-major without padding, then,
 // when the checkpoint carries an adaptive rule's state, every m_l and then
-// every v_l in the same shapes.  The header's checksum is FNV-1a (64-bit)
-// over the payload bytes.
+// every v_l in the same shapes.  The header's checksum (ckpt_hash) runs the
+// FNV-1a step over the payload's 64-bit words in four interleaved lanes.
 namespace {
 
 constexpr char kCkptMagic[8] = {'M', 'L', 'P', 'C', 'K', 'P', 'T', '1'};
-constexpr uint32_t kCkptVersion = 1;
+constexpr uint32_t kCkptVersion = 2;
 
 struct CkptHeader {
     char magic[8];
@@ -1429,13 +1429,43 @@ struct CkptHeader {
 };
 static_assert(sizeof(CkptHeader) == 136, "checkpoint header layout: no implicit padding");
 
-uint64_t fnv1a(const unsigned char* p, size_t n) {
-    uint64_t h = 1469598103934665603ull;
-    for (size_t i = 0; i < n; ++i) {
-        h ^= p[i];
-        h *= 1099511628211ull;
+// FNV-1a, 64-bit (Fowler, Noll and Vo): offset basis 0xcbf29ce484222325,
+// prime 0x100000001b3.
+constexpr uint64_t kFnvBasis = 0xcbf29ce484222325ull;
+constexpr uint64_t kFnvPrime = 0x100000001b3ull;
+
+// Payload checksum: the bytes read as little-endian 64-bit words (a last
+// 4-byte remainder zero-extended); word i goes to lane i mod 4, each lane
+// starting at the FNV-1a basis and taking h = (h ^ word) * prime; the result
+// is byte-wise FNV-1a over the four lanes' 32 little-endian bytes, lane 0
+// first.  Four independent multiply chains: several GB/s on one host core,
+// where byte-wise FNV-1a over the whole payload ran near 1 GB/s.
+uint64_t ckpt_hash(const unsigned char* p, size_t n) {
+    uint64_t h[4] = {kFnvBasis, kFnvBasis, kFnvBasis, kFnvBasis};
+    const size_t nw = n / 8;
+    size_t i = 0;
+    for (; i + 4 <= nw; i += 4) {
+        uint64_t w[4];
+        std::memcpy(w, p + 8 * i, 32);
+        for (int l = 0; l < 4; ++l) h[l] = (h[l] ^ w[l]) * kFnvPrime;
     }
-    return h;
+    for (; i < nw; ++i) {
+        uint64_t w;
+        std::memcpy(&w, p + 8 * i, 8);
+        h[i % 4] = (h[i % 4] ^ w) * kFnvPrime;
+    }
+    if (n % 8) {
+        uint64_t w = 0;
+        std::memcpy(&w, p + 8 * nw, n % 8);
+        h[nw % 4] = (h[nw % 4] ^ w) * kFnvPrime;
+    }
+    uint64_t r = kFnvBasis;
+    for (int l = 0; l < 4; ++l)
+        for (int b = 0; b < 8; ++b) {
+            r ^= (h[l] >> (8 * b)) & 0xffu;
+            r *= kFnvPrime;
+        }
+    return r;
 }
 
 size_t ckpt_payload(int L, const int32_t* dims, bool moments) {
@@ -1484,7 +1514,7 @@ mlp_status ckpt_check(const void* src, size_t bytes, CkptHeader* h, std::string*
         *why = buf;
         return MLP_ERR_ARG;
     }
-    if (fnv1a((const unsigned char*)src + sizeof(CkptHeader), want) != h->checksum) {
+    if (ckpt_hash((const unsigned char*)src + sizeof(CkptHeader), want) != h->checksum) {
         *why = "checkpoint checksum mismatch (payload damaged)";
         return MLP_ERR_ARG;
     }
@@ -1532,7 +1562,7 @@ mlp_status mlp_save_checkpoint(mlp_ctx* c, void* dst, size_t bytes, int32_t with
             off += n;
         }
     if (e != hipSuccess) return hip_fail(c, e, "mlp_save_checkpoint");
-    h.checksum = fnv1a(out, h.payload_bytes);
+    h.checksum = ckpt_hash(out, h.payload_bytes);
     std::memcpy(dst, &h, sizeof h);
     return MLP_OK;
 }

@@ -174,12 +174,47 @@ def test_checkpoint_info_reads_the_documented_format():
     assert binding.checkpoint_info(_checkpoint((4, 4)))["optimizer"] == binding.OPT_SGD
 
 
+def test_checkpoint_checksum_pins():
+    """The format's checksum, pinned outside its own code: byte-wise FNV-1a-64
+    against the published test vectors, and the four-lane fold on short
+    payloads written out by hand (word i into lane i mod 4, a 4-byte tail
+    zero-extended, then FNV-1a over the lanes' bytes)."""
+    assert ckpt_format.fnv1a(b"") == 0xcbf29ce484222325
+    assert ckpt_format.fnv1a(b"a") == 0xaf63dc4c8601ec8c
+    assert ckpt_format.fnv1a(b"foobar") == 0x85944171f73967e8
+    B, P, M = 0xcbf29ce484222325, 0x100000001b3, (1 << 64) - 1
+
+    def fold(lanes):
+        r = B
+        for x in lanes:
+            for k in range(8):
+                r = ((r ^ ((x >> (8 * k)) & 0xFF)) * P) & M
+        return r
+
+    assert ckpt_format.checksum(b"") == fold([B, B, B, B])
+    payload = bytes(range(1, 13))                       # 12 bytes: one word and a 4-byte tail
+    w0 = int.from_bytes(payload[:8], "little")
+    w1 = int.from_bytes(payload[8:] + b"\0\0\0\0", "little")
+    assert ckpt_format.checksum(payload) == fold([((B ^ w0) * P) & M, ((B ^ w1) * P) & M, B, B])
+    payload = bytes((7 * i + 3) & 0xFF for i in range(40))   # five words: lane 0 takes words 0 and 4
+    w = [int.from_bytes(payload[8 * i:8 * i + 8], "little") for i in range(5)]
+    lane0 = (((((B ^ w[0]) * P) & M) ^ w[4]) * P) & M
+    assert ckpt_format.checksum(payload) == fold([lane0] + [((B ^ w[i]) * P) & M for i in (1, 2, 3)])
+    # one flipped bit anywhere changes it
+    base = ckpt_format.checksum(payload)
+    for i in (0, 17, 39):
+        bad = bytearray(payload)
+        bad[i] ^= 0x10
+        assert ckpt_format.checksum(bytes(bad)) != base
+
+
 def _damaged():
     good = _checkpoint((6, 4, 3))
     yield "truncated header", good[:100]
     yield "truncated payload", good[:-4]
     yield "magic", b"X" + good[1:]
-    yield "version", good[:8] + struct.pack("<I", 2) + good[12:]
+    yield "version 1 (another checksum)", good[:8] + struct.pack("<I", 1) + good[12:]
+    yield "version 3", good[:8] + struct.pack("<I", 3) + good[12:]
     yield "layers", good[:12] + struct.pack("<I", 0) + good[16:]
     yield "rule", good[:20] + struct.pack("<I", 9) + good[24:]
     yield "width", good[:24] + struct.pack("<i", -1) + good[28:]

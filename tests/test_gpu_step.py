@@ -767,7 +767,7 @@ def test_checkpoint_payload_decodes_from_the_documented_layout(torch_dev):
     ck = net.save_checkpoint(with_optimizer=True)
     h = ckpt_format.parse(ck)
     n_w = sum(a * b for a, b in zip(dims[:-1], dims[1:]))
-    assert h["magic"] == b"MLPCKPT1" and h["version"] == 1 and h["n_layers"] == 2
+    assert h["magic"] == b"MLPCKPT1" and h["version"] == ckpt_format.VERSION and h["n_layers"] == 2
     assert h["dims"] == list(dims) and h["unused_dims"] == [0] * (17 - len(dims))
     assert h["precision"] == binding.MLP_F32 and h["optimizer"] == binding.OPT_ADAM
     assert h["betas"] == (_f32(b1), _f32(b2), _f32(eps)) and h["reserved"] == (0, 0)
