@@ -16,7 +16,9 @@ input, through the C ABI.  Inputs are generated from fixed seeds, copied to
 HBM before the timed region, and reused cyclically (the batch-1024 workload
 draws a fresh batch for each of its 100 steps).  W untimed warm-up steps,
 then K steps bracketed by device synchronisations (asynchronous launches:
-the headline).  Then up to 50 synchronous steps (the loss read back after
+the headline); when the W steps take less than --min-warmup-ms (100 ms),
+untimed steps continue until that much time has passed, so that the timed
+steps do not catch the GPU ramping up from idle.  Then up to 50 synchronous steps (the loss read back after
 each one) give `sync_ms_per_step`.  For batches of at most 8 rows (float32,
 SGD) the same K steps also run as one `mlp_train_steps` call, whose
 first-layer update launch makes the next step's first forward too:
@@ -64,6 +66,10 @@ def parse():
     ap.add_argument("--tune", type=int, default=0, metavar="R",
                     help="before timing, let the library choose tile shapes and K splits by timing "
                          "candidates over R steps each (mlp_tune); 0 = the planner's defaults")
+    ap.add_argument("--min-warmup-ms", type=float, default=100.0,
+                    help="after the W warm-up steps, keep running untimed steps until this much "
+                         "wall time has passed since the first, so the GPU leaves its idle clocks "
+                         "before the timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--profile-steps", type=int, default=None,
@@ -420,8 +426,19 @@ def measure(w, args, dev, want_cpu, want_masks):
             else:
                 net.train_step_async(xb, tb, w.lr, loss_dev)
 
+    # W warm-up steps, then more untimed steps until at least
+    # --min-warmup-ms of GPU work has run: after an idle GPU (the previous
+    # workload's CPU baseline) a handful of short steps do not reach steady
+    # clocks (bf16 wide step: 0.725-0.735 ms/step after 5 warm-up steps,
+    # 0.677-0.678 after 50 or more)
+    t0 = time.perf_counter()
     run(args.warmup)
     torch.cuda.synchronize()
+    extra = 0
+    while (time.perf_counter() - t0) * 1e3 < args.min_warmup_ms:
+        run(1, args.warmup + extra)
+        torch.cuda.synchronize()
+        extra += 1
     t0 = time.perf_counter()
     run(args.steps, args.warmup)
     torch.cuda.synchronize()
@@ -499,6 +516,8 @@ def measure(w, args, dev, want_cpu, want_masks):
         # read once, each output written once), and their rate over the step
         "step_bytes": int(step_bytes),
         "step_gbps": round(step_bytes * steps_per_s / 1e9, 2),
+        # untimed steps run after the W warm-up steps to reach --min-warmup-ms
+        "extra_warmup_steps": extra,
         "sync_ms_per_step": round(sync_ms, 5) if sync_ms is not None else None,
         # K steps as one mlp_train_steps call (first-layer passes fused across steps)
         "run_ms_per_step": round(run_ms, 5) if run_ms is not None else None,
