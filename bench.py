@@ -84,19 +84,28 @@ def parse():
     return ap.parse_args()
 
 
+def _code_only(text):
+    """C/C++ source without comments, trailing blanks and empty lines."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def source_digest():
     """sha256 over the HIP/C++ sources of the library (kernel identity):
     source files only, so that build artefacts or editor files beside them
-    do not change it."""
+    do not change it, and their code only, so that an edited comment does
+    not either."""
     import glob
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mlp_gemm_softmax_amd", "csrc")
     files = [f for ext in ("hip", "hpp", "cpp", "h") for f in glob.glob(os.path.join(csrc, f"*.{ext}"))]
     for f in sorted(files):
-        with open(f, "rb") as fh:
+        with open(f, encoding="utf-8") as fh:
             h.update(os.path.basename(f).encode())
-            h.update(fh.read())
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 
@@ -298,7 +307,7 @@ def summarize(outdir, w, steps, warmup):
     roof = line["roofline"]
     dom = [i for i, (nm, _) in enumerate(slots) if nm == roof["kernel"]][0]
     lines = [f"# rocprofv3 summary: workload `{w}`", "",
-             f"Kernel source digest (sha256 of the .hip/.hpp/.cpp/.h files in mlp_gemm_softmax_amd/csrc): `{source_digest()}`", "",
+             f"Kernel source digest (sha256 of the code, comments removed, of the .hip/.hpp/.cpp/.h files in mlp_gemm_softmax_amd/csrc): `{source_digest()}`", "",
              "Commands (repository root on one MI355X; OUT is the output folder):", "",
              "```", TRACE_CMD.format(w=w, s=steps, wu=warmup),
              PMC_CMD.format(c="FETCH_SIZE", d="fetch", w=w),

@@ -75,9 +75,11 @@ __global__ __launch_bounds__(NW * kWave) void skinny_nn(SkinnyParams p) {
     // (not __restrict__: with MBT > 0 the same rows are written through p.wout)
     const float* W = p.B;
     const float* __restrict__ X = p.A + (int64_t)(mok ? j : 0) * p.K;
-    // One block is in flight ahead of the one being multiplied (deeper
-    // look-ahead measured slower: 45-48 us against 43 for the 4096 x 11008
-    // forward at batch 8).  Loads use clamped in-range addresses; values
+    // One block is in flight ahead of the one being multiplied in the plain
+    // forward (deeper look-ahead measured slower: 45-48 us against 43 for the
+    // 4096 x 11008 forward at batch 8); two with MBT > 0, whose per-block
+    // update lengthens the chain from load to use (measured 1-2 us faster
+    // per 4096 x 11008 pass).  Loads use clamped in-range addresses; values
     // past the slice or past N are zeroed where they are multiplied.
     const float4v zero = {0.f, 0.f, 0.f, 0.f};
     constexpr int kAhead = UPD ? 2 : 1;

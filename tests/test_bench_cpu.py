@@ -89,6 +89,23 @@ def test_source_digest_ignores_non_source_files(tmp_path, monkeypatch):
     assert bench.source_digest() != d0
 
 
+def test_source_digest_ignores_comments_only(tmp_path, monkeypatch):
+    """Comment and blank-line edits keep the kernel-source digest (the code
+    is the same); any code edit, a constant or an added file, changes it."""
+    csrc = tmp_path / "mlp_gemm_softmax_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (csrc / "k.hip").write_text("int f() { return 1; }  // one\n")
+    base = bench.source_digest()
+    (csrc / "k.hip").write_text("/* a block\n comment */\nint f() { return 1; }  // two\n\n")
+    assert bench.source_digest() == base
+    (csrc / "k.hip").write_text("int f() { return 2; }  // one\n")
+    assert bench.source_digest() != base
+    (csrc / "k.hip").write_text("int f() { return 1; }  // one\n")
+    (csrc / "g.hpp").write_text("#pragma once\n")
+    assert bench.source_digest() != base
+
+
 def test_recorded_traffic_needs_the_same_sources_and_kernel(tmp_path, monkeypatch):
     csrc = tmp_path / "mlp_gemm_softmax_amd" / "csrc"
     csrc.mkdir(parents=True)
