@@ -1209,3 +1209,36 @@ def test_train_steps_graph_replay_matches_eager(torch_dev):
             assert torch.equal(a, b), f"replay {rep}: W{l} differs"
     eager.close()
     graphed.close()
+
+
+@pytest.mark.parametrize("dims,B", [((1024, 1100, 260), 8), ((4096, 11008, 4096), 8)])
+def test_train_steps_after_tuning_match_single_steps(torch_dev, dims, B):
+    """After mlp_tune (which may change the first forward's K split, and so
+    the merged first-layer launch's), a run of steps from given weights is
+    bitwise the same session's single steps from the same weights."""
+    from mlp_gemm_softmax_amd import binding
+    torch, dev = torch_dev
+    _announce(f"train_steps after tune dims={dims} B={B}")
+    Ws = synth.make_weights(dims, "glorot", seed=71)
+    steps, lr = 3, 0.05
+    bs = [synth.make_batch(B, dims[0], dims[-1], "normal", seed=72, step=s)[:2] for s in range(steps)]
+    xd, td = P.to_dev([np.stack([b[0] for b in bs]), np.stack([b[1] for b in bs])], dev)
+    net = make_net(dims, B, "f32", Ws, dev)
+    net.tune(xd[0], td[0], 2)
+    out = []
+    for mode in ("run", "single"):
+        net.set_params(P.to_dev(Ws, dev))
+        losses = torch.full((steps,), float("nan"), dtype=torch.float32, device=dev)
+        if mode == "run":
+            net.train_steps(xd, td, lr, losses)
+        else:
+            for s in range(steps):
+                net.train_step_async(xd[s], td[s], lr, losses[s:s + 1])
+        torch.cuda.synchronize()
+        acts = [net.read_state(binding.STATE_ACT, l).cpu().numpy() for l in range(1, len(dims) - 1)]
+        out.append((losses.cpu().numpy(), [w.cpu().numpy() for w in net.read_params()], acts))
+    net.close()
+    (la, wa, aa), (lb, wb, ab) = out
+    assert np.all(np.isfinite(la)) and np.array_equal(la.view(np.uint32), lb.view(np.uint32))
+    for u, v in zip(wa + aa, wb + ab):
+        assert np.array_equal(u.view(np.uint32), v.view(np.uint32))
