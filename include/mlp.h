@@ -69,7 +69,8 @@ typedef enum mlp_status {
     MLP_ERR_SHAPE = 2,      /* dims or batch outside the supported range */
     MLP_ERR_WORKSPACE = 3,  /* workspace null, too small or misaligned */
     MLP_ERR_HIP = 4,        /* a HIP runtime call failed */
-    MLP_ERR_STATE = 5       /* context poisoned by an earlier HIP failure */
+    MLP_ERR_STATE = 5,      /* context poisoned by an earlier HIP failure */
+    MLP_ERR_GUARD = 6       /* a guard band of the workspace was overwritten (MLP_DEBUG_GUARDS) */
 } mlp_status;
 
 typedef enum mlp_precision {
@@ -117,12 +118,15 @@ int32_t mlp_abi_version(void);
  * (README "Environment variables": buffers are planned at build with
  * lifetime aliasing, MEGANEURA_NO_ALIAS / MEGANEURA_DUMP_PLAN) made static:
  * weights, activations, masks, a ping-pong pair of gradient buffers, split-K
- * partials and counters, laid out once for this shape. */
+ * partials and counters, laid out once for this shape.  Each buffer starts
+ * on a 256-byte boundary and is followed by a guard band of at least 256
+ * bytes (see mlp_set_debug). */
 size_t mlp_workspace_bytes(const mlp_config* cfg);
 
 /* Create a context that lives in `workspace` (device memory of at least
  * mlp_workspace_bytes(cfg) bytes, 256-byte aligned, owned by the caller).
- * Enqueues the zeroing of the library's counters on cfg->stream.  The
+ * Enqueues the zeroing of the library's counters and the filling of the
+ * guard bands (hipMemsetAsync) on cfg->stream.  The
  * weights are undefined until mlp_set_params has been called for every
  * layer.  The analogue of the README's build_session: kernels are compiled
  * ahead of time, so this only plans buffers and launch shapes. */
@@ -359,6 +363,39 @@ int32_t mlp_profile_slots(const mlp_ctx* ctx);
 mlp_status mlp_profile_read(mlp_ctx* ctx, int32_t idx, char* name, size_t name_len,
                             double* total_ms, int64_t* launches,
                             double* flops, double* bytes);
+
+/* Debug modes (README "Environment variables": MEGANEURA_SERIAL_DISPATCH
+ * runs one dispatch at a time to bisect a failure, MEGANEURA_PIN_BUFS pins
+ * buffers to bisect aliasing corruption; README "Debugging": failures come
+ * back as structured errors that name what went wrong).
+ *   MLP_DEBUG_SYNC   -- after every kernel launch the stream is synchronised,
+ *                       so a HIP error that shows only at execution is
+ *                       reported (MLP_ERR_HIP) with the name of that launch
+ *                       (the profile slot name) in mlp_last_error.  Launch
+ *                       errors name their launch in every mode.
+ *   MLP_DEBUG_GUARDS -- after every call that runs kernels (mlp_forward,
+ *                       mlp_forward_probs, mlp_train_step[_async],
+ *                       mlp_train_steps, mlp_grads, mlp_tune) the stream is
+ *                       synchronised and every guard band of the workspace
+ *                       is compared with the pattern mlp_create wrote there
+ *                       (bytes 0xA5).  A changed band means a write past the
+ *                       end of the buffer before it: the call returns
+ *                       MLP_ERR_GUARD, mlp_last_error names the buffer and
+ *                       the first changed byte, the bands are rewritten and
+ *                       the context is poisoned as after a HIP failure (the
+ *                       weights may be damaged; mlp_set_params or
+ *                       mlp_load_checkpoint for every layer clears it).
+ * Both make the calls above wait for the device, and neither applies while
+ * the stream is being captured into a graph.  The checks are host work
+ * outside the kernels, so a step's results are the same in every mode. */
+typedef enum mlp_debug_flags {
+    MLP_DEBUG_SYNC = 1,
+    MLP_DEBUG_GUARDS = 2
+} mlp_debug_flags;
+
+/* Set the debug modes (an OR of mlp_debug_flags; 0 = off, the default).
+ * Errors: MLP_ERR_ARG for a NULL context or unknown bits. */
+mlp_status mlp_set_debug(mlp_ctx* ctx, int32_t flags);
 
 /* Name of a status code ("MLP_OK", ...; "MLP_ERR_UNKNOWN" otherwise), a
  * static string.  With mlp_last_error, the structured errors of README

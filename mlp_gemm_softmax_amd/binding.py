@@ -15,7 +15,8 @@ from typing import List, Optional, Sequence
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmlp.so")
 
-MLP_OK, MLP_ERR_ARG, MLP_ERR_SHAPE, MLP_ERR_WORKSPACE, MLP_ERR_HIP, MLP_ERR_STATE = range(6)
+MLP_OK, MLP_ERR_ARG, MLP_ERR_SHAPE, MLP_ERR_WORKSPACE, MLP_ERR_HIP, MLP_ERR_STATE, MLP_ERR_GUARD = range(7)
+DEBUG_SYNC, DEBUG_GUARDS = 1, 2
 MLP_F32, MLP_BF16 = 0, 1
 STATE_ACT, STATE_MASK, STATE_DLOGITS, STATE_LOGITS = range(4)
 OPT_SGD, OPT_ADAM, OPT_LAPROP = range(3)
@@ -55,6 +56,7 @@ SIGNATURES = {
     "mlp_set_optimizer": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_float, _c.c_float, _c.c_float,
                                      _c.c_void_p, _c.c_size_t]),
     "mlp_profile_enable": (_c.c_int, [_c.c_void_p, _c.c_int32]),
+    "mlp_set_debug": (_c.c_int, [_c.c_void_p, _c.c_int32]),
     "mlp_profile_reset": (_c.c_int, [_c.c_void_p]),
     "mlp_profile_slots": (_c.c_int32, [_c.c_void_p]),
     "mlp_profile_read": (_c.c_int, [_c.c_void_p, _c.c_int32, _c.c_char_p, _c.c_size_t,
@@ -350,6 +352,13 @@ class Mlp:
         t = torch.empty(shape, dtype=dtype, device=self.device)
         self._check(lib().mlp_read_state(self._h, which, layer, ctypes.c_void_p(t.data_ptr())))
         return t
+
+    # -- debug modes ---------------------------------------------------------
+    def set_debug(self, flags: int):
+        """OR of DEBUG_SYNC (wait after every launch, name the failing one)
+        and DEBUG_GUARDS (check the workspace's guard bands after every call
+        that runs kernels); 0 turns both off."""
+        self._check(lib().mlp_set_debug(self._h, int(flags)))
 
     # -- per-launch timing -----------------------------------------------------
     def profile(self, enable: bool = True):

@@ -63,6 +63,8 @@ constexpr int kMaxLayers = 16;
 constexpr int kMaxDim = 1 << 20;
 constexpr int kSkinnyMaxBatch = 16;
 constexpr size_t kAlign = 256;
+constexpr size_t kGuardBytes = 256;       // least guard band after a workspace buffer
+constexpr unsigned char kGuardByte = 0xA5;
 
 thread_local std::string g_create_error;
 
@@ -130,6 +132,18 @@ struct mlp_ctx {
     unsigned params_set = 0;   // bit l: W_l written since creation / poisoning
     bool poisoned = false;
     std::string err;
+    std::string failed_launch;   // slot of the launch whose HIP call failed, if any
+
+    // Guard bands: a run of kGuardByte after every sub-buffer of the
+    // workspace (from the buffer's last byte to the next buffer), filled at
+    // creation and compared on the host when MLP_DEBUG_GUARDS is set.
+    struct Guard {
+        std::string after;   // buffer the band follows
+        size_t off, len;     // byte range in the workspace
+    };
+    std::vector<Guard> guards;
+    char* base = nullptr;
+    unsigned debug = 0;        // MLP_DEBUG_* flags
 
     // update rule of a training step: SGD (no state), or Adam / LaProp with
     // moments in caller memory given to mlp_set_optimizer, applied by the dW
@@ -404,6 +418,11 @@ void build_slots(mlp_ctx* c) {
 
 // ---------------------------------------------------------------- launches --
 
+bool capturing(hipStream_t s) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(s, &st) == hipSuccess && st != hipStreamCaptureStatusNone;
+}
+
 struct Runner {
     mlp_ctx* c;
     int kind = kStep;
@@ -434,6 +453,16 @@ struct Runner {
         if (b && e) {
             hipEventRecord(e, c->stream);
             c->pending.push_back({kind, slot_id, b, e});
+        }
+        // Serial mode: wait for each launch so that a failure that shows only
+        // at execution is charged to the launch that caused it.
+        if (err == hipSuccess && (c->debug & MLP_DEBUG_SYNC) && !capturing(c->stream))
+            err = hipStreamSynchronize(c->stream);
+        if (err != hipSuccess) {
+            if (slot_id >= 0 && slot_id < (int)c->slots[kind].size())
+                c->failed_launch = c->slots[kind][slot_id].name;
+            else
+                c->failed_launch = "launch " + std::to_string(slot_id);
         }
     }
 };
@@ -784,7 +813,52 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
 mlp_status hip_fail(mlp_ctx* c, hipError_t e, const char* what) {
     c->poisoned = true;
     c->params_set = 0;
-    return set_err(c, MLP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    std::string at;
+    if (!c->failed_launch.empty()) at = " (launch " + c->failed_launch + ")";
+    c->failed_launch.clear();
+    return set_err(c, MLP_ERR_HIP, "%s%s: %s", what, at.c_str(), hipGetErrorString(e));
+}
+
+// Writes the guard pattern into every band (creation, and after a band was
+// found overwritten).
+hipError_t fill_guards(mlp_ctx* c) {
+    for (const mlp_ctx::Guard& g : c->guards) {
+        const hipError_t e = hipMemsetAsync(c->base + g.off, kGuardByte, g.len, c->stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// With MLP_DEBUG_GUARDS: waits for the stream and compares every guard band
+// with its pattern.  A band that changed means a kernel wrote past the end
+// of the buffer before it; the call fails with MLP_ERR_GUARD naming that
+// buffer, the context is poisoned (the weights may be damaged) and the
+// bands are rewritten.  Skipped while the stream is being captured.
+mlp_status debug_check(mlp_ctx* c, const char* what) {
+    if (!(c->debug & MLP_DEBUG_GUARDS) || capturing(c->stream)) return MLP_OK;
+    hipError_t e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return hip_fail(c, e, what);
+    size_t most = 0;
+    for (const mlp_ctx::Guard& g : c->guards) most = std::max(most, g.len);
+    std::vector<unsigned char> h(most);
+    for (const mlp_ctx::Guard& g : c->guards) {
+        e = hipMemcpy(h.data(), c->base + g.off, g.len, hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return hip_fail(c, e, what);
+        for (size_t i = 0; i < g.len; ++i) {
+            if (h[i] == kGuardByte) continue;
+            c->poisoned = true;
+            c->params_set = 0;
+            const unsigned v = h[i];
+            e = fill_guards(c);
+            if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+            if (e != hipSuccess) return hip_fail(c, e, what);
+            return set_err(c, MLP_ERR_GUARD,
+                           "%s: guard band after %s overwritten at byte %zu past the buffer's end "
+                           "(0x%02x, workspace offset %zu)",
+                           what, g.after.c_str(), i, v, g.off + i);
+        }
+    }
+    return MLP_OK;
 }
 
 mlp_status check_ready(mlp_ctx* c) {
@@ -821,11 +895,17 @@ mlp_status collect_profile(mlp_ctx* c) {
 
 // ---------------------------------------------------------------- layout --
 
+// Sequential carve of the workspace: every buffer starts on a kAlign
+// boundary and is followed by a guard band that runs from its last byte up
+// to the next boundary plus kGuardBytes.
 struct Layout_ {
     size_t off = 0;
-    size_t take(size_t bytes) {
+    std::vector<mlp_ctx::Guard> guards;
+    size_t take(size_t bytes, std::string name) {
         const size_t o = off;
-        off = align_up(off + std::max<size_t>(bytes, 1), kAlign);
+        const size_t end = align_up(o + bytes, kAlign) + kGuardBytes;
+        guards.push_back({std::move(name), o + bytes, end - (o + bytes)});
+        off = end;
         return o;
     }
 };
@@ -938,22 +1018,27 @@ size_t plan_and_carve(mlp_ctx* c, char* base) {
 
     Layout_ lay;
     size_t oW[kMaxLayers], oWb[kMaxLayers], oA[kMaxLayers], oM[kMaxLayers];
-    for (int l = 0; l < L; ++l) oW[l] = c->external_w ? 0 : lay.take((size_t)c->dims[l] * c->dims[l + 1] * 4);
-    for (int l = 0; l < L; ++l) oWb[l] = c->bf16 ? lay.take((size_t)c->dims[l] * c->dims[l + 1] * 2) : 0;
-    for (int l = 1; l < L; ++l) oA[l] = lay.take((size_t)B * c->dims[l] * e);
-    for (int l = 1; l < L; ++l) oM[l] = lay.take((size_t)B * c->dims[l]);
-    const size_t oXb = c->bf16 ? lay.take((size_t)B * c->dims[0] * 2) : 0;
-    const size_t oLog = lay.take((size_t)B * C * 4);
-    const size_t oDl = lay.take((size_t)B * C * 4);
-    const size_t oDlb = c->bf16 ? lay.take((size_t)B * C * 2) : 0;
-    const size_t oDz0 = lay.take((size_t)B * max_hidden * e);
-    const size_t oDz1 = lay.take((size_t)B * max_hidden * e);
+    const std::string sl[kMaxLayers + 1] = {"0", "1", "2", "3", "4", "5", "6", "7", "8",
+                                            "9", "10", "11", "12", "13", "14", "15", "16"};
+    for (int l = 0; l < L; ++l)
+        oW[l] = c->external_w ? 0 : lay.take((size_t)c->dims[l] * c->dims[l + 1] * 4, "W" + sl[l]);
+    for (int l = 0; l < L; ++l)
+        oWb[l] = c->bf16 ? lay.take((size_t)c->dims[l] * c->dims[l + 1] * 2, "W" + sl[l] + " (bf16)") : 0;
+    for (int l = 1; l < L; ++l) oA[l] = lay.take((size_t)B * c->dims[l] * e, "a" + sl[l]);
+    for (int l = 1; l < L; ++l) oM[l] = lay.take((size_t)B * c->dims[l], "mask" + sl[l]);
+    const size_t oXb = c->bf16 ? lay.take((size_t)B * c->dims[0] * 2, "x (bf16)") : 0;
+    const size_t oLog = lay.take((size_t)B * C * 4, "logits");
+    const size_t oDl = lay.take((size_t)B * C * 4, "dlogits");
+    const size_t oDlb = c->bf16 ? lay.take((size_t)B * C * 2, "dlogits (bf16)") : 0;
+    const size_t oDz0 = lay.take((size_t)B * max_hidden * e, "dz0");
+    const size_t oDz1 = lay.take((size_t)B * max_hidden * e, "dz1");
     c->partial_cap = max_partial;
     c->ticket_cap = max_tickets;
-    const size_t oPart = lay.take(max_partial * 4);
-    const size_t oTick = lay.take((max_tickets + 1) * sizeof(unsigned));
-    const size_t oRow = lay.take((size_t)B * 4);
-    const size_t oLoss = lay.take(16);
+    const size_t oPart = lay.take(max_partial * 4, "split-K partials");
+    // counters, the cross-entropy's included, zeroed as whole float4s
+    const size_t oTick = lay.take(align_up((max_tickets + 1) * sizeof(unsigned), 16), "counters");
+    const size_t oRow = lay.take((size_t)B * 4, "row losses");
+    const size_t oLoss = lay.take(16, "loss");
     for (auto& v : c->slots) v.clear();
     if (base) {
         for (int l = 0; l < L; ++l) {
@@ -975,13 +1060,13 @@ size_t plan_and_carve(mlp_ctx* c, char* base) {
         c->xent_ticket = c->tickets + max_tickets;
         c->rowloss = (float*)(base + oRow);
         c->loss_slot = (float*)(base + oLoss);
+        c->base = base;
+        c->guards = std::move(lay.guards);
     }
     return lay.off;
 }
 
-size_t tickets_bytes(mlp_ctx* c) {
-    return (size_t)((char*)c->rowloss - (char*)c->tickets);
-}
+size_t tickets_bytes(const mlp_ctx* c) { return align_up((c->ticket_cap + 1) * sizeof(unsigned), 16); }
 
 }  // namespace
 
@@ -999,6 +1084,7 @@ const char* mlp_status_string(mlp_status s) {
     case MLP_ERR_WORKSPACE: return "MLP_ERR_WORKSPACE";
     case MLP_ERR_HIP: return "MLP_ERR_HIP";
     case MLP_ERR_STATE: return "MLP_ERR_STATE";
+    case MLP_ERR_GUARD: return "MLP_ERR_GUARD";
     }
     return "MLP_ERR_UNKNOWN";
 }
@@ -1049,13 +1135,23 @@ mlp_status mlp_create(const mlp_config* cfg, void* workspace, size_t bytes, mlp_
             return MLP_ERR_HIP;
         }
     }
-    const hipError_t e = hipMemsetAsync(c->tickets, 0, tickets_bytes(c), c->stream);
+    hipError_t e = hipMemsetAsync(c->tickets, 0, tickets_bytes(c), c->stream);
+    if (e == hipSuccess) e = fill_guards(c);
     if (e != hipSuccess) {
-        set_err(nullptr, MLP_ERR_HIP, "zeroing counters: %s", hipGetErrorString(e));
+        set_err(nullptr, MLP_ERR_HIP, "zeroing counters and filling guard bands: %s", hipGetErrorString(e));
         delete c;
         return MLP_ERR_HIP;
     }
     *out = c;
+    return MLP_OK;
+}
+
+mlp_status mlp_set_debug(mlp_ctx* c, int32_t flags) {
+    if (!c) return MLP_ERR_ARG;
+    c->err.clear();
+    if (flags & ~(MLP_DEBUG_SYNC | MLP_DEBUG_GUARDS))
+        return set_err(c, MLP_ERR_ARG, "unknown debug flags 0x%x", (unsigned)flags);
+    c->debug = (unsigned)flags;
     return MLP_OK;
 }
 
@@ -1115,6 +1211,8 @@ mlp_status mlp_forward(mlp_ctx* c, const float* x, float* logits, const float* l
         e = hipMemcpyAsync(logits, c->logits, (size_t)c->B * c->dims[c->L] * 4, hipMemcpyDeviceToDevice,
                            c->stream);
     if (e != hipSuccess) return hip_fail(c, e, "mlp_forward");
+    st = debug_check(c, "mlp_forward");
+    if (st != MLP_OK) return st;
     if (labels && loss) return read_loss(c, loss);
     return MLP_OK;
 }
@@ -1126,7 +1224,7 @@ mlp_status mlp_forward_probs(mlp_ctx* c, const float* x, float* probs) {
     if (!probs || !aligned16(probs)) return set_err(c, MLP_ERR_ARG, "probs must be a 16-byte aligned device pointer");
     const hipError_t e = enqueue(c, Mode::Forward, x, nullptr, 0.f, nullptr, nullptr, probs);
     if (e != hipSuccess) return hip_fail(c, e, "mlp_forward_probs");
-    return MLP_OK;
+    return debug_check(c, "mlp_forward_probs");
 }
 
 mlp_status mlp_train_step_async(mlp_ctx* c, const float* x, const float* labels, float lr, float* loss_dev) {
@@ -1150,7 +1248,7 @@ mlp_status mlp_train_step_async(mlp_ctx* c, const float* x, const float* labels,
     }
     const hipError_t e = enqueue(c, Mode::Train, x, labels, lr, nullptr, loss_dev);
     if (e != hipSuccess) return hip_fail(c, e, "mlp_train_step");
-    return MLP_OK;
+    return debug_check(c, "mlp_train_step");
 }
 
 mlp_status mlp_train_steps(mlp_ctx* c, int32_t n, const float* x, const float* labels, float lr,
@@ -1183,7 +1281,7 @@ mlp_status mlp_train_steps(mlp_ctx* c, int32_t n, const float* x, const float* l
                                      loss_dev ? loss_dev + s : nullptr, nullptr, fuse && s > 0, xn);
         if (e != hipSuccess) return hip_fail(c, e, "mlp_train_steps");
     }
-    return MLP_OK;
+    return debug_check(c, "mlp_train_steps");
 }
 
 }  // extern "C"
@@ -1330,6 +1428,8 @@ mlp_status mlp_grads(mlp_ctx* c, const float* x, const float* labels, float* con
         e = hipMemcpyAsync(dlogits, c->dlogits, (size_t)c->B * c->dims[c->L] * 4, hipMemcpyDeviceToDevice,
                            c->stream);
     if (e != hipSuccess) return hip_fail(c, e, "mlp_grads");
+    st = debug_check(c, "mlp_grads");
+    if (st != MLP_OK) return st;
     if (loss) return read_loss(c, loss);
     return MLP_OK;
 }
@@ -1837,7 +1937,7 @@ mlp_status mlp_tune(mlp_ctx* c, const float* x, const float* labels, int32_t rep
     c->profiling = prof;
     if (e != hipSuccess) return hip_fail(c, e, "mlp_tune");
     build_slots(c);   // plan changes can change which launches are fused
-    return MLP_OK;
+    return debug_check(c, "mlp_tune");
 }
 
 mlp_status mlp_read_state(mlp_ctx* c, int32_t which, int32_t layer, void* dst) {

@@ -39,9 +39,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = _lib()
-    names = [lib.mlp_status_string(i).decode() for i in range(6)]
+    names = [lib.mlp_status_string(i).decode() for i in range(8)]
     assert names == ["MLP_OK", "MLP_ERR_ARG", "MLP_ERR_SHAPE", "MLP_ERR_WORKSPACE",
-                     "MLP_ERR_HIP", "MLP_ERR_STATE"]
+                     "MLP_ERR_HIP", "MLP_ERR_STATE", "MLP_ERR_GUARD", "MLP_ERR_UNKNOWN"]
 
 
 def _cfg(dims, batch, precision=binding.MLP_F32):
@@ -143,6 +143,7 @@ def test_null_context_calls():
     assert lib.mlp_grads(None, None, None, None, None, None) == binding.MLP_ERR_ARG
     assert lib.mlp_read_state(None, 0, 1, None) == binding.MLP_ERR_ARG
     assert lib.mlp_profile_enable(None, 1) == binding.MLP_ERR_ARG
+    assert lib.mlp_set_debug(None, binding.DEBUG_SYNC) == binding.MLP_ERR_ARG
     assert lib.mlp_profile_slots(None) == 0
     lib.mlp_destroy(None)
 
