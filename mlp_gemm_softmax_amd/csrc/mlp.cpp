@@ -435,8 +435,10 @@ struct Runner {
             c->event_pool.pop_back();
             return e;
         }
+        // device-scope release: a default event's system-scope release
+        // writes the L2 back around every launch, which would be timed too
         hipEvent_t e = nullptr;
-        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        if (hipEventCreateWithFlags(&e, hipEventReleaseToDevice) != hipSuccess) return nullptr;
         return e;
     }
 
