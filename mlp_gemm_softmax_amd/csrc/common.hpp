@@ -96,6 +96,24 @@ __device__ __forceinline__ uint8_t load_coherent(const uint8_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Mean of n <= 64 row losses, written by lane 0 of the calling wavefront:
+// lane b takes row b, then the wavefront butterfly, then the other three
+// wavefronts' (zero) sums.  These are the additions, in their order, of the
+// softmax-CE kernels' own closing mean over 256 threads for n <= 64, so a
+// mean taken here has the same bits.
+__device__ __forceinline__ void mean_rows_wave(const float* rowloss, int n, float inv_n, float* out) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float s = 0.f;
+    if (lane < n) s += load_coherent(rowloss + lane);
+    s = wave_sum(s);
+    if (lane == 0) {
+        float tot = 0.f;
+        tot += s;
+        for (int w = 1; w < 4; ++w) tot += 0.f;
+        *out = tot * inv_n;
+    }
+}
+
 // Wait until this thread's stores are acknowledged (and keep the compiler
 // from moving memory operations across the wait).
 __device__ __forceinline__ void wait_stores() {

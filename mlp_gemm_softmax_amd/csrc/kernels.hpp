@@ -108,6 +108,12 @@ struct SkinnyParams {
     float* v;
     OptScalars opt;    // Adapt: the step's scalars
     const float* grad; // NN with fused update: G [MB][N] of the previous step (act: its input a)
+    // NT with fused update: with loss set, wavefront 0 of workgroup 0 also
+    // writes the mean of the MB row losses, which the softmax-CE launch
+    // before it left undone (XentParams::defer_mean); MB <= 64
+    const float* rowloss = nullptr;
+    float* loss = nullptr;
+    float inv_b = 0.f;
 };
 struct SkinnyLaunch {
     Layout layout;
@@ -136,6 +142,7 @@ struct XentParams {
     unsigned* ticket;      // zeroed counter
     int B, C;
     float inv_b;
+    bool defer_mean = false;   // write the row losses only; the next launch takes their mean
 };
 hipError_t launch_xent(const XentParams& p, int* grid_out, hipStream_t s);
 // Split-K sum of the logits product's partials [splits][B][C] (split order),

@@ -655,6 +655,10 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
     if (mode == Mode::Forward && !labels) return r.err;
 
     // ---- loss
+    // In skinny sessions with a hidden layer the launch after the softmax-CE
+    // is the last layer's fused dX + dW pass; it takes the mean of the row
+    // losses, so the softmax-CE launch ends without its ticketed mean.
+    const bool defer_mean = c->skinny && !use_head && L >= 2 && B <= 64 && mode != Mode::Forward;
     if (use_head) {
         if (!fuse_head) r.run(slot++, [&] { return launch_head(head_params(c->head_rb), c->stream); });
     } else {
@@ -670,6 +674,7 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
             xp.B = B;
             xp.C = C;
             xp.inv_b = 1.0f / (float)B;
+            xp.defer_mean = defer_mean;
             if (xent_fused(c)) return launch_splitk_xent(xp, c->partials, c->fwd[L - 1].splits, c->logits, c->stream);
             return launch_xent(xp, nullptr, c->stream);
         });
@@ -745,6 +750,11 @@ hipError_t enqueue(mlp_ctx* c, Mode mode, const float* x, const float* labels, f
                 sp.kchunk = c->sdx[l].kchunk;
                 sp.partials = c->partials;
                 sp.tickets = c->tickets;
+                if (defer_mean && l == L - 1) {
+                    sp.rowloss = c->rowloss;
+                    sp.loss = loss_dev ? loss_dev : c->loss_slot;
+                    sp.inv_b = 1.0f / (float)B;
+                }
                 return launch_skinny(sl, sp, c->stream);
             });
             G = out;

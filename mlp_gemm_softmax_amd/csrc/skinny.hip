@@ -277,6 +277,7 @@ __global__ __launch_bounds__(NW * kWave) void skinny_ntu(SkinnyParams p) {
     const int k0 = rg * 16 * RG;
     const int i = lane & 15, g = lane >> 4;
     const bool bok = i < p.MB;
+    if (p.loss && blockIdx.x == 0 && wave == 0) mean_rows_wave(p.rowloss, p.MB, p.inv_b, p.loss);
     const int cbeg = cs * p.kchunk, cend = min(p.N, cbeg + p.kchunk);
     const int nq = ((cend - cbeg + 32 * NW - 1) / (32 * NW)) * 32;   // slice, multiple of 32
     const int nbeg = cbeg + wave * nq;

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void xent_lane(XentParams p) {
         }
         store_coherent(p.rowloss + row, st * lse - stz);
     }
-    if (last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
+    if (!p.defer_mean && last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
 }
 
 // One wavefront per row, whole row in registers (C <= 64 * VPT); rows are
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void xent_wave(XentParams p) {
         }
         if (lane == 0) store_coherent(p.rowloss + row, st * lse - stz);
     }
-    if (last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
+    if (!p.defer_mean && last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
 }
 
 // Split-K sum and softmax-CE in one pass, for an output layer whose logits
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void splitk_xent_kernel(XentParams p, con
         }
         if (lane == 0) store_coherent(p.rowloss + row, st * lse - stz);
     }
-    if (last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
+    if (!p.defer_mean && last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
 }
 
 // One workgroup per row, for few wide rows (B small, C large): the row is
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void xent_group(XentParams p) {
         }
     }
     if (tid == 0) store_coherent(p.rowloss + row, st * lse - stz);
-    if (last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
+    if (!p.defer_mean && last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
 }
 
 // Any C: running (max, sum) per lane in one sweep, merged across lanes, then
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void xent_stream(XentParams p) {
         }
         if (lane == 0) store_coherent(p.rowloss + row, st * lse - stz);
     }
-    if (last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
+    if (!p.defer_mean && last_arrival(p.ticket, gridDim.x, &s_last)) finish_mean(p);
 }
 
 // Class probabilities of each row (inference): the same normalisation as the

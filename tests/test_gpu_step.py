@@ -327,6 +327,44 @@ def test_fused_splitk_loss_matches_forward(torch_dev):
     net.close()
 
 
+@pytest.mark.parametrize("dims,B", [((256, 520, 64), 8), ((96, 160, 132, 40), 5), ((1024, 1100, 260), 16),
+                                    ((4096, 11008, 4096), 8)])
+def test_skinny_step_loss_equals_forward_loss(torch_dev, dims, B):
+    """In skinny sessions the softmax-CE launch of a step leaves the mean of
+    the row losses to the fused dX + dW launch after it, which must give the
+    bits of the forward's loss (there the softmax-CE launch takes the mean
+    itself): through mlp_grads, mlp_train_step, a device loss and a run of
+    steps."""
+    torch, dev = torch_dev
+    _announce(f"skinny deferred mean dims={dims} B={B}")
+    Ws = synth.make_weights(dims, "glorot", seed=B + 31)
+    x, t, _ = synth.make_batch(B, dims[0], dims[-1], "normal", seed=B + 32)
+    net = make_net(dims, B, "f32", Ws, dev)
+    xd, td = P.to_dev([x, t], dev)
+    names = []
+    net.profile(True)
+    _, floss = net.forward(xd, td)
+    gloss, _, _ = net.grads(xd, td)
+    names = [r["name"] for r in net.profile_read()]
+    net.profile(False)
+    assert "softmax_xent" in names and any(n.startswith("skinny_nt_") for n in names), names
+    assert np.float32(gloss) == np.float32(floss)
+    sloss = net.train_step(xd, td, 0.05)
+    assert np.float32(sloss) == np.float32(floss)
+    # the updated weights give a new forward loss; the next step's device loss matches it
+    _, floss2 = net.forward(xd, td)
+    ld = torch.full((2,), float("nan"), dtype=torch.float32, device=dev)
+    net.train_step_async(xd, td, 0.05, ld[0:1])
+    torch.cuda.synchronize()
+    assert np.float32(ld[0].item()) == np.float32(floss2)
+    if (B * dims[0]) % 4 == 0 and (B * dims[-1]) % 4 == 0:
+        _, floss3 = net.forward(xd, td)
+        net.train_steps(torch.stack([xd, xd]), torch.stack([td, td]), 0.05, ld)
+        torch.cuda.synchronize()
+        assert np.float32(ld[0].item()) == np.float32(floss3)
+    net.close()
+
+
 def test_dlogits_rows_sum_to_zero(torch_dev):
     """P2 on the GPU: row sums of dlogits vanish to float32 rounding.
 
