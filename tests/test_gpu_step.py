@@ -668,9 +668,11 @@ def test_adaptive_profile_slots_and_errors(torch_dev):
         snet.set_params(P.to_dev(Ws, dev))
         snet.set_optimizer("adam")
         torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=side):
-            with pytest.raises(binding.MlpError) as ei:
-                snet.train_step_async(xd, td, 0.01)
+        # the refused step leaves the capture empty, which torch reports
+        with pytest.warns(UserWarning, match="empty"):
+            with torch.cuda.graph(g, stream=side):
+                with pytest.raises(binding.MlpError) as ei:
+                    snet.train_step_async(xd, td, 0.01)
         assert ei.value.status == binding.MLP_ERR_ARG
     snet.close()
     net.close()
