@@ -192,3 +192,29 @@ def test_tuning_candidates_stay_inside_their_buffers(torch_dev, dims, B, precisi
     net.grads(xd, td)
     net.train_step(xd, td, 0.05)
     net.close()
+
+
+@pytest.mark.parametrize("dims,B,precision,rule", [((256, 520, 64), 8, "f32", "adam"),
+                                                   ((200, 300, 36), 64, "f32", "laprop"),
+                                                   ((2056, 4096, 1024), 2048, "bf16", "adam")])
+def test_debug_modes_with_adaptive_rules(torch_dev, dims, B, precision, rule):
+    """Adam / LaProp steps (the moments live in caller memory, outside the
+    workspace) keep the guard bands intact and give the bits of the same
+    steps without the debug modes."""
+    from mlp_gemm_softmax_amd import binding
+    torch, dev = torch_dev
+    _announce(f"debug {rule} dims={dims} B={B} {precision}")
+    Ws = synth.make_weights(dims, "glorot", seed=sum(dims) + 7)
+    x, t, _ = synth.make_batch(B, dims[0], dims[-1], "normal", seed=B + 13)
+    xd, td = P.to_dev([x, t], dev)
+    out = []
+    for flags in (0, binding.DEBUG_SYNC | binding.DEBUG_GUARDS):
+        net = _net(dims, B, precision, Ws, dev, flags)
+        net.set_optimizer(rule, 0.9, 0.999, 1e-8)
+        losses = [np.float32(net.train_step(xd, td, 1e-3)) for _ in range(3)]
+        out.append((losses, [w.cpu().numpy() for w in net.read_params()]))
+        net.close()
+    (la, wa), (lb, wb) = out
+    assert np.array_equal(np.array(la, np.float32).view(np.uint32), np.array(lb, np.float32).view(np.uint32))
+    for u, v in zip(wa, wb):
+        assert np.array_equal(_bits(u), _bits(v))
