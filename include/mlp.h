@@ -41,6 +41,11 @@
  *     inputs must be ready in that stream's order.  One context may be used
  *     by one host thread at a time; calls on one context are not
  *     re-entrant.
+ *   - Values are not checked.  A NaN in x, the labels or the weights
+ *     propagates: the ReLU keeps a NaN pre-activation (as the definition
+ *     a = z * [z > 0] does), so it reaches the logits and the loss, and the
+ *     call returns MLP_OK; weights updated by such a step are not meaningful
+ *     (README "Debugging" leaves reports of NaN outputs to a separate scan).
  *   - Every argument is checked before anything is enqueued (README
  *     "Contents": a restore is validated in full before it changes any
  *     state; the same rule applies to every call here): on an error return the

@@ -42,6 +42,11 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
     return __uint_as_float(((uint32_t)h) << 16);
 }
 
+// The ReLU value max(v, 0) with a NaN kept: the definition a = z * [z > 0]
+// gives NaN for a NaN pre-activation, so a NaN input reaches the logits and
+// the loss instead of vanishing here.  The mask [v > 0] is 0 for it.
+__device__ __forceinline__ float relu_value(float v) { return v <= 0.f ? 0.f : v; }
+
 // Butterfly (xor) reductions over the 64 lanes of a wavefront.  At every
 // stage lane i combines v_i with v_{i^m} and lane i^m combines the same two
 // values, so all lanes finish with one bitwise-identical result and the order

@@ -15,7 +15,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, int row, int col, 
         p.C[o] = v;
     } else if constexpr (EPI == Epi::ReluMask) {
         const bool pos = v > 0.f;
-        const float a = pos ? v : 0.f;
+        const float a = relu_value(v);
         if (p.Cb) p.Cb[o] = f32_to_bf16(a); else p.C[o] = a;
         p.mask[o] = pos ? 1 : 0;
     } else if constexpr (EPI == Epi::MaskMul) {

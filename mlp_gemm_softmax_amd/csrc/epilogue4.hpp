@@ -50,7 +50,7 @@ __device__ __forceinline__ void epilogue4(const GemmParams& p, int row, int col,
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const bool pos = v[c] > 0.f;
-            a[c] = pos ? v[c] : 0.f;
+            a[c] = relu_value(v[c]);
             m |= (pos ? 1u : 0u) << (8 * c);
         }
         // the next launch reads the activations, so they stay cached; the

@@ -258,7 +258,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_small16_kernel(GemmParams p, Tai
                 if constexpr (HEAD) {
                     const int64_t o = (int64_t)row * p.ldc + col;
                     const bool pos = v[e] > 0.f;
-                    store_coherent(p.C + o, pos ? v[e] : 0.f);
+                    store_coherent(p.C + o, relu_value(v[e]));
                     store_coherent(p.mask + o, (uint8_t)(pos ? 1 : 0));
                 } else {
                     epilogue<EPI>(p, row, col, v[e]);

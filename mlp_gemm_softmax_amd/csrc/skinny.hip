@@ -232,8 +232,8 @@ __global__ __launch_bounds__(NW * kWave) void skinny_nn(SkinnyParams p) {
             if constexpr (EPI == Epi::ReluMask) {
                 uchar4 mk;
                 mk.x = v.x > 0.f; mk.y = v.y > 0.f; mk.z = v.z > 0.f; mk.w = v.w > 0.f;
-                v.x = mk.x ? v.x : 0.f; v.y = mk.y ? v.y : 0.f;
-                v.z = mk.z ? v.z : 0.f; v.w = mk.w ? v.w : 0.f;
+                v.x = relu_value(v.x); v.y = relu_value(v.y);
+                v.z = relu_value(v.z); v.w = relu_value(v.w);
                 *reinterpret_cast<uchar4*>(p.mask + o) = mk;
             }
             *reinterpret_cast<float4*>(p.C + o) = v;

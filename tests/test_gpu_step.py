@@ -365,6 +365,33 @@ def test_skinny_step_loss_equals_forward_loss(torch_dev, dims, B):
     net.close()
 
 
+@pytest.mark.parametrize("dims,B,precision", [((96, 160, 40), 64, "f32"),      # tiled kernels
+                                              ((784, 128, 10), 32, "f32"),      # fused output layer
+                                              ((256, 520, 64), 8, "f32"),       # skinny kernels
+                                              ((200, 300, 36), 64, "bf16"),
+                                              ((1024, 2048, 1040), 2048, "f32"),  # 256x256 tiles, split logits
+                                              ((5, 3), 3, "f32")])             # no hidden layer
+def test_nan_input_reaches_the_loss(torch_dev, dims, B, precision):
+    """A NaN in x is not masked: the ReLU keeps it (a = z * [z > 0] is NaN for
+    a NaN z), so the row's logits and the loss are NaN and the calls return
+    MLP_OK; the other rows' logits stay finite."""
+    torch, dev = torch_dev
+    _announce(f"nan input dims={dims} B={B} {precision}")
+    Ws = synth.make_weights(dims, "glorot", seed=71)
+    x, t, _ = synth.make_batch(B, dims[0], dims[-1], "normal", seed=72)
+    x[0, 0] = np.nan
+    net = make_net(dims, B, precision, Ws, dev)
+    xd, td = P.to_dev([x, t], dev)
+    logits, floss = net.forward(xd, td)
+    lg = logits.cpu().numpy()
+    assert np.all(np.isnan(lg[0])) and np.all(np.isfinite(lg[1:]))
+    assert np.isnan(floss)
+    probs = net.forward_probs(xd).cpu().numpy()
+    assert np.all(np.isnan(probs[0])) and np.all(np.isfinite(probs[1:]))
+    assert np.isnan(net.train_step(xd, td, 0.05))
+    net.close()
+
+
 def test_dlogits_rows_sum_to_zero(torch_dev):
     """P2 on the GPU: row sums of dlogits vanish to float32 rounding.
 
