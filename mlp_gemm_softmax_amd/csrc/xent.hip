@@ -21,6 +21,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxGroups = 256;
+// mean_rows_wave (the mean taken by the next launch in skinny steps) repeats
+// finish_mean's additions for four wavefronts; both must change together.
+static_assert(kThreads / kWave == 4, "finish_mean and mean_rows_wave add four wavefront sums");
 
 __device__ void finish_mean(const XentParams& p) {
     // Last workgroup only: fixed-order sum of the row losses.
