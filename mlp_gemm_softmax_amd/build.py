@@ -89,6 +89,32 @@ def build_host_sanitized(verbose: bool = True, jobs: int | None = None) -> str:
     return _build(OUT_SAN, BUILD_DIR_SAN, SAN_FLAGS, verbose, jobs)
 
 
+C_CLIENT_SRC = os.path.join(ROOT, "tests", "abi_c_step.c")
+C_CLIENT = os.path.join(HERE, "c_client_step")
+
+
+def build_c_client(verbose: bool = True) -> str | None:
+    """Compile the C test client of the ABI (``tests/abi_c_step.c``: a training
+    step driven from C with hipMalloc'd memory) next to libmlp.so, which it
+    links through an ``$ORIGIN`` rpath; returns its path, or None without gcc."""
+    cc = shutil.which("gcc")
+    if cc is None:
+        if verbose:
+            print("gcc not found: C test client not built")
+        return None
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = [cc, "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-pedantic", "-D__HIP_PLATFORM_AMD__",
+           "-isystem", os.path.join(rocm, "include"), f"-I{os.path.join(ROOT, 'include')}", C_CLIENT_SRC,
+           f"-L{HERE}", "-lmlp", f"-L{os.path.join(rocm, 'lib')}", "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}", "-o", C_CLIENT]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"C client build failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    if verbose:
+        print(f"built {C_CLIENT}")
+    return C_CLIENT
+
+
 def sanitizer_runtime() -> str | None:
     """Path of the AddressSanitizer runtime of ROCm's clang (to preload into
     a process that loads libmlp_hostsan.so), or None."""
@@ -101,4 +127,5 @@ if __name__ == "__main__":
         build_host_sanitized()
     else:
         build()
+        build_c_client()
     sys.exit(0)
