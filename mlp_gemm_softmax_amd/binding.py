@@ -181,6 +181,13 @@ class Mlp:
         self._loss = ctypes.c_float(0.0)
 
     # -- plumbing -------------------------------------------------------------
+    def _handoff(self):
+        """Order the caller's current stream after the work just enqueued on
+        the session's stream, so tensors it filled can be used there."""
+        cur = self.torch.cuda.current_stream(self.device)
+        if cur != self.stream:
+            cur.wait_stream(self.stream)
+
     def _check(self, st: int):
         if st != MLP_OK:
             raise MlpError(st, lib().mlp_last_error(self._h).decode())
@@ -265,6 +272,7 @@ class Mlp:
                                  device=self.device)
             self._check(lib().mlp_read_params(self._h, l, ctypes.c_void_p(t.data_ptr())))
             out.append(t)
+        self._handoff()
         return out
 
     def forward(self, x, labels=None, want_loss: bool = True):
@@ -277,6 +285,7 @@ class Mlp:
         self._check(lib().mlp_forward(self._h, ctypes.c_void_p(x.data_ptr()),
                                       ctypes.c_void_p(logits.data_ptr()),
                                       ctypes.c_void_p(_ptr(labels)), loss_p))
+        self._handoff()
         return logits, (self._loss.value if loss_p is not None else None)
 
     def tune(self, x, labels, repeats: int = 3):
@@ -295,6 +304,7 @@ class Mlp:
         self._dev_f32(probs, (B, C))
         self._check(lib().mlp_forward_probs(self._h, ctypes.c_void_p(x.data_ptr()),
                                             ctypes.c_void_p(probs.data_ptr())))
+        self._handoff()
         return probs
 
     def forward_async(self, x, logits):
@@ -339,6 +349,7 @@ class Mlp:
         self._check(lib().mlp_grads(self._h, ctypes.c_void_p(x.data_ptr()),
                                     ctypes.c_void_p(labels.data_ptr()), arr,
                                     ctypes.c_void_p(dl.data_ptr()), ctypes.byref(self._loss)))
+        self._handoff()
         return self._loss.value, dws, dl
 
     def read_state(self, which: int, layer: int = 0):
@@ -351,6 +362,7 @@ class Mlp:
             dtype = torch.float32
         t = torch.empty(shape, dtype=dtype, device=self.device)
         self._check(lib().mlp_read_state(self._h, which, layer, ctypes.c_void_p(t.data_ptr())))
+        self._handoff()
         return t
 
     # -- debug modes ---------------------------------------------------------

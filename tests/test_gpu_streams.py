@@ -71,3 +71,42 @@ def test_concurrent_sessions_match_separate_runs(torch_dev, a, b):
     for ws_a, ws_t in zip(A[2:], T[2:]):
         for u, v in zip(ws_a, ws_t):
             assert np.array_equal(u.view(np.uint32), v.view(np.uint32))
+
+
+def test_sessions_on_host_threads(torch_dev):
+    """Two host threads, each creating and driving its own session on its own
+    stream (ctypes releases the interpreter lock during the library calls, so
+    creation, planning and launches overlap on the host): the results equal
+    those of the same sessions run one after the other."""
+    import threading
+    torch, dev = torch_dev
+    print("\n[case] sessions on two host threads", flush=True)
+    cases = [((200, 300, 36), 64, "f32", 5), ((256, 520, 64), 8, "f32", 6)]
+
+    def drive(case, res, idx):
+        dims, B, precision, seed = case
+        s = torch.cuda.Stream()
+        net, xd, td = _session(torch, dev, dims, B, precision, seed, s)
+        torch.cuda.default_stream(dev).synchronize()   # the batches were copied on the default stream
+        with torch.cuda.stream(s):
+            losses = torch.zeros(40, dtype=torch.float32, device=dev)
+            for k in range(40):
+                net.train_step_async(xd[k % 4], td[k % 4], 0.05, losses[k:k + 1])
+        s.synchronize()
+        res[idx] = (losses.cpu().numpy(), [w.cpu().numpy() for w in net.read_params()])
+        net.close()
+
+    seq = [None, None]
+    for i, c in enumerate(cases):
+        drive(c, seq, i)
+    par = [None, None]
+    threads = [threading.Thread(target=drive, args=(c, par, i)) for i, c in enumerate(cases)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=120)
+    assert all(r is not None for r in par)
+    for (la, wa), (lb, wb) in zip(seq, par):
+        assert np.array_equal(la.view(np.uint32), lb.view(np.uint32))
+        for u, v in zip(wa, wb):
+            assert np.array_equal(u.view(np.uint32), v.view(np.uint32))
