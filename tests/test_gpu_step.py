@@ -248,6 +248,47 @@ def test_edge_shapes(torch_dev, dims, B, precision):
     net.close()
 
 
+def _sweep_cases():
+    """Seeded draws of small shapes from the widths kernels treat specially
+    (1, odd, one less or more than a tile edge, the MNIST widths, a skinny
+    multiple of 4) and batches from 1 to 40: every kernel family meets ragged
+    edges at several of its branch points."""
+    rng = np.random.default_rng([2026, 12])
+    widths = [1, 4, 7, 8, 10, 16, 31, 33, 64, 100, 128, 260]
+    batches = [1, 2, 3, 7, 8, 12, 16, 17, 33, 40]
+    cases = []
+    for k in range(40):
+        L = int(rng.integers(1, 4))
+        dims = tuple(int(rng.choice(widths)) for _ in range(L + 1))
+        B = int(rng.choice(batches))
+        precision = "bf16" if k % 4 == 3 else "f32"
+        cases.append((dims, B, precision))
+    return cases
+
+
+def _sweep_cases_medium():
+    """Seeded medium shapes: tiled, split-K and large-tile plans with ragged
+    tiles, the fused output layer, and skinny batches with K splits."""
+    rng = np.random.default_rng([2026, 13])
+    widths = [12, 36, 96, 200, 300, 520, 784, 1000, 1040, 2056]
+    batches = [5, 8, 16, 64, 128, 300, 512, 1024]
+    cases = []
+    for k in range(24):
+        L = int(rng.integers(1, 4))
+        dims = tuple(int(rng.choice(widths)) for _ in range(L + 1))
+        B = int(rng.choice(batches))
+        precision = "bf16" if k % 3 == 2 else "f32"
+        cases.append((dims, B, precision))
+    return cases
+
+
+@pytest.mark.parametrize("dims,B,precision", _sweep_cases() + _sweep_cases_medium())
+def test_shape_sweep(torch_dev, dims, B, precision):
+    """Gradients and the update against the oracle at the contract's gates on
+    seeded small shapes (the edge-shape checks, drawn rather than listed)."""
+    test_edge_shapes(torch_dev, dims, B, precision)
+
+
 @pytest.mark.parametrize("dims,B,precision", [((784, 128, 10), 32, "f32"),
                                               ((1024, 4096, 4096, 1000), 4096, "f32"),
                                               ((1024, 4096, 4096, 1000), 4096, "bf16")])
