@@ -1196,7 +1196,21 @@ STEPS_CASES = [
 ]
 
 
-@pytest.mark.parametrize("dims,B,precision,opt,steps", STEPS_CASES)
+def _steps_sweep():
+    """Seeded skinny shapes for runs of steps (widths multiples of 4, at most 8
+    rows: the first-layer update fused with the next forward)."""
+    rng = np.random.default_rng([2026, 14])
+    widths = [4, 8, 12, 36, 64, 100, 260, 516, 1028, 2052]
+    cases = []
+    for _ in range(16):
+        L = int(rng.integers(1, 4))
+        dims = tuple(int(rng.choice(widths)) for _ in range(L + 1))
+        B = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8]))
+        cases.append((dims, B, "f32", "sgd", 3))
+    return cases
+
+
+@pytest.mark.parametrize("dims,B,precision,opt,steps", STEPS_CASES + _steps_sweep())
 def test_train_steps_match_single_steps(torch_dev, dims, B, precision, opt, steps):
     """mlp_train_steps over n batches equals n mlp_train_step_async calls on
     the same batches, bit for bit: weights, per-step losses, and the last
