@@ -88,7 +88,10 @@ def check_masks(ref, B, dims, precision, label="", limit_band=True, self_counts=
         assert out == 0, f"{label} layer {l}: {out} mask bits differ outside the rounding band"
         frac = ad / float(B * dims[l])
         if limit_band:
-            assert frac <= MAX_ADOPTED[precision], f"{label} layer {l}: {ad} band bits differ ({frac:.2e})"
+            # a fraction cap, with a floor of two bits: a layer of a few dozen
+            # units cannot adopt a fraction below one bit's share
+            assert ad <= max(MAX_ADOPTED[precision] * B * dims[l], 2), \
+                f"{label} layer {l}: {ad} band bits differ ({frac:.2e})"
 
 
 def check_mask_self_consistency(x, Ws, masks, acts, precision, label=""):

@@ -615,8 +615,21 @@ ADAPTIVE_CASES = [
 ]
 
 
+def _adaptive_sweep():
+    """Seeded shapes for the adaptive rules (both contracts, every plan family)."""
+    rng = np.random.default_rng([2026, 15])
+    widths = [4, 12, 31, 64, 100, 260, 520, 1040]
+    cases = []
+    for k in range(8):
+        L = int(rng.integers(1, 4))
+        dims = tuple(int(rng.choice(widths)) for _ in range(L + 1))
+        B = int(rng.choice([3, 8, 16, 40, 128, 512]))
+        cases.append((dims, B, "bf16" if k % 4 == 3 else "f32", False))
+    return cases
+
+
 @pytest.mark.parametrize("rule", ["adam", "laprop"])
-@pytest.mark.parametrize("dims,B,precision,exact", ADAPTIVE_CASES)
+@pytest.mark.parametrize("dims,B,precision,exact", ADAPTIVE_CASES + _adaptive_sweep())
 def test_adaptive_update_parity(torch_dev, rule, dims, B, precision, exact):
     """Three Adam / LaProp steps against the oracle's rule applied to the
     oracle's own gradients.  Before each step the GPU gradients (same
@@ -1075,7 +1088,21 @@ PROBS_CASES = [
 ]
 
 
-@pytest.mark.parametrize("dims,B,precision", PROBS_CASES)
+def _probs_sweep():
+    """Seeded shapes for class probabilities (epilogue-normalised and
+    row-softmax paths, narrow and wide class counts)."""
+    rng = np.random.default_rng([2026, 16])
+    widths = [1, 7, 10, 16, 33, 100, 300, 1000, 4100]
+    cases = []
+    for k in range(10):
+        L = int(rng.integers(1, 4))
+        dims = tuple(int(rng.choice(widths[:-1])) for _ in range(L)) + (int(rng.choice(widths)),)
+        B = int(rng.choice([1, 5, 8, 32, 100, 1024]))
+        cases.append((dims, B, "bf16" if k % 4 == 3 else "f32"))
+    return cases
+
+
+@pytest.mark.parametrize("dims,B,precision", PROBS_CASES + _probs_sweep())
 def test_forward_probs_parity(torch_dev, dims, B, precision):
     """Inference probabilities against the oracle's softmax of its forward
     logits.  With every logit within delta = tol * max|z_ref| of the oracle
