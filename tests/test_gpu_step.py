@@ -761,9 +761,23 @@ def test_adaptive_profile_slots_and_errors(torch_dev):
 
 # ------------------------------------------------------------- checkpoints --
 
+def _ckpt_sweep():
+    """Seeded shapes and rules (SGD included) for the checkpoint round trip."""
+    rng = np.random.default_rng([2026, 18])
+    widths = [4, 12, 33, 64, 100, 260, 1040]
+    rules = ["sgd", "adam", "laprop"]
+    cases = []
+    for k in range(9):
+        L = int(rng.integers(1, 4))
+        dims = tuple(int(rng.choice(widths)) for _ in range(L + 1))
+        B = int(rng.choice([2, 8, 16, 64, 256]))
+        cases.append((dims, B, "bf16" if k % 3 == 2 else "f32", rules[k % 3]))
+    return cases
+
+
 @pytest.mark.parametrize("dims,B,precision,rule", [((96, 160, 130, 40), 128, "f32", "adam"),
                                                    ((256, 520, 64), 8, "f32", "laprop"),
-                                                   ((120, 136, 24), 256, "bf16", "adam")])
+                                                   ((120, 136, 24), 256, "bf16", "adam")] + _ckpt_sweep())
 def test_checkpoint_resumes_training_bit_for_bit(torch_dev, dims, B, precision, rule):
     """Save after two steps (weights, moments, step count), restore into a
     fresh session and continue: the next steps equal those of the session

@@ -53,6 +53,20 @@ def test_static_step_matches_workspace_step(torch_dev):
         _run_pair(torch, dev, dims, B, seed=300 + i)
 
 
+def test_static_step_seeded_sequence(torch_dev):
+    """Twelve seeded configurations in a row (widths 4-1040, batches 1-512),
+    each re-planned in the same static buffer: every one matches the
+    workspace step bit for bit."""
+    torch, dev = torch_dev
+    rng = np.random.default_rng([2026, 17])
+    widths = [4, 10, 31, 64, 100, 260, 520, 1040]
+    for i in range(12):
+        L = int(rng.integers(1, 4))
+        dims = tuple(int(rng.choice(widths)) for _ in range(L + 1))
+        B = int(rng.choice([1, 3, 8, 16, 64, 512]))
+        _run_pair(torch, dev, dims, B, seed=500 + i)
+
+
 def test_static_step_after_a_larger_one_and_errors(torch_dev):
     """A larger configuration, then a smaller one (the second call re-plans
     in the buffer the first one filled); a configuration beyond the buffer
