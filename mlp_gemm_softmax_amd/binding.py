@@ -152,9 +152,31 @@ def _ptr(t) -> int:
     return 0 if t is None else int(t.data_ptr())
 
 
+def debug_flags_from_env(value: str | None = None) -> int:
+    """Debug modes named by the MLP_DEBUG environment variable (or `value`):
+    a comma-separated list of ``sync`` (a wait after every launch) and
+    ``guards`` (workspace guard bands checked after every call); empty or
+    unset means none.  The library reads no environment itself: as the
+    README's environment variables are resolved into a session's
+    configuration at creation, this binding resolves MLP_DEBUG when it
+    creates a session."""
+    if value is None:
+        value = os.environ.get("MLP_DEBUG", "")
+    names = {"sync": DEBUG_SYNC, "guards": DEBUG_GUARDS}
+    flags = 0
+    for part in value.replace(" ", "").split(","):
+        if not part:
+            continue
+        if part not in names:
+            raise ValueError(f"MLP_DEBUG: unknown mode {part!r} (known: sync, guards)")
+        flags |= names[part]
+    return flags
+
+
 class Mlp:
     """One static-shape MLP on one GPU: weights and scratch in a torch-owned
-    workspace, steps enqueued on the given (default: current) torch stream."""
+    workspace, steps enqueued on the given (default: current) torch stream.
+    The debug modes MLP_DEBUG names are set on every new session."""
 
     def __init__(self, dims: Sequence[int], batch: int, precision: str = "f32",
                  device: str = "cuda", stream=None):
@@ -179,6 +201,9 @@ class Mlp:
             raise MlpError(st, L.mlp_last_error(None).decode())
         self._h = handle
         self._loss = ctypes.c_float(0.0)
+        flags = debug_flags_from_env()
+        if flags:
+            self.set_debug(flags)
 
     # -- plumbing -------------------------------------------------------------
     def _handoff(self):

@@ -264,3 +264,15 @@ def test_checkpoint_info_rejects_damage(what, buf):
     with pytest.raises(binding.MlpError) as ei:
         binding.checkpoint_info(buf)
     assert ei.value.status == binding.MLP_ERR_ARG, what
+
+
+@pytest.mark.parametrize("value,flags", [("", 0), ("sync", binding.DEBUG_SYNC), ("guards", binding.DEBUG_GUARDS),
+                                         ("sync,guards", binding.DEBUG_SYNC | binding.DEBUG_GUARDS),
+                                         (" guards , sync ", binding.DEBUG_SYNC | binding.DEBUG_GUARDS)])
+def test_debug_flags_from_env(value, flags):
+    assert binding.debug_flags_from_env(value) == flags
+
+
+def test_debug_flags_from_env_rejects_unknown_modes():
+    with pytest.raises(ValueError):
+        binding.debug_flags_from_env("sync,verbose")

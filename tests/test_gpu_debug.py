@@ -218,3 +218,22 @@ def test_debug_modes_with_adaptive_rules(torch_dev, dims, B, precision, rule):
     assert np.array_equal(np.array(la, np.float32).view(np.uint32), np.array(lb, np.float32).view(np.uint32))
     for u, v in zip(wa, wb):
         assert np.array_equal(_bits(u), _bits(v))
+
+
+def test_debug_modes_from_the_environment(torch_dev, monkeypatch):
+    """MLP_DEBUG=guards turns the guard check on for every new session."""
+    from mlp_gemm_softmax_amd import binding
+    torch, dev = torch_dev
+    monkeypatch.setenv("MLP_DEBUG", "guards")
+    dims, B = (96, 160, 40), 64
+    Ws = synth.make_weights(dims, "glorot", seed=9)
+    x, t, _ = synth.make_batch(B, dims[0], dims[-1], "normal", seed=10)
+    xd, td = P.to_dev([x, t], dev)
+    net = binding.Mlp(dims, B, "f32", device=str(dev))
+    net.set_params(P.to_dev(Ws, dev))
+    net.train_step(xd, td, 0.05)
+    net.workspace[net.workspace.numel() - 1] = 0
+    with pytest.raises(binding.MlpError) as ei:
+        net.train_step(xd, td, 0.05)
+    assert ei.value.status == binding.MLP_ERR_GUARD
+    net.close()
